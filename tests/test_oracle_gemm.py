@@ -1,0 +1,145 @@
+"""Pins for the oracle's GEMM references.
+
+Brute force with exact rational sums on tiny shapes, and closed forms:
+identity weights reproduce the dequantized activations, one-hot activation
+rows select weight columns, constant operands give K * a * w.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import (
+    MXFP4,
+    MXFP8,
+    decode_bf16,
+    dequant_mx,
+    gemm_bf16_ref,
+    gemm_mx_ref,
+    gemm_nvfp4_ref,
+    normwise_error,
+    quantize_mx,
+    quantize_nvfp4,
+    unpack_fp4,
+)
+from oracle import exact
+from microscaling_quantized_diffusion_amd.inputs import bf16_bits_from_f32
+
+
+def _exact_dot_mx(a_codes, a_scales, w_codes, w_scales, scheme, m, n, K):
+    """sum_k dec(a)*2^(sa-127) * dec(w)*2^(sw-127), in Fractions from the code tables."""
+    table = dict(exact.e4m3_table() if not scheme.packed else exact.e2m1_table())
+    sign = 0x80 if not scheme.packed else 0x8
+
+    def val(code, scale):
+        mag = table[code & ~sign & (0x7F if not scheme.packed else 0x7)]
+        v = -mag if code & sign else mag
+        return v * Fraction(2) ** (int(scale) - 127)
+
+    ac = unpack_fp4(a_codes) if scheme.packed else a_codes
+    wc = unpack_fp4(w_codes) if scheme.packed else w_codes
+    s = Fraction(0)
+    for k in range(K):
+        s += val(int(ac[m, k]), a_scales[m, k // 32]) * val(int(wc[n, k]), w_scales[n, k // 32])
+    return s
+
+
+@pytest.mark.parametrize("scheme", [MXFP8, MXFP4], ids=["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (2, 3, 64), (3, 17, 96), (17, 2, 256)])
+def test_mx_gemm_brute_force(scheme, M, N, K):
+    rng = np.random.default_rng(M * 100 + N * 10 + K)
+    a = bf16_bits_from_f32((rng.standard_normal((M, K)) * np.exp(rng.normal(0, 1, (M, 1)))).astype(np.float32))
+    w = bf16_bits_from_f32((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    ac, asc = quantize_mx(a, scheme)
+    wc, wsc = quantize_mx(w, scheme)
+    ref = gemm_mx_ref(ac, asc, wc, wsc, scheme)
+    for m in range(M):
+        for n in range(N):
+            ex = _exact_dot_mx(ac, asc, wc, wsc, scheme, m, n, K)
+            assert abs(Fraction(ref[m, n]) - ex) <= abs(ex) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 300)
+
+
+def test_nvfp4_gemm_brute_force():
+    rng = np.random.default_rng(4)
+    M, N, K = 3, 5, 64
+    a = bf16_bits_from_f32(rng.standard_t(4, (M, K)).astype(np.float32))
+    w = bf16_bits_from_f32((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    ac, asc, ats = quantize_nvfp4(a)
+    wc, wsc, wts = quantize_nvfp4(w)
+    ref = gemm_nvfp4_ref(ac, asc, ats, wc, wsc, wts)
+    e2 = dict(exact.e2m1_table())
+    e4 = dict(exact.e4m3_table())
+    ua, uw = unpack_fp4(ac), unpack_fp4(wc)
+
+    def val(code, sc, ts):
+        mag = e2[int(code) & 7]
+        return (-mag if int(code) & 8 else mag) * e4[int(sc)] * Fraction(float(ts))
+
+    for m in range(M):
+        for n in range(N):
+            ex = sum(val(ua[m, k], asc[m, k // 16], ats) * val(uw[n, k], wsc[n, k // 16], wts) for k in range(K))
+            assert abs(Fraction(ref[m, n]) - ex) <= abs(ex) * Fraction(1, 10 ** 12)
+
+
+def test_bf16_gemm_brute_force_with_bias():
+    rng = np.random.default_rng(2)
+    M, N, K = 4, 3, 40
+    a = bf16_bits_from_f32(rng.standard_normal((M, K)).astype(np.float32))
+    w = bf16_bits_from_f32(rng.standard_normal((N, K)).astype(np.float32))
+    bias = bf16_bits_from_f32(rng.standard_normal(N).astype(np.float32))
+    ref = gemm_bf16_ref(a, w, bias)
+    for m in range(M):
+        for n in range(N):
+            ex = sum(exact.bf16_value(int(a[m, k])) * exact.bf16_value(int(w[n, k])) for k in range(K))
+            ex += exact.bf16_value(int(bias[n]))
+            assert abs(Fraction(ref[m, n]) - ex) <= abs(ex) * Fraction(1, 10 ** 12)
+
+
+@pytest.mark.parametrize("scheme", [MXFP8, MXFP4], ids=["mxfp8", "mxfp4"])
+def test_identity_weights_reproduce_dequantized_activations(scheme):
+    rng = np.random.default_rng(8)
+    K = 128
+    a = bf16_bits_from_f32(rng.standard_normal((9, K)).astype(np.float32))
+    eye = bf16_bits_from_f32(np.eye(K, dtype=np.float32))
+    ac, asc = quantize_mx(a, scheme)
+    wc, wsc = quantize_mx(eye, scheme)
+    ref = gemm_mx_ref(ac, asc, wc, wsc, scheme)
+    assert np.array_equal(ref, dequant_mx(ac, asc, scheme))
+
+
+def test_one_hot_rows_select_weight_columns():
+    rng = np.random.default_rng(12)
+    K, N = 64, 7
+    w = bf16_bits_from_f32(rng.standard_normal((N, K)).astype(np.float32))
+    wc, wsc = quantize_mx(w, MXFP8)
+    onehot = np.zeros((K, K), np.float32)
+    onehot[np.arange(K), np.arange(K)] = 2.0
+    ac, asc = quantize_mx(bf16_bits_from_f32(onehot), MXFP8)
+    ref = gemm_mx_ref(ac, asc, wc, wsc, MXFP8)
+    assert np.array_equal(ref, 2.0 * dequant_mx(wc, wsc, MXFP8).T)
+
+
+def test_constant_operands():
+    K = 96
+    a = bf16_bits_from_f32(np.full((2, K), 1.5, np.float32))
+    w = bf16_bits_from_f32(np.full((3, K), -0.375, np.float32))
+    for scheme in (MXFP8, MXFP4):
+        ac, asc = quantize_mx(a, scheme)
+        wc, wsc = quantize_mx(w, scheme)
+        assert np.all(gemm_mx_ref(ac, asc, wc, wsc, scheme) == K * 1.5 * -0.375)
+    # NVFP4: choose G = 2688 * 2^-k so that ts = 2^-k is exact and the block reproduces G
+    a = bf16_bits_from_f32(np.full((2, K), 2.625, np.float32))
+    w = bf16_bits_from_f32(np.full((3, K), -0.65625, np.float32))
+    ac, asc, ats = quantize_nvfp4(a)
+    wc, wsc, wts = quantize_nvfp4(w)
+    assert float(ats) == 2.0 ** -10 and float(wts) == 2.0 ** -12
+    assert np.all(gemm_nvfp4_ref(ac, asc, ats, wc, wsc, wts) == K * 2.625 * -0.65625)
+
+
+def test_normwise_error():
+    r = np.array([[1.0, -4.0], [0.0, 2.0]])
+    assert normwise_error(r, r) == 0.0
+    assert normwise_error(r + np.array([[0.0, 0.004], [0.0, 0.0]]), r) == pytest.approx(1e-3)
+    assert normwise_error(np.array([[np.nan, 0], [0, 0]]), r) == float("inf")
+    assert decode_bf16(np.array([0x3F80], np.uint16))[0] == 1.0

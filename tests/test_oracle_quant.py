@@ -1,0 +1,289 @@
+"""Pins for the oracle's MXFP8 / MXFP4 / NVFP4 quantizers.
+
+Pinned by: hand-worked golden blocks (tests/golden), the exact Fraction
+reference (an argmin over the code table, sharing no code with the vector
+quantizer), and invariants that follow from the definitions (scale
+bracketing, block max code range, round trip, NVFP4 G-block scale).
+"""
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import (
+    MXFP4,
+    MXFP8,
+    decode_bf16,
+    decode_e2m1,
+    decode_e4m3,
+    dequant_mx,
+    dequant_nvfp4,
+    nvfp4_tensor_scale,
+    quantize_mx,
+    quantize_nvfp4,
+    should_quantize,
+    unpack_fp4,
+)
+from oracle import exact
+from microscaling_quantized_diffusion_amd.inputs import bf16_bits_from_f32
+
+
+def _parse_blocks(path, block_len):
+    blocks, ts = [], None
+    cur = None
+    with open(path) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            parts = line.split()
+            if parts[0] == "tensor_scale":
+                ts = float(parts[1])
+            elif parts[0] == "block":
+                if len(parts) == 3:
+                    scheme, scale = parts[1], int(parts[2], 16)
+                else:
+                    scheme, scale = "nvfp4", int(parts[1], 16)
+                cur = {"scheme": scheme, "scale": scale, "bits": [], "codes": []}
+                blocks.append(cur)
+            else:
+                cur["bits"].append(int(parts[0], 16))
+                cur["codes"].append(int(parts[1], 16))
+    for b in blocks:
+        n = len(b["bits"])
+        b["bits"] += [0] * (block_len - n)
+        b["codes"] += [0] * (block_len - n)
+    return blocks, ts
+
+
+def test_mx_worked_blocks(golden_dir):
+    blocks, _ = _parse_blocks(os.path.join(golden_dir, "mx_worked_blocks.txt"), 32)
+    assert len(blocks) == 6
+    for b in blocks:
+        scheme = MXFP8 if b["scheme"] == "mxfp8" else MXFP4
+        bits = np.array([b["bits"]], dtype=np.uint16)
+        codes, scales = quantize_mx(bits, scheme)
+        if scheme.packed:
+            codes = unpack_fp4(codes)
+        assert int(scales[0, 0]) == b["scale"], b
+        assert list(codes[0].astype(int)) == b["codes"], b
+        # the exact reference agrees too
+        sc, ec = exact.mx_block(b["bits"], scheme.elem.name)
+        assert sc == b["scale"] and ec == b["codes"]
+
+
+def test_nvfp4_worked_tensor(golden_dir):
+    blocks, ts_want = _parse_blocks(os.path.join(golden_dir, "nvfp4_worked_tensor.txt"), 16)
+    assert len(blocks) == 4
+    bits = np.array([sum((b["bits"] for b in blocks), [])], dtype=np.uint16)
+    codes, scales, ts = quantize_nvfp4(bits)
+    assert float(ts) == ts_want
+    assert list(scales[0].astype(int)) == [b["scale"] for b in blocks]
+    assert list(unpack_fp4(codes)[0].astype(int)) == sum((b["codes"] for b in blocks), [])
+
+
+def _random_blocks(rng, n_blocks, block):
+    """bf16 blocks mixing normal, tiny, subnormal, huge, zero and constant content."""
+    out = []
+    for i in range(n_blocks):
+        kind = i % 6
+        if kind == 0:
+            x = rng.standard_normal(block) * np.exp(rng.normal(0, 4))
+        elif kind == 1:
+            x = rng.standard_t(2, block) * 2.0 ** rng.integers(-140, -110)
+        elif kind == 2:
+            x = rng.standard_normal(block) * 2.0 ** rng.integers(100, 126)
+        elif kind == 3:
+            x = np.zeros(block)
+            x[rng.integers(0, block)] = rng.standard_normal()
+        elif kind == 4:
+            x = np.full(block, rng.standard_normal())
+        else:
+            x = rng.standard_normal(block) * 2.0 ** rng.integers(-20, 20, size=block)
+        out.append(bf16_bits_from_f32(x.astype(np.float32)))
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("scheme", [MXFP8, MXFP4], ids=["mxfp8", "mxfp4"])
+def test_mx_matches_exact_reference(scheme):
+    rng = np.random.default_rng(7)
+    blocks = _random_blocks(rng, 120, 32)
+    codes, scales = quantize_mx(blocks.reshape(4, -1), scheme)
+    codes = unpack_fp4(codes) if scheme.packed else codes
+    codes = codes.reshape(120, 32)
+    scales = scales.reshape(120)
+    for i in range(120):
+        sc, ec = exact.mx_block([int(v) for v in blocks[i]], scheme.elem.name)
+        assert int(scales[i]) == sc, i
+        assert list(codes[i].astype(int)) == ec, i
+
+
+@pytest.mark.parametrize("scheme", [MXFP8, MXFP4], ids=["mxfp8", "mxfp4"])
+def test_mx_scale_bracketing_and_block_max(scheme):
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((64, 1024)) * np.exp(rng.normal(0, 3, size=(64, 1))) * 2.0 ** rng.integers(-60, 60, (64, 32)).repeat(32, 1)
+    bits = bf16_bits_from_f32(x.astype(np.float32))
+    codes, scales = quantize_mx(bits, scheme)
+    codes = unpack_fp4(codes) if scheme.packed else codes
+    v = np.abs(decode_bf16(bits)).reshape(64, 32, 32)
+    amax = v.max(-1)
+    e = scales.astype(np.int64) - 127
+    emax = scheme.elem.emax
+    unclamped = (e > -127) & (amax > 0)
+    lo = np.ldexp(1.0, e + emax)
+    assert np.all(lo[unclamped] <= amax[unclamped])
+    assert np.all(amax[unclamped] < 2 * lo[unclamped])
+    mag = codes.reshape(64, 32, 32).astype(np.int64) & (0x7F if not scheme.packed else 0x7)
+    dec = decode_e4m3 if not scheme.packed else decode_e2m1
+    maxval = dec(mag).max(-1)
+    if scheme is MXFP8:
+        assert np.all((maxval[unclamped] >= 256) & (maxval[unclamped] <= 448))
+    else:
+        assert np.all(np.isin(maxval[unclamped], [4.0, 6.0]))
+
+
+@pytest.mark.parametrize("scheme", [MXFP8, MXFP4], ids=["mxfp8", "mxfp4"])
+def test_mx_round_trip(scheme):
+    """quant(dequant(q)) == q whenever the dequantized block is exact in bf16 and holds a top-binade code."""
+    rng = np.random.default_rng(3)
+    rows, K = 256, 256
+    nb = K // 32
+    if scheme is MXFP8:
+        mags = rng.integers(0, 0x7F, size=(rows, K))
+        top = rng.integers(0x78, 0x7F, size=(rows, nb))  # 256..448
+        sign = 0x80
+    else:
+        mags = rng.integers(0, 8, size=(rows, K))
+        top = rng.integers(6, 8, size=(rows, nb))  # 4 or 6
+        sign = 0x8
+    mags = mags.reshape(rows, nb, 32)
+    mags[:, :, 0] = top
+    codes = (mags | (rng.integers(0, 2, size=mags.shape) * sign)).reshape(rows, K)
+    # keep every value inside the bf16 normal range
+    scales = rng.integers(127 - 100, 127 + 100, size=(rows, nb)).astype(np.uint8)
+    packed = ((codes[:, 0::2] & 0xF) | ((codes[:, 1::2] & 0xF) << 4)).astype(np.uint8) if scheme.packed else codes.astype(np.uint8)
+    deq = dequant_mx(packed, scales, scheme)
+    bits = bf16_bits_from_f32(deq.astype(np.float32))
+    assert np.array_equal(decode_bf16(bits), deq)  # exact in bf16
+    c2, s2 = quantize_mx(bits, scheme)
+    assert np.array_equal(s2, scales)
+    assert np.array_equal(c2, packed)
+
+
+def test_mx_nonfinite_and_zero_blocks():
+    bits = np.zeros((1, 96), dtype=np.uint16)
+    bits[0, 3] = 0x7FC0  # NaN in block 0
+    bits[0, 40] = 0xFF80  # -Inf in block 1
+    codes, scales = quantize_mx(bits, MXFP8)
+    assert list(scales[0]) == [0xFF, 0xFF, 0x00]
+    assert not codes.any()
+
+
+def test_nvfp4_matches_exact_reference():
+    rng = np.random.default_rng(5)
+    x = rng.standard_t(4, size=(8, 256)) * np.exp(rng.normal(0, 2, size=(8, 1)))
+    x[2, 16:32] = 0.0
+    x[3, :16] *= 1e-30
+    bits = bf16_bits_from_f32(x.astype(np.float32))
+    codes, scales, ts = quantize_nvfp4(bits)
+    ts_exact = exact.nvfp4_tensor_scale([int(b) for b in bits.ravel()])
+    assert Fraction(float(ts)) == ts_exact
+    codes = unpack_fp4(codes)
+    for r in range(8):
+        for j in range(16):
+            blk = [int(v) for v in bits[r, 16 * j:16 * j + 16]]
+            sc, ec = exact.nvfp4_block(blk, ts_exact)
+            assert int(scales[r, j]) == sc, (r, j)
+            assert list(codes[r, 16 * j:16 * j + 16].astype(int)) == ec, (r, j)
+
+
+def test_nvfp4_block_scale_sweep_exact():
+    """Block scale for every third bf16 block-amax from the E4M3 underflow region up to G, at a non-dyadic ts."""
+    g_bits = int(bf16_bits_from_f32(np.array([1234.5], np.float32))[0])
+    ts = exact.nvfp4_tensor_scale([g_bits])
+    assert ts.denominator & (ts.denominator - 1) == 0  # float32 value
+    # every positive bf16 whose B/(6 ts) falls in [2^-12, 2^10]
+    cand = np.arange(1, 0x7F80, dtype=np.uint16)
+    vals = decode_bf16(cand)
+    q = vals / (6 * float(ts))
+    g_val = float(exact.bf16_value(g_bits))
+    cand = cand[(q >= 2.0 ** -12) & (vals <= g_val)][::3]
+    rows = np.zeros((cand.size + 1, 16), dtype=np.uint16)
+    rows[0, 0] = g_bits
+    rows[1:, 0] = cand
+    _, scales, ts_o = quantize_nvfp4(rows)
+    assert Fraction(float(ts_o)) == ts
+    for i, b in enumerate(cand):
+        want = exact.e4m3_encode(exact.bf16_value(int(b)) / (6 * ts), False)
+        want = max(want, 1)
+        assert int(scales[i + 1, 0]) == want, hex(int(b))
+
+
+def test_nvfp4_element_sweep_exact():
+    """Every finite bf16 element value against a few block scales, exact reference."""
+    g_bits = int(bf16_bits_from_f32(np.array([300.0], np.float32))[0])
+    ts = exact.nvfp4_tensor_scale([g_bits])
+    allb = np.arange(0, 0x7F80, dtype=np.uint16)
+    for b_val in (300.0, 3.0, 0.07):
+        bb = int(bf16_bits_from_f32(np.array([b_val], np.float32))[0])
+        bmax = exact.bf16_value(bb)
+        xs = allb[np.abs(decode_bf16(allb)) <= float(bmax)]
+        xs = np.concatenate([xs, xs | 0x8000])[::7]
+        n = xs.size
+        nrow = (n + 14) // 15
+        rows = np.zeros((nrow + 1, 16), dtype=np.uint16)
+        rows[0, 0] = g_bits
+        rows[1:, 0] = bb
+        flat = np.zeros(nrow * 15, dtype=np.uint16)
+        flat[:n] = xs
+        rows[1:, 1:] = flat.reshape(nrow, 15)
+        codes, scales, ts_o = quantize_nvfp4(rows)
+        codes = unpack_fp4(codes)
+        sc = int(scales[1, 0])
+        assert np.all(scales[1:, 0] == sc)
+        want_sc, _ = exact.nvfp4_block([bb] + [0] * 15, ts)
+        assert sc == want_sc
+        denom = exact._minifloat_value(sc, 4, 3, 7) * ts
+        got = codes[1:, 1:].ravel()[:n]
+        for x, c in zip(xs, got):
+            want = exact.e2m1_encode(exact.bf16_value(int(x)) / denom, bool(int(x) >> 15))
+            assert int(c) == want, (hex(int(x)), b_val)
+
+
+def test_nvfp4_invariants():
+    rng = np.random.default_rng(9)
+    x = rng.standard_t(4, size=(64, 512)).astype(np.float32)
+    bits = bf16_bits_from_f32(x)
+    codes, scales, ts = quantize_nvfp4(bits)
+    v = decode_bf16(bits)
+    # the block holding the tensor maximum gets the largest scale 448
+    r, c = np.unravel_index(np.argmax(np.abs(v)), v.shape)
+    assert scales[r, c // 16] == 0x7E
+    # |deq - x| is at most half a grid step of the element's block, or saturation
+    deq = dequant_nvfp4(codes, scales, ts)
+    step_unit = decode_e4m3(scales).repeat(16, axis=1) * float(ts)
+    err = np.abs(deq - v)
+    # E2M1 half-steps: 0.25 below 2, 0.5 in [2, 4), 1 in [4, 6]
+    half = np.where(np.abs(v) < 2 * step_unit, 0.25, np.where(np.abs(v) < 4 * step_unit, 0.5, 1.0)) * step_unit
+    sat = np.abs(v) > 6 * step_unit
+    assert np.all((err <= half * (1 + 1e-12)) | sat)
+
+
+def test_nvfp4_zero_and_nonfinite():
+    z = np.zeros((2, 32), dtype=np.uint16)
+    z[1, 5] = 0x8000
+    codes, scales, ts = quantize_nvfp4(z)
+    assert float(ts) == 1.0 and not scales.any()
+    assert unpack_fp4(codes)[1, 5] == 0x8
+    z[0, 0] = 0x7F80
+    codes, scales, ts = quantize_nvfp4(z)
+    assert np.isnan(ts) and np.all(scales == 0x7F) and not codes.any()
+
+
+def test_should_quantize_rule():
+    assert should_quantize(1024, 1024, 1024)
+    assert not should_quantize(1023, 4096, 4096)
+    assert not should_quantize(1, 3072, 18432)
+    assert should_quantize(4608, 3072, 12288)
