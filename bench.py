@@ -1,0 +1,239 @@
+"""Benchmark: block-scaled GEMM TFLOP/s at FLUX DiT shapes on one MI355X.
+
+One step = one pass of the hot path over one batch: selective dispatch,
+dynamic MXFP8 quantization of the bf16 activations and the block-scaled GEMM
+with its bf16 epilogue, i.e. one ``mxq_quant_gemm_fused`` call on the FLUX-dev
+MLP up-projection at 1024x1024 (M = 4608 tokens, K = 3072, N = 12288).
+Weights are quantized once before timing.  Inputs rotate through several
+resident copies so the working set exceeds the 256 MB Infinity Cache.
+
+Prints ONE JSON line.  ``--all`` adds the other FLUX-shaped workloads
+(MXFP4 single-stream linears, NVFP4 at 2048x2048, one double-stream block
+with selective bf16 fallback) under "extra".
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-scaled GEMM TFLOP/s at FLUX DiT shapes (MXFP8/MXFP4); % of MFMA peak"
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"mxfp8": 5000.0, "mxfp4": 10100.0, "nvfp4": 2500.0, "bf16": 2500.0}
+PEAK_HBM_GBS = 8000.0
+GEMM_SRC = os.path.join(ROOT, "microscaling_quantized_diffusion_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mxfp8_flux_mlp_up_traffic.txt")
+
+
+def _src_sha() -> str:
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic_bytes():
+    """HBM bytes per GEMM launch from the committed counter summary, if it matches the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("gemm_source_sha256_16") != _src_sha():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _upload(bits, dev):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def _time_loop(fn, iters, warmup):
+    """Average milliseconds per call, HIP events on torch's current stream (the stream the library launches on)."""
+    import torch
+
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(iters):
+        fn(i)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / iters
+
+
+def run_layer(layer, dev, steps, warmup, rotate, seed=0):
+    """Time fused / GEMM-only / quantize-only for one linear; returns a dict of figures."""
+    import torch
+
+    from microscaling_quantized_diffusion_amd import mxq
+
+    a_bits, w_bits = __import__("microscaling_quantized_diffusion_amd.inputs", fromlist=["x"]).make_layer_inputs(
+        layer, seed=seed)
+    M, K, N = layer.M, layer.K, layer.N
+    flops = 2.0 * M * N * K
+    quantized = mxq.should_quantize(M, K, N)
+    a0 = _upload(a_bits, dev)
+    w0 = _upload(w_bits, dev)
+    As = [a0] + [a0.clone() for _ in range(rotate - 1)]
+    res = {"layer": layer.name, "M": M, "K": K, "N": N, "gflop": flops / 1e9}
+    if not quantized:
+        Ws = [w0] + [w0.clone() for _ in range(rotate - 1)]
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ms = _time_loop(lambda i: mxq.gemm_bf16(As[i % rotate], Ws[i % rotate], None, out), steps, warmup)
+        w_bytes = N * K * 2
+        res.update(path="bf16", ms=ms, tflops=flops / ms / 1e9,
+                   gbs=(w_bytes + M * K * 2 + M * N * 2) / ms / 1e6)
+        return res
+    fmt = layer.fmt
+    qw0 = mxq.quantize(fmt, w0)
+    Ws = [qw0] + [mxq.QTensor(fmt, qw0.codes.clone(), qw0.scales.clone(),
+                              None if qw0.tensor_scale is None else qw0.tensor_scale.clone(), K)
+                  for _ in range(rotate - 1)]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mxq.workspace_bytes(fmt, M, K, True), dtype=torch.uint8, device=dev)
+    ms_fused = _time_loop(lambda i: mxq.quant_gemm_fused(As[i % rotate], Ws[i % rotate], None, out, ws), steps, warmup)
+    qa = [mxq.quantize(fmt, a) for a in As]
+    ms_gemm = _time_loop(lambda i: mxq.gemm(qa[i % rotate], Ws[i % rotate], None, out), steps, warmup)
+    ms_quant = _time_loop(lambda i: mxq.quantize(fmt, As[i % rotate], qa[i % rotate]), steps, warmup)
+    code_b = M * K * (1.0 if fmt == "mxfp8" else 0.5)
+    scale_b = M * K / (16 if fmt == "nvfp4" else 32)
+    quant_bytes = M * K * 2 + code_b + scale_b
+    res.update(path=fmt, ms=ms_fused, tflops=flops / ms_fused / 1e9, gemm_ms=ms_gemm,
+               gemm_tflops=flops / ms_gemm / 1e9, quant_ms=ms_quant, quant_gbs=quant_bytes / ms_quant / 1e6,
+               pct_peak_fused=100.0 * flops / ms_fused / 1e9 / PEAK_TFLOPS[fmt],
+               pct_peak_gemm=100.0 * flops / ms_gemm / 1e9 / PEAK_TFLOPS[fmt])
+    del As, Ws, qa, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(layer, sample_rows):
+    """Time the CPU oracle (quantize A, dequantize both operands, fp64 GEMM) on a row sample of the workload."""
+    import oracle
+    from microscaling_quantized_diffusion_amd.inputs import make_layer_inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = None
+    a_bits, w_bits = make_layer_inputs(layer, seed=0)
+    a_s = np.ascontiguousarray(a_bits[:sample_rows])
+    scheme = oracle.MXFP8 if layer.fmt == "mxfp8" else oracle.MXFP4
+    t0 = time.perf_counter()
+    ac, asc = oracle.quantize_mx(a_s, scheme)
+    wc, wsc = oracle.quantize_mx(w_bits, scheme)
+    ref = oracle.gemm_mx_ref(ac, asc, wc, wsc, scheme)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * sample_rows * layer.N * layer.K
+    del ref
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": blas_threads,
+        "kind": "oracle",
+        "sample": (f"{sample_rows} of {layer.M} activation rows: oracle MX quantization of the sample and of all "
+                   f"{layer.N}x{layer.K} weights, fp64 dequantized GEMM; {dt:.1f} s; os.cpu_count()={os.cpu_count()}, "
+                   f"affinity={len(os.sched_getaffinity(0))}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=8, help="resident input copies cycled through (cold L2/MALL)")
+    ap.add_argument("--workload", default="flux_mlp_up_mxfp8")
+    ap.add_argument("--all", action="store_true", help="also time the other FLUX-shaped workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path runs on a single "
+              "MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from microscaling_quantized_diffusion_amd import mxq
+    from microscaling_quantized_diffusion_amd.inputs import WORKLOADS
+
+    mxq.lib()  # fail loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    layer = WORKLOADS[args.workload].layers[0]
+    print(f"# timing {args.workload} {layer.M}x{layer.K}x{layer.N} {layer.fmt}", file=sys.stderr, flush=True)
+    r = run_layer(layer, dev, args.steps, args.warmup, args.rotate)
+
+    flops = 2.0 * layer.M * layer.N * layer.K
+    gemm_s = r["gemm_ms"] / 1e3
+    traffic = _traffic_bytes()
+    line = {
+        "metric": METRIC,
+        "value": round(r["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3" if layer.fmt == "mxfp8" else ("fp4_e2m1" if layer.fmt == "mxfp4" else "f16"),
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": layer.M, "K": layer.K, "N": layer.N, "format": layer.fmt,
+                   "step": "mxq_quant_gemm_fused (dynamic activation quantization + block-scaled GEMM)",
+                   "weights": "pre-quantized before timing", "rotating_copies": args.rotate},
+        "pct_of_mfma_peak": round(r["pct_peak_fused"], 2),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": f"gemm_kernel<{layer.fmt}>",
+            "achieved": round(flops / gemm_s / 1e12, 2),
+            "peak": PEAK_TFLOPS[layer.fmt],
+            "unit": "TFLOP/s",
+            "frac": round(flops / gemm_s / 1e12 / PEAK_TFLOPS[layer.fmt], 4),
+            "traffic": traffic,
+            "algorithmic_bytes": layer.M * layer.K + layer.N * layer.K + (layer.M + layer.N) * layer.K // 32
+            + layer.M * layer.N * 2,
+            "gemm_ms": round(r["gemm_ms"], 5),
+        },
+        "quantizer": {"ms": round(r["quant_ms"], 5), "GB/s": round(r["quant_gbs"], 1),
+                      "frac_of_hbm": round(r["quant_gbs"] / PEAK_HBM_GBS, 4)},
+    }
+    if args.all:
+        extra = []
+        for name in ("flux_single_mxfp4", "flux_2048_nvfp4", "flux_double_block_b1", "flux_double_block_b4"):
+            for i, ly in enumerate(WORKLOADS[name].layers):
+                print(f"# timing {name}/{ly.name}", file=sys.stderr, flush=True)
+                e = run_layer(ly, dev, max(10, args.steps // 2), 3, min(args.rotate, 4), seed=i)
+                e["workload"] = name
+                extra.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in e.items()})
+        line["extra"] = extra
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(layer, args.cpu_rows)
+        line["cpu_baseline"]["value"] = round(line["cpu_baseline"]["value"], 6)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * mxq.h -- C ABI of the microscaling-quantized GEMM library for MI355X (gfx950).
+ *
+ * The library quantizes bf16 activations into block-scaled ("microscaling")
+ * formats and multiplies them with pre-quantized weights on the GPU, the
+ * inference recipe of the aitrends.kr article "Accelerating diffusion-model
+ * inference with MXFP8 and NVFP4 quantization on NVIDIA B200":
+ *   - "Section details": weights quantized once when the pipeline is loaded,
+ *     activations quantized dynamically on every call (the TorchAO
+ *     NVFP4 dynamic-activation / NVFP4-weight configuration);
+ *   - Glossary "Microscaling Formats": a block of 16-32 elements shares one
+ *     scale; "MXFP8": the OCP standard 8-bit format; "NVFP4": 4-bit format;
+ *   - second "Evidence" block: layers with min(M, K, N) < 1024 stay in bf16.
+ * Element / scale encodings follow the OCP Microscaling Formats v1.0
+ * specification, which the Glossary entry for MXFP8 names.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - GEMM: out[M, N] = A[M, K] * W[N, K]^T (+ bias[N]); W is a linear layer's
+ *    weight stored out-features by in-features.  Blocks run along K.
+ *  - Layouts are dense row-major with K innermost:
+ *      bf16 A [M, K], W [N, K], out [M, N], bias [N];
+ *      MXFP8 codes  uint8 [rows, K]     E4M3, scales uint8 [rows, K/32] E8M0;
+ *      MXFP4 codes  uint8 [rows, K/2]   E2M1, element 2j in the low nibble of
+ *                                        byte j; scales uint8 [rows, K/32] E8M0;
+ *      NVFP4 codes  uint8 [rows, K/2]   E2M1 (same packing), scales uint8
+ *                                        [rows, K/16] E4M3, plus one float32
+ *                                        per-tensor scale in device memory.
+ *  - Every pointer is caller-owned DEVICE memory (the library never
+ *    allocates or frees).  Base pointers of A, W, codes, out and workspace
+ *    must be 16-byte aligned; scale and bias pointers need no alignment.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    stream-ordered and return before the GPU work completes; device faults
+ *    surface at the caller's next synchronisation.  Calls on different
+ *    streams with disjoint outputs and workspaces may run concurrently.
+ *  - Arguments are validated on the host before anything is enqueued; on
+ *    any error nothing is launched.  M == 0 or N == 0 (or rows == 0) is a
+ *    successful no-op.  K must be a positive multiple of the block size
+ *    (32 for MX formats, 16 for NVFP4) wherever K is used.
+ *  - No global state: the library keeps nothing between calls.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXQ_ABI_VERSION 1
+
+typedef enum {
+  MXQ_FMT_MXFP8 = 1, /* E4M3 codes, E8M0 scale per 32 K-elements */
+  MXQ_FMT_MXFP4 = 2, /* E2M1 codes, E8M0 scale per 32 K-elements */
+  MXQ_FMT_NVFP4 = 3  /* E2M1 codes, E4M3 scale per 16 K-elements, fp32 per-tensor scale */
+} mxq_format;
+
+typedef enum {
+  MXQ_OK = 0,
+  MXQ_ERR_NULL = 1,        /* a required pointer is NULL */
+  MXQ_ERR_FORMAT = 2,      /* unknown mxq_format */
+  MXQ_ERR_SHAPE = 3,       /* negative size, or K not a positive multiple of the block */
+  MXQ_ERR_ALIGN = 4,       /* a 16-byte-aligned pointer is misaligned */
+  MXQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than mxq_workspace_bytes() */
+  MXQ_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
+  MXQ_ERR_LAUNCH = 7       /* a kernel launch failed (hipGetLastError after launch) */
+} mxq_status;
+
+/*
+ * Quantize a bf16 matrix x [rows, cols] along cols (dynamic activation
+ * quantization, and the offline weight quantization of the same article's
+ * "Section details").
+ *
+ * MX formats (OCP MX v1.0 shared exponent): per block of 32, amax = max|x|,
+ * e = clamp(floor(log2 amax) - emax, -127, 127) with emax = 8 (E4M3) or
+ * 2 (E2M1), e = -127 for an all-zero block; scale byte = e + 127; codes are
+ * x / 2^e rounded to nearest-even with saturation at +-448 / +-6 (never NaN);
+ * signed zeros keep their sign.  A block holding NaN/Inf gets scale 0xFF and
+ * zero codes.
+ *
+ * NVFP4: ts = RN_fp32(G / 2688) with G = max|x| over the whole tensor
+ * (G = 0 gives ts = 1); per block of 16 with amax B, the E4M3 scale is the
+ * round-to-nearest-even (saturating) encoding of B / (6 ts), raised to 0x01
+ * if it rounds to zero, and 0x00 for an all-zero block; codes are the E2M1
+ * encoding of x / (dec(scale) * ts), each quotient rounded once.  Any NaN/Inf
+ * in the tensor gives ts = NaN, scales 0x7F and zero codes.
+ *
+ *   fmt            MXQ_FMT_*
+ *   x_bf16         device, bf16 [rows, cols], 16-byte aligned
+ *   rows, cols     rows >= 0; cols a positive multiple of the block size
+ *   codes          device, out: uint8 [rows, cols] (MXFP8) or [rows, cols/2]
+ *   scales         device, out: uint8 [rows, cols/32] (MX) or [rows, cols/16]
+ *   tensor_scale   device float[1], out (NVFP4, required); must be NULL for MX
+ *   workspace      device scratch of mxq_workspace_bytes(fmt, rows, cols, 0)
+ *                  bytes (0 for MX, where it may be NULL)
+ *   stream         hipStream_t
+ */
+mxq_status mxq_quantize(mxq_format fmt, const void* x_bf16, int64_t rows, int64_t cols, void* codes,
+                        void* scales, float* tensor_scale, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * Block-scaled GEMM on already-quantized operands:
+ *   out[m, n] = sum_k deq(A)[m, k] * deq(W)[n, k] (+ bias[n]), rounded to bf16
+ * (nearest-even) from an fp32 accumulator.  deq is the format's decoding
+ * (MX: code * 2^(scale-127); NVFP4: code * dec_E4M3(scale) * tensor scale).
+ * This is the low-precision GEMM of the article's "Section details".
+ *
+ *   a_codes/a_scales   device, A quantized as by mxq_quantize (rows = M)
+ *   a_tensor_scale     device float[1] (NVFP4, required); NULL for MX
+ *   w_codes/w_scales   device, W [N, K] quantized (rows = N)
+ *   w_tensor_scale     device float[1] (NVFP4, required); NULL for MX
+ *   bias_bf16          device bf16 [N] or NULL
+ *   out_bf16           device bf16 [M, N], 16-byte aligned
+ */
+mxq_status mxq_gemm(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void* a_codes, const void* a_scales,
+                    const float* a_tensor_scale, const void* w_codes, const void* w_scales,
+                    const float* w_tensor_scale, const void* bias_bf16, void* out_bf16, void* stream);
+
+/*
+ * Dynamic activation quantization followed by the block-scaled GEMM, in one
+ * call: A (bf16) is quantized once into `workspace`, then multiplied with the
+ * pre-quantized W.  Results are identical to mxq_quantize + mxq_gemm.
+ *
+ *   a_bf16         device bf16 [M, K], 16-byte aligned
+ *   w_*            as in mxq_gemm
+ *   workspace      device scratch, at least mxq_workspace_bytes(fmt, M, K, 1)
+ *                  bytes, 16-byte aligned; its contents are overwritten
+ */
+mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void* a_bf16,
+                                const void* w_codes, const void* w_scales, const float* w_tensor_scale,
+                                const void* bias_bf16, void* out_bf16, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * bf16 GEMM for layers left unquantized by the selective rule:
+ *   out[m, n] = sum_k A[m, k] * W[n, k] (+ bias[n]) with bf16 inputs, an fp32
+ * accumulator and a nearest-even bf16 result.  K >= 1 (no block constraint).
+ *   a_bf16 [M, K], w_bf16 [N, K], out_bf16 [M, N]: device, 16-byte aligned.
+ */
+mxq_status mxq_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* a_bf16, const void* w_bf16,
+                         const void* bias_bf16, void* out_bf16, void* stream);
+
+/*
+ * Workspace bytes needed by mxq_quantize (fused = 0) or mxq_quant_gemm_fused
+ * (fused = 1) for an [M, K] activation.  Returns 0 for invalid arguments and
+ * for MX quantization (which needs none).
+ */
+size_t mxq_workspace_bytes(mxq_format fmt, int64_t M, int64_t K, int fused);
+
+/*
+ * Selective quantization rule: 1 iff min(M, K, N) >= 1024, else 0 (layers
+ * too small for quantization to pay off stay bf16; aitrends.kr article,
+ * second "Evidence" block).  Advisory: callers choose the entry point.
+ */
+int mxq_should_quantize(int64_t M, int64_t K, int64_t N);
+
+/* Static description of a status code; never NULL. */
+const char* mxq_status_string(mxq_status s);
+
+/* MXQ_ABI_VERSION of the loaded library. */
+int mxq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

@@ -1,0 +1,167 @@
+// Host side of the C ABI declared in include/mxq.h: argument validation,
+// workspace layout and kernel dispatch.  Every check runs before anything is
+// enqueued, so a failing call launches nothing.
+#include <string.h>
+
+#include "mxq_internal.h"
+
+using namespace mxq;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int block_of(mxq_format fmt) { return fmt == MXQ_FMT_NVFP4 ? 16 : 32; }
+
+bool valid_format(mxq_format fmt) {
+  return fmt == MXQ_FMT_MXFP8 || fmt == MXQ_FMT_MXFP4 || fmt == MXQ_FMT_NVFP4;
+}
+
+// K must be a positive multiple of the block; sizes must fit the kernels'
+// 32-bit row/column indices.
+bool valid_k(mxq_format fmt, int64_t K) { return K > 0 && K % block_of(fmt) == 0 && K <= (1 << 30); }
+bool valid_dim(int64_t d) { return d >= 0 && d <= (int64_t)1 << 30; }
+
+size_t code_bytes(mxq_format fmt, int64_t rows, int64_t K) {
+  return (size_t)rows * (size_t)(fmt == MXQ_FMT_MXFP8 ? K : K / 2);
+}
+size_t scale_bytes(mxq_format fmt, int64_t rows, int64_t K) { return (size_t)rows * (size_t)(K / block_of(fmt)); }
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Fused workspace: [A codes | A scales | tensor scale (NVFP4) | amax partials (NVFP4)],
+// each section 256-byte aligned.
+struct FusedLayout {
+  size_t codes, scales, ts, partials, total;
+};
+FusedLayout fused_layout(mxq_format fmt, int64_t M, int64_t K) {
+  FusedLayout L{};
+  L.codes = 0;
+  L.scales = round256(code_bytes(fmt, M, K));
+  L.ts = L.scales + round256(scale_bytes(fmt, M, K));
+  L.partials = L.ts + (fmt == MXQ_FMT_NVFP4 ? 256 : 0);
+  L.total = L.partials + (fmt == MXQ_FMT_NVFP4 ? round256((size_t)nvfp4_partials_count(M * K) * 4) : 0);
+  return L;
+}
+
+mxq_status launch_status(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_ERR_LAUNCH; }
+
+int elem_of(mxq_format fmt) { return fmt == MXQ_FMT_MXFP8 ? 1 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+int mxq_abi_version(void) { return MXQ_ABI_VERSION; }
+
+const char* mxq_status_string(mxq_status s) {
+  switch (s) {
+    case MXQ_OK: return "ok";
+    case MXQ_ERR_NULL: return "a required pointer is NULL";
+    case MXQ_ERR_FORMAT: return "unknown format";
+    case MXQ_ERR_SHAPE: return "invalid shape (negative size, or K not a positive multiple of the block)";
+    case MXQ_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MXQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case MXQ_ERR_UNSUPPORTED: return "unsupported request";
+    case MXQ_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int mxq_should_quantize(int64_t M, int64_t K, int64_t N) {
+  int64_t mn = M < K ? M : K;
+  mn = mn < N ? mn : N;
+  return mn >= 1024 ? 1 : 0;
+}
+
+size_t mxq_workspace_bytes(mxq_format fmt, int64_t M, int64_t K, int fused) {
+  if (!valid_format(fmt) || !valid_dim(M) || !valid_k(fmt, K)) return 0;
+  if (fused) return fused_layout(fmt, M, K).total;
+  if (fmt == MXQ_FMT_NVFP4) return round256((size_t)nvfp4_partials_count(M * K) * 4);
+  return 0;
+}
+
+mxq_status mxq_quantize(mxq_format fmt, const void* x_bf16, int64_t rows, int64_t cols, void* codes, void* scales,
+                        float* tensor_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_format(fmt)) return MXQ_ERR_FORMAT;
+  if (!valid_dim(rows) || !valid_k(fmt, cols)) return MXQ_ERR_SHAPE;
+  if (!x_bf16 || !codes || !scales) return MXQ_ERR_NULL;
+  if (fmt == MXQ_FMT_NVFP4 && !tensor_scale) return MXQ_ERR_NULL;
+  if (fmt != MXQ_FMT_NVFP4 && tensor_scale) return MXQ_ERR_UNSUPPORTED;
+  if (!aligned16(x_bf16) || !aligned16(codes)) return MXQ_ERR_ALIGN;
+  const size_t need = mxq_workspace_bytes(fmt, rows, cols, 0);
+  if (need && (!workspace || workspace_bytes < need)) return MXQ_ERR_WORKSPACE;
+  if (need && !aligned16(workspace)) return MXQ_ERR_ALIGN;
+  if (rows == 0) return MXQ_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (fmt == MXQ_FMT_NVFP4)
+    return launch_status(launch_nvfp4_quant((const uint16_t*)x_bf16, rows, cols, (uint8_t*)codes, (uint8_t*)scales,
+                                            tensor_scale, (uint32_t*)workspace, s));
+  return launch_status(
+      launch_mx_quant(elem_of(fmt), (const uint16_t*)x_bf16, rows, cols, (uint8_t*)codes, (uint8_t*)scales, s));
+}
+
+mxq_status mxq_gemm(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void* a_codes, const void* a_scales,
+                    const float* a_tensor_scale, const void* w_codes, const void* w_scales,
+                    const float* w_tensor_scale, const void* bias_bf16, void* out_bf16, void* stream) {
+  if (!valid_format(fmt)) return MXQ_ERR_FORMAT;
+  if (!valid_dim(M) || !valid_dim(N) || !valid_k(fmt, K)) return MXQ_ERR_SHAPE;
+  if (!a_codes || !a_scales || !w_codes || !w_scales || !out_bf16) return MXQ_ERR_NULL;
+  if (fmt == MXQ_FMT_NVFP4 && (!a_tensor_scale || !w_tensor_scale)) return MXQ_ERR_NULL;
+  if (fmt != MXQ_FMT_NVFP4 && (a_tensor_scale || w_tensor_scale)) return MXQ_ERR_UNSUPPORTED;
+  if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
+  if (M == 0 || N == 0) return MXQ_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (fmt == MXQ_FMT_NVFP4)
+    return launch_status(launch_nvfp4_gemm(M, N, K, (const uint8_t*)a_codes, (const uint8_t*)a_scales, a_tensor_scale,
+                                           (const uint8_t*)w_codes, (const uint8_t*)w_scales, w_tensor_scale,
+                                           (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s));
+  return launch_status(launch_mx_gemm(elem_of(fmt), M, N, K, (const uint8_t*)a_codes, (const uint8_t*)a_scales,
+                                      (const uint8_t*)w_codes, (const uint8_t*)w_scales, (const uint16_t*)bias_bf16,
+                                      (uint16_t*)out_bf16, s));
+}
+
+mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void* a_bf16,
+                                const void* w_codes, const void* w_scales, const float* w_tensor_scale,
+                                const void* bias_bf16, void* out_bf16, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (!valid_format(fmt)) return MXQ_ERR_FORMAT;
+  if (!valid_dim(M) || !valid_dim(N) || !valid_k(fmt, K)) return MXQ_ERR_SHAPE;
+  if (!a_bf16 || !w_codes || !w_scales || !out_bf16) return MXQ_ERR_NULL;
+  if (fmt == MXQ_FMT_NVFP4 && !w_tensor_scale) return MXQ_ERR_NULL;
+  if (fmt != MXQ_FMT_NVFP4 && w_tensor_scale) return MXQ_ERR_UNSUPPORTED;
+  if (!aligned16(a_bf16) || !aligned16(w_codes) || !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
+  const FusedLayout L = fused_layout(fmt, M, K);
+  if (!workspace || workspace_bytes < L.total) return MXQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MXQ_ERR_ALIGN;
+  if (M == 0 || N == 0) return MXQ_OK;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  uint8_t* a_codes = ws + L.codes;
+  uint8_t* a_scales = ws + L.scales;
+  hipError_t e;
+  if (fmt == MXQ_FMT_NVFP4) {
+    float* a_ts = (float*)(ws + L.ts);
+    e = launch_nvfp4_quant((const uint16_t*)a_bf16, M, K, a_codes, a_scales, a_ts, (uint32_t*)(ws + L.partials), s);
+    if (e != hipSuccess) return MXQ_ERR_LAUNCH;
+    e = launch_nvfp4_gemm(M, N, K, a_codes, a_scales, a_ts, (const uint8_t*)w_codes, (const uint8_t*)w_scales,
+                          w_tensor_scale, (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s);
+    return launch_status(e);
+  }
+  e = launch_mx_quant(elem_of(fmt), (const uint16_t*)a_bf16, M, K, a_codes, a_scales, s);
+  if (e != hipSuccess) return MXQ_ERR_LAUNCH;
+  e = launch_mx_gemm(elem_of(fmt), M, N, K, a_codes, a_scales, (const uint8_t*)w_codes, (const uint8_t*)w_scales,
+                     (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s);
+  return launch_status(e);
+}
+
+mxq_status mxq_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* a_bf16, const void* w_bf16,
+                         const void* bias_bf16, void* out_bf16, void* stream) {
+  if (!valid_dim(M) || !valid_dim(N) || K <= 0 || K > (1 << 30)) return MXQ_ERR_SHAPE;
+  if (!a_bf16 || !w_bf16 || !out_bf16) return MXQ_ERR_NULL;
+  if (!aligned16(a_bf16) || !aligned16(w_bf16) || !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
+  if (M == 0 || N == 0) return MXQ_OK;
+  return launch_status(launch_bf16_gemm(M, N, K, (const uint16_t*)a_bf16, (const uint16_t*)w_bf16,
+                                        (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, (hipStream_t)stream));
+}
+
+}  // extern "C"

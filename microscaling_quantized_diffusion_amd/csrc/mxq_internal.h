@@ -1,0 +1,61 @@
+// Internal declarations shared by the HIP translation units of libmxq.
+// Nothing here is part of the public ABI (include/mxq.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mxq.h"
+
+namespace mxq {
+
+// ---------------------------------------------------------------- launchers
+// Each launcher enqueues its kernels on `stream` and returns the HIP error of
+// the launch (hipSuccess when nothing failed).  Shapes are already validated.
+
+// MX quantizer: x bf16 [rows, cols] -> codes / E8M0 scales.  elem: 1 = E4M3, 2 = E2M1.
+hipError_t launch_mx_quant(int elem, const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
+                           uint8_t* scales, hipStream_t stream);
+
+// NVFP4 quantizer (two kernels: global-amax partials, then block quantization).
+// `partials` holds nvfp4_partials_count(rows*cols) uint32 values.
+int64_t nvfp4_partials_count(int64_t n_elems);
+hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                              float* tensor_scale, uint32_t* partials, hipStream_t stream);
+
+// MX GEMM (elem: 1 = E4M3, 2 = E2M1).
+hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                          const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                          const uint16_t* bias, uint16_t* out, hipStream_t stream);
+
+// NVFP4 GEMM.
+hipError_t launch_nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                             const float* a_ts, const uint8_t* w_codes, const uint8_t* w_scales,
+                             const float* w_ts, const uint16_t* bias, uint16_t* out, hipStream_t stream);
+
+// bf16 GEMM.
+hipError_t launch_bf16_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* a, const uint16_t* w,
+                            const uint16_t* bias, uint16_t* out, hipStream_t stream);
+
+// ------------------------------------------------------------ device helpers
+
+// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Remap a linear workgroup id so that each of the 8 XCDs (which receive
+// workgroups round-robin) works on one contiguous range of ids.
+__device__ __forceinline__ uint32_t xcd_contiguous_id(uint32_t id, uint32_t n) {
+  const uint32_t xcds = 8;
+  uint32_t per = n / xcds;  // ids [0, per*xcds) are remapped; the tail keeps its id
+  if (id >= per * xcds) return id;
+  return (id % xcds) * per + id / xcds;
+}
+
+}  // namespace mxq

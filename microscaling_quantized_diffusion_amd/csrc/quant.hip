@@ -1,0 +1,325 @@
+// Dynamic block-scaled quantizers for gfx950: MXFP8 / MXFP4 (E8M0 scale per
+// 32 elements) and NVFP4-style (E4M3 scale per 16 elements + fp32 tensor
+// scale).  Method: aitrends.kr "Accelerating diffusion-model inference with
+// MXFP8 and NVFP4 quantization on NVIDIA B200", Glossary ("Microscaling
+// Formats", "MXFP8", "NVFP4") and "Section details" (dynamic activation
+// quantization, dynamic per-tensor scale); encodings and the shared-exponent
+// rule of the OCP Microscaling Formats v1.0 specification.
+//
+// Both quantizers are HBM-streaming kernels: every lane owns one 16-byte
+// chunk (8 bf16) per iteration, loaded with one 128-bit load, so a wave reads
+// 1 KiB of contiguous memory per instruction.  A 32-element MX block is four
+// consecutive lanes (a DPP quad), a 16-element NVFP4 block two lanes; block
+// maxima are exchanged with DPP quad permutes, no LDS.  All rounding
+// decisions are taken in integer arithmetic on the bf16 bit patterns (MX) or
+// by exact comparisons against per-block thresholds (NVFP4), so codes are
+// bit-exact by construction.
+#include "mxq_internal.h"
+
+namespace mxq {
+namespace {
+
+template <int ELEM>
+struct ElemFmt;
+template <>
+struct ElemFmt<1> {  // E4M3: bias 7, 3 mantissa bits, max 448 = 1.75 * 2^8
+  static constexpr int MBITS = 3, EMIN = -6, EMAX = 8, MAXCODE = 0x7E, SIGN_SHIFT = 7;
+};
+template <>
+struct ElemFmt<2> {  // E2M1: bias 1, 1 mantissa bit, max 6 = 1.5 * 2^2
+  static constexpr int MBITS = 1, EMIN = 0, EMAX = 2, MAXCODE = 0x7, SIGN_SHIFT = 3;
+};
+
+__device__ __forceinline__ uint32_t quad_swap1(uint32_t v) {  // lanes 0<->1, 2<->3 of each quad
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t quad_swap2(uint32_t v) {  // lanes 0<->2, 1<->3 of each quad
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+}
+
+// Largest |x| (as bf16 magnitude bits) of the 8 elements in a 16-byte chunk.
+// For finite values the magnitude order equals the integer order of the bits;
+// NaN and Inf compare above every finite value (>= 0x7F80).
+__device__ __forceinline__ uint32_t chunk_absmax_bits(const uint4& v) {
+  uint32_t m0 = max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu);
+  uint32_t m1 = max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu);
+  uint32_t m2 = max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu);
+  uint32_t m3 = max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu);
+  return max(max(m0, m1), max(m2, m3));
+}
+
+// Encode one bf16 element x (bits h) as x / 2^e, rounded to nearest even and
+// saturated.  C = EMIN - MBITS + 134 + e is a per-block constant.
+//
+// x = sig * 2^(Eb' - 134) with sig the 8-bit significand (implicit bit
+// included for normal bf16) and Eb' = max(biased exponent, 1).  With
+// L = floor(log2 sig), the target grid exponent is
+// Ev = max(L + Eb' - 134 - e, EMIN); the grid step is 2^(Ev - MBITS), i.e. a
+// right shift of sig by sh = Ev - MBITS - Eb' + 134 + e
+//   = max(L - MBITS, C - Eb'),
+// and the code is (Ev - EMIN) << MBITS plus the rounded quotient, where
+// Ev - EMIN = sh - C + Eb'.  A carry of the rounded quotient into the next
+// binade yields the next code, since codes are monotone in the value.
+template <int ELEM>
+__device__ __forceinline__ uint32_t mx_encode(uint32_t h, int C) {
+  using F = ElemFmt<ELEM>;
+  const uint32_t a = h & 0x7FFFu;
+  const uint32_t sign = ((h >> 15) & 1u) << F::SIGN_SHIFT;
+  if (a == 0) return sign;
+  const uint32_t Eb = a >> 7;
+  const uint32_t sig = Eb ? ((a & 0x7Fu) | 0x80u) : a;
+  const int Ebp = Eb ? (int)Eb : 1;
+  const int L = Eb ? 7 : (31 - __clz(sig));
+  const int sh = max(L - F::MBITS, C - Ebp);
+  uint32_t q;
+  if (sh <= 0) {
+    q = sig << (-sh);
+  } else if (sh > 9) {
+    q = 0;  // sig < 2^8 < half a step
+  } else {
+    const uint32_t qt = sig >> sh;
+    const uint32_t rem = sig & ((1u << sh) - 1u);
+    const uint32_t half = 1u << (sh - 1);
+    q = qt + ((rem > half || (rem == half && (qt & 1u))) ? 1u : 0u);
+  }
+  int code = ((sh - C + Ebp) << F::MBITS) + (int)q;
+  code = min(code, F::MAXCODE);
+  return (uint32_t)code | sign;
+}
+
+// One lane = one 16-byte chunk (8 consecutive bf16); four lanes = one
+// 32-element block.  nchunks is a multiple of 4 and every quad of lanes
+// starts on a block boundary, so the whole quad is active together.
+template <int ELEM>
+__global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__ x, uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales, int64_t nchunks) {
+  using F = ElemFmt<ELEM>;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunks; i += stride) {
+    const uint4 v = x[i];
+    uint32_t m = chunk_absmax_bits(v);
+    m = max(m, quad_swap1(m));
+    m = max(m, quad_swap2(m));
+
+    uint32_t scale_byte;
+    uint32_t c[8];
+    if (m >= 0x7F80u) {  // NaN or Inf in the block
+      scale_byte = 0xFFu;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = 0;
+    } else {
+      int e;
+      if (m == 0) {
+        e = -127;
+      } else {
+        const int Eb = (int)(m >> 7);
+        const int fl = Eb ? Eb - 127 : (31 - __clz(m)) - 133;  // floor(log2 amax)
+        e = min(max(fl - F::EMAX, -127), 127);
+      }
+      scale_byte = (uint32_t)(e + 127);
+      const int C = F::EMIN - F::MBITS + 134 + e;
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[2 * j] = mx_encode<ELEM>(w[j] & 0xFFFFu, C);
+        c[2 * j + 1] = mx_encode<ELEM>(w[j] >> 16, C);
+      }
+    }
+    if (ELEM == 1) {
+      uint2 o;
+      o.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+      o.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+      reinterpret_cast<uint2*>(codes)[i] = o;
+    } else {
+      uint32_t o = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o |= c[j] << (4 * j);
+      reinterpret_cast<uint32_t*>(codes)[i] = o;
+    }
+    if ((i & 3) == 0) scales[i >> 2] = (uint8_t)scale_byte;
+  }
+}
+
+// ----------------------------------------------------------------- NVFP4
+
+constexpr int kNvPartialsMax = 1024;
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// Phase 1: per-workgroup maxima of the bf16 magnitude bits.
+__global__ __launch_bounds__(256) void absmax_partials_kernel(const uint4* __restrict__ x, int64_t nchunks,
+                                                              uint32_t* __restrict__ partials) {
+  __shared__ uint32_t red[4];
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunks; i += stride)
+    m = max(m, chunk_absmax_bits(x[i]));
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partials[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// E4M3 code of a positive, finite double q (nearest even, saturating at 448).
+__device__ __forceinline__ uint32_t e4m3_encode_pos(double q) {
+  if (q >= 448.0) return 0x7Eu;
+  const uint64_t u = (uint64_t)__double_as_longlong(q);
+  const int E = (int)((u >> 52) & 0x7FF) - 1023;
+  if (E >= -6) {
+    const uint64_t mant = u & 0xFFFFFFFFFFFFFull;
+    uint32_t c = ((uint32_t)(E + 7) << 3) | (uint32_t)(mant >> 49);
+    const uint64_t rem = mant & ((1ull << 49) - 1);
+    const uint64_t half = 1ull << 48;
+    c += (rem > half || (rem == half && (c & 1u))) ? 1u : 0u;
+    return c;
+  }
+  return (uint32_t)rint(q * 512.0);  // subnormal grid step 2^-9; rint rounds half to even
+}
+
+__device__ __forceinline__ double e4m3_decode_pos(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xF, m = c & 7;
+  if (e == 0) return (double)m * 0x1p-9;
+  return (double)__uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Smallest float32 bit pattern V such that, for a non-negative float32 |x|,
+// |x| >= V holds exactly when |x| is above the midpoint T, or equal to it and
+// the tie goes up (tie_up).  U = T rounded up to float32; if T is a float32,
+// a tie that goes down needs |x| > T, i.e. |x| >= next float after T.
+__device__ __forceinline__ uint32_t midpoint_threshold(double T, bool tie_up) {
+  const float f = (float)T;
+  uint32_t ub = __float_as_uint(f);
+  if ((double)f < T) ub += 1u;
+  const bool exact = (double)__uint_as_float(ub) == T;
+  return (exact && !tie_up) ? ub + 1u : ub;
+}
+
+// Phase 2: per 16-element block (two lanes), scale and element codes.
+__global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restrict__ x, int64_t nchunks,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                          float* __restrict__ ts_out,
+                                                          const uint32_t* __restrict__ partials, int npartials) {
+  __shared__ uint32_t red[4];
+  uint32_t g = 0;
+  for (int j = threadIdx.x; j < npartials; j += 256) g = max(g, partials[j]);
+  g = wave_max(g);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = g;
+  __syncthreads();
+  g = max(max(red[0], red[1]), max(red[2], red[3]));
+
+  const bool nonfinite = g >= 0x7F80u;
+  float ts;
+  if (nonfinite) {
+    ts = __uint_as_float(0x7FC00000u);
+  } else if (g == 0) {
+    ts = 1.0f;
+  } else {
+    // G / 2688 in double is correctly rounded; its float32 rounding is then the
+    // correctly rounded quotient: G has 8 significant bits and 2688 = 2^7 * 21,
+    // so the exact quotient is either short or has a binary expansion of
+    // period <= 6, never within 2^-53 of a float32 rounding midpoint.
+    ts = (float)((double)bf16_to_f32(g) / 2688.0);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = ts;
+
+  const double ts64 = (double)ts;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunks; i += stride) {
+    const uint4 v = x[i];
+    uint32_t b = chunk_absmax_bits(v);
+    b = max(b, quad_swap1(b));  // lanes (2t, 2t+1) share a 16-element block
+
+    uint32_t sc;
+    uint32_t V[7];
+    if (nonfinite) {
+      sc = 0x7Fu;
+#pragma unroll
+      for (int j = 0; j < 7; ++j) V[j] = 0xFFFFFFFFu;
+    } else if (b == 0) {
+      sc = 0;
+#pragma unroll
+      for (int j = 0; j < 7; ++j) V[j] = 0xFFFFFFFFu;
+    } else {
+      // block scale: one rounding of B / (6 ts); operands exact in double and
+      // the division correctly rounded, so the E4M3 rounding sees the exact
+      // quotient's decisions (a non-tie quotient is >= ~2^-32 relative away
+      // from any E4M3 midpoint).
+      const double q = (double)bf16_to_f32(b) / (6.0 * ts64);
+      sc = e4m3_encode_pos(q);
+      if (sc == 0) sc = 1;
+      const double s = e4m3_decode_pos(sc) * ts64;  // <= 28 significant bits: exact
+      // E2M1 midpoints between codes j and j+1; ties go to the even code, i.e.
+      // up for odd j.  t * s has <= 31 significant bits: exact in double.
+      V[0] = midpoint_threshold(0.25 * s, false);
+      V[1] = midpoint_threshold(0.75 * s, true);
+      V[2] = midpoint_threshold(1.25 * s, false);
+      V[3] = midpoint_threshold(1.75 * s, true);
+      V[4] = midpoint_threshold(2.5 * s, false);
+      V[5] = midpoint_threshold(3.5 * s, true);
+      V[6] = midpoint_threshold(5.0 * s, false);
+    }
+
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t h = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
+      const uint32_t a = (h & 0x7FFFu) << 16;  // |x| as float32 bits
+      uint32_t k = 0;
+#pragma unroll
+      for (int t = 0; t < 7; ++t) k += (a >= V[t]) ? 1u : 0u;
+      if (!nonfinite) k |= (h >> 12) & 8u;  // sign bit
+      o |= k << (4 * j);
+    }
+    reinterpret_cast<uint32_t*>(codes)[i] = o;
+    if ((i & 1) == 0) scales[i >> 1] = (uint8_t)sc;
+  }
+}
+
+int grid_for(int64_t nchunks, int64_t cap) {
+  int64_t g = (nchunks + 255) / 256;
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_mx_quant(int elem, const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
+                           uint8_t* scales, hipStream_t stream) {
+  const int64_t nchunks = rows * cols / 8;
+  if (nchunks == 0) return hipSuccess;
+  const int grid = grid_for(nchunks, 1 << 20);
+  if (elem == 1)
+    hipLaunchKernelGGL(mx_quant_kernel<1>, dim3(grid), dim3(256), 0, stream, (const uint4*)x, codes, scales, nchunks);
+  else
+    hipLaunchKernelGGL(mx_quant_kernel<2>, dim3(grid), dim3(256), 0, stream, (const uint4*)x, codes, scales, nchunks);
+  return hipGetLastError();
+}
+
+int64_t nvfp4_partials_count(int64_t n_elems) {
+  const int64_t nchunks = n_elems / 8;
+  int64_t p = (nchunks + 2047) / 2048;  // >= 8 chunks per lane before capping
+  if (p > kNvPartialsMax) p = kNvPartialsMax;
+  if (p < 1) p = 1;
+  return p;
+}
+
+hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                              float* tensor_scale, uint32_t* partials, hipStream_t stream) {
+  const int64_t nchunks = rows * cols / 8;
+  const int P = (int)nvfp4_partials_count(rows * cols);
+  hipLaunchKernelGGL(absmax_partials_kernel, dim3(P), dim3(256), 0, stream, (const uint4*)x, nchunks, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int grid = grid_for(nchunks, 2048);
+  hipLaunchKernelGGL(nvfp4_quant_kernel, dim3(grid), dim3(256), 0, stream, (const uint4*)x, nchunks, codes, scales,
+                     tensor_scale, (const uint32_t*)partials, P);
+  return hipGetLastError();
+}
+
+}  // namespace mxq

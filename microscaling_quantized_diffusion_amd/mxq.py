@@ -1,0 +1,225 @@
+"""Python binding of libmxq (ctypes): argument marshalling only.
+
+Every step of the quantization and GEMM runs in the library's HIP kernels;
+torch is used here only to allocate device memory and to name the current
+HIP stream.  If the library is not built, every call raises: there is no
+fallback implementation.
+
+Names mirror include/mxq.h.  Formats: "mxfp8", "mxfp4", "nvfp4".
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libmxq.so")
+
+FORMATS = {"mxfp8": 1, "mxfp4": 2, "nvfp4": 3}
+BLOCK = {"mxfp8": 32, "mxfp4": 32, "nvfp4": 16}
+
+MXQ_OK = 0
+STATUS_NAMES = {
+    0: "MXQ_OK",
+    1: "MXQ_ERR_NULL",
+    2: "MXQ_ERR_FORMAT",
+    3: "MXQ_ERR_SHAPE",
+    4: "MXQ_ERR_ALIGN",
+    5: "MXQ_ERR_WORKSPACE",
+    6: "MXQ_ERR_UNSUPPORTED",
+    7: "MXQ_ERR_LAUNCH",
+}
+
+# (name, restype, argtypes) of every exported entry point
+_VP, _I64, _SZ, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+SIGNATURES = {
+    "mxq_quantize": (_I, [_I, _VP, _I64, _I64, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "mxq_gemm": (_I, [_I, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "mxq_quant_gemm_fused": (_I, [_I, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "mxq_gemm_bf16": (_I, [_I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
+    "mxq_workspace_bytes": (_SZ, [_I, _I64, _I64, _I]),
+    "mxq_should_quantize": (_I, [_I64, _I64, _I64]),
+    "mxq_status_string": (ctypes.c_char_p, [_I]),
+    "mxq_abi_version": (_I, []),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class MxqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS_NAMES.get(status, status)} ({lib().mxq_status_string(status).decode()})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmxq.so (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m microscaling_quantized_diffusion_amd.build`")
+        so = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(so, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = so
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MXQ_OK:
+        raise MxqError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _fmt(fmt: str) -> int:
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown format {fmt!r}")
+    return FORMATS[fmt]
+
+
+def _require(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
+
+
+def code_cols(fmt: str, K: int) -> int:
+    return K if fmt == "mxfp8" else K // 2
+
+
+@dataclass
+class QTensor:
+    """A quantized [rows, K] matrix: codes, scales and (NVFP4) the device per-tensor scale."""
+
+    fmt: str
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tensor_scale: Optional[torch.Tensor]
+    K: int
+
+    @property
+    def rows(self) -> int:
+        return self.codes.shape[0]
+
+
+def abi_version() -> int:
+    return lib().mxq_abi_version()
+
+
+def should_quantize(M: int, K: int, N: int) -> bool:
+    return bool(lib().mxq_should_quantize(M, K, N))
+
+
+def workspace_bytes(fmt: str, M: int, K: int, fused: bool) -> int:
+    return int(lib().mxq_workspace_bytes(_fmt(fmt), M, K, 1 if fused else 0))
+
+
+def quantize(fmt: str, x: torch.Tensor, out: Optional[QTensor] = None,
+             workspace: Optional[torch.Tensor] = None) -> QTensor:
+    """mxq_quantize: bf16 [rows, K] -> QTensor (codes, scales, tensor scale)."""
+    _require(x, torch.bfloat16, "x")
+    rows, K = x.shape
+    f = _fmt(fmt)
+    dev = x.device
+    if out is None:
+        codes = torch.empty((rows, code_cols(fmt, K)), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, K // BLOCK[fmt]), dtype=torch.uint8, device=dev)
+        ts = torch.empty(1, dtype=torch.float32, device=dev) if fmt == "nvfp4" else None
+        out = QTensor(fmt, codes, scales, ts, K)
+    need = workspace_bytes(fmt, rows, K, False)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mxq_quantize", lib().mxq_quantize(f, _ptr(x), rows, K, _ptr(out.codes), _ptr(out.scales),
+                                              _ptr(out.tensor_scale), _ptr(workspace), wsz, _stream(x)))
+    return out
+
+
+def gemm(a: QTensor, w: QTensor, bias: Optional[torch.Tensor] = None,
+         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mxq_gemm: quantized A [M, K] x quantized W [N, K]^T -> bf16 [M, N]."""
+    if a.fmt != w.fmt or a.K != w.K:
+        raise ValueError("A and W must share format and K")
+    M, N = a.rows, w.rows
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.codes.device)
+    _check("mxq_gemm", lib().mxq_gemm(_fmt(a.fmt), M, N, a.K, _ptr(a.codes), _ptr(a.scales), _ptr(a.tensor_scale),
+                                      _ptr(w.codes), _ptr(w.scales), _ptr(w.tensor_scale), _ptr(bias), _ptr(out),
+                                      _stream(out)))
+    return out
+
+
+def quant_gemm_fused(a: torch.Tensor, w: QTensor, bias: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mxq_quant_gemm_fused: bf16 A [M, K] quantized on the fly, times quantized W [N, K]^T -> bf16 [M, N]."""
+    _require(a, torch.bfloat16, "a")
+    M, K = a.shape
+    if K != w.K:
+        raise ValueError("K mismatch")
+    N = w.rows
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    need = workspace_bytes(w.fmt, M, K, True)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=a.device)
+    wsz = workspace.numel() * workspace.element_size()
+    _check("mxq_quant_gemm_fused",
+           lib().mxq_quant_gemm_fused(_fmt(w.fmt), M, N, K, _ptr(a), _ptr(w.codes), _ptr(w.scales),
+                                      _ptr(w.tensor_scale), _ptr(bias), _ptr(out), _ptr(workspace), wsz, _stream(a)))
+    return out
+
+
+def gemm_bf16(a: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mxq_gemm_bf16: bf16 A [M, K] x bf16 W [N, K]^T -> bf16 [M, N]."""
+    _require(a, torch.bfloat16, "a")
+    _require(w, torch.bfloat16, "w")
+    M, K = a.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _check("mxq_gemm_bf16", lib().mxq_gemm_bf16(M, N, K, _ptr(a), _ptr(w), _ptr(bias), _ptr(out), _stream(a)))
+    return out
+
+
+@dataclass
+class QuantLinear:
+    """A linear layer's weight prepared for selective quantization.
+
+    The weight is quantized once (offline, outside any timed region); the bf16
+    copy is kept for calls whose shape falls under the min(M, K, N) < 1024 rule.
+    """
+
+    fmt: str
+    weight_bf16: Optional[torch.Tensor]
+    qweight: Optional[QTensor]
+    bias: Optional[torch.Tensor] = None
+
+    @classmethod
+    def from_weight(cls, fmt: str, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                    keep_bf16: bool = True, quantize_weight: bool = True) -> "QuantLinear":
+        qw = quantize(fmt, w) if quantize_weight else None
+        return cls(fmt, w if keep_bf16 else None, qw, bias)
+
+    def __call__(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+        M, K = x.shape
+        N = (self.qweight.rows if self.qweight is not None else self.weight_bf16.shape[0])
+        if self.qweight is not None and should_quantize(M, K, N):
+            return quant_gemm_fused(x, self.qweight, self.bias, out, workspace)
+        if self.weight_bf16 is None:
+            raise ValueError("layer falls back to bf16 but holds no bf16 weight")
+        return gemm_bf16(x, self.weight_bf16, self.bias, out)

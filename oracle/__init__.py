@@ -64,6 +64,10 @@ from .quant import (  # noqa: F401
     unpack_fp4,
 )
 from .gemm import (  # noqa: F401
+    bf16_half_ulp,
+    bf16_round,
+    gemm_error,
+    rounding_mismatch_rate,
     gemm_bf16_ref,
     gemm_mx_ref,
     gemm_nvfp4_ref,

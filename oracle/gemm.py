@@ -16,7 +16,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import decode_bf16
+from .formats import decode_bf16, floor_log2
 from .quant import Scheme, dequant_mx, dequant_nvfp4
 
 
@@ -62,3 +62,69 @@ def normwise_error(y: np.ndarray, r: np.ndarray) -> float:
     if denom == 0.0:
         return 0.0 if num == 0.0 else float("inf")
     return num / denom
+
+
+def bf16_round(r: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value (ties to even), returned as float64.
+
+    bf16 keeps 8 significant bits: the step is 2**(floor(log2|r|) - 7) for
+    normal magnitudes and 2**-133 below 2**-126.  Overflow is not expected
+    from these GEMMs and raises.
+    """
+    r = np.asarray(r, dtype=np.float64)
+    a = np.abs(r)
+    e = np.where(a == 0, -126, np.maximum(floor_log2(np.where(a == 0, 1.0, a)), -126))
+    step_exp = e - 7
+    q = np.rint(np.ldexp(a, -step_exp))
+    out = np.copysign(np.ldexp(q, step_exp), r)
+    if np.any(np.abs(out) > 3.3895313892515355e38):
+        raise OverflowError("value beyond the bf16 range")
+    return out
+
+
+def bf16_half_ulp(y: np.ndarray) -> np.ndarray:
+    """Half the bf16 spacing at bf16 values y: 2**(floor(log2|y|) - 8), or 2**-134 below 2**-126."""
+    a = np.abs(np.asarray(y, dtype=np.float64))
+    e = np.where(a == 0, -126, np.maximum(floor_log2(np.where(a == 0, 1.0, a)), -126))
+    return np.ldexp(1.0, e - 8)
+
+
+def gemm_error(y: np.ndarray, r: np.ndarray) -> float:
+    """Normwise error of a bf16 GEMM result beyond its own output rounding.
+
+    max_i max(|y_i - r_i| - halfulp_bf16(y_i), 0) / max_i |r_i|.  A result y_i
+    obtained by rounding an accumulator a_i to bf16 satisfies
+    |y_i - a_i| <= halfulp(y_i), so this bounds the accumulator's error
+    |a_i - r_i|.  The output rounding itself may reach 2**-8 of max|r|
+    (8 significant bits), which is why it is separated from the 2e-3 gate.
+    Infinite if y holds NaN or Inf.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    if not np.all(np.isfinite(y)):
+        return float("inf")
+    if r.size == 0:
+        return 0.0
+    denom = float(np.abs(r).max())
+    excess = np.maximum(np.abs(y - r) - bf16_half_ulp(y), 0.0)
+    num = float(excess.max())
+    if denom == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return num / denom
+
+
+def rounding_mismatch_rate(y: np.ndarray, r: np.ndarray, rel: float = 1.0 / 16) -> float:
+    """Fraction of the outputs with |r_i| >= rel * max|r| whose bf16 value differs from bf16_round(r_i).
+
+    A correctly rounding fp32-accumulating kernel differs only where r_i lies
+    within its accumulation error of a rounding midpoint; a truncating or
+    double-rounding epilogue differs on a large fraction.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    if r.size == 0:
+        return 0.0
+    sel = np.abs(r) >= rel * np.abs(r).max()
+    if not np.any(sel):
+        return 0.0
+    return float(np.mean(y[sel] != bf16_round(r[sel])))

@@ -132,8 +132,11 @@ def nvfp4_tensor_scale(bits: np.ndarray) -> np.float32:
     return f
 
 
-def quantize_nvfp4(bits: np.ndarray):
+def quantize_nvfp4(bits: np.ndarray, ts=None):
     """NVFP4-style quantization: E2M1 codes, E4M3 scale per 16 elements, fp32 per-tensor scale.
+
+    ``ts`` may be given to quantize a subset of a tensor's rows with the
+    per-tensor scale of the whole tensor (``nvfp4_tensor_scale(full)``).
 
       1. ts = nvfp4_tensor_scale(x)  (global amax G; ts = RN_fp32(G/2688));
       2. per 16-block with amax B: B = 0 gives sc = 0x00; otherwise
@@ -150,7 +153,7 @@ def quantize_nvfp4(bits: np.ndarray):
     """
     b = _check_bits(bits, 16)
     rows, K = b.shape
-    ts = nvfp4_tensor_scale(b)
+    ts = nvfp4_tensor_scale(b) if ts is None else np.float32(ts)
     if np.isnan(ts):
         return (np.zeros((rows, K // 2), np.uint8), np.full((rows, K // 16), 0x7F, np.uint8), ts)
     x = decode_bf16(b).reshape(rows, K // 16, 16)

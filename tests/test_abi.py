@@ -1,0 +1,105 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and rejects invalid arguments on the host before anything is launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests._util import ROOT, ensure_built
+from microscaling_quantized_diffusion_amd import mxq
+
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ensure_built()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(mxq.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings(lib):
+    assert mxq.abi_version() == 1
+    for s in range(8):
+        assert lib.mxq_status_string(s)
+    assert b"unknown" in lib.mxq_status_string(99)
+
+
+def test_should_quantize(lib):
+    assert mxq.should_quantize(1024, 1024, 1024)
+    assert not mxq.should_quantize(1, 3072, 18432)
+    assert not mxq.should_quantize(4608, 3072, 1023)
+    assert mxq.should_quantize(4608, 15360, 3072)
+
+
+def test_workspace_sizes(lib):
+    assert mxq.workspace_bytes("mxfp8", 4608, 3072, False) == 0
+    fused = mxq.workspace_bytes("mxfp8", 4608, 3072, True)
+    assert fused >= 4608 * 3072 + 4608 * 96
+    assert mxq.workspace_bytes("mxfp4", 4608, 3072, True) >= 4608 * 1536 + 4608 * 96
+    assert mxq.workspace_bytes("nvfp4", 16896, 3072, True) >= 16896 * 1536 + 16896 * 192 + 4
+    assert mxq.workspace_bytes("nvfp4", 64, 64, False) > 0
+    assert lib.mxq_workspace_bytes(9, 16, 32, 1) == 0
+    assert lib.mxq_workspace_bytes(1, 16, 33, 1) == 0
+
+
+P = 4096  # a fake, 16-byte-aligned device address; never dereferenced by these calls
+
+
+def test_quantize_argument_errors(lib):
+    q = lib.mxq_quantize
+    assert q(7, P, 4, 32, P, P, None, None, 0, None) == 2  # format
+    assert q(1, P, -1, 32, P, P, None, None, 0, None) == 3  # negative rows
+    assert q(1, P, 4, 33, P, P, None, None, 0, None) == 3  # K not a multiple of 32
+    assert q(3, P, 4, 24, P, P, P, P, 1 << 20, None) == 3  # NVFP4 K not a multiple of 16
+    assert q(1, P, 4, 0, P, P, None, None, 0, None) == 3  # K = 0
+    assert q(1, None, 4, 32, P, P, None, None, 0, None) == 1  # null input
+    assert q(1, P, 4, 32, P, None, None, None, 0, None) == 1  # null scales
+    assert q(3, P, 4, 32, P, P, None, P, 1 << 20, None) == 1  # NVFP4 needs the tensor scale
+    assert q(1, P + 2, 4, 32, P, P, None, None, 0, None) == 4  # misaligned input
+    assert q(3, P, 4, 32, P, P, P, None, 0, None) == 5  # NVFP4 needs a workspace
+    assert q(3, P, 4, 32, P, P, P, P, 8, None) == 5  # too small
+    assert q(1, P, 0, 32, P, P, None, None, 0, None) == 0  # empty: no-op
+
+
+def test_gemm_argument_errors(lib):
+    g = lib.mxq_gemm
+    assert g(0, 4, 4, 32, P, P, None, P, P, None, None, P, None) == 2
+    assert g(1, 4, -4, 32, P, P, None, P, P, None, None, P, None) == 3
+    assert g(2, 4, 4, 48, P, P, None, P, P, None, None, P, None) == 3
+    assert g(1, 4, 4, 32, None, P, None, P, P, None, None, P, None) == 1
+    assert g(3, 4, 4, 32, P, P, None, P, P, P, None, P, None) == 1
+    assert g(1, 4, 4, 32, P, P, None, P, P, None, None, P + 8, None) == 4
+    assert g(1, 0, 4, 32, P, P, None, P, P, None, None, P, None) == 0
+    assert g(1, 4, 0, 32, P, P, None, P, P, None, None, P, None) == 0
+
+
+def test_fused_argument_errors(lib):
+    f = lib.mxq_quant_gemm_fused
+    need = lib.mxq_workspace_bytes(1, 64, 64, 1)
+    assert f(1, 64, 64, 64, P, P, P, None, None, P, None, need, None) == 5
+    assert f(1, 64, 64, 64, P, P, P, None, None, P, P, need - 1, None) == 5
+    assert f(1, 64, 64, 64, P, P, P, None, None, P, P + 4, need, None) == 4
+    assert f(3, 64, 64, 64, P, P, P, None, None, P, P, 1 << 20, None) == 1
+    assert f(1, 0, 64, 64, P, P, P, None, None, P, P, need, None) == 0
+
+
+def test_bf16_argument_errors(lib):
+    b = lib.mxq_gemm_bf16
+    assert b(4, 4, 0, P, P, None, P, None) == 3
+    assert b(4, 4, 8, None, P, None, P, None) == 1
+    assert b(4, 4, 8, P, P + 1, None, P, None) == 4
+    assert b(0, 4, 8, P, P, None, P, None) == 0

@@ -1,0 +1,174 @@
+"""GPU parity of mxq_quantize against the CPU oracle: codes, scales and the
+NVFP4 tensor scale must match byte for byte."""
+
+import numpy as np
+import pytest
+
+import oracle
+from microscaling_quantized_diffusion_amd.inputs import WORKLOADS, bf16_bits_from_f32, make_layer_inputs
+from tests._util import gpu_or_skip, log_case, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return gpu_or_skip()
+
+
+def _gpu_quant(fmt, bits, dev):
+    import torch
+
+    from microscaling_quantized_diffusion_amd import mxq
+
+    q = mxq.quantize(fmt, to_dev(bits, dev))
+    torch.cuda.synchronize()
+    ts = None if q.tensor_scale is None else np.float32(q.tensor_scale.cpu().numpy()[0])
+    return q.codes.cpu().numpy(), q.scales.cpu().numpy(), ts
+
+
+def _oracle_quant(fmt, bits):
+    if fmt == "nvfp4":
+        return oracle.quantize_nvfp4(bits)
+    c, s = oracle.quantize_mx(bits, oracle.MXFP8 if fmt == "mxfp8" else oracle.MXFP4)
+    return c, s, None
+
+
+def _assert_same(fmt, bits, dev):
+    gc, gs, gts = _gpu_quant(fmt, bits, dev)
+    oc, os_, ots = _oracle_quant(fmt, bits)
+    bad_s = np.argwhere(gs != os_)
+    assert bad_s.size == 0, f"{fmt}: {len(bad_s)} scale mismatches, first {bad_s[:3].tolist()}"
+    bad_c = np.argwhere(gc != oc)
+    assert bad_c.size == 0, f"{fmt}: {len(bad_c)} code mismatches, first {bad_c[:3].tolist()}"
+    if fmt == "nvfp4":
+        g32 = np.array([gts], np.float32).view(np.uint32)[0]
+        o32 = np.array([ots], np.float32).view(np.uint32)[0]
+        assert (np.isnan(gts) and np.isnan(ots)) or g32 == o32, (gts, ots)
+
+
+FMTS = ["mxfp8", "mxfp4", "nvfp4"]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_config1_activation(fmt, dev):
+    """1024 x 1024 activation of the single-GEMM workload (N(0,1) rows times exp(N(0,0.5)))."""
+    a, _ = make_layer_inputs(WORKLOADS["mxfp8_1024"].layers[0], seed=0)
+    log_case("quant config1", fmt)
+    _assert_same(fmt, a, dev)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rows,K", [(1, 32), (37, 96), (3, 2048), (129, 160)])
+def test_ragged_shapes(fmt, rows, K, dev):
+    rng = np.random.default_rng(rows * 7 + K)
+    x = rng.standard_normal((rows, K)) * np.exp(rng.normal(0, 2, (rows, 1)))
+    log_case("quant ragged", fmt, rows, K)
+    _assert_same(fmt, bf16_bits_from_f32(x.astype(np.float32)), dev)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_outlier_and_student_t(fmt, dev):
+    a, _ = make_layer_inputs(WORKLOADS["flux_mlp_up_mxfp8"].layers[0], seed=0, M=256, N=16)
+    log_case("quant outlier", fmt)
+    _assert_same(fmt, a, dev)
+    a, _ = make_layer_inputs(WORKLOADS["flux_2048_nvfp4"].layers[0], seed=0, M=256, N=16)
+    log_case("quant student_t", fmt)
+    _assert_same(fmt, a, dev)
+
+
+def _pinned_sweep(block, lo_binades, hi_binades):
+    """Rows of blocks [pin, x...] where the pin sets the block maximum's binade
+    and the other elements sweep every bf16 pattern (both signs) from
+    lo_binades below to hi_binades above the pin's binade, subnormals included
+    near the bottom of the range."""
+    rows = []
+    rng = np.random.default_rng(17)
+    per = block - 1
+    for Ep in range(0, 255):
+        pin_m = int(rng.integers(0, 128))
+        pin = (Ep << 7) | pin_m
+        if pin == 0:
+            pin = 1
+        e_lo, e_hi = max(0, Ep - lo_binades), min(254, Ep + hi_binades)
+        mags = np.arange(e_lo << 7, (e_hi << 7) + 128, dtype=np.uint32)
+        vals = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
+        nblk = (vals.size + per - 1) // per
+        pad = np.zeros(nblk * per, np.uint16)
+        pad[: vals.size] = vals
+        blk = np.empty((nblk, block), np.uint16)
+        blk[:, 0] = pin
+        blk[:, 1:] = pad.reshape(nblk, per)
+        rows.append(blk.reshape(-1))
+    width = max(r.size for r in rows)
+    width = (width + block - 1) // block * block
+    out = np.zeros((len(rows), width), np.uint16)
+    for i, r in enumerate(rows):
+        out[i, : r.size] = r
+    return out
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_mx_exhaustive_element_sweep(fmt, dev):
+    """Every element pattern within 12 binades below (and 1 above) every possible block-max binade."""
+    bits = _pinned_sweep(32, 12, 1)
+    log_case("quant mx sweep", fmt, bits.shape)
+    _assert_same(fmt, bits, dev)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_all_bf16_patterns(fmt, dev):
+    """All 65536 bit patterns (NaN and Inf included) in natural order."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(64, 1024)
+    if fmt == "nvfp4":
+        # a non-finite value anywhere poisons the whole tensor: check finite rows
+        # and the poisoned case separately
+        finite = bits[(bits & 0x7F80) != 0x7F80]
+        finite = finite[: finite.size // 1024 * 1024].reshape(-1, 1024)
+        log_case("quant all patterns finite", fmt)
+        _assert_same(fmt, finite, dev)
+    log_case("quant all patterns", fmt)
+    _assert_same(fmt, bits, dev)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_zero_tensor(fmt, dev):
+    bits = np.zeros((4, 64), np.uint16)
+    bits[1, 3] = 0x8000
+    log_case("quant zeros", fmt)
+    _assert_same(fmt, bits, dev)
+
+
+def test_nvfp4_tensor_scale_sweep(dev):
+    """ts = RN_fp32(G/2688) for G over a spread of bf16 values, including exact ties of the block scale."""
+    rng = np.random.default_rng(4)
+    gs = list(range(0x0001, 0x7F80, 97)) + [0x4528, 0x3F80, 0x7F7F, 0x0001, 0x0080]
+    for g in gs:
+        x = rng.standard_normal((2, 32)).astype(np.float32)
+        bits = bf16_bits_from_f32(x)
+        gval = oracle.decode_bf16(np.array([g], np.uint16))[0]
+        vals = oracle.decode_bf16(bits)
+        bits[np.abs(vals) >= gval] = 0
+        bits[0, 5] = g
+        _assert_same("nvfp4", bits, dev)
+
+
+def test_nvfp4_block_and_element_sweep(dev):
+    """Block maxima over 12 binades below each tensor-max binade with all element patterns beneath them."""
+    for g_bits in (0x4528, 0x3FC1, 0x1234, 0x7000):
+        sweep = _pinned_sweep(16, 10, 0)
+        gval = oracle.decode_bf16(np.array([g_bits], np.uint16))[0]
+        vals = oracle.decode_bf16(sweep)
+        sweep = sweep.copy()
+        sweep[~(np.abs(vals) < gval)] = 0  # keep G the tensor maximum
+        sweep[0, 0] = g_bits
+        log_case("nvfp4 sweep", hex(g_bits), sweep.shape)
+        _assert_same("nvfp4", sweep, dev)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_deterministic(fmt, dev):
+    a, _ = make_layer_inputs(WORKLOADS["mxfp8_1024"].layers[0], seed=3, M=300, K=512, N=8)
+    r1 = _gpu_quant(fmt, a, dev)
+    r2 = _gpu_quant(fmt, a, dev)
+    assert np.array_equal(r1[0], r2[0]) and np.array_equal(r1[1], r2[1])

@@ -143,3 +143,49 @@ def test_normwise_error():
     assert normwise_error(r + np.array([[0.0, 0.004], [0.0, 0.0]]), r) == pytest.approx(1e-3)
     assert normwise_error(np.array([[np.nan, 0], [0, 0]]), r) == float("inf")
     assert decode_bf16(np.array([0x3F80], np.uint16))[0] == 1.0
+
+
+def test_bf16_round_matches_torch_on_float32_values():
+    """torch rounds float32 to bfloat16 to nearest even; on float32 inputs (no double rounding) both agree."""
+    import torch
+
+    from oracle import bf16_round
+
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal(200000) * np.exp(rng.normal(0, 20, 200000))).astype(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) < 3.0e38)]
+    x = np.concatenate([x, np.float32([0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 2.0 ** -130, 1e-45])])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = bf16_round(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_round_midpoints_from_float64():
+    from oracle import bf16_round
+
+    # exact ties go to the even significand; anything above a tie goes up
+    assert bf16_round(np.array([1.0 + 2 ** -8]))[0] == 1.0
+    assert bf16_round(np.array([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
+    assert bf16_round(np.array([1.0 + 2 ** -8 + 2 ** -40]))[0] == 1.0 + 2 ** -7
+    assert bf16_round(np.array([-(2.0 ** -134)]))[0] == 0.0  # half of the smallest subnormal: tie to 0
+    assert bf16_round(np.array([3 * 2.0 ** -134]))[0] == 2.0 ** -132
+
+
+def test_gemm_error_separates_output_rounding():
+    from oracle import bf16_half_ulp, bf16_round, gemm_error, rounding_mismatch_rate
+
+    rng = np.random.default_rng(3)
+    r = rng.standard_normal((64, 64)) * 3.0
+    r[0, 0] = 1.0 + 2 ** -8 - 2 ** -30  # max|r| just above a power of two: rounding error near 2^-8 relative
+    y = bf16_round(r)
+    assert normwise_error(y, r) > 2e-3  # plain normwise error charges the rounding
+    assert gemm_error(y, r) == 0.0  # correctly rounded output: no error beyond the rounding
+    assert rounding_mismatch_rate(y, r) == 0.0
+    # an accumulator error of 1e-2 * max|r| on one element is charged in full minus that element's half ulp
+    y2 = y.copy()
+    y2[5, 5] = bf16_round(np.array([r[5, 5] + 0.01 * np.abs(r).max()]))[0]
+    e = gemm_error(y2, r)
+    assert 0.009 < e < 0.011
+    # truncation toward zero instead of rounding shows up as mismatches
+    trunc = np.sign(r) * np.floor(np.abs(r) / (2 * bf16_half_ulp(r))) * (2 * bf16_half_ulp(r))
+    assert rounding_mismatch_rate(trunc, r) > 0.3
