@@ -12,10 +12,12 @@
 // layers stay in bf16).
 //
 // Data flow per workgroup (one BM x BN output tile):
-//   global --128-bit loads--> VGPR staging --ds_write_b128--> LDS (double
-//   buffer; every row holds one 128-byte K slab; 16-byte chunks are XOR-
-//   swizzled by row) --ds_read_b128--> MFMA operands.  Per-lane scales are
-//   read from global memory one K step ahead.
+//   global --buffer_load_dwordx4 ... lds (LDS DMA, no VGPR staging)--> LDS
+//   (two stages; every row holds one 128-byte K slab; 16-byte chunks are
+//   XOR-swizzled by row) --ds_read_b128--> MFMA operands.  The loads of K
+//   step k+1 are in flight while step k computes.  The buffer resource spans
+//   the tile's rows only, so rows past M / N and the K tail read as zeros.
+//   Per-lane scale bytes are read from global memory one K step ahead.
 //
 // Operand layouts (measured on gfx950):
 //   scaled 16x16x128: lane l serves row l % 16 and K-quarter q = l / 16;
@@ -35,6 +37,8 @@
 // codes (8 elements, inside one 16-element block) is widened with
 // v_cvt_scalef32_pk_f16_fp4 (unit scale) and multiplied by the block scale
 // with v_pk_mul_f16; the tensor scales multiply the fp32 result.
+#include <utility>
+
 #include "mxq_internal.h"
 
 namespace mxq {
@@ -49,9 +53,28 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 enum Mode { MX8 = 1, MX4 = 2, NV4 = 3, BF16 = 4 };
 
-// XOR swizzle of the 16-byte chunk index by row: 16 rows reading the same
-// logical chunk hit distinct banks with either 32 or 64 LDS banks.
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1, so
+// that I can feed immediate operands (MFMA scale byte selects).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int FMT, int OPA, int OPB>
+__device__ __forceinline__ v4f mfma_scaled(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, FMT, OPA, sa, OPB, sb);
+}
+
+// XOR swizzles of the 16-byte chunk index by row, chosen by measurement on
+// gfx950 (SQ_LDS_BANK_CONFLICT = 0 for the operand read pattern):
+//   swz  : 16 consecutive rows read the same logical chunk (16x16 operands)
+//   swz32: 32 consecutive rows read the same logical chunk (32x32 operands)
+__device__ __forceinline__ int swz(int r) { return r & 7; }
+__device__ __forceinline__ int swz32(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ v8i as_v8i(const uint4& lo, const uint4& hi) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -79,26 +102,34 @@ __device__ __forceinline__ void nv4_dequant_dword(uint32_t x, h2 s2, h2 (&o)[4])
   o[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3) * s2;
 }
 
+// Buffer resource over a tile's rows: loads at offsets >= num_records return
+// zeros, which pads rows beyond M / N and the K tail with zero codes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 template <int MODE, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
     const uint8_t* __restrict__ Ws, const float* __restrict__ a_ts, const float* __restrict__ w_ts,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N, int K) {
-  constexpr int NT = 64 * WM * WN;
+  constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   constexpr int TJ = WTM / 16, TI = WTN / 16;  // 16x16 MFMA tiles per wave (M, N)
-  static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "tile/threads mismatch");
-  constexpr int LOADS_A = BM * 8 / NT, LOADS = (BM + BN) * 8 / NT;
+  constexpr int ROWS = BM + BN;                // LDS rows per stage (A rows, then W rows)
+  constexpr int GROUPS = ROWS / 8;             // 8-row (1 KiB) groups, one wave-wide load each
+  static_assert(BM % 16 == 0 && BN % 16 == 0 && GROUPS % NW == 0, "tile/wave mismatch");
+  constexpr int PER_WAVE = GROUPS / NW;
   // scale bytes per lane per K step and row: MX8 1, MX4 2 (E8M0); NV4 4 (E4M3)
   constexpr int NSC = (MODE == MX8) ? 1 : (MODE == MX4) ? 2 : (MODE == NV4) ? 4 : 0;
   constexpr int NSC1 = NSC > 0 ? NSC : 1;
   constexpr int FMT = (MODE == MX8) ? 0 : 4;  // cbsz / blgp: 0 = FP8 E4M3, 4 = FP4 E2M1
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * 128];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // 2 stages x ROWS x 128 bytes
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int q = lane >> 4, r16 = lane & 15;
 
@@ -117,56 +148,58 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
   const int SK = (MODE == NV4) ? K / 16 : K / 32;                     // scale bytes per row
   const int nk = (KB + 127) / 128;                                    // K steps
 
-  // ---- global -> VGPR staging -> LDS
-  uint4 stage[LOADS];
-  auto load_step = [&](int ks) {
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * KB, (uint32_t)min(BM, M - m0) * (uint32_t)KB);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * KB, (uint32_t)min(BN, N - n0) * (uint32_t)KB);
+
+  // ---- global -> LDS without VGPR staging: each lane moves one 16-byte chunk.
+  // LDS row r of group g holds chunk (lane & 7) at physical slot (lane & 7),
+  // i.e. logical chunk (lane & 7) ^ swz(r) of the tile row.
+  auto issue_stage = [&](int ks, int stage) {
+    uint8_t* sbase = smem + stage * (ROWS * 128);
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const bool isA = u < LOADS_A;
-      const int cc = isA ? tid + u * NT : tid + (u - LOADS_A) * NT;
-      const int row = cc >> 3, ch = cc & 7;
-      const int kb = ks * 128 + ch * 16;
-      const int grow = (isA ? m0 : n0) + row;
-      const bool ok = (grow < (isA ? M : N)) && (kb < KB);
-      const uint8_t* src = (isA ? A : W) + (size_t)grow * KB + kb;
-      stage[u] = ok ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_step = [&](int buf) {
-    uint8_t* sA = smem + buf * (BM + BN) * 128;
-    uint8_t* sW = sA + BM * 128;
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const bool isA = u < LOADS_A;
-      const int cc = isA ? tid + u * NT : tid + (u - LOADS_A) * NT;
-      const int row = cc >> 3, ch = cc & 7;
-      *reinterpret_cast<uint4*>((isA ? sA : sW) + row * 128 + ((ch ^ swz(row)) << 4)) = stage[u];
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int g = wave * PER_WAVE + u;
+      const int r = g * 8 + (lane >> 3);
+      const bool isA = g * 8 < BM;
+      const int rr = isA ? r : r - BM;
+      const int kb = ks * 128 + (((lane & 7) ^ swz(r)) << 4);
+      const uint32_t off = kb < KB ? (uint32_t)rr * (uint32_t)KB + (uint32_t)kb : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rw, &sbase[g * 1024], 16, off, 0, 0, 0);
     }
   };
 
-  // ---- per-lane scale bytes of one K step
-  // MX: slot h -> K-block 4*MFMA_PER_STEP*ks + 4h + q.
+  // ---- per-lane scale bytes of one K step, four per VGPR.
+  // MX: slot h -> K-block 4*NSC*ks + 4h + q.
   // NV4: slots {2q, 2q+1, 8+2q, 9+2q} of the step's 16 blocks (chunk q and 4+q).
+  // Slot (t, h) of tile t lives in byte (t*NSC + h) % 4 of word (t*NSC + h) / 4.
+  constexpr int SWW = (TI * NSC1 + 3) / 4, SWA = (TJ * NSC1 + 3) / 4;
   auto scale_block = [&](int ks, int h) -> int {
     if (MODE == NV4) return ks * 16 + (h >> 1) * 8 + 2 * q + (h & 1);
     return ks * (4 * NSC) + 4 * h + q;
   };
-  int scW[TI][NSC1], scA[TJ][NSC1];
-  auto load_scales = [&](int ks, int (&sw)[TI][NSC1], int (&sa)[TJ][NSC1]) {
+  uint32_t scW[SWW], scA[SWA];
+  auto load_scales = [&](int ks, uint32_t (&sw)[SWW], uint32_t (&sa)[SWA]) {
+#pragma unroll
+    for (int w = 0; w < SWW; ++w) sw[w] = 0;
+#pragma unroll
+    for (int w = 0; w < SWA; ++w) sa[w] = 0;
     if (NSC == 0) return;
-    const int pad = (MODE == NV4) ? 0 : 127;
 #pragma unroll
     for (int h = 0; h < NSC; ++h) {
       const int kblk = scale_block(ks, h);
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
         const int n = n0 + wn * WTN + 16 * i + r16;
-        sw[i][h] = (n < N && kblk < SK) ? (int)Ws[(size_t)n * SK + kblk] : pad;
+        const uint32_t b = (n < N && kblk < SK) ? (uint32_t)Ws[(size_t)n * SK + kblk] : 0u;
+        const int L = i * NSC + h;
+        sw[L / 4] |= b << (8 * (L % 4));
       }
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int m = m0 + wm * WTM + 16 * j + r16;
-        sa[j][h] = (m < M && kblk < SK) ? (int)As[(size_t)m * SK + kblk] : pad;
+        const uint32_t b = (m < M && kblk < SK) ? (uint32_t)As[(size_t)m * SK + kblk] : 0u;
+        const int L = j * NSC + h;
+        sa[L / 4] |= b << (8 * (L % 4));
       }
     }
   };
@@ -177,27 +210,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  load_step(0);
+  issue_stage(0, 0);
   load_scales(0, scW, scA);
-  store_step(0);
-  __syncthreads();
 
   for (int ks = 0; ks < nk; ++ks) {
+    // stage ks&1 has landed for every wave, and every wave is done reading
+    // stage (ks+1)&1 from the previous step
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     const bool more = ks + 1 < nk;
-    if (more) load_step(ks + 1);
-    int nscW[TI][NSC1], nscA[TJ][NSC1];
+    if (more) issue_stage(ks + 1, (ks + 1) & 1);
+    uint32_t nscW[SWW], nscA[SWA];
     if (more) load_scales(ks + 1, nscW, nscA);
 
-    const uint8_t* sA = smem + (ks & 1) * (BM + BN) * 128;
+    const uint8_t* sA = smem + (ks & 1) * (ROWS * 128);
     const uint8_t* sW = sA + BM * 128;
-    uint4 fw[TI][2], fa[TJ][2];
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int row = wn * WTN + 16 * i + r16;
-      const uint8_t* base = sW + row * 128;
-      fw[i][0] = *reinterpret_cast<const uint4*>(base + ((q ^ swz(row)) << 4));
-      fw[i][1] = *reinterpret_cast<const uint4*>(base + (((4 + q) ^ swz(row)) << 4));
-    }
+    uint4 fa[TJ][2];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int row = wm * WTM + 16 * j + r16;
@@ -205,77 +233,73 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
       fa[j][0] = *reinterpret_cast<const uint4*>(base + ((q ^ swz(row)) << 4));
       fa[j][1] = *reinterpret_cast<const uint4*>(base + (((4 + q) ^ swz(row)) << 4));
     }
-
-    if constexpr (MODE == MX8) {
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              as_v8i(fw[i][0], fw[i][1]), as_v8i(fa[j][0], fa[j][1]), acc[i][j], FMT, FMT, 0, scW[i][0], 0,
-              scA[j][0]);
-    } else if constexpr (MODE == MX4) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int j = 0; j < TJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                as_v8i_lo(fw[i][h]), as_v8i_lo(fa[j][h]), acc[i][j], FMT, FMT, 0, scW[i][h], 0, scA[j][h]);
-    } else if constexpr (MODE == BF16) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int j = 0; j < TJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, fw[i][h]),
-                                                                 __builtin_bit_cast(v8bf, fa[j][h]), acc[i][j], 0,
-                                                                 0, 0);
-    } else {  // NV4: 8 f16 MFMAs per step, one per dword d of (chunk q | chunk 4+q)
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const int half = d >> 2, dw = d & 3;
-        const int slot = half * 2 + (dw >> 1);  // 16-element block of this dword
-        v8h wa[TI], ab[TJ];
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          const uint32_t x = (dw == 0) ? fw[i][half].x : (dw == 1) ? fw[i][half].y : (dw == 2) ? fw[i][half].z
-                                                                                             : fw[i][half].w;
-          const _Float16 s = e4m3_to_f16((uint32_t)scW[i][slot]);
-          h2 o[4];
-          nv4_dequant_dword(x, h2{s, s}, o);
-          wa[i] = v8h{o[0].x, o[0].y, o[1].x, o[1].y, o[2].x, o[2].y, o[3].x, o[3].y};
-        }
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const uint32_t x = (dw == 0) ? fa[j][half].x : (dw == 1) ? fa[j][half].y : (dw == 2) ? fa[j][half].z
-                                                                                             : fa[j][half].w;
-          const _Float16 s = e4m3_to_f16((uint32_t)scA[j][slot]);
-          h2 o[4];
-          nv4_dequant_dword(x, h2{s, s}, o);
-          ab[j] = v8h{o[0].x, o[0].y, o[1].x, o[1].y, o[2].x, o[2].y, o[3].x, o[3].y};
-        }
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int j = 0; j < TJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[i], ab[j], acc[i][j], 0, 0, 0);
+    static_for<TI>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      uint4 fw[2];
+      {
+        const int row = wn * WTN + 16 * i + r16;
+        const uint8_t* base = sW + row * 128;
+        fw[0] = *reinterpret_cast<const uint4*>(base + ((q ^ swz(row)) << 4));
+        fw[1] = *reinterpret_cast<const uint4*>(base + (((4 + q) ^ swz(row)) << 4));
       }
-    }
+      if constexpr (MODE == MX8) {
+        constexpr int LW = i;
+        static_for<TJ>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          acc[i][j] = mfma_scaled<FMT, LW % 4, j % 4>(as_v8i(fw[0], fw[1]), as_v8i(fa[j][0], fa[j][1]), acc[i][j],
+                                                      (int)scW[LW / 4], (int)scA[j / 4]);
+        });
+      } else if constexpr (MODE == MX4) {
+        static_for<2>([&](auto hc) {
+          constexpr int h = decltype(hc)::value;
+          constexpr int LW = i * 2 + h;
+          static_for<TJ>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int LA = j * 2 + h;
+            acc[i][j] = mfma_scaled<FMT, LW % 4, LA % 4>(as_v8i_lo(fw[h]), as_v8i_lo(fa[j][h]), acc[i][j],
+                                                         (int)scW[LW / 4], (int)scA[LA / 4]);
+          });
+        });
+      } else if constexpr (MODE == BF16) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, fw[h]),
+                                                                 __builtin_bit_cast(v8bf, fa[j][h]), acc[i][j], 0, 0,
+                                                                 0);
+      } else {  // NV4: 8 f16 MFMAs per step, one per dword d of (chunk q | chunk 4+q)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          const int half = d >> 2, dw = d & 3;
+          const int slot = half * 2 + (dw >> 1);  // 16-element block of this dword
+          const uint32_t xw = (dw == 0) ? fw[half].x : (dw == 1) ? fw[half].y : (dw == 2) ? fw[half].z : fw[half].w;
+          const int LW = i * 4 + slot;
+          const _Float16 sw16 = e4m3_to_f16((scW[LW / 4] >> (8 * (LW % 4))) & 0xFFu);
+          h2 ow[4];
+          nv4_dequant_dword(xw, h2{sw16, sw16}, ow);
+          const v8h wa = v8h{ow[0].x, ow[0].y, ow[1].x, ow[1].y, ow[2].x, ow[2].y, ow[3].x, ow[3].y};
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+            const uint32_t xa = (dw == 0) ? fa[j][half].x : (dw == 1) ? fa[j][half].y : (dw == 2) ? fa[j][half].z
+                                                                                               : fa[j][half].w;
+            const int LA = j * 4 + slot;
+            const _Float16 sa16 = e4m3_to_f16((scA[LA / 4] >> (8 * (LA % 4))) & 0xFFu);
+            h2 oa[4];
+            nv4_dequant_dword(xa, h2{sa16, sa16}, oa);
+            const v8h ab = v8h{oa[0].x, oa[0].y, oa[1].x, oa[1].y, oa[2].x, oa[2].y, oa[3].x, oa[3].y};
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, ab, acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    });
 
     if (more) {
-      store_step((ks + 1) & 1);
 #pragma unroll
-      for (int h = 0; h < NSC1; ++h) {
+      for (int w = 0; w < SWW; ++w) scW[w] = nscW[w];
 #pragma unroll
-        for (int i = 0; i < TI; ++i) scW[i][h] = nscW[i][h];
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) scA[j][h] = nscA[j][h];
-      }
+      for (int w = 0; w < SWA; ++w) scA[w] = nscA[w];
     }
-    __syncthreads();
   }
 
   // ---- epilogue: (x tensor scales) (+ bias) -> bf16 RNE -> global
@@ -316,9 +340,216 @@ template <int MODE, int BM, int BN, int WM, int WN>
 hipError_t launch_tiled(int64_t M, int64_t N, int64_t K, const void* a, const uint8_t* as, const void* w,
                         const uint8_t* ws, const float* a_ts, const float* w_ts, const uint16_t* bias, uint16_t* out,
                         hipStream_t stream) {
+  constexpr size_t lds = 2 * (size_t)(BM + BN) * 128;
+  auto kern = gemm_kernel<MODE, BM, BN, WM, WN>;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<MODE, BM, BN, WM, WN>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
-                     (const uint8_t*)a, as, (const uint8_t*)w, ws, a_ts, w_ts, bias, out, (int)M, (int)N, (int)K);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(64 * WM * WN), lds, stream, (const uint8_t*)a, as,
+                     (const uint8_t*)w, ws, a_ts, w_ts, bias, out, (int)M, (int)N, (int)K);
+  return hipGetLastError();
+}
+
+
+// ------------------------------------------------------------------------
+// MX fast path: 32x32x64 scaled MFMA with codes and E8M0 scales staged
+// together by LDS DMA.  Requires K to be a multiple of one 128-byte code slab
+// (K % 128 == 0 for MXFP8, K % 256 == 0 for MXFP4) so that every K step holds
+// whole 4- or 8-byte scale groups per row.
+//
+// 32x32x64 operand layout (measured): lane l serves row l % 32 and K-half
+// q = l / 32 of a 64-wide K step;
+//   FP8: bytes 0-15 = K [16q, 16q+16), bytes 16-31 = K [32+16q, +16)
+//   FP4: bytes 0-15 = K [32q, 32q+32), low nibble first
+//   scale byte of lane l: K-block q of row l % 32.
+// A 128-byte slab row therefore feeds FP8 MFMA t (t = 0, 1) from chunks
+// (4t + q, 4t + 2 + q) with scale block 2t + q, and FP4 MFMA t (t = 0..3)
+// from chunk 2t + q with scale block 2t + q: every lane reads chunks
+// q, 2+q, 4+q, 6+q of each of its rows.  On gfx950 the FP4 rate doubles only
+// with this 32x32x64 shape (measured 9.2 vs 4.7 PFLOP/s register-only).
+// Output layout: lane l holds out^T[n = 8*(v/4) + 4*q + v%4][m = l % 32].
+template <int ELEM, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void mx32_gemm_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
+    const uint8_t* __restrict__ Ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N,
+    int K) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+  constexpr int TJ = WTM / 32, TI = WTN / 32;  // 32x32 MFMA tiles per wave (M, N)
+  constexpr int ROWS = BM + BN;
+  constexpr int GROUPS = ROWS / 8;             // 1 KiB code groups per stage
+  static_assert(BM % 32 == 0 && BN % 32 == 0 && GROUPS % NW == 0, "tile/wave mismatch");
+  constexpr int PER_WAVE = GROUPS / NW;
+  constexpr int SB = (ELEM == 1) ? 4 : 8;      // scale bytes per row per K step
+  constexpr int SDW = SB / 4;                  // scale dwords per row per K step
+  constexpr int SGROUPS = ROWS * SDW / 64;     // wave-wide 4-byte scale loads per stage
+  static_assert((ROWS * SDW) % 64 == 0, "scale groups");
+  constexpr int CODE_BYTES = ROWS * 128;
+  constexpr int STAGE = CODE_BYTES + ROWS * SB;
+  constexpr int FMT = (ELEM == 1) ? 0 : 4;
+  constexpr int NT = (ELEM == 1) ? 2 : 4;      // MFMAs per 128-byte slab
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // 2 stages
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int q = lane >> 5, r32 = lane & 31;
+
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const uint32_t id = xcd_contiguous_id(blockIdx.x, gridDim.x);
+  constexpr int GROUP = 8;
+  const int group = (int)(id / (uint32_t)(GROUP * tiles_n));
+  const int first_m = group * GROUP;
+  const int gsz = min(tiles_m - first_m, GROUP);
+  const int tm = first_m + (int)(id % (uint32_t)gsz);
+  const int tn = (int)((id % (uint32_t)(GROUP * tiles_n)) / (uint32_t)gsz);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int KB = (ELEM == 1) ? K : K / 2;
+  const int SK = K / 32;
+  const int nk = KB / 128;
+  const uint32_t rows_a = (uint32_t)min(BM, M - m0), rows_w = (uint32_t)min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * KB, rows_a * (uint32_t)KB);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * KB, rows_w * (uint32_t)KB);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(As + (size_t)m0 * SK, rows_a * (uint32_t)SK);
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(Ws + (size_t)n0 * SK, rows_w * (uint32_t)SK);
+
+  // codes: LDS row r holds logical chunk (lane & 7) ^ swz32(r) in slot lane & 7;
+  // scales: [row][SDW] dwords after the code rows.
+  auto issue_stage = [&](int ks, int stage) {
+    uint8_t* sbase = smem + stage * STAGE;
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int g = wave * PER_WAVE + u;
+      const int r = g * 8 + (lane >> 3);
+      const bool isA = g * 8 < BM;
+      const int rr = isA ? r : r - BM;
+      const uint32_t off = (uint32_t)rr * (uint32_t)KB + (uint32_t)(ks * 128 + (((lane & 7) ^ swz32(r)) << 4));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rw, &sbase[g * 1024], 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = wave; u < SGROUPS; u += NW) {
+      const int e = u * 64 + lane;  // dword index in [row][SDW]
+      const int r = e / SDW, d = e % SDW;
+      const bool isA = (u * 64) / SDW < BM;  // wave-uniform: BM*SDW is a multiple of 64
+      const int rr = isA ? r : r - BM;
+      const uint32_t off = (uint32_t)rr * (uint32_t)SK + (uint32_t)(ks * SB + 4 * d);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rsa : rsw, &sbase[CODE_BYTES + u * 256], 4, off, 0, 0, 0);
+    }
+  };
+
+  typedef float v16f __attribute__((ext_vector_type(16)));
+  v16f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
+
+  issue_stage(0, 0);
+  for (int ks = 0; ks < nk; ++ks) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (ks + 1 < nk) issue_stage(ks + 1, (ks + 1) & 1);
+
+    const uint8_t* sA = smem + (ks & 1) * STAGE;
+    const uint8_t* sW = sA + BM * 128;
+    const uint32_t* sS = reinterpret_cast<const uint32_t*>(sA + CODE_BYTES);
+    // scale words: shift so byte 0 / byte 2 hold K-blocks q / 2+q of each dword
+    uint32_t scw[TI][SDW], sca[TJ][SDW];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int row = BM + wn * WTN + 32 * i + r32;
+#pragma unroll
+      for (int d = 0; d < SDW; ++d) scw[i][d] = sS[row * SDW + d] >> (8 * q);
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int row = wm * WTM + 32 * j + r32;
+#pragma unroll
+      for (int d = 0; d < SDW; ++d) sca[j][d] = sS[row * SDW + d] >> (8 * q);
+    }
+    uint4 fa[TJ][4];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int row = wm * WTM + 32 * j + r32;
+      const uint8_t* base = sA + row * 128;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) fa[j][c] = *reinterpret_cast<const uint4*>(base + (((2 * c + q) ^ swz32(row)) << 4));
+    }
+    static_for<TI>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      uint4 fw[4];
+      {
+        const int row = wn * WTN + 32 * i + r32;
+        const uint8_t* base = sW + row * 128;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) fw[c] = *reinterpret_cast<const uint4*>(base + (((2 * c + q) ^ swz32(row)) << 4));
+      }
+      static_for<NT>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        constexpr int D = (ELEM == 1) ? 0 : t / 2;           // scale dword
+        constexpr int OP = (ELEM == 1) ? 2 * t : 2 * (t % 2);  // byte within it
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          if constexpr (ELEM == 1) {
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                as_v8i(fw[2 * t], fw[2 * t + 1]), as_v8i(fa[j][2 * t], fa[j][2 * t + 1]), acc[i][j], FMT, FMT, OP,
+                (int)scw[i][D], OP, (int)sca[j][D]);
+          } else {
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_v8i_lo(fw[t]), as_v8i_lo(fa[j][t]),
+                                                                        acc[i][j], FMT, FMT, OP, (int)scw[i][D], OP,
+                                                                        (int)sca[j][D]);
+          }
+        }
+      });
+    });
+  }
+
+  // ---- epilogue: (+ bias) -> bf16 RNE -> global
+  const bool vec_ok = (N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int n = n0 + wn * WTN + 32 * i + 8 * g + 4 * q;
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (bias) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) bv[v] = (n + v < N) ? bf16_to_f32(bias[n + v]) : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int m = m0 + wm * WTM + 32 * j + r32;
+        if (m >= M) continue;
+        uint32_t h[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) h[v] = f32_to_bf16_rne(acc[i][j][4 * g + v] + bv[v]);
+        uint16_t* dst = out + (size_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (n + v < N) dst[v] = (uint16_t)h[v];
+        }
+      }
+    }
+  }
+}
+
+template <int ELEM, int BM, int BN, int WM, int WN>
+hipError_t launch_mx32(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as, const uint8_t* w,
+                       const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream) {
+  constexpr size_t lds = 2 * ((size_t)(BM + BN) * 128 + (size_t)(BM + BN) * (ELEM == 1 ? 4 : 8));
+  auto kern = mx32_gemm_kernel<ELEM, BM, BN, WM, WN>;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(64 * WM * WN), lds, stream, a, as, w, ws, bias, out, (int)M,
+                     (int)N, (int)K);
   return hipGetLastError();
 }
 
@@ -403,20 +634,42 @@ __global__ __launch_bounds__(256) void bf16_generic_kernel(const uint16_t* __res
 
 }  // namespace
 
+// Tile shapes (BM activation rows x BN weight rows, WM x WN waves).
+#ifndef MXQ_TILE_MX
+#define MXQ_TILE_MX 256, 256, 2, 2
+#endif
+#ifndef MXQ_TILE_NV4
+#define MXQ_TILE_NV4 128, 128, 2, 2
+#endif
+#ifndef MXQ_TILE_BF16
+#define MXQ_TILE_BF16 256, 256, 2, 2
+#endif
+
+#ifndef MXQ_TILE_MX32
+#define MXQ_TILE_MX32 256, 256, 2, 2
+#endif
+
 hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                           const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
                           const uint16_t* bias, uint16_t* out, hipStream_t stream) {
+  // whole 128-byte slabs per row and 4-byte aligned scale rows: the 32x32x64
+  // path with DMA-staged scales
+  const bool scales_aligned = (((uintptr_t)a_scales | (uintptr_t)w_scales) & 3) == 0;
+  if (elem == 1 && K % 128 == 0 && scales_aligned)
+    return launch_mx32<1, MXQ_TILE_MX32>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+  if (elem == 2 && K % 256 == 0 && scales_aligned)
+    return launch_mx32<2, MXQ_TILE_MX32>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
   if (elem == 1)
-    return launch_tiled<MX8, 128, 128, 2, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, nullptr, nullptr, bias,
+    return launch_tiled<MX8, MXQ_TILE_MX>(M, N, K, a_codes, a_scales, w_codes, w_scales, nullptr, nullptr, bias,
                                              out, stream);
-  return launch_tiled<MX4, 128, 128, 2, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, nullptr, nullptr, bias, out,
+  return launch_tiled<MX4, MXQ_TILE_MX>(M, N, K, a_codes, a_scales, w_codes, w_scales, nullptr, nullptr, bias, out,
                                            stream);
 }
 
 hipError_t launch_nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                              const float* a_ts, const uint8_t* w_codes, const uint8_t* w_scales,
                              const float* w_ts, const uint16_t* bias, uint16_t* out, hipStream_t stream) {
-  return launch_tiled<NV4, 128, 128, 2, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, a_ts, w_ts, bias, out,
+  return launch_tiled<NV4, MXQ_TILE_NV4>(M, N, K, a_codes, a_scales, w_codes, w_scales, a_ts, w_ts, bias, out,
                                            stream);
 }
 
@@ -440,7 +693,7 @@ hipError_t launch_bf16_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* a, 
                          (int)K, rows_per_wg);
     return hipGetLastError();
   }
-  return launch_tiled<BF16, 128, 128, 2, 2>(M, N, K, a, nullptr, w, nullptr, nullptr, nullptr, bias, out, stream);
+  return launch_tiled<BF16, MXQ_TILE_BF16>(M, N, K, a, nullptr, w, nullptr, nullptr, nullptr, bias, out, stream);
 }
 
 }  // namespace mxq
