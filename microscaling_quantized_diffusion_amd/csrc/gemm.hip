@@ -109,6 +109,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
+// LDS DMA of `bytes` per lane (lane i lands at lds + i * bytes).  Kept as a
+// plain device function: the builtin inside a generic lambda fails the host
+// pass's substitution and drops the kernel's launch stub.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, off, 0, 0, 0);
+}
+
 template <int MODE, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
@@ -553,6 +564,281 @@ hipError_t launch_mx32(int64_t M, int64_t N, int64_t K, const uint8_t* a, const 
   return hipGetLastError();
 }
 
+
+// ------------------------------------------------------------------------
+// MX main path: BM x 256 tile (BM = 128 or 256), four waves (2 x 2) with
+// fp32 accumulators, 32x32x64 scaled MFMA, and an NS-stage LDS ring of
+// 64-byte K slabs filled by LDS DMA NS-1 stages ahead of use.  Each stage
+// lives in its own __shared__ array (the K loop is unrolled by a multiple of
+// NS), so the compiler's DMA tracking waits only on the stage being read;
+// cross-wave visibility comes from an explicit vmcnt wait on the wave's own
+// DMA followed by a fence-free s_barrier.  Operand fragments are
+// double-buffered in registers: the fragments of stage k+1 are read while the
+// MFMAs of stage k issue.  One K stage holds one 32x32x64 FP8 MFMA or two FP4
+// MFMAs per output tile; in both formats lane (r, q) reads 16-byte chunks q
+// and 2+q of row r (swizzled by (r >> 2) & 3 for conflict-free 64-byte rows).
+// Scales: one dword per row per stage (FP4: K-blocks 4ks..4ks+3; FP8: the
+// dword of the stage pair, K-blocks 4(ks/2)..+3), staged with the codes.
+// With BM = 128 and NS = 3 a workgroup uses 78 KiB of LDS and 128
+// accumulators per lane, so two workgroups share a CU and one's epilogue and
+// pipeline fill overlap the other's MFMAs.
+// Requires K % 128 == 0 (MXFP8) or K % 256 == 0 (MXFP4) and 4-byte aligned
+// scale rows.
+__device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
+
+template <int ELEM, int BM, int NS, bool DB>
+__global__ __launch_bounds__(256, 2) void mxp_gemm_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
+    const uint8_t* __restrict__ Ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N,
+    int K) {
+  constexpr int BN = 256, WM = 2, WN = 2, NW = 4;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TJ = WTM / 32, TI = WTN / 32;  // 32 x 32 tiles per wave (M, N)
+  constexpr int ROWS = BM + BN;
+  constexpr int CODE_BYTES = ROWS * 64;
+  constexpr int SROWS = (ROWS + 255) / 256 * 256;  // scale rows rounded to whole DMA groups of all waves
+  constexpr int STAGE = CODE_BYTES + SROWS * 4;
+  constexpr int CGROUPS = CODE_BYTES / 1024;   // wave-wide 16-byte DMAs per stage
+  constexpr int SGROUPS = SROWS * 4 / 256;     // wave-wide 4-byte DMAs per stage
+  static_assert(CGROUPS % NW == 0 && SGROUPS % NW == 0, "groups");
+  static_assert(NS == 3 || NS == 4, "stages");
+  constexpr int CPW = CGROUPS / NW, SPW = SGROUPS / NW;
+  constexpr int PER_WAVE = CPW + SPW;          // VMEM instructions per wave per stage
+  constexpr int FMT = (ELEM == 1) ? 0 : 4;
+
+  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[NS == 4 ? STAGE : 16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int q = lane >> 5, r32 = lane & 31;
+
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const uint32_t id = xcd_contiguous_id(blockIdx.x, gridDim.x);
+  constexpr int GROUP = 8;
+  const int group = (int)(id / (uint32_t)(GROUP * tiles_n));
+  const int first_m = group * GROUP;
+  const int gsz = min(tiles_m - first_m, GROUP);
+  const int tm = first_m + (int)(id % (uint32_t)gsz);
+  const int tn = (int)((id % (uint32_t)(GROUP * tiles_n)) / (uint32_t)gsz);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int KB = (ELEM == 1) ? K : K / 2;
+  const int SK = K / 32;
+  const int nks = KB / 64;
+  const uint32_t rows_a = (uint32_t)min(BM, M - m0), rows_w = (uint32_t)min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * KB, rows_a * (uint32_t)KB);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * KB, rows_w * (uint32_t)KB);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(As + (size_t)m0 * SK, rows_a * (uint32_t)SK);
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(Ws + (size_t)n0 * SK, rows_w * (uint32_t)SK);
+
+  // per-lane DMA source offsets without the K-step term
+  uint32_t coff[CPW];
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) {
+    const int g = wave * CPW + u;
+    const int r = g * 16 + (lane >> 2);
+    const int rr = (g * 16 < BM) ? r : r - BM;
+    coff[u] = (uint32_t)rr * (uint32_t)KB + (uint32_t)(((lane & 3) ^ swz64(r)) << 4);
+  }
+  uint32_t soff[SPW];
+#pragma unroll
+  for (int u = 0; u < SPW; ++u) {
+    const int gi = wave * SPW + u;
+    const int r = gi * 64 + lane;
+    soff[u] = r < BM ? (uint32_t)r * (uint32_t)SK : r < ROWS ? (uint32_t)(r - BM) * (uint32_t)SK : kOutOfRange;
+  }
+  // `st` is one of the stage arrays, passed by reference so that the DMA
+  // builtin sees the __shared__ object itself
+  auto issue = [&](auto& st, int ks) {
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const int g = wave * CPW + u;
+      lds_dma16(g * 16 < BM ? ra : rw, &st[g * 1024], coff[u] + (uint32_t)(ks * 64));
+    }
+    const uint32_t sk = (ELEM == 1) ? (uint32_t)(4 * (ks >> 1)) : (uint32_t)(4 * ks);
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+      const int gi = wave * SPW + u;
+      // out-of-range scale rows carry offsets >= 2^31 and stay out of range
+      lds_dma4(gi * 64 < BM ? rsa : rsw, &st[CODE_BYTES + gi * 256], soff[u] + sk);
+    }
+  };
+
+  struct Frag {
+    uint4 a[TJ][2], w[TI][2];
+    uint32_t sa[TJ], sw[TI];
+  };
+  // one stage's operands (chunks q and 2+q of each row) and raw scale words;
+  // the scale bytes are selected at MFMA time so that nothing consumes these
+  // loads before the next step
+  auto read = [&](const auto& st, Frag& f) {
+    const uint32_t* ss = reinterpret_cast<const uint32_t*>(st + CODE_BYTES);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int row = wm * WTM + 32 * j + r32;
+      const uint8_t* b = st + row * 64;
+      f.a[j][0] = *reinterpret_cast<const uint4*>(b + ((q ^ swz64(row)) << 4));
+      f.a[j][1] = *reinterpret_cast<const uint4*>(b + (((2 + q) ^ swz64(row)) << 4));
+      f.sa[j] = ss[row];
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int row = BM + wn * WTN + 32 * i + r32;
+      const uint8_t* b = st + row * 64;
+      f.w[i][0] = *reinterpret_cast<const uint4*>(b + ((q ^ swz64(row)) << 4));
+      f.w[i][1] = *reinterpret_cast<const uint4*>(b + (((2 + q) ^ swz64(row)) << 4));
+      f.sw[i] = ss[row];
+    }
+  };
+
+  typedef float v16f __attribute__((ext_vector_type(16)));
+  v16f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
+
+  // MFMAs of one stage; FP8 stage ks takes byte 2*(ks&1)+q of the pair dword,
+  // FP4 bytes q (first MFMA) and 2+q (second)
+  auto compute = [&](const Frag& f, int ks) {
+    const int sh = (ELEM == 1) ? 8 * (2 * (ks & 1) + q) : 8 * q;
+    uint32_t sw[TI], sa[TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) sw[i] = f.sw[i] >> sh;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) sa[j] = f.sa[j] >> sh;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        if constexpr (ELEM == 1) {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_v8i(f.w[i][0], f.w[i][1]),
+                                                                      as_v8i(f.a[j][0], f.a[j][1]), acc[i][j], FMT,
+                                                                      FMT, 0, (int)sw[i], 0, (int)sa[j]);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_v8i_lo(f.w[i][0]), as_v8i_lo(f.a[j][0]),
+                                                                      acc[i][j], FMT, FMT, 0, (int)sw[i], 0,
+                                                                      (int)sa[j]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_v8i_lo(f.w[i][1]), as_v8i_lo(f.a[j][1]),
+                                                                      acc[i][j], FMT, FMT, 2, (int)sw[i], 2,
+                                                                      (int)sa[j]);
+        }
+      }
+    }
+  };
+
+  // the wave's own DMA of stage ks is complete when at most `pending`
+  // stages issued after it are still in flight
+  auto wait_own = [&](int pending) {
+    if (pending >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER_WAVE) : "memory");
+    else if (pending == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER_WAVE) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  // Stage arrays are always selected at compile time and passed by
+  // reference: an LDS address handed to the DMA builtin as a plain pointer
+  // value (runtime-selected, or returned from a helper) makes the host pass
+  // drop the kernel's launch stub.
+  auto slot = [&](auto ic) -> decltype(auto) {
+    constexpr int I = decltype(ic)::value;
+    if constexpr (I == 0) return (st0);
+    else if constexpr (I == 1) return (st1);
+    else if constexpr (I == 2) return (st2);
+    else return (st3);
+  };
+  // prologue: stages 0..NS-2 in flight
+  static_for<NS - 1>([&](auto ic) {
+    constexpr int I = decltype(ic)::value;
+    if (I < nks) issue(slot(ic), I);
+  });
+  Frag f0, f1;
+  if constexpr (DB) {  // stage 0 visible to every wave; its fragments read
+    wait_own(min(NS - 2, nks - 1));
+    __builtin_amdgcn_s_barrier();
+    read(st0, f0);
+  }
+
+  // one pipeline step for stage ks held in slot S (fragments in fc):
+  // own DMA of stage ks+1 done -> barrier -> DMA stage ks+NS-1 into slot of
+  // stage ks-1 (read by every wave one step ago) -> read stage ks+1 -> MFMAs
+  // of stage ks.  The read of the next slot is unconditional: past the last
+  // stage it reads stale, in-bounds LDS that is never used.
+  // Without register double buffering (DB = false): own DMA of stage ks
+  // done -> barrier -> DMA stage ks+NS-1 into the slot of stage ks-1 -> read
+  // stage ks -> MFMAs; the second workgroup on the CU covers the read latency.
+  auto step = [&](auto slot_c, int ks, Frag& fc, Frag& fn) {
+    constexpr int S = decltype(slot_c)::value;
+    const auto prev = std::integral_constant<int, (S + NS - 1) % NS>{};
+    if constexpr (DB) {
+      wait_own(min(NS - 3, nks - ks - 2));
+      __builtin_amdgcn_s_barrier();
+      if (ks + NS - 1 < nks) issue(slot(prev), ks + NS - 1);
+      read(slot(std::integral_constant<int, (S + 1) % NS>{}), fn);
+      compute(fc, ks);
+    } else {
+      wait_own(min(NS - 2, nks - ks - 1));
+      __builtin_amdgcn_s_barrier();
+      if (ks + NS - 1 < nks) issue(slot(prev), ks + NS - 1);
+      read(slot(slot_c), fc);
+      compute(fc, ks);
+    }
+  };
+  constexpr int UNROLL = (NS == 4) ? 4 : 6;  // multiple of NS and of the 2 fragment buffers
+  for (int ks = 0; ks < nks; ks += UNROLL) {
+    static_for<UNROLL>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      if (ks + u < nks) {
+        if constexpr (u % 2 == 0) step(std::integral_constant<int, u % NS>{}, ks + u, f0, f1);
+        else step(std::integral_constant<int, u % NS>{}, ks + u, f1, f0);
+      }
+    });
+  }
+
+  // ---- epilogue: (+ bias) -> bf16 RNE -> global
+  const bool vec_ok = (N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int n = n0 + wn * WTN + 32 * i + 8 * g + 4 * q;
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (bias) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) bv[v] = (n + v < N) ? bf16_to_f32(bias[n + v]) : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int m = m0 + wm * WTM + 32 * j + r32;
+        if (m >= M) continue;
+        uint32_t h[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) h[v] = f32_to_bf16_rne(acc[i][j][4 * g + v] + bv[v]);
+        uint16_t* dst = out + (size_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (n + v < N) dst[v] = (uint16_t)h[v];
+        }
+      }
+    }
+  }
+}
+
+template <int ELEM, int BM, int NS, bool DB>
+hipError_t launch_mxp(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as, const uint8_t* w,
+                      const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + 255) / 256);
+  hipLaunchKernelGGL((mxp_gemm_kernel<ELEM, BM, NS, DB>), dim3((unsigned)tiles), dim3(256), 0, stream, a, as, w, ws,
+                     bias, out, (int)M, (int)N, (int)K);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- skinny M
 // out[m, n] for M <= MMAX rows of activations: HBM-bound streaming of W.
 // The activations sit in LDS; each wave walks whole W rows, lanes split K in
@@ -646,7 +932,7 @@ __global__ __launch_bounds__(256) void bf16_generic_kernel(const uint16_t* __res
 #endif
 
 #ifndef MXQ_TILE_MX32
-#define MXQ_TILE_MX32 256, 256, 2, 2
+#define MXQ_TILE_MX32 256, 256, 4, 2
 #endif
 
 hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
@@ -655,6 +941,13 @@ hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8
   // whole 128-byte slabs per row and 4-byte aligned scale rows: the 32x32x64
   // path with DMA-staged scales
   const bool scales_aligned = (((uintptr_t)a_scales | (uintptr_t)w_scales) & 3) == 0;
+#ifndef MXQ_MXP
+#define MXQ_MXP 128, 3, false
+#endif
+  if (elem == 1 && K % 128 == 0 && scales_aligned)
+    return launch_mxp<1, MXQ_MXP>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+  if (elem == 2 && K % 256 == 0 && scales_aligned)
+    return launch_mxp<2, MXQ_MXP>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
   if (elem == 1 && K % 128 == 0 && scales_aligned)
     return launch_mx32<1, MXQ_TILE_MX32>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
   if (elem == 2 && K % 256 == 0 && scales_aligned)
