@@ -72,9 +72,7 @@ __device__ __forceinline__ v4f mfma_scaled(const v8i& a, const v8i& b, const v4f
 // XOR swizzles of the 16-byte chunk index by row, chosen by measurement on
 // gfx950 (SQ_LDS_BANK_CONFLICT = 0 for the operand read pattern):
 //   swz  : 16 consecutive rows read the same logical chunk (16x16 operands)
-//   swz32: 32 consecutive rows read the same logical chunk (32x32 operands)
 __device__ __forceinline__ int swz(int r) { return r & 7; }
-__device__ __forceinline__ int swz32(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ v8i as_v8i(const uint4& lo, const uint4& hi) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -119,6 +117,16 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, u
 __device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, off, 0, 0, 0);
 }
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  Issued through
+// the builtin rather than inline asm so that the compiler's own wait
+// bookkeeping sees it; an asm wait is invisible to it, and it then re-waits
+// on DMA that was issued after the asm wait.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 template <int MODE, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
@@ -140,7 +148,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // 2 stages x ROWS x 128 bytes
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wm = wave / WN, wn = wave % WN;
   const int q = lane >> 4, r16 = lane & 15;
 
@@ -227,7 +235,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
   for (int ks = 0; ks < nk; ++ks) {
     // stage ks&1 has landed for every wave, and every wave is done reading
     // stage (ks+1)&1 from the previous step
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmcnt<0>();
     __syncthreads();
     const bool more = ks + 1 < nk;
     if (more) issue_stage(ks + 1, (ks + 1) & 1);
@@ -364,257 +372,67 @@ hipError_t launch_tiled(int64_t M, int64_t N, int64_t K, const void* a, const ui
 
 
 // ------------------------------------------------------------------------
-// MX fast path: 32x32x64 scaled MFMA with codes and E8M0 scales staged
-// together by LDS DMA.  Requires K to be a multiple of one 128-byte code slab
-// (K % 128 == 0 for MXFP8, K % 256 == 0 for MXFP4) so that every K step holds
-// whole 4- or 8-byte scale groups per row.
-//
-// 32x32x64 operand layout (measured): lane l serves row l % 32 and K-half
-// q = l / 32 of a 64-wide K step;
-//   FP8: bytes 0-15 = K [16q, 16q+16), bytes 16-31 = K [32+16q, +16)
-//   FP4: bytes 0-15 = K [32q, 32q+32), low nibble first
-//   scale byte of lane l: K-block q of row l % 32.
-// A 128-byte slab row therefore feeds FP8 MFMA t (t = 0, 1) from chunks
-// (4t + q, 4t + 2 + q) with scale block 2t + q, and FP4 MFMA t (t = 0..3)
-// from chunk 2t + q with scale block 2t + q: every lane reads chunks
-// q, 2+q, 4+q, 6+q of each of its rows.  On gfx950 the FP4 rate doubles only
-// with this 32x32x64 shape (measured 9.2 vs 4.7 PFLOP/s register-only).
-// Output layout: lane l holds out^T[n = 8*(v/4) + 4*q + v%4][m = l % 32].
-template <int ELEM, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void mx32_gemm_kernel(
+// MX main path.  A BM x BN output tile per workgroup (default 256 x 256,
+// eight waves as 4 x 2, each 64 x 128 with fp32 accumulators), 32x32x64
+// scaled MFMA, and an NS-stage LDS ring of SLAB-byte K slabs (default two
+// stages of 128 bytes, i.e. 128 FP8 or 256 FP4 elements per row) filled by
+// LDS DMA.  Each stage lives in its own __shared__ array (the K loop is
+// unrolled by a multiple of NS), so the compiler's DMA tracking waits only on
+// the stage being read; cross-wave visibility comes from a vmcnt wait on the
+// wave's own DMA followed by a fence-free s_barrier.
+// Measured on gfx950: LDS-DMA throughput from L2 depends on the contiguous
+// bytes each instruction reads per row (32 B: 8, 64 B: 16, 128 B: 29 TB/s),
+// so 128-byte slabs (a whole cache line per row) beat deeper rings of 64-byte
+// slabs, and a 256 x 256 tile (128 MACs per staged byte) beats 128 x 256.
+// Per 64 K-bytes of a slab one 32x32x64 FP8 MFMA (two FP4 MFMAs) per 32 x 32
+// output tile; lane (r, q) reads 16-byte chunks 4h + q and 4h + 2 + q of row
+// r for each 64-byte half h of the slab (64-byte rows: swizzle (r >> 2) & 3,
+// 128-byte rows: (r >> 1) & 7, both conflict-free for this pattern).
+// Scales: one dword per row per 64 slab bytes (FP4: K-blocks 4c..4c+3 of
+// 64-byte chunk c; FP8: the dword of the chunk pair), staged with the codes.
+// PFD > 0 turns half of the waves into L2 prefetchers running PFD stages
+// ahead (measured slower on the FLUX shapes; kept as a tuning option).
+// Requires K % 128 == 0 (MXFP8) or K % 256 == 0 (MXFP4) and 4-byte aligned
+// scale rows.
+template <int ELEM, int BM, int BN, int WM, int WN, int NS, bool DB, int SLAB, int PFD>
+__global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1) void mxp_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
     const uint8_t* __restrict__ Ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N,
     int K) {
   constexpr int NW = WM * WN;
-  constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
-  constexpr int TJ = WTM / 32, TI = WTN / 32;  // 32x32 MFMA tiles per wave (M, N)
-  constexpr int ROWS = BM + BN;
-  constexpr int GROUPS = ROWS / 8;             // 1 KiB code groups per stage
-  static_assert(BM % 32 == 0 && BN % 32 == 0 && GROUPS % NW == 0, "tile/wave mismatch");
-  constexpr int PER_WAVE = GROUPS / NW;
-  constexpr int SB = (ELEM == 1) ? 4 : 8;      // scale bytes per row per K step
-  constexpr int SDW = SB / 4;                  // scale dwords per row per K step
-  constexpr int SGROUPS = ROWS * SDW / 64;     // wave-wide 4-byte scale loads per stage
-  static_assert((ROWS * SDW) % 64 == 0, "scale groups");
-  constexpr int CODE_BYTES = ROWS * 128;
-  constexpr int STAGE = CODE_BYTES + ROWS * SB;
-  constexpr int FMT = (ELEM == 1) ? 0 : 4;
-  constexpr int NT = (ELEM == 1) ? 2 : 4;      // MFMAs per 128-byte slab
-
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // 2 stages
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-  const int q = lane >> 5, r32 = lane & 31;
-
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const uint32_t id = xcd_contiguous_id(blockIdx.x, gridDim.x);
-  constexpr int GROUP = 8;
-  const int group = (int)(id / (uint32_t)(GROUP * tiles_n));
-  const int first_m = group * GROUP;
-  const int gsz = min(tiles_m - first_m, GROUP);
-  const int tm = first_m + (int)(id % (uint32_t)gsz);
-  const int tn = (int)((id % (uint32_t)(GROUP * tiles_n)) / (uint32_t)gsz);
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  const int KB = (ELEM == 1) ? K : K / 2;
-  const int SK = K / 32;
-  const int nk = KB / 128;
-  const uint32_t rows_a = (uint32_t)min(BM, M - m0), rows_w = (uint32_t)min(BN, N - n0);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * KB, rows_a * (uint32_t)KB);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * KB, rows_w * (uint32_t)KB);
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(As + (size_t)m0 * SK, rows_a * (uint32_t)SK);
-  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(Ws + (size_t)n0 * SK, rows_w * (uint32_t)SK);
-
-  // codes: LDS row r holds logical chunk (lane & 7) ^ swz32(r) in slot lane & 7;
-  // scales: [row][SDW] dwords after the code rows.
-  auto issue_stage = [&](int ks, int stage) {
-    uint8_t* sbase = smem + stage * STAGE;
-#pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) {
-      const int g = wave * PER_WAVE + u;
-      const int r = g * 8 + (lane >> 3);
-      const bool isA = g * 8 < BM;
-      const int rr = isA ? r : r - BM;
-      const uint32_t off = (uint32_t)rr * (uint32_t)KB + (uint32_t)(ks * 128 + (((lane & 7) ^ swz32(r)) << 4));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rw, &sbase[g * 1024], 16, off, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = wave; u < SGROUPS; u += NW) {
-      const int e = u * 64 + lane;  // dword index in [row][SDW]
-      const int r = e / SDW, d = e % SDW;
-      const bool isA = (u * 64) / SDW < BM;  // wave-uniform: BM*SDW is a multiple of 64
-      const int rr = isA ? r : r - BM;
-      const uint32_t off = (uint32_t)rr * (uint32_t)SK + (uint32_t)(ks * SB + 4 * d);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rsa : rsw, &sbase[CODE_BYTES + u * 256], 4, off, 0, 0, 0);
-    }
-  };
-
-  typedef float v16f __attribute__((ext_vector_type(16)));
-  v16f acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
-
-  issue_stage(0, 0);
-  for (int ks = 0; ks < nk; ++ks) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (ks + 1 < nk) issue_stage(ks + 1, (ks + 1) & 1);
-
-    const uint8_t* sA = smem + (ks & 1) * STAGE;
-    const uint8_t* sW = sA + BM * 128;
-    const uint32_t* sS = reinterpret_cast<const uint32_t*>(sA + CODE_BYTES);
-    // scale words: shift so byte 0 / byte 2 hold K-blocks q / 2+q of each dword
-    uint32_t scw[TI][SDW], sca[TJ][SDW];
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int row = BM + wn * WTN + 32 * i + r32;
-#pragma unroll
-      for (int d = 0; d < SDW; ++d) scw[i][d] = sS[row * SDW + d] >> (8 * q);
-    }
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int row = wm * WTM + 32 * j + r32;
-#pragma unroll
-      for (int d = 0; d < SDW; ++d) sca[j][d] = sS[row * SDW + d] >> (8 * q);
-    }
-    uint4 fa[TJ][4];
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int row = wm * WTM + 32 * j + r32;
-      const uint8_t* base = sA + row * 128;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) fa[j][c] = *reinterpret_cast<const uint4*>(base + (((2 * c + q) ^ swz32(row)) << 4));
-    }
-    static_for<TI>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      uint4 fw[4];
-      {
-        const int row = wn * WTN + 32 * i + r32;
-        const uint8_t* base = sW + row * 128;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) fw[c] = *reinterpret_cast<const uint4*>(base + (((2 * c + q) ^ swz32(row)) << 4));
-      }
-      static_for<NT>([&](auto tc) {
-        constexpr int t = decltype(tc)::value;
-        constexpr int D = (ELEM == 1) ? 0 : t / 2;           // scale dword
-        constexpr int OP = (ELEM == 1) ? 2 * t : 2 * (t % 2);  // byte within it
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          if constexpr (ELEM == 1) {
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                as_v8i(fw[2 * t], fw[2 * t + 1]), as_v8i(fa[j][2 * t], fa[j][2 * t + 1]), acc[i][j], FMT, FMT, OP,
-                (int)scw[i][D], OP, (int)sca[j][D]);
-          } else {
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_v8i_lo(fw[t]), as_v8i_lo(fa[j][t]),
-                                                                        acc[i][j], FMT, FMT, OP, (int)scw[i][D], OP,
-                                                                        (int)sca[j][D]);
-          }
-        }
-      });
-    });
-  }
-
-  // ---- epilogue: (+ bias) -> bf16 RNE -> global
-  const bool vec_ok = (N & 3) == 0;
-#pragma unroll
-  for (int i = 0; i < TI; ++i) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int n = n0 + wn * WTN + 32 * i + 8 * g + 4 * q;
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (bias) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) bv[v] = (n + v < N) ? bf16_to_f32(bias[n + v]) : 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int m = m0 + wm * WTM + 32 * j + r32;
-        if (m >= M) continue;
-        uint32_t h[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) h[v] = f32_to_bf16_rne(acc[i][j][4 * g + v] + bv[v]);
-        uint16_t* dst = out + (size_t)m * N + n;
-        if (vec_ok && n + 3 < N) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        } else {
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (n + v < N) dst[v] = (uint16_t)h[v];
-        }
-      }
-    }
-  }
-}
-
-template <int ELEM, int BM, int BN, int WM, int WN>
-hipError_t launch_mx32(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as, const uint8_t* w,
-                       const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream) {
-  constexpr size_t lds = 2 * ((size_t)(BM + BN) * 128 + (size_t)(BM + BN) * (ELEM == 1 ? 4 : 8));
-  auto kern = mx32_gemm_kernel<ELEM, BM, BN, WM, WN>;
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (attr != hipSuccess) return attr;
-  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(64 * WM * WN), lds, stream, a, as, w, ws, bias, out, (int)M,
-                     (int)N, (int)K);
-  return hipGetLastError();
-}
-
-
-// ------------------------------------------------------------------------
-// MX main path: BM x 256 tile (BM = 128 or 256), four waves (2 x 2) with
-// fp32 accumulators, 32x32x64 scaled MFMA, and an NS-stage LDS ring of
-// 64-byte K slabs filled by LDS DMA NS-1 stages ahead of use.  Each stage
-// lives in its own __shared__ array (the K loop is unrolled by a multiple of
-// NS), so the compiler's DMA tracking waits only on the stage being read;
-// cross-wave visibility comes from an explicit vmcnt wait on the wave's own
-// DMA followed by a fence-free s_barrier.  Operand fragments are
-// double-buffered in registers: the fragments of stage k+1 are read while the
-// MFMAs of stage k issue.  One K stage holds one 32x32x64 FP8 MFMA or two FP4
-// MFMAs per output tile; in both formats lane (r, q) reads 16-byte chunks q
-// and 2+q of row r (swizzled by (r >> 2) & 3 for conflict-free 64-byte rows).
-// Scales: one dword per row per stage (FP4: K-blocks 4ks..4ks+3; FP8: the
-// dword of the stage pair, K-blocks 4(ks/2)..+3), staged with the codes.
-// With BM = 128 and NS = 3 a workgroup uses 78 KiB of LDS and 128
-// accumulators per lane, so two workgroups share a CU and one's epilogue and
-// pipeline fill overlap the other's MFMAs.
-// Requires K % 128 == 0 (MXFP8) or K % 256 == 0 (MXFP4) and 4-byte aligned
-// scale rows.
-__device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
-
-template <int ELEM, int BM, int NS, bool DB>
-__global__ __launch_bounds__(256, 2) void mxp_gemm_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
-    const uint8_t* __restrict__ Ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N,
-    int K) {
-  constexpr int BN = 256, WM = 2, WN = 2, NW = 4;
+  constexpr int NDW = PFD > 0 ? NW / 2 : NW;   // waves that stage operands (the rest prefetch into L2)
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TJ = WTM / 32, TI = WTN / 32;  // 32 x 32 tiles per wave (M, N)
   constexpr int ROWS = BM + BN;
-  constexpr int CODE_BYTES = ROWS * 64;
-  constexpr int SROWS = (ROWS + 255) / 256 * 256;  // scale rows rounded to whole DMA groups of all waves
+  constexpr int H = SLAB / 64;                 // 64-byte halves per slab
+  constexpr int CPR = SLAB / 16;               // 16-byte chunks per row
+  constexpr int RPG = 64 / CPR;                // rows per wave-wide DMA
+  constexpr int CODE_BYTES = ROWS * SLAB;
+  constexpr int SROWS = (ROWS * H + 64 * NDW - 1) / (64 * NDW) * (64 * NDW);  // scale dwords: whole DMA groups of all waves
   constexpr int STAGE = CODE_BYTES + SROWS * 4;
   constexpr int CGROUPS = CODE_BYTES / 1024;   // wave-wide 16-byte DMAs per stage
   constexpr int SGROUPS = SROWS * 4 / 256;     // wave-wide 4-byte DMAs per stage
-  static_assert(CGROUPS % NW == 0 && SGROUPS % NW == 0, "groups");
-  static_assert(NS == 3 || NS == 4, "stages");
-  constexpr int CPW = CGROUPS / NW, SPW = SGROUPS / NW;
+  static_assert(CGROUPS % NDW == 0 && SGROUPS % NDW == 0, "groups");
+  static_assert(PFD == 0 || ROWS % (64 * (NW - NDW)) == 0, "prefetch rows");
+  static_assert(NS >= 2 && NS <= 4, "stages");
+  static_assert(!DB || NS >= 3, "register double buffering reads the next stage while the one after is in flight");
+  static_assert(BM % (64 / H) == 0 && BM % RPG == 0, "a DMA group never straddles the A/W boundary");
+  constexpr int CPW = CGROUPS / NDW, SPW = SGROUPS / NDW;
   constexpr int PER_WAVE = CPW + SPW;          // VMEM instructions per wave per stage
   constexpr int FMT = (ELEM == 1) ? 0 : 4;
 
   __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[NS >= 3 ? STAGE : 16];
   __shared__ __attribute__((aligned(16))) uint8_t st3[NS == 4 ? STAGE : 16];
+  // landing area of the L2 prefetches (never read)
+  __shared__ __attribute__((aligned(16))) uint8_t pfd[PFD > 0 ? 256 * (NW - NDW) : 16];
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wm = wave / WN, wn = wave % WN;
   const int q = lane >> 5, r32 = lane & 31;
+  auto swzr = [](int r) { return SLAB == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7); };
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const uint32_t id = xcd_contiguous_id(blockIdx.x, gridDim.x);
@@ -628,7 +446,7 @@ __global__ __launch_bounds__(256, 2) void mxp_gemm_kernel(
 
   const int KB = (ELEM == 1) ? K : K / 2;
   const int SK = K / 32;
-  const int nks = KB / 64;
+  const int nks = KB / SLAB;
   const uint32_t rows_a = (uint32_t)min(BM, M - m0), rows_w = (uint32_t)min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * KB, rows_a * (uint32_t)KB);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * KB, rows_w * (uint32_t)KB);
@@ -639,17 +457,21 @@ __global__ __launch_bounds__(256, 2) void mxp_gemm_kernel(
   uint32_t coff[CPW];
 #pragma unroll
   for (int u = 0; u < CPW; ++u) {
-    const int g = wave * CPW + u;
-    const int r = g * 16 + (lane >> 2);
-    const int rr = (g * 16 < BM) ? r : r - BM;
-    coff[u] = (uint32_t)rr * (uint32_t)KB + (uint32_t)(((lane & 3) ^ swz64(r)) << 4);
+    const int g = (wave % NDW) * CPW + u;
+    const int r = g * RPG + lane / CPR;
+    const int rr = (g * RPG < BM) ? r : r - BM;
+    coff[u] = (uint32_t)rr * (uint32_t)KB + (uint32_t)(((lane % CPR) ^ swzr(r)) << 4);
   }
+  // scale dword e = row * H + h (h = 64-byte half of the slab)
   uint32_t soff[SPW];
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
-    const int gi = wave * SPW + u;
-    const int r = gi * 64 + lane;
-    soff[u] = r < BM ? (uint32_t)r * (uint32_t)SK : r < ROWS ? (uint32_t)(r - BM) * (uint32_t)SK : kOutOfRange;
+    const int e = ((wave % NDW) * SPW + u) * 64 + lane;
+    const int r = e / H, h = e % H;
+    // FP8 with 128-byte slabs: both halves use the dword of their chunk pair
+    const uint32_t hoff = (ELEM == 1 && SLAB == 128) ? 0u : (uint32_t)(4 * h);
+    soff[u] = r < BM ? (uint32_t)r * (uint32_t)SK + hoff
+            : r < ROWS ? (uint32_t)(r - BM) * (uint32_t)SK + hoff : kOutOfRange;
   }
   // `st` is one of the stage arrays, passed by reference so that the DMA
   // builtin sees the __shared__ object itself
@@ -657,42 +479,65 @@ __global__ __launch_bounds__(256, 2) void mxp_gemm_kernel(
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
       const int g = wave * CPW + u;
-      lds_dma16(g * 16 < BM ? ra : rw, &st[g * 1024], coff[u] + (uint32_t)(ks * 64));
+      lds_dma16(g * RPG < BM ? ra : rw, &st[g * 1024], coff[u] + (uint32_t)(ks * SLAB));
     }
-    const uint32_t sk = (ELEM == 1) ? (uint32_t)(4 * (ks >> 1)) : (uint32_t)(4 * ks);
+    // 64-byte chunk c = ks*H + h: FP4 dword 4c, FP8 dword 4*(c/2) (pair)
+    const uint32_t sk = (ELEM == 1) ? (SLAB == 64 ? (uint32_t)(4 * (ks >> 1)) : (uint32_t)(4 * ks))
+                                    : (uint32_t)(4 * H * ks);
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
       const int gi = wave * SPW + u;
       // out-of-range scale rows carry offsets >= 2^31 and stay out of range
-      lds_dma4(gi * 64 < BM ? rsa : rsw, &st[CODE_BYTES + gi * 256], soff[u] + sk);
+      lds_dma4((gi * 64) / H < BM ? rsa : rsw, &st[CODE_BYTES + gi * 256], soff[u] + sk);
+    }
+  };
+  // L2 prefetch of stage ks by the waves that stage nothing: one dword per
+  // row and slab, landing in a scratch LDS area.  These waves never wait on
+  // them inside the K loop, so up to PFD stages of misses overlap the
+  // MFMAs; the staging DMA of that stage then hits L2.
+  constexpr int PF_ROWS = PFD > 0 ? ROWS / (NW - NDW) : 64;
+  auto prefetch = [&](int ks) {
+    const int p = wave - NDW;
+#pragma unroll
+    for (int u = 0; u < PF_ROWS / 64; ++u) {
+      const int r0 = p * PF_ROWS + u * 64;
+      const int rr = (r0 < BM ? r0 : r0 - BM) + lane;
+      lds_dma4(r0 < BM ? ra : rw, &pfd[p * 256], (uint32_t)rr * (uint32_t)KB + (uint32_t)(ks * SLAB));
     }
   };
 
-  struct Frag {
+  // operands of one 64-byte half of a slab, with raw scale words; the scale
+  // bytes are selected at MFMA time so that nothing consumes these loads
+  // before the MFMAs
+  struct Half {
     uint4 a[TJ][2], w[TI][2];
     uint32_t sa[TJ], sw[TI];
   };
-  // one stage's operands (chunks q and 2+q of each row) and raw scale words;
-  // the scale bytes are selected at MFMA time so that nothing consumes these
-  // loads before the next step
-  auto read = [&](const auto& st, Frag& f) {
+  struct Frag {
+    Half h[H];
+  };
+  auto read_half = [&](const auto& st, Half& f, int h) {
     const uint32_t* ss = reinterpret_cast<const uint32_t*>(st + CODE_BYTES);
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int row = wm * WTM + 32 * j + r32;
-      const uint8_t* b = st + row * 64;
-      f.a[j][0] = *reinterpret_cast<const uint4*>(b + ((q ^ swz64(row)) << 4));
-      f.a[j][1] = *reinterpret_cast<const uint4*>(b + (((2 + q) ^ swz64(row)) << 4));
-      f.sa[j] = ss[row];
+      const uint8_t* b = st + row * SLAB;
+      f.a[j][0] = *reinterpret_cast<const uint4*>(b + (((4 * h + q) ^ swzr(row)) << 4));
+      f.a[j][1] = *reinterpret_cast<const uint4*>(b + (((4 * h + 2 + q) ^ swzr(row)) << 4));
+      f.sa[j] = ss[row * H + h];
     }
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int row = BM + wn * WTN + 32 * i + r32;
-      const uint8_t* b = st + row * 64;
-      f.w[i][0] = *reinterpret_cast<const uint4*>(b + ((q ^ swz64(row)) << 4));
-      f.w[i][1] = *reinterpret_cast<const uint4*>(b + (((2 + q) ^ swz64(row)) << 4));
-      f.sw[i] = ss[row];
+      const uint8_t* b = st + row * SLAB;
+      f.w[i][0] = *reinterpret_cast<const uint4*>(b + (((4 * h + q) ^ swzr(row)) << 4));
+      f.w[i][1] = *reinterpret_cast<const uint4*>(b + (((4 * h + 2 + q) ^ swzr(row)) << 4));
+      f.sw[i] = ss[row * H + h];
     }
+  };
+  auto read = [&](const auto& st, Frag& f) {
+#pragma unroll
+    for (int h = 0; h < H; ++h) read_half(st, f.h[h], h);
   };
 
   typedef float v16f __attribute__((ext_vector_type(16)));
@@ -702,10 +547,11 @@ __global__ __launch_bounds__(256, 2) void mxp_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
 
-  // MFMAs of one stage; FP8 stage ks takes byte 2*(ks&1)+q of the pair dword,
-  // FP4 bytes q (first MFMA) and 2+q (second)
-  auto compute = [&](const Frag& f, int ks) {
-    const int sh = (ELEM == 1) ? 8 * (2 * (ks & 1) + q) : 8 * q;
+  // MFMAs of one half-slab.  64-byte chunk c = ks*H + h: FP8 takes byte
+  // 2*(c&1)+q of its pair dword, FP4 bytes q (first MFMA) and 2+q (second).
+  auto compute_half = [&](const Half& f, int ks, int h) {
+    const int c = ks * H + h;
+    const int sh = (ELEM == 1) ? 8 * (2 * (c & 1) + q) : 8 * q;
     uint32_t sw[TI], sa[TJ];
 #pragma unroll
     for (int i = 0; i < TI; ++i) sw[i] = f.sw[i] >> sh;
@@ -716,27 +562,29 @@ __global__ __launch_bounds__(256, 2) void mxp_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         if constexpr (ELEM == 1) {
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_v8i(f.w[i][0], f.w[i][1]),
-                                                                      as_v8i(f.a[j][0], f.a[j][1]), acc[i][j], FMT,
-                                                                      FMT, 0, (int)sw[i], 0, (int)sa[j]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              as_v8i(f.w[i][0], f.w[i][1]), as_v8i(f.a[j][0], f.a[j][1]), acc[i][j], FMT, FMT, 0, (int)sw[i], 0,
+              (int)sa[j]);
         } else {
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_v8i_lo(f.w[i][0]), as_v8i_lo(f.a[j][0]),
-                                                                      acc[i][j], FMT, FMT, 0, (int)sw[i], 0,
-                                                                      (int)sa[j]);
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_v8i_lo(f.w[i][1]), as_v8i_lo(f.a[j][1]),
-                                                                      acc[i][j], FMT, FMT, 2, (int)sw[i], 2,
-                                                                      (int)sa[j]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              as_v8i_lo(f.w[i][0]), as_v8i_lo(f.a[j][0]), acc[i][j], FMT, FMT, 0, (int)sw[i], 0, (int)sa[j]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              as_v8i_lo(f.w[i][1]), as_v8i_lo(f.a[j][1]), acc[i][j], FMT, FMT, 2, (int)sw[i], 2, (int)sa[j]);
         }
       }
     }
   };
+  auto compute = [&](const Frag& f, int ks) {
+#pragma unroll
+    for (int h = 0; h < H; ++h) compute_half(f.h[h], ks, h);
+  };
 
-  // the wave's own DMA of stage ks is complete when at most `pending`
-  // stages issued after it are still in flight
+  // the wave's own DMA of a stage is complete when at most `pending` stages
+  // issued after it are still in flight
   auto wait_own = [&](int pending) {
-    if (pending >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER_WAVE) : "memory");
-    else if (pending == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER_WAVE) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (pending >= 2) wait_vmcnt<2 * PER_WAVE < 64 ? 2 * PER_WAVE : 0>();
+    else if (pending == 1) wait_vmcnt<PER_WAVE>();
+    else wait_vmcnt<0>();
   };
 
   // Stage arrays are always selected at compile time and passed by
@@ -750,53 +598,79 @@ __global__ __launch_bounds__(256, 2) void mxp_gemm_kernel(
     else if constexpr (I == 2) return (st2);
     else return (st3);
   };
-  // prologue: stages 0..NS-2 in flight
-  static_for<NS - 1>([&](auto ic) {
-    constexpr int I = decltype(ic)::value;
-    if (I < nks) issue(slot(ic), I);
-  });
-  Frag f0, f1;
-  if constexpr (DB) {  // stage 0 visible to every wave; its fragments read
-    wait_own(min(NS - 2, nks - 1));
-    __builtin_amdgcn_s_barrier();
-    read(st0, f0);
-  }
-
-  // one pipeline step for stage ks held in slot S (fragments in fc):
-  // own DMA of stage ks+1 done -> barrier -> DMA stage ks+NS-1 into slot of
-  // stage ks-1 (read by every wave one step ago) -> read stage ks+1 -> MFMAs
-  // of stage ks.  The read of the next slot is unconditional: past the last
-  // stage it reads stale, in-bounds LDS that is never used.
-  // Without register double buffering (DB = false): own DMA of stage ks
-  // done -> barrier -> DMA stage ks+NS-1 into the slot of stage ks-1 -> read
-  // stage ks -> MFMAs; the second workgroup on the CU covers the read latency.
-  auto step = [&](auto slot_c, int ks, Frag& fc, Frag& fn) {
-    constexpr int S = decltype(slot_c)::value;
-    const auto prev = std::integral_constant<int, (S + NS - 1) % NS>{};
-    if constexpr (DB) {
-      wait_own(min(NS - 3, nks - ks - 2));
-      __builtin_amdgcn_s_barrier();
-      if (ks + NS - 1 < nks) issue(slot(prev), ks + NS - 1);
-      read(slot(std::integral_constant<int, (S + 1) % NS>{}), fn);
-      compute(fc, ks);
+  // The K loop, instantiated separately for the staging waves and the
+  // prefetching waves so that the compiler's own wait bookkeeping in the
+  // latter never sees staging DMA and never waits on the prefetches.
+  auto run = [&](auto pf_c) {
+    constexpr bool PFW = decltype(pf_c)::value;
+    // prologue: stages 0..NS-2 in flight (prefetchers: the PFD stages after)
+    if constexpr (!PFW) {
+      static_for<NS - 1>([&](auto ic) {
+        constexpr int I = decltype(ic)::value;
+        if (I < nks) issue(slot(ic), I);
+      });
     } else {
-      wait_own(min(NS - 2, nks - ks - 1));
-      __builtin_amdgcn_s_barrier();
-      if (ks + NS - 1 < nks) issue(slot(prev), ks + NS - 1);
-      read(slot(slot_c), fc);
-      compute(fc, ks);
+      static_for<PFD>([&](auto ic) {
+        constexpr int I = decltype(ic)::value;
+        if (NS - 1 + I < nks) prefetch(NS - 1 + I);
+      });
     }
-  };
-  constexpr int UNROLL = (NS == 4) ? 4 : 6;  // multiple of NS and of the 2 fragment buffers
-  for (int ks = 0; ks < nks; ks += UNROLL) {
-    static_for<UNROLL>([&](auto uc) {
-      constexpr int u = decltype(uc)::value;
-      if (ks + u < nks) {
-        if constexpr (u % 2 == 0) step(std::integral_constant<int, u % NS>{}, ks + u, f0, f1);
-        else step(std::integral_constant<int, u % NS>{}, ks + u, f1, f0);
+    Frag f0, f1;
+    if constexpr (DB) {  // stage 0 visible to every wave; its fragments read
+      if constexpr (!PFW) wait_own(min(NS - 2, nks - 1));
+      __builtin_amdgcn_s_barrier();
+      read(st0, f0);
+    }
+
+    // With register double buffering (DB): own DMA of stage ks+1 done ->
+    // barrier -> DMA stage ks+NS-1 into the slot of stage ks-1 (read by
+    // every wave one step ago) -> read stage ks+1 -> MFMAs of stage ks; the
+    // read of the next slot is unconditional (past the last stage it reads
+    // stale, in-bounds LDS that is never used).  Without (DB = false): own
+    // DMA of stage ks done -> barrier -> DMA stage ks+NS-1 into the slot of
+    // stage ks-1 -> read stage ks -> MFMAs.  Prefetchers replace the DMA
+    // with the L2 prefetch of stage ks+NS-1+PFD and have nothing to wait on.
+    auto step = [&](auto slot_c, int ks, Frag& fc, Frag& fn) {
+      constexpr int S = decltype(slot_c)::value;
+      const auto prev = std::integral_constant<int, (S + NS - 1) % NS>{};
+      if constexpr (!PFW) wait_own(DB ? min(NS - 3, nks - ks - 2) : min(NS - 2, nks - ks - 1));
+      __builtin_amdgcn_s_barrier();
+      if constexpr (!PFW) {
+        if (ks + NS - 1 < nks) issue(slot(prev), ks + NS - 1);
+      } else {
+        if (ks + NS - 1 + PFD < nks) prefetch(ks + NS - 1 + PFD);
       }
-    });
-  }
+      if constexpr (DB) {
+        read(slot(std::integral_constant<int, (S + 1) % NS>{}), fn);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(fc, ks);
+      } else {
+        // each half's reads all ahead of its first MFMA: one LDS round trip
+        // per half instead of one per reused operand register
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+          read_half(slot(slot_c), fc.h[0], h);
+          __builtin_amdgcn_sched_barrier(0);
+          compute_half(fc.h[0], ks, h);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    constexpr int UNROLL = (NS == 4) ? 4 : (NS == 3) ? 6 : 2;  // multiple of NS and of the 2 fragment buffers
+    for (int ks = 0; ks < nks; ks += UNROLL) {
+      static_for<UNROLL>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if (ks + u < nks) {
+          if constexpr (u % 2 == 0) step(std::integral_constant<int, u % NS>{}, ks + u, f0, f1);
+          else step(std::integral_constant<int, u % NS>{}, ks + u, f1, f0);
+        }
+      });
+    }
+    // drain the prefetches before this workgroup's LDS can be handed on
+    if constexpr (PFW) wait_vmcnt<0>();
+  };
+  if (PFD > 0 && wave >= NDW) run(std::true_type{});
+  else run(std::false_type{});
 
   // ---- epilogue: (+ bias) -> bf16 RNE -> global
   const bool vec_ok = (N & 3) == 0;
@@ -814,28 +688,29 @@ __global__ __launch_bounds__(256, 2) void mxp_gemm_kernel(
       for (int j = 0; j < TJ; ++j) {
         const int m = m0 + wm * WTM + 32 * j + r32;
         if (m >= M) continue;
-        uint32_t h[4];
+        uint32_t hv[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) h[v] = f32_to_bf16_rne(acc[i][j][4 * g + v] + bv[v]);
+        for (int v = 0; v < 4; ++v) hv[v] = f32_to_bf16_rne(acc[i][j][4 * g + v] + bv[v]);
         uint16_t* dst = out + (size_t)m * N + n;
         if (vec_ok && n + 3 < N) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+          *reinterpret_cast<uint2*>(dst) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
         } else {
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            if (n + v < N) dst[v] = (uint16_t)h[v];
+            if (n + v < N) dst[v] = (uint16_t)hv[v];
         }
       }
     }
   }
 }
 
-template <int ELEM, int BM, int NS, bool DB>
+template <int ELEM, int BM, int BN, int WM, int WN, int NS, bool DB, int SLAB, int PFD>
 hipError_t launch_mxp(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as, const uint8_t* w,
                       const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream) {
-  const int64_t tiles = ((M + BM - 1) / BM) * ((N + 255) / 256);
-  hipLaunchKernelGGL((mxp_gemm_kernel<ELEM, BM, NS, DB>), dim3((unsigned)tiles), dim3(256), 0, stream, a, as, w, ws,
-                     bias, out, (int)M, (int)N, (int)K);
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL((mxp_gemm_kernel<ELEM, BM, BN, WM, WN, NS, DB, SLAB, PFD>), dim3((unsigned)tiles), dim3(64 * WM * WN),
+                     0, stream, a, as, w,
+                     ws, bias, out, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
@@ -931,9 +806,6 @@ __global__ __launch_bounds__(256) void bf16_generic_kernel(const uint16_t* __res
 #define MXQ_TILE_BF16 256, 256, 2, 2
 #endif
 
-#ifndef MXQ_TILE_MX32
-#define MXQ_TILE_MX32 256, 256, 4, 2
-#endif
 
 hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                           const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
@@ -942,16 +814,12 @@ hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8
   // path with DMA-staged scales
   const bool scales_aligned = (((uintptr_t)a_scales | (uintptr_t)w_scales) & 3) == 0;
 #ifndef MXQ_MXP
-#define MXQ_MXP 128, 3, false
+#define MXQ_MXP 256, 256, 4, 2, 2, false, 128, 0
 #endif
   if (elem == 1 && K % 128 == 0 && scales_aligned)
     return launch_mxp<1, MXQ_MXP>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
   if (elem == 2 && K % 256 == 0 && scales_aligned)
     return launch_mxp<2, MXQ_MXP>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
-  if (elem == 1 && K % 128 == 0 && scales_aligned)
-    return launch_mx32<1, MXQ_TILE_MX32>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
-  if (elem == 2 && K % 256 == 0 && scales_aligned)
-    return launch_mx32<2, MXQ_TILE_MX32>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
   if (elem == 1)
     return launch_tiled<MX8, MXQ_TILE_MX>(M, N, K, a_codes, a_scales, w_codes, w_scales, nullptr, nullptr, bias,
                                              out, stream);
