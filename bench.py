@@ -167,6 +167,9 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time the other FLUX-shaped workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, run three plain device-to-device copies of MIB MiB (the reference kernel "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path runs on a single "
@@ -206,7 +209,7 @@ def main():
         "pct_of_mfma_peak": round(r["pct_peak_fused"], 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": f"gemm_kernel<{layer.fmt}>",
+            "kernel": f"mxp_gemm_kernel<{'FP8' if layer.fmt == 'mxfp8' else 'FP4'}, 256x256>",
             "achieved": round(flops / gemm_s / 1e12, 2),
             "peak": PEAK_TFLOPS[layer.fmt],
             "unit": "TFLOP/s",
@@ -228,6 +231,15 @@ def main():
                 e["workload"] = name
                 extra.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in e.items()})
         line["extra"] = extra
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copied {n} bytes three times", file=sys.stderr, flush=True)
+        del src, dst
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(layer, args.cpu_rows)

@@ -127,6 +127,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
 }
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (0x7 << 4)); }
 
 template <int MODE, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
@@ -415,7 +417,7 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
   static_assert(CGROUPS % NDW == 0 && SGROUPS % NDW == 0, "groups");
   static_assert(PFD == 0 || ROWS % (64 * (NW - NDW)) == 0, "prefetch rows");
   static_assert(NS >= 2 && NS <= 4, "stages");
-  static_assert(!DB || NS >= 3, "register double buffering reads the next stage while the one after is in flight");
+
   static_assert(BM % (64 / H) == 0 && BM % RPG == 0, "a DMA group never straddles the A/W boundary");
   constexpr int CPW = CGROUPS / NDW, SPW = SGROUPS / NDW;
   constexpr int PER_WAVE = CPW + SPW;          // VMEM instructions per wave per stage
@@ -578,11 +580,67 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
 #pragma unroll
     for (int h = 0; h < H; ++h) compute_half(f.h[h], ks, h);
   };
+  // One half-slab with the W tiles streamed through two register slots:
+  // the A tiles and W tile 0 are read first, then the reads of W tile i+1
+  // are placed ahead of the MFMAs of W tile i (sched_group_barrier), so the
+  // wave's own LDS reads overlap its MFMAs.  Each lane reads its scale bytes
+  // directly (byte loads), so no VALU work sits between a read and its MFMA:
+  // 64-byte chunk c = ks*H + h, FP8 byte 2*(c&1)+q of the pair dword, FP4
+  // bytes q and 2+q.
+  auto stream_half = [&](const auto& st, int ks, int h) {
+    const uint8_t* sb = st + CODE_BYTES;
+    const int c = ks * H + h;
+    const int b0 = (ELEM == 1) ? 2 * (c & 1) + q : q;
+    constexpr int NSC = (ELEM == 1) ? 1 : 2;  // scale bytes per row and MFMA group
+    uint4 a[TJ][2], w[2][2];
+    uint32_t sa[TJ][NSC], sw[2][NSC];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int row = wm * WTM + 32 * j + r32;
+      const uint8_t* b = st + row * SLAB;
+      a[j][0] = *reinterpret_cast<const uint4*>(b + (((4 * h + q) ^ swzr(row)) << 4));
+      a[j][1] = *reinterpret_cast<const uint4*>(b + (((4 * h + 2 + q) ^ swzr(row)) << 4));
+#pragma unroll
+      for (int e = 0; e < NSC; ++e) sa[j][e] = sb[(row * H + h) * 4 + b0 + 2 * e];
+    }
+    auto read_w = [&](int i, int slot_i) {
+      const int row = BM + wn * WTN + 32 * i + r32;
+      const uint8_t* b = st + row * SLAB;
+      w[slot_i][0] = *reinterpret_cast<const uint4*>(b + (((4 * h + q) ^ swzr(row)) << 4));
+      w[slot_i][1] = *reinterpret_cast<const uint4*>(b + (((4 * h + 2 + q) ^ swzr(row)) << 4));
+#pragma unroll
+      for (int e = 0; e < NSC; ++e) sw[slot_i][e] = sb[(row * H + h) * 4 + b0 + 2 * e];
+    };
+    read_w(0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, (2 + NSC) * (TJ + 1), 0);
+    static_for<TI>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + 1 < TI) read_w(i + 1, (i + 1) & 1);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        if constexpr (ELEM == 1) {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              as_v8i(w[i & 1][0], w[i & 1][1]), as_v8i(a[j][0], a[j][1]), acc[i][j], FMT, FMT, 0,
+              (int)sw[i & 1][0], 0, (int)sa[j][0]);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              as_v8i_lo(w[i & 1][0]), as_v8i_lo(a[j][0]), acc[i][j], FMT, FMT, 0, (int)sw[i & 1][0], 0,
+              (int)sa[j][0]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              as_v8i_lo(w[i & 1][1]), as_v8i_lo(a[j][1]), acc[i][j], FMT, FMT, 0, (int)sw[i & 1][1], 0,
+              (int)sa[j][1]);
+        }
+      }
+      if constexpr (i + 1 < TI) __builtin_amdgcn_sched_group_barrier(0x100, 2 + NSC, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, ELEM == 1 ? TJ : 2 * TJ, 0);
+    });
+  };
 
   // the wave's own DMA of a stage is complete when at most `pending` stages
   // issued after it are still in flight
   auto wait_own = [&](int pending) {
-    if (pending >= 2) wait_vmcnt<2 * PER_WAVE < 64 ? 2 * PER_WAVE : 0>();
+    if (pending >= 3) wait_vmcnt<3 * PER_WAVE < 64 ? 3 * PER_WAVE : 0>();
+    else if (pending == 2) wait_vmcnt<2 * PER_WAVE < 64 ? 2 * PER_WAVE : 0>();
     else if (pending == 1) wait_vmcnt<PER_WAVE>();
     else wait_vmcnt<0>();
   };
@@ -603,68 +661,54 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
   // latter never sees staging DMA and never waits on the prefetches.
   auto run = [&](auto pf_c) {
     constexpr bool PFW = decltype(pf_c)::value;
-    // prologue: stages 0..NS-2 in flight (prefetchers: the PFD stages after)
-    if constexpr (!PFW) {
-      static_for<NS - 1>([&](auto ic) {
-        constexpr int I = decltype(ic)::value;
-        if (I < nks) issue(slot(ic), I);
-      });
-    } else {
-      static_for<PFD>([&](auto ic) {
-        constexpr int I = decltype(ic)::value;
-        if (NS - 1 + I < nks) prefetch(NS - 1 + I);
-      });
-    }
-    Frag f0, f1;
-    if constexpr (DB) {  // stage 0 visible to every wave; its fragments read
-      if constexpr (!PFW) wait_own(min(NS - 2, nks - 1));
-      __builtin_amdgcn_s_barrier();
-      read(st0, f0);
-    }
-
-    // With register double buffering (DB): own DMA of stage ks+1 done ->
-    // barrier -> DMA stage ks+NS-1 into the slot of stage ks-1 (read by
-    // every wave one step ago) -> read stage ks+1 -> MFMAs of stage ks; the
-    // read of the next slot is unconditional (past the last stage it reads
-    // stale, in-bounds LDS that is never used).  Without (DB = false): own
-    // DMA of stage ks done -> barrier -> DMA stage ks+NS-1 into the slot of
-    // stage ks-1 -> read stage ks -> MFMAs.  Prefetchers replace the DMA
-    // with the L2 prefetch of stage ks+NS-1+PFD and have nothing to wait on.
-    auto step = [&](auto slot_c, int ks, Frag& fc, Frag& fn) {
-      constexpr int S = decltype(slot_c)::value;
-      const auto prev = std::integral_constant<int, (S + NS - 1) % NS>{};
-      if constexpr (!PFW) wait_own(DB ? min(NS - 3, nks - ks - 2) : min(NS - 2, nks - ks - 1));
-      __builtin_amdgcn_s_barrier();
+    {
+      // prologue: stages 0..NS-2 in flight (prefetchers: the PFD stages after)
       if constexpr (!PFW) {
-        if (ks + NS - 1 < nks) issue(slot(prev), ks + NS - 1);
+        static_for<NS - 1>([&](auto ic) {
+          constexpr int I = decltype(ic)::value;
+          if (I < nks) issue(slot(ic), I);
+        });
       } else {
-        if (ks + NS - 1 + PFD < nks) prefetch(ks + NS - 1 + PFD);
+        static_for<PFD>([&](auto ic) {
+          constexpr int I = decltype(ic)::value;
+          if (NS - 1 + I < nks) prefetch(NS - 1 + I);
+        });
       }
-      if constexpr (DB) {
-        read(slot(std::integral_constant<int, (S + 1) % NS>{}), fn);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(fc, ks);
-      } else {
+      Frag f;
+      // own DMA of stage ks done -> barrier -> DMA stage ks+NS-1 into the
+      // slot of stage ks-1 (read by every wave one step ago) -> read stage
+      // ks -> MFMAs.  Prefetchers replace the DMA with the L2 prefetch of
+      // stage ks+NS-1+PFD and have nothing to wait on.
+      auto step = [&](auto slot_c, int ks) {
+        constexpr int S = decltype(slot_c)::value;
+        const auto prev = std::integral_constant<int, (S + NS - 1) % NS>{};
+        if constexpr (!PFW) wait_own(min(NS - 2, nks - ks - 1));
+        __builtin_amdgcn_s_barrier();
+        if constexpr (!PFW) {
+          if (ks + NS - 1 < nks) issue(slot(prev), ks + NS - 1);
+        } else {
+          if (ks + NS - 1 + PFD < nks) prefetch(ks + NS - 1 + PFD);
+        }
         // each half's reads all ahead of its first MFMA: one LDS round trip
         // per half instead of one per reused operand register
 #pragma unroll
         for (int h = 0; h < H; ++h) {
-          read_half(slot(slot_c), fc.h[0], h);
-          __builtin_amdgcn_sched_barrier(0);
-          compute_half(fc.h[0], ks, h);
+          if constexpr (DB) {
+            stream_half(slot(slot_c), ks, h);
+          } else {
+            read_half(slot(slot_c), f.h[0], h);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_half(f.h[0], ks, h);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
+      };
+      for (int ks = 0; ks < nks; ks += NS) {
+        static_for<NS>([&](auto uc) {
+          constexpr int u = decltype(uc)::value;
+          if (ks + u < nks) step(std::integral_constant<int, u>{}, ks + u);
+        });
       }
-    };
-    constexpr int UNROLL = (NS == 4) ? 4 : (NS == 3) ? 6 : 2;  // multiple of NS and of the 2 fragment buffers
-    for (int ks = 0; ks < nks; ks += UNROLL) {
-      static_for<UNROLL>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        if (ks + u < nks) {
-          if constexpr (u % 2 == 0) step(std::integral_constant<int, u % NS>{}, ks + u, f0, f1);
-          else step(std::integral_constant<int, u % NS>{}, ks + u, f1, f0);
-        }
-      });
     }
     // drain the prefetches before this workgroup's LDS can be handed on
     if constexpr (PFW) wait_vmcnt<0>();
@@ -672,32 +716,90 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
   if (PFD > 0 && wave >= NDW) run(std::true_type{});
   else run(std::false_type{});
 
-  // ---- epilogue: (+ bias) -> bf16 RNE -> global
-  const bool vec_ok = (N & 3) == 0;
+  // ---- epilogue: (+ bias) -> bf16 RNE -> global.
+  // Each wave stages its WTM x WTN bf16 sub-tile through the (now idle)
+  // stage buffers, row-major with a 16-byte pad per row, and writes it back
+  // as 16-byte stores that cover whole row segments (WTN * 2 contiguous
+  // bytes per row) instead of the accumulator layout's scattered 8-byte
+  // pieces, so that L2 sees full-line writes.
+  constexpr int EPI_PITCH = WTN * 2 + 16;
+  constexpr int EPI_BYTES = WTM * EPI_PITCH;
+  constexpr bool LDS_EPI = NW % 2 == 0 && (NW / 2) * EPI_BYTES <= STAGE;
+  auto out_value = [&](int i, int j, int g, int v, const float (&bv)[4]) {
+    return f32_to_bf16_rne(acc[i][j][4 * g + v] + bv[v]);
+  };
+  auto load_bias = [&](int n, float (&bv)[4]) {
 #pragma unroll
-  for (int i = 0; i < TI; ++i) {
+    for (int v = 0; v < 4; ++v) bv[v] = (bias && n + v < N) ? bf16_to_f32(bias[n + v]) : 0.f;
+  };
+  if constexpr (LDS_EPI) {
+    // every wave is past its last LDS read and every DMA has landed
+    __builtin_amdgcn_s_barrier();
+    uint8_t* region = (wave < NW / 2 ? st0 : st1) + (wave % (NW / 2)) * EPI_BYTES;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int n = n0 + wn * WTN + 32 * i + 8 * g + 4 * q;
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (bias) {
+    for (int i = 0; i < TI; ++i) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) bv[v] = (n + v < N) ? bf16_to_f32(bias[n + v]) : 0.f;
+      for (int g = 0; g < 4; ++g) {
+        float bv[4];
+        load_bias(n0 + wn * WTN + 32 * i + 8 * g + 4 * q, bv);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const uint32_t lo = out_value(i, j, g, 0, bv) | (out_value(i, j, g, 1, bv) << 16);
+          const uint32_t hi = out_value(i, j, g, 2, bv) | (out_value(i, j, g, 3, bv) << 16);
+          *reinterpret_cast<uint2*>(region + (32 * j + r32) * EPI_PITCH + (32 * i + 8 * g + 4 * q) * 2) =
+              make_uint2(lo, hi);
+        }
       }
+    }
+    // the wave reads back what its own lanes wrote
+    wait_lgkmcnt0();
+    __builtin_amdgcn_wave_barrier();
+    constexpr int CPRO = WTN * 2 / 16;  // 16-byte chunks per sub-tile row
+    constexpr int RPI = 64 / CPRO;      // rows per wave-wide read
+    static_assert(64 % CPRO == 0 && WTM % RPI == 0, "epilogue read shape");
+    const bool vec16 = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+    const int c = lane % CPRO;
+    const int n = n0 + wn * WTN + 8 * c;
+#pragma unroll 4
+    for (int it = 0; it < WTM / RPI; ++it) {
+      const int lr = it * RPI + lane / CPRO;
+      const uint4 val = *reinterpret_cast<const uint4*>(region + lr * EPI_PITCH + 16 * c);
+      const int m = m0 + wm * WTM + lr;
+      if (m >= M) continue;
+      uint16_t* dst = out + (size_t)m * N + n;
+      if (vec16 && n + 8 <= N) {
+        *reinterpret_cast<uint4*>(dst) = val;
+      } else {
+        const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int m = m0 + wm * WTM + 32 * j + r32;
-        if (m >= M) continue;
-        uint32_t hv[4];
+        for (int e = 0; e < 8; ++e)
+          if (n + e < N) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  } else {
+    const bool vec_ok = (N & 3) == 0;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) hv[v] = f32_to_bf16_rne(acc[i][j][4 * g + v] + bv[v]);
-        uint16_t* dst = out + (size_t)m * N + n;
-        if (vec_ok && n + 3 < N) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
-        } else {
+    for (int i = 0; i < TI; ++i) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (n + v < N) dst[v] = (uint16_t)hv[v];
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WTN + 32 * i + 8 * g + 4 * q;
+        float bv[4];
+        load_bias(n, bv);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int m = m0 + wm * WTM + 32 * j + r32;
+          if (m >= M) continue;
+          uint32_t hv[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) hv[v] = out_value(i, j, g, v, bv);
+          uint16_t* dst = out + (size_t)m * N + n;
+          if (vec_ok && n + 3 < N) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (n + v < N) dst[v] = (uint16_t)hv[v];
+          }
         }
       }
     }
@@ -814,7 +916,7 @@ hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8
   // path with DMA-staged scales
   const bool scales_aligned = (((uintptr_t)a_scales | (uintptr_t)w_scales) & 3) == 0;
 #ifndef MXQ_MXP
-#define MXQ_MXP 256, 256, 4, 2, 2, false, 128, 0
+#define MXQ_MXP 256, 256, 4, 2, 2, true, 128, 0
 #endif
   if (elem == 1 && K % 128 == 0 && scales_aligned)
     return launch_mxp<1, MXQ_MXP>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
