@@ -107,15 +107,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-// LDS DMA of `bytes` per lane (lane i lands at lds + i * bytes).  Kept as a
-// plain device function: the builtin inside a generic lambda fails the host
+// LDS DMA of `bytes` per lane (lane i lands at lds + i * bytes) from byte
+// voff + soff of the buffer; voff is the per-lane part, soff a wave-uniform
+// one (the instruction's scalar offset), so that a loop-invariant voff needs
+// no temporary register whose reuse would force a wait on the DMA.  Kept as
+// plain device functions: the builtin inside a generic lambda fails the host
 // pass's substitution and drops the kernel's launch stub.
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, off, 0, 0, 0);
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
 }
-__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, off, 0, 0, 0);
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
 }
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  Issued through
@@ -374,67 +377,78 @@ hipError_t launch_tiled(int64_t M, int64_t N, int64_t K, const void* a, const ui
 
 
 // ------------------------------------------------------------------------
-// MX main path.  A BM x BN output tile per workgroup (default 256 x 256,
-// eight waves as 4 x 2, each 64 x 128 with fp32 accumulators), 32x32x64
-// scaled MFMA, and an NS-stage LDS ring of SLAB-byte K slabs (default two
-// stages of 128 bytes, i.e. 128 FP8 or 256 FP4 elements per row) filled by
-// LDS DMA.  Each stage lives in its own __shared__ array (the K loop is
-// unrolled by a multiple of NS), so the compiler's DMA tracking waits only on
-// the stage being read; cross-wave visibility comes from a vmcnt wait on the
-// wave's own DMA followed by a fence-free s_barrier.
-// Measured on gfx950: LDS-DMA throughput from L2 depends on the contiguous
-// bytes each instruction reads per row (32 B: 8, 64 B: 16, 128 B: 29 TB/s),
-// so 128-byte slabs (a whole cache line per row) beat deeper rings of 64-byte
-// slabs, and a 256 x 256 tile (128 MACs per staged byte) beats 128 x 256.
-// Per 64 K-bytes of a slab one 32x32x64 FP8 MFMA (two FP4 MFMAs) per 32 x 32
-// output tile; lane (r, q) reads 16-byte chunks 4h + q and 4h + 2 + q of row
-// r for each 64-byte half h of the slab (64-byte rows: swizzle (r >> 2) & 3,
-// 128-byte rows: (r >> 1) & 7, both conflict-free for this pattern).
-// Scales: one dword per row per 64 slab bytes (FP4: K-blocks 4c..4c+3 of
-// 64-byte chunk c; FP8: the dword of the chunk pair), staged with the codes.
-// PFD > 0 turns half of the waves into L2 prefetchers running PFD stages
-// ahead (measured slower on the FLUX shapes; kept as a tuning option).
-// Requires K % 128 == 0 (MXFP8) or K % 256 == 0 (MXFP4) and 4-byte aligned
-// scale rows.
-template <int ELEM, int BM, int BN, int WM, int WN, int NS, bool DB, int SLAB, int PFD>
+// MX main path.  One BM x BN output tile per workgroup (default 256 x 256,
+// eight waves as 4 x 2, each 64 x 128 outputs in fp32 accumulators), 32x32x64
+// scaled MFMA, and an NS-stage LDS ring of SLAB-byte K slabs (SLAB = 128:
+// 128 FP8 / 256 FP4 elements per row; SLAB = 64: half that) filled by LDS DMA
+// NS-1 stages ahead of use.
+//
+// * Staging.  Measured on gfx950, L2 -> LDS DMA throughput tracks the
+//   contiguous bytes each instruction reads per row (32 B: 8, 64 B: 16,
+//   128 B: 29 TB/s), and a 256 x 256 tile needs 128 MACs per staged byte.
+//   Each stage lives in its own __shared__ array and the loop is unrolled by
+//   NS, so that every array is named at compile time: the compiler then
+//   tracks the DMA per array and never waits on a stage other than the one
+//   being read.  The per-lane source offset is a loop-invariant register and
+//   the K step goes into the instruction's scalar offset (a temporary offset
+//   register, once reused, makes the compiler wait for the DMA).  Cross-wave
+//   visibility: wait for the wave's own DMA (vmcnt through the builtin, which
+//   the compiler's bookkeeping sees), then s_barrier.
+// * Scales ride with the codes of each stage: per row one dword of E8M0
+//   bytes (FP8: K-blocks 4p .. 4p+3 of the stage's 256-byte K pair, fetched
+//   again by the second 64-byte stage of the pair; FP4: SLAB/64 dwords).
+// * LDS layout.  Row r's SLAB bytes at r * SLAB, its 16-byte chunks
+//   XOR-swizzled by (r >> 1) & 7 (128-byte rows) or (r >> 2) & 3 (64-byte
+//   rows), both measured conflict-free for the operand reads.
+// * Operands.  Lane (r, q) of a 32x32x64 MFMA holds 16-byte chunks 4h + q
+//   and 4h + 2 + q of row r for the 64-byte half h of a slab.  Each wave
+//   streams its W tiles through two register slots: the reads of W tile i+1
+//   are placed ahead of the MFMAs of W tile i (sched_group_barrier) and scale
+//   bytes are read per lane (byte loads), so no VALU work sits between an LDS
+//   read and its MFMA.  Lane q's scale is that of K-block q of the MFMA's 64
+//   K-elements: FP8 block 2c + q of 64-byte chunk c, FP4 blocks 4c + q and
+//   4c + 2 + q for its two MFMAs.
+// * Epilogue.  (+ bias) -> bf16 RNE; each wave stages 32 output rows at a
+//   time through the idle stage buffers (16-byte row pad) and writes whole
+//   256-byte row segments with 16-byte stores, so L2 sees full-line writes.
+// Requires K % (2 * SLAB) == 0 (FP8: 128-element K pairs) or K % (2 * SLAB)
+// == 0 in elements for FP4 (K % 256 at SLAB = 128), and 4-byte aligned scale
+// rows.
+template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS>
 __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1) void mxp_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
     const uint8_t* __restrict__ Ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N,
     int K) {
   constexpr int NW = WM * WN;
-  constexpr int NDW = PFD > 0 ? NW / 2 : NW;   // waves that stage operands (the rest prefetch into L2)
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TJ = WTM / 32, TI = WTN / 32;  // 32 x 32 tiles per wave (M, N)
   constexpr int ROWS = BM + BN;
   constexpr int H = SLAB / 64;                 // 64-byte halves per slab
   constexpr int CPR = SLAB / 16;               // 16-byte chunks per row
-  constexpr int RPG = 64 / CPR;                // rows per wave-wide DMA
+  constexpr int RPG = 64 / CPR;                // rows per wave-wide code DMA
   constexpr int CODE_BYTES = ROWS * SLAB;
-  constexpr int SROWS = (ROWS * H + 64 * NDW - 1) / (64 * NDW) * (64 * NDW);  // scale dwords: whole DMA groups of all waves
-  constexpr int STAGE = CODE_BYTES + SROWS * 4;
-  constexpr int CGROUPS = CODE_BYTES / 1024;   // wave-wide 16-byte DMAs per stage
-  constexpr int SGROUPS = SROWS * 4 / 256;     // wave-wide 4-byte DMAs per stage
-  static_assert(CGROUPS % NDW == 0 && SGROUPS % NDW == 0, "groups");
-  static_assert(PFD == 0 || ROWS % (64 * (NW - NDW)) == 0, "prefetch rows");
+  constexpr int SDW = (ELEM == 1) ? 1 : H;     // scale dwords per row and stage
+  constexpr int SGROUPS = ((ROWS * SDW + 63) / 64 + NW - 1) / NW * NW;  // wave-wide 4-byte scale DMAs per stage
+  constexpr int STAGE = CODE_BYTES + SGROUPS * 256;
+  constexpr int CGROUPS = CODE_BYTES / 1024;   // wave-wide 16-byte code DMAs per stage
+  static_assert(SLAB == 64 || SLAB == 128, "slab");
   static_assert(NS >= 2 && NS <= 4, "stages");
-
-  static_assert(BM % (64 / H) == 0 && BM % RPG == 0, "a DMA group never straddles the A/W boundary");
-  constexpr int CPW = CGROUPS / NDW, SPW = SGROUPS / NDW;
-  constexpr int PER_WAVE = CPW + SPW;          // VMEM instructions per wave per stage
+  static_assert(CGROUPS % NW == 0 && SGROUPS % NW == 0, "DMA groups per wave");
+  static_assert(BM % RPG == 0 && (BM * SDW) % 64 == 0, "a DMA group never straddles the A/W boundary");
+  constexpr int CPW = CGROUPS / NW, SPW = SGROUPS / NW;
+  constexpr int PER_WAVE = CPW + SPW;          // VMEM instructions per wave and stage
   constexpr int FMT = (ELEM == 1) ? 0 : 4;
 
   __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st2[NS >= 3 ? STAGE : 16];
   __shared__ __attribute__((aligned(16))) uint8_t st3[NS == 4 ? STAGE : 16];
-  // landing area of the L2 prefetches (never read)
-  __shared__ __attribute__((aligned(16))) uint8_t pfd[PFD > 0 ? 256 * (NW - NDW) : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wm = wave / WN, wn = wave % WN;
   const int q = lane >> 5, r32 = lane & 31;
-  auto swzr = [](int r) { return SLAB == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7); };
+  auto swz = [](int r) { return SLAB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); };
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const uint32_t id = xcd_contiguous_id(blockIdx.x, gridDim.x);
@@ -455,91 +469,43 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(As + (size_t)m0 * SK, rows_a * (uint32_t)SK);
   const __amdgpu_buffer_rsrc_t rsw = make_rsrc(Ws + (size_t)n0 * SK, rows_w * (uint32_t)SK);
 
-  // per-lane DMA source offsets without the K-step term
+  // per-lane code DMA offsets without the K-step term: group g covers rows
+  // RPG*g .. RPG*g+RPG-1, lane l row RPG*g + l/CPR, chunk l%CPR (swizzled)
   uint32_t coff[CPW];
 #pragma unroll
   for (int u = 0; u < CPW; ++u) {
-    const int g = (wave % NDW) * CPW + u;
+    const int g = wave * CPW + u;
     const int r = g * RPG + lane / CPR;
     const int rr = (g * RPG < BM) ? r : r - BM;
-    coff[u] = (uint32_t)rr * (uint32_t)KB + (uint32_t)(((lane % CPR) ^ swzr(r)) << 4);
+    coff[u] = (uint32_t)rr * (uint32_t)KB + (uint32_t)(((lane % CPR) ^ swz(r)) << 4);
   }
-  // scale dword e = row * H + h (h = 64-byte half of the slab)
+  // per-lane scale DMA offsets without the K-step term: element e = row*SDW+d
   uint32_t soff[SPW];
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
-    const int e = ((wave % NDW) * SPW + u) * 64 + lane;
-    const int r = e / H, h = e % H;
-    // FP8 with 128-byte slabs: both halves use the dword of their chunk pair
-    const uint32_t hoff = (ELEM == 1 && SLAB == 128) ? 0u : (uint32_t)(4 * h);
-    soff[u] = r < BM ? (uint32_t)r * (uint32_t)SK + hoff
-            : r < ROWS ? (uint32_t)(r - BM) * (uint32_t)SK + hoff : kOutOfRange;
+    const int e = (wave * SPW + u) * 64 + lane;
+    const int r = e / SDW, d = e % SDW;
+    soff[u] = r < BM ? (uint32_t)r * (uint32_t)SK + 4 * d
+            : r < ROWS ? (uint32_t)(r - BM) * (uint32_t)SK + 4 * d : kOutOfRange;
   }
-  // `st` is one of the stage arrays, passed by reference so that the DMA
-  // builtin sees the __shared__ object itself
+  // Stage arrays are passed by reference so that the DMA builtin sees the
+  // __shared__ object itself (a runtime-selected or returned LDS pointer makes
+  // the host pass drop the kernel's launch stub).
   auto issue = [&](auto& st, int ks) {
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
       const int g = wave * CPW + u;
-      lds_dma16(g * RPG < BM ? ra : rw, &st[g * 1024], coff[u] + (uint32_t)(ks * SLAB));
+      lds_dma16(g * RPG < BM ? ra : rw, &st[g * 1024], coff[u], (uint32_t)(ks * SLAB));
     }
-    // 64-byte chunk c = ks*H + h: FP4 dword 4c, FP8 dword 4*(c/2) (pair)
-    const uint32_t sk = (ELEM == 1) ? (SLAB == 64 ? (uint32_t)(4 * (ks >> 1)) : (uint32_t)(4 * ks))
-                                    : (uint32_t)(4 * H * ks);
+    // scale bytes of stage ks: FP8 the dword of its 128-element K pair, FP4
+    // the SDW dwords of its 64-byte halves
+    const uint32_t sk = (ELEM == 1) ? (uint32_t)(4 * ((ks * SLAB) / 128)) : (uint32_t)(4 * SDW * ks);
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
       const int gi = wave * SPW + u;
-      // out-of-range scale rows carry offsets >= 2^31 and stay out of range
-      lds_dma4((gi * 64) / H < BM ? rsa : rsw, &st[CODE_BYTES + gi * 256], soff[u] + sk);
+      // out-of-range rows carry offsets >= 2^31 and stay out of range
+      lds_dma4((gi * 64) / SDW < BM ? rsa : rsw, &st[CODE_BYTES + gi * 256], soff[u], sk);
     }
-  };
-  // L2 prefetch of stage ks by the waves that stage nothing: one dword per
-  // row and slab, landing in a scratch LDS area.  These waves never wait on
-  // them inside the K loop, so up to PFD stages of misses overlap the
-  // MFMAs; the staging DMA of that stage then hits L2.
-  constexpr int PF_ROWS = PFD > 0 ? ROWS / (NW - NDW) : 64;
-  auto prefetch = [&](int ks) {
-    const int p = wave - NDW;
-#pragma unroll
-    for (int u = 0; u < PF_ROWS / 64; ++u) {
-      const int r0 = p * PF_ROWS + u * 64;
-      const int rr = (r0 < BM ? r0 : r0 - BM) + lane;
-      lds_dma4(r0 < BM ? ra : rw, &pfd[p * 256], (uint32_t)rr * (uint32_t)KB + (uint32_t)(ks * SLAB));
-    }
-  };
-
-  // operands of one 64-byte half of a slab, with raw scale words; the scale
-  // bytes are selected at MFMA time so that nothing consumes these loads
-  // before the MFMAs
-  struct Half {
-    uint4 a[TJ][2], w[TI][2];
-    uint32_t sa[TJ], sw[TI];
-  };
-  struct Frag {
-    Half h[H];
-  };
-  auto read_half = [&](const auto& st, Half& f, int h) {
-    const uint32_t* ss = reinterpret_cast<const uint32_t*>(st + CODE_BYTES);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int row = wm * WTM + 32 * j + r32;
-      const uint8_t* b = st + row * SLAB;
-      f.a[j][0] = *reinterpret_cast<const uint4*>(b + (((4 * h + q) ^ swzr(row)) << 4));
-      f.a[j][1] = *reinterpret_cast<const uint4*>(b + (((4 * h + 2 + q) ^ swzr(row)) << 4));
-      f.sa[j] = ss[row * H + h];
-    }
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int row = BM + wn * WTN + 32 * i + r32;
-      const uint8_t* b = st + row * SLAB;
-      f.w[i][0] = *reinterpret_cast<const uint4*>(b + (((4 * h + q) ^ swzr(row)) << 4));
-      f.w[i][1] = *reinterpret_cast<const uint4*>(b + (((4 * h + 2 + q) ^ swzr(row)) << 4));
-      f.sw[i] = ss[row * H + h];
-    }
-  };
-  auto read = [&](const auto& st, Frag& f) {
-#pragma unroll
-    for (int h = 0; h < H; ++h) read_half(st, f.h[h], h);
   };
 
   typedef float v16f __attribute__((ext_vector_type(16)));
@@ -549,67 +515,30 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
 
-  // MFMAs of one half-slab.  64-byte chunk c = ks*H + h: FP8 takes byte
-  // 2*(c&1)+q of its pair dword, FP4 bytes q (first MFMA) and 2+q (second).
-  auto compute_half = [&](const Half& f, int ks, int h) {
-    const int c = ks * H + h;
-    const int sh = (ELEM == 1) ? 8 * (2 * (c & 1) + q) : 8 * q;
-    uint32_t sw[TI], sa[TJ];
-#pragma unroll
-    for (int i = 0; i < TI; ++i) sw[i] = f.sw[i] >> sh;
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) sa[j] = f.sa[j] >> sh;
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        if constexpr (ELEM == 1) {
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              as_v8i(f.w[i][0], f.w[i][1]), as_v8i(f.a[j][0], f.a[j][1]), acc[i][j], FMT, FMT, 0, (int)sw[i], 0,
-              (int)sa[j]);
-        } else {
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              as_v8i_lo(f.w[i][0]), as_v8i_lo(f.a[j][0]), acc[i][j], FMT, FMT, 0, (int)sw[i], 0, (int)sa[j]);
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              as_v8i_lo(f.w[i][1]), as_v8i_lo(f.a[j][1]), acc[i][j], FMT, FMT, 2, (int)sw[i], 2, (int)sa[j]);
-        }
-      }
-    }
-  };
-  auto compute = [&](const Frag& f, int ks) {
-#pragma unroll
-    for (int h = 0; h < H; ++h) compute_half(f.h[h], ks, h);
-  };
-  // One half-slab with the W tiles streamed through two register slots:
-  // the A tiles and W tile 0 are read first, then the reads of W tile i+1
-  // are placed ahead of the MFMAs of W tile i (sched_group_barrier), so the
-  // wave's own LDS reads overlap its MFMAs.  Each lane reads its scale bytes
-  // directly (byte loads), so no VALU work sits between a read and its MFMA:
-  // 64-byte chunk c = ks*H + h, FP8 byte 2*(c&1)+q of the pair dword, FP4
-  // bytes q and 2+q.
+  // One 64-byte half h of stage ks from the stage array `st`.
   auto stream_half = [&](const auto& st, int ks, int h) {
-    const uint8_t* sb = st + CODE_BYTES;
-    const int c = ks * H + h;
-    const int b0 = (ELEM == 1) ? 2 * (c & 1) + q : q;
     constexpr int NSC = (ELEM == 1) ? 1 : 2;  // scale bytes per row and MFMA group
+    const uint8_t* sb = st + CODE_BYTES;
+    const int c = ks * H + h;                 // 64-byte chunk index along K
+    const int b0 = (ELEM == 1) ? 2 * (c & 1) + q : 4 * h + q;
     uint4 a[TJ][2], w[2][2];
     uint32_t sa[TJ][NSC], sw[2][NSC];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int row = wm * WTM + 32 * j + r32;
       const uint8_t* b = st + row * SLAB;
-      a[j][0] = *reinterpret_cast<const uint4*>(b + (((4 * h + q) ^ swzr(row)) << 4));
-      a[j][1] = *reinterpret_cast<const uint4*>(b + (((4 * h + 2 + q) ^ swzr(row)) << 4));
+      a[j][0] = *reinterpret_cast<const uint4*>(b + (((4 * h + q) ^ swz(row)) << 4));
+      a[j][1] = *reinterpret_cast<const uint4*>(b + (((4 * h + 2 + q) ^ swz(row)) << 4));
 #pragma unroll
-      for (int e = 0; e < NSC; ++e) sa[j][e] = sb[(row * H + h) * 4 + b0 + 2 * e];
+      for (int e = 0; e < NSC; ++e) sa[j][e] = sb[row * 4 * SDW + b0 + 2 * e];
     }
     auto read_w = [&](int i, int slot_i) {
       const int row = BM + wn * WTN + 32 * i + r32;
       const uint8_t* b = st + row * SLAB;
-      w[slot_i][0] = *reinterpret_cast<const uint4*>(b + (((4 * h + q) ^ swzr(row)) << 4));
-      w[slot_i][1] = *reinterpret_cast<const uint4*>(b + (((4 * h + 2 + q) ^ swzr(row)) << 4));
+      w[slot_i][0] = *reinterpret_cast<const uint4*>(b + (((4 * h + q) ^ swz(row)) << 4));
+      w[slot_i][1] = *reinterpret_cast<const uint4*>(b + (((4 * h + 2 + q) ^ swz(row)) << 4));
 #pragma unroll
-      for (int e = 0; e < NSC; ++e) sw[slot_i][e] = sb[(row * H + h) * 4 + b0 + 2 * e];
+      for (int e = 0; e < NSC; ++e) sw[slot_i][e] = sb[row * 4 * SDW + b0 + 2 * e];
     };
     read_w(0, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, (2 + NSC) * (TJ + 1), 0);
@@ -644,11 +573,6 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
     else if (pending == 1) wait_vmcnt<PER_WAVE>();
     else wait_vmcnt<0>();
   };
-
-  // Stage arrays are always selected at compile time and passed by
-  // reference: an LDS address handed to the DMA builtin as a plain pointer
-  // value (runtime-selected, or returned from a helper) makes the host pass
-  // drop the kernel's launch stub.
   auto slot = [&](auto ic) -> decltype(auto) {
     constexpr int I = decltype(ic)::value;
     if constexpr (I == 0) return (st0);
@@ -656,115 +580,75 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
     else if constexpr (I == 2) return (st2);
     else return (st3);
   };
-  // The K loop, instantiated separately for the staging waves and the
-  // prefetching waves so that the compiler's own wait bookkeeping in the
-  // latter never sees staging DMA and never waits on the prefetches.
-  auto run = [&](auto pf_c) {
-    constexpr bool PFW = decltype(pf_c)::value;
-    {
-      // prologue: stages 0..NS-2 in flight (prefetchers: the PFD stages after)
-      if constexpr (!PFW) {
-        static_for<NS - 1>([&](auto ic) {
-          constexpr int I = decltype(ic)::value;
-          if (I < nks) issue(slot(ic), I);
-        });
-      } else {
-        static_for<PFD>([&](auto ic) {
-          constexpr int I = decltype(ic)::value;
-          if (NS - 1 + I < nks) prefetch(NS - 1 + I);
-        });
-      }
-      Frag f;
-      // own DMA of stage ks done -> barrier -> DMA stage ks+NS-1 into the
-      // slot of stage ks-1 (read by every wave one step ago) -> read stage
-      // ks -> MFMAs.  Prefetchers replace the DMA with the L2 prefetch of
-      // stage ks+NS-1+PFD and have nothing to wait on.
-      auto step = [&](auto slot_c, int ks) {
-        constexpr int S = decltype(slot_c)::value;
-        const auto prev = std::integral_constant<int, (S + NS - 1) % NS>{};
-        if constexpr (!PFW) wait_own(min(NS - 2, nks - ks - 1));
-        __builtin_amdgcn_s_barrier();
-        if constexpr (!PFW) {
-          if (ks + NS - 1 < nks) issue(slot(prev), ks + NS - 1);
-        } else {
-          if (ks + NS - 1 + PFD < nks) prefetch(ks + NS - 1 + PFD);
-        }
-        // each half's reads all ahead of its first MFMA: one LDS round trip
-        // per half instead of one per reused operand register
-#pragma unroll
-        for (int h = 0; h < H; ++h) {
-          if constexpr (DB) {
-            stream_half(slot(slot_c), ks, h);
-          } else {
-            read_half(slot(slot_c), f.h[0], h);
-            __builtin_amdgcn_sched_barrier(0);
-            compute_half(f.h[0], ks, h);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      };
-      for (int ks = 0; ks < nks; ks += NS) {
-        static_for<NS>([&](auto uc) {
-          constexpr int u = decltype(uc)::value;
-          if (ks + u < nks) step(std::integral_constant<int, u>{}, ks + u);
-        });
-      }
-    }
-    // drain the prefetches before this workgroup's LDS can be handed on
-    if constexpr (PFW) wait_vmcnt<0>();
-  };
-  if (PFD > 0 && wave >= NDW) run(std::true_type{});
-  else run(std::false_type{});
 
-  // ---- epilogue: (+ bias) -> bf16 RNE -> global.
-  // Each wave stages its WTM x WTN bf16 sub-tile through the (now idle)
-  // stage buffers, row-major with a 16-byte pad per row, and writes it back
-  // as 16-byte stores that cover whole row segments (WTN * 2 contiguous
-  // bytes per row) instead of the accumulator layout's scattered 8-byte
-  // pieces, so that L2 sees full-line writes.
-  constexpr int EPI_PITCH = WTN * 2 + 16;
-  constexpr int EPI_BYTES = WTM * EPI_PITCH;
-  constexpr bool LDS_EPI = NW % 2 == 0 && (NW / 2) * EPI_BYTES <= STAGE;
-  auto out_value = [&](int i, int j, int g, int v, const float (&bv)[4]) {
-    return f32_to_bf16_rne(acc[i][j][4 * g + v] + bv[v]);
-  };
-  auto load_bias = [&](int n, float (&bv)[4]) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) bv[v] = (bias && n + v < N) ? bf16_to_f32(bias[n + v]) : 0.f;
-  };
-  if constexpr (LDS_EPI) {
-    // every wave is past its last LDS read and every DMA has landed
+  // prologue: stages 0 .. NS-2 in flight
+  static_for<NS - 1>([&](auto ic) {
+    if (decltype(ic)::value < nks) issue(slot(ic), decltype(ic)::value);
+  });
+  // Step ks: own DMA of stage ks done -> barrier (every wave is past stage
+  // ks-1) -> DMA stage ks+NS-1 into the slot of stage ks-1 -> MFMAs of stage
+  // ks, one 64-byte half at a time.
+  auto step = [&](auto u_c, int ks) {
+    constexpr int u = decltype(u_c)::value;
+    wait_own(min(NS - 2, nks - ks - 1));
     __builtin_amdgcn_s_barrier();
-    uint8_t* region = (wave < NW / 2 ? st0 : st1) + (wave % (NW / 2)) * EPI_BYTES;
+    if (ks + NS - 1 < nks) issue(slot(std::integral_constant<int, (u + NS - 1) % NS>{}), ks + NS - 1);
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      stream_half(slot(u_c), ks, h);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int ks = 0; ks < nks; ks += NS) {
+    static_for<NS>([&](auto uc) {
+      if (ks + decltype(uc)::value < nks) step(uc, ks + decltype(uc)::value);
+    });
+  }
+
+  // ---- epilogue: (+ bias) -> bf16 RNE -> global, 32 rows per pass
+  constexpr int EPI_PITCH = WTN * 2 + 16;
+  constexpr int EPI_BYTES = 32 * EPI_PITCH;
+  constexpr int WPS = STAGE / EPI_BYTES;       // waves staged per stage array
+  static_assert(WPS >= 1 && WPS * NS >= NW, "epilogue staging fits the stage buffers");
+  constexpr int CPRO = WTN * 2 / 16;  // 16-byte chunks per sub-tile row
+  constexpr int RPI = 64 / CPRO;      // rows per wave-wide read
+  static_assert(64 % CPRO == 0 && 32 % RPI == 0, "epilogue read shape");
+  // every wave is past its last LDS read and every DMA has landed
+  __builtin_amdgcn_s_barrier();
+  const int ea = wave / WPS;
+  uint8_t* region = (ea == 0 ? st0 : ea == 1 ? st1 : ea == 2 ? st2 : st3) + (wave % WPS) * EPI_BYTES;
+  const bool vec16 = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+  const int cc = lane % CPRO;
+  const int n = n0 + wn * WTN + 8 * cc;
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    if (j > 0) {  // the previous pass's reads are done before its rows are overwritten
+      wait_lgkmcnt0();
+      __builtin_amdgcn_wave_barrier();
+    }
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        float bv[4];
-        load_bias(n0 + wn * WTN + 32 * i + 8 * g + 4 * q, bv);
+        uint32_t hv[4];
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const uint32_t lo = out_value(i, j, g, 0, bv) | (out_value(i, j, g, 1, bv) << 16);
-          const uint32_t hi = out_value(i, j, g, 2, bv) | (out_value(i, j, g, 3, bv) << 16);
-          *reinterpret_cast<uint2*>(region + (32 * j + r32) * EPI_PITCH + (32 * i + 8 * g + 4 * q) * 2) =
-              make_uint2(lo, hi);
+        for (int v = 0; v < 4; ++v) {
+          const int nb = n0 + wn * WTN + 32 * i + 8 * g + 4 * q + v;
+          const float bvv = (bias && nb < N) ? bf16_to_f32(bias[nb]) : 0.f;
+          hv[v] = f32_to_bf16_rne(acc[i][j][4 * g + v] + bvv);
         }
+        *reinterpret_cast<uint2*>(region + r32 * EPI_PITCH + (32 * i + 8 * g + 4 * q) * 2) =
+            make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
       }
     }
     // the wave reads back what its own lanes wrote
     wait_lgkmcnt0();
     __builtin_amdgcn_wave_barrier();
-    constexpr int CPRO = WTN * 2 / 16;  // 16-byte chunks per sub-tile row
-    constexpr int RPI = 64 / CPRO;      // rows per wave-wide read
-    static_assert(64 % CPRO == 0 && WTM % RPI == 0, "epilogue read shape");
-    const bool vec16 = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
-    const int c = lane % CPRO;
-    const int n = n0 + wn * WTN + 8 * c;
-#pragma unroll 4
-    for (int it = 0; it < WTM / RPI; ++it) {
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
       const int lr = it * RPI + lane / CPRO;
-      const uint4 val = *reinterpret_cast<const uint4*>(region + lr * EPI_PITCH + 16 * c);
-      const int m = m0 + wm * WTM + lr;
+      const uint4 val = *reinterpret_cast<const uint4*>(region + lr * EPI_PITCH + 16 * cc);
+      const int m = m0 + wm * WTM + 32 * j + lr;
       if (m >= M) continue;
       uint16_t* dst = out + (size_t)m * N + n;
       if (vec16 && n + 8 <= N) {
@@ -776,43 +660,15 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
           if (n + e < N) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
       }
     }
-  } else {
-    const bool vec_ok = (N & 3) == 0;
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WTN + 32 * i + 8 * g + 4 * q;
-        float bv[4];
-        load_bias(n, bv);
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int m = m0 + wm * WTM + 32 * j + r32;
-          if (m >= M) continue;
-          uint32_t hv[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) hv[v] = out_value(i, j, g, v, bv);
-          uint16_t* dst = out + (size_t)m * N + n;
-          if (vec_ok && n + 3 < N) {
-            *reinterpret_cast<uint2*>(dst) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
-          } else {
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (n + v < N) dst[v] = (uint16_t)hv[v];
-          }
-        }
-      }
-    }
   }
 }
 
-template <int ELEM, int BM, int BN, int WM, int WN, int NS, bool DB, int SLAB, int PFD>
+template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS>
 hipError_t launch_mxp(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as, const uint8_t* w,
                       const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((mxp_gemm_kernel<ELEM, BM, BN, WM, WN, NS, DB, SLAB, PFD>), dim3((unsigned)tiles), dim3(64 * WM * WN),
-                     0, stream, a, as, w,
-                     ws, bias, out, (int)M, (int)N, (int)K);
+  hipLaunchKernelGGL((mxp_gemm_kernel<ELEM, BM, BN, WM, WN, SLAB, NS>), dim3((unsigned)tiles), dim3(64 * WM * WN),
+                     0, stream, a, as, w, ws, bias, out, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
@@ -912,15 +768,15 @@ __global__ __launch_bounds__(256) void bf16_generic_kernel(const uint16_t* __res
 hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                           const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
                           const uint16_t* bias, uint16_t* out, hipStream_t stream) {
-  // whole 128-byte slabs per row and 4-byte aligned scale rows: the 32x32x64
-  // path with DMA-staged scales
+  // whole 128-element FP8 K pairs / 256-element FP4 slabs and 4-byte aligned
+  // scale rows: the 32x32x64 path with LDS-DMA staging
   const bool scales_aligned = (((uintptr_t)a_scales | (uintptr_t)w_scales) & 3) == 0;
 #ifndef MXQ_MXP
-#define MXQ_MXP 256, 256, 4, 2, 2, true, 128, 0
+#define MXQ_MXP 256, 256, 4, 2, 128, 2
 #endif
-  if (elem == 1 && K % 128 == 0 && scales_aligned)
+  if (scales_aligned && elem == 1 && K % 128 == 0)
     return launch_mxp<1, MXQ_MXP>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
-  if (elem == 2 && K % 256 == 0 && scales_aligned)
+  if (scales_aligned && elem == 2 && K % 256 == 0)
     return launch_mxp<2, MXQ_MXP>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
   if (elem == 1)
     return launch_tiled<MX8, MXQ_TILE_MX>(M, N, K, a_codes, a_scales, w_codes, w_scales, nullptr, nullptr, bias,
