@@ -50,6 +50,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 enum Mode { MX8 = 1, MX4 = 2, NV4 = 3, BF16 = 4 };
 
@@ -377,6 +378,70 @@ hipError_t launch_tiled(int64_t M, int64_t N, int64_t K, const void* a, const ui
 
 
 // ------------------------------------------------------------------------
+// Epilogue shared by the 32x32-MFMA kernels: out = acc * oscale (+ bias)
+// rounded to bf16 (nearest even).  The wave's WTM x WTN sub-tile is staged 32
+// rows at a time through `region` (its own EPI_BYTES of idle LDS, 16-byte row
+// pad) and written back as 16-byte stores covering whole row segments
+// (WTN * 2 contiguous bytes per row), so L2 sees full-line writes instead of
+// the accumulator layout's scattered 8-byte pieces.  Lane (r32, q) holds, for
+// the 32 x 32 tile (i, j), output row 32j + r32 and columns 32i + 8g + 4q + v
+// in acc[i][j][4g + v].
+template <int TI, int TJ, int WTM, int WTN>
+__device__ __forceinline__ void store_tile_bf16(const v16f (&acc)[TI][TJ], float oscale, uint8_t* region,
+                                                const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
+                                                int M, int N, int mw, int nw, int lane) {
+  constexpr int EPI_PITCH = WTN * 2 + 16;
+  constexpr int CPRO = WTN * 2 / 16;  // 16-byte chunks per sub-tile row
+  constexpr int RPI = 64 / CPRO;      // rows per wave-wide read
+  static_assert(64 % CPRO == 0 && 32 % RPI == 0, "epilogue read shape");
+  const int q = lane >> 5, r32 = lane & 31;
+  const bool vec16 = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+  const int cc = lane % CPRO;
+  const int n = nw + 8 * cc;
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    if (j > 0) {  // the previous pass's reads are done before its rows are overwritten
+      wait_lgkmcnt0();
+      __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint32_t hv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int nb = nw + 32 * i + 8 * g + 4 * q + v;
+          const float bvv = (bias && nb < N) ? bf16_to_f32(bias[nb]) : 0.f;
+          hv[v] = f32_to_bf16_rne(acc[i][j][4 * g + v] * oscale + bvv);
+        }
+        *reinterpret_cast<uint2*>(region + r32 * EPI_PITCH + (32 * i + 8 * g + 4 * q) * 2) =
+            make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+      }
+    }
+    // the wave reads back what its own lanes wrote
+    wait_lgkmcnt0();
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int lr = it * RPI + lane / CPRO;
+      const uint4 val = *reinterpret_cast<const uint4*>(region + lr * EPI_PITCH + 16 * cc);
+      const int m = mw + 32 * j + lr;
+      if (m >= M) continue;
+      uint16_t* dst = out + (size_t)m * N + n;
+      if (vec16 && n + 8 <= N) {
+        *reinterpret_cast<uint4*>(dst) = val;
+      } else {
+        const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < N) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
 // MX main path.  One BM x BN output tile per workgroup (default 256 x 256,
 // eight waves as 4 x 2, each 64 x 128 outputs in fp32 accumulators), 32x32x64
 // scaled MFMA, and an NS-stage LDS ring of SLAB-byte K slabs (SLAB = 128:
@@ -508,7 +573,6 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
     }
   };
 
-  typedef float v16f __attribute__((ext_vector_type(16)));
   v16f acc[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
@@ -605,62 +669,15 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
     });
   }
 
-  // ---- epilogue: (+ bias) -> bf16 RNE -> global, 32 rows per pass
-  constexpr int EPI_PITCH = WTN * 2 + 16;
-  constexpr int EPI_BYTES = 32 * EPI_PITCH;
+  // ---- epilogue: (+ bias) -> bf16 RNE -> global
+  constexpr int EPI_BYTES = 32 * (WTN * 2 + 16);
   constexpr int WPS = STAGE / EPI_BYTES;       // waves staged per stage array
   static_assert(WPS >= 1 && WPS * NS >= NW, "epilogue staging fits the stage buffers");
-  constexpr int CPRO = WTN * 2 / 16;  // 16-byte chunks per sub-tile row
-  constexpr int RPI = 64 / CPRO;      // rows per wave-wide read
-  static_assert(64 % CPRO == 0 && 32 % RPI == 0, "epilogue read shape");
   // every wave is past its last LDS read and every DMA has landed
   __builtin_amdgcn_s_barrier();
   const int ea = wave / WPS;
   uint8_t* region = (ea == 0 ? st0 : ea == 1 ? st1 : ea == 2 ? st2 : st3) + (wave % WPS) * EPI_BYTES;
-  const bool vec16 = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
-  const int cc = lane % CPRO;
-  const int n = n0 + wn * WTN + 8 * cc;
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    if (j > 0) {  // the previous pass's reads are done before its rows are overwritten
-      wait_lgkmcnt0();
-      __builtin_amdgcn_wave_barrier();
-    }
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint32_t hv[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int nb = n0 + wn * WTN + 32 * i + 8 * g + 4 * q + v;
-          const float bvv = (bias && nb < N) ? bf16_to_f32(bias[nb]) : 0.f;
-          hv[v] = f32_to_bf16_rne(acc[i][j][4 * g + v] + bvv);
-        }
-        *reinterpret_cast<uint2*>(region + r32 * EPI_PITCH + (32 * i + 8 * g + 4 * q) * 2) =
-            make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
-      }
-    }
-    // the wave reads back what its own lanes wrote
-    wait_lgkmcnt0();
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int it = 0; it < 32 / RPI; ++it) {
-      const int lr = it * RPI + lane / CPRO;
-      const uint4 val = *reinterpret_cast<const uint4*>(region + lr * EPI_PITCH + 16 * cc);
-      const int m = m0 + wm * WTM + 32 * j + lr;
-      if (m >= M) continue;
-      uint16_t* dst = out + (size_t)m * N + n;
-      if (vec16 && n + 8 <= N) {
-        *reinterpret_cast<uint4*>(dst) = val;
-      } else {
-        const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (n + e < N) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
-      }
-    }
-  }
+  store_tile_bf16<TI, TJ, WTM, WTN>(acc, 1.0f, region, bias, out, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
 template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS>
@@ -670,6 +687,187 @@ hipError_t launch_mxp(int64_t M, int64_t N, int64_t K, const uint8_t* a, const u
   hipLaunchKernelGGL((mxp_gemm_kernel<ELEM, BM, BN, WM, WN, SLAB, NS>), dim3((unsigned)tiles), dim3(64 * WM * WN),
                      0, stream, a, as, w, ws, bias, out, (int)M, (int)N, (int)K);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------
+// NVFP4 main path.  E2M1 codes with an E4M3 scale per 16 K-elements and a
+// per-tensor fp32 scale on each operand.  The E4M3 block scale is not a power
+// of two, so it cannot ride on the scaled MFMA's E8M0 port, and e2m1 * e4m3
+// needs up to 6 significant bits, more than FP8 or FP4 hold; it lies in
+// [2^-10, 2688] and is exact in f16.  So every code is dequantized in
+// registers to f16 (v_cvt_scalef32_pk_f16_fp4 at unit scale, then one
+// v_pk_mul_f16 by the block scale: measured on gfx950, the conversion's own
+// fp32 scale operand applies only its power of two), fed to 32x32x16 f16
+// MFMA with fp32 accumulators, and the tensor scales multiply the result.
+//
+// Tile, staging and epilogue follow the MX main path: 256 x 256 outputs, eight
+// waves as 4 x 2, a two-stage LDS-DMA ring whose stage holds 128 code bytes
+// (256 elements) per row plus that row's 16 scale bytes (one 16-byte DMA per
+// row), loop-invariant per-lane DMA offsets with the K step in the scalar
+// offset, and the LDS-staged bf16 epilogue.  Each operand dword (8 codes of
+// one 16-element block) is dequantized once per stage and reused by every
+// MFMA that needs it.  Lane (r, q) feeds the 16-K MFMA m (0..7) of the
+// 64-byte half h with the 8 codes at elements 8 (m % 4) .. of 16-byte chunk
+// 4h + q (m < 4) or 4h + 2 + q (m >= 4) of row r; A and W use the same K
+// order, so the sum over K is unchanged.
+// Requires K % 256 == 0 and 16-byte aligned scale rows.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1) void nv4_gemm_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ a_ts,
+    const uint8_t* __restrict__ W, const uint8_t* __restrict__ Ws, const float* __restrict__ w_ts,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N, int K) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TJ = WTM / 32, TI = WTN / 32;
+  constexpr int ROWS = BM + BN;
+  constexpr int SLAB = 128, H = 2;
+  constexpr int CODE_BYTES = ROWS * SLAB;
+  constexpr int STAGE = CODE_BYTES + ROWS * 16;
+  constexpr int CGROUPS = CODE_BYTES / 1024, SGROUPS = ROWS * 16 / 1024;
+  static_assert(CGROUPS % NW == 0 && SGROUPS % NW == 0 && BM % 64 == 0, "DMA groups");
+  constexpr int CPW = CGROUPS / NW, SPW = SGROUPS / NW;
+
+  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wm = wave / WN, wn = wave % WN;
+  const int q = lane >> 5, r32 = lane & 31;
+  auto swz = [](int r) { return (r >> 1) & 7; };
+
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const uint32_t id = xcd_contiguous_id(blockIdx.x, gridDim.x);
+  constexpr int GROUP = 8;
+  const int group = (int)(id / (uint32_t)(GROUP * tiles_n));
+  const int first_m = group * GROUP;
+  const int gsz = min(tiles_m - first_m, GROUP);
+  const int tm = first_m + (int)(id % (uint32_t)gsz);
+  const int tn = (int)((id % (uint32_t)(GROUP * tiles_n)) / (uint32_t)gsz);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int KB = K / 2, SK = K / 16;
+  const int nks = KB / SLAB;
+  const uint32_t rows_a = (uint32_t)min(BM, M - m0), rows_w = (uint32_t)min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * KB, rows_a * (uint32_t)KB);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * KB, rows_w * (uint32_t)KB);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(As + (size_t)m0 * SK, rows_a * (uint32_t)SK);
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(Ws + (size_t)n0 * SK, rows_w * (uint32_t)SK);
+
+  uint32_t coff[CPW];
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) {
+    const int g = wave * CPW + u;
+    const int r = g * 8 + lane / 8;
+    const int rr = (g * 8 < BM) ? r : r - BM;
+    coff[u] = (uint32_t)rr * (uint32_t)KB + (uint32_t)(((lane % 8) ^ swz(r)) << 4);
+  }
+  // scale DMA group gi: rows 64 gi .. 64 gi + 63, 16 bytes each
+  uint32_t soff[SPW];
+#pragma unroll
+  for (int u = 0; u < SPW; ++u) {
+    const int r = (wave * SPW + u) * 64 + lane;
+    soff[u] = (uint32_t)(r < BM ? r : r - BM) * (uint32_t)SK;
+  }
+  auto issue = [&](auto& st, int ks) {
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const int g = wave * CPW + u;
+      lds_dma16(g * 8 < BM ? ra : rw, &st[g * 1024], coff[u], (uint32_t)(ks * SLAB));
+    }
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+      const int gi = wave * SPW + u;
+      lds_dma16(gi * 64 < BM ? rsa : rsw, &st[CODE_BYTES + gi * 1024], soff[u], (uint32_t)(ks * 16));
+    }
+  };
+
+  v16f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
+
+  // 8 codes (one dword) times a block scale -> one f16 MFMA operand
+  auto deq = [](uint32_t x, h2 s) -> v8h {
+    const h2 o0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0) * s;
+    const h2 o1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 1) * s;
+    const h2 o2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2) * s;
+    const h2 o3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3) * s;
+    return v8h{o0.x, o0.y, o1.x, o1.y, o2.x, o2.y, o3.x, o3.y};
+  };
+  // one row's operands for a half: code chunks 4h+q, 4h+2+q and the E4M3
+  // scales of their blocks (2q, 2q+1 of the half in sc[0], 4+2q, 5+2q in sc[1])
+  struct RowOps {
+    uint4 c[2];
+    h2 sc[2];
+  };
+  auto read_row = [&](const auto& st, int row, int h, RowOps& o) {
+    const uint8_t* b = st + row * SLAB;
+    o.c[0] = *reinterpret_cast<const uint4*>(b + (((4 * h + q) ^ swz(row)) << 4));
+    o.c[1] = *reinterpret_cast<const uint4*>(b + (((4 * h + 2 + q) ^ swz(row)) << 4));
+    const uint2 s8 = *reinterpret_cast<const uint2*>(st + CODE_BYTES + row * 16 + 8 * h);
+    o.sc[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s8.x >> (16 * q), 1.0f, false);
+    o.sc[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s8.y >> (16 * q), 1.0f, false);
+  };
+  auto operand = [&](const RowOps& o, int m) -> v8h {
+    const uint4& c = o.c[m >> 2];
+    const uint32_t x = ((m & 3) == 0) ? c.x : ((m & 3) == 1) ? c.y : ((m & 3) == 2) ? c.z : c.w;
+    const _Float16 s = o.sc[m >> 2][(m & 3) >> 1];
+    return deq(x, h2{s, s});
+  };
+  auto half_step = [&](const auto& st, int h) {
+    RowOps ra_[TJ], rw_[TI];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) read_row(st, wm * WTM + 32 * j + r32, h, ra_[j]);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) read_row(st, BM + wn * WTN + 32 * i + r32, h, rw_[i]);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      v8h av[TJ], wv[TI];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) av[j] = operand(ra_[j], m);
+#pragma unroll
+      for (int i = 0; i < TI; ++i) wv[i] = operand(rw_[i], m);
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[i], av[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  auto slot = [&](auto ic) -> decltype(auto) {
+    if constexpr (decltype(ic)::value == 0) return (st0);
+    else return (st1);
+  };
+  if (nks > 0) issue(st0, 0);
+  // own DMA of stage ks done -> barrier (every wave is past stage ks-1) ->
+  // DMA stage ks+1 into the other slot -> MFMAs of stage ks
+  auto step = [&](auto u_c, int ks) {
+    constexpr int u = decltype(u_c)::value;
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (ks + 1 < nks) issue(slot(std::integral_constant<int, 1 - u>{}), ks + 1);
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      half_step(slot(u_c), h);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int ks = 0; ks < nks; ks += 2) {
+    static_for<2>([&](auto uc) {
+      if (ks + decltype(uc)::value < nks) step(uc, ks + decltype(uc)::value);
+    });
+  }
+
+  // ---- epilogue: acc * ts_a * ts_w (+ bias) -> bf16 RNE -> global
+  constexpr int EPI_BYTES = 32 * (WTN * 2 + 16);
+  constexpr int WPS = STAGE / EPI_BYTES;
+  static_assert(WPS >= 1 && WPS * 2 >= NW, "epilogue staging fits the stage buffers");
+  __builtin_amdgcn_s_barrier();
+  uint8_t* region = (wave / WPS == 0 ? st0 : st1) + (wave % WPS) * EPI_BYTES;
+  store_tile_bf16<TI, TJ, WTM, WTN>(acc, a_ts[0] * w_ts[0], region, bias, out, M, N, m0 + wm * WTM, n0 + wn * WTN,
+                                    lane);
 }
 
 // ---------------------------------------------------------------- skinny M
@@ -788,6 +986,15 @@ hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8
 hipError_t launch_nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                              const float* a_ts, const uint8_t* w_codes, const uint8_t* w_scales,
                              const float* w_ts, const uint16_t* bias, uint16_t* out, hipStream_t stream) {
+  // whole 256-element stages and 16-byte aligned scale rows: the 32x32x16 f16
+  // path with LDS-DMA staging
+  const bool scales_aligned = (((uintptr_t)a_scales | (uintptr_t)w_scales) & 15) == 0;
+  if (K % 256 == 0 && scales_aligned) {
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    hipLaunchKernelGGL((nv4_gemm_kernel<256, 256, 4, 2>), dim3((unsigned)tiles), dim3(512), 0, stream, a_codes,
+                       a_scales, a_ts, w_codes, w_scales, w_ts, bias, out, (int)M, (int)N, (int)K);
+    return hipGetLastError();
+  }
   return launch_tiled<NV4, MXQ_TILE_NV4>(M, N, K, a_codes, a_scales, w_codes, w_scales, a_ts, w_ts, bias, out,
                                            stream);
 }
