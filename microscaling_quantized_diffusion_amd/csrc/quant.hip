@@ -10,24 +10,27 @@
 // chunk (8 bf16) per iteration, loaded with one 128-bit load, so a wave reads
 // 1 KiB of contiguous memory per instruction.  A 32-element MX block is four
 // consecutive lanes (a DPP quad), a 16-element NVFP4 block two lanes; block
-// maxima are exchanged with DPP quad permutes, no LDS.  All rounding
-// decisions are taken in integer arithmetic on the bf16 bit patterns (MX) or
-// by exact comparisons against per-block thresholds (NVFP4), so codes are
-// bit-exact by construction.
+// maxima are exchanged with DPP quad permutes, no LDS.  The shared exponent
+// comes from integer arithmetic on the bf16 bit patterns; MX element codes
+// from the hardware bf16 -> FP8 / FP4 conversions, whose rounding was
+// measured equal to the definition for every input (FP8 after a clamp, see
+// below); NVFP4 codes, whose divisor is not a power of two, from exact
+// comparisons against per-block thresholds.
 #include "mxq_internal.h"
 
 namespace mxq {
 namespace {
 
+// emax: exponent of the element format's largest power of two
 template <int ELEM>
 struct ElemFmt;
 template <>
-struct ElemFmt<1> {  // E4M3: bias 7, 3 mantissa bits, max 448 = 1.75 * 2^8
-  static constexpr int MBITS = 3, EMIN = -6, EMAX = 8, MAXCODE = 0x7E, SIGN_SHIFT = 7;
+struct ElemFmt<1> {  // E4M3: max 448 = 1.75 * 2^8
+  static constexpr int EMAX = 8;
 };
 template <>
-struct ElemFmt<2> {  // E2M1: bias 1, 1 mantissa bit, max 6 = 1.5 * 2^2
-  static constexpr int MBITS = 1, EMIN = 0, EMAX = 2, MAXCODE = 0x7, SIGN_SHIFT = 3;
+struct ElemFmt<2> {  // E2M1: max 6 = 1.5 * 2^2
+  static constexpr int EMAX = 2;
 };
 
 __device__ __forceinline__ uint32_t quad_swap1(uint32_t v) {  // lanes 0<->1, 2<->3 of each quad
@@ -48,43 +51,47 @@ __device__ __forceinline__ uint32_t chunk_absmax_bits(const uint4& v) {
   return max(max(m0, m1), max(m2, m3));
 }
 
-// Encode one bf16 element x (bits h) as x / 2^e, rounded to nearest even and
-// saturated.  C = EMIN - MBITS + 134 + e is a per-block constant.
-//
-// x = sig * 2^(Eb' - 134) with sig the 8-bit significand (implicit bit
-// included for normal bf16) and Eb' = max(biased exponent, 1).  With
-// L = floor(log2 sig), the target grid exponent is
-// Ev = max(L + Eb' - 134 - e, EMIN); the grid step is 2^(Ev - MBITS), i.e. a
-// right shift of sig by sh = Ev - MBITS - Eb' + 134 + e
-//   = max(L - MBITS, C - Eb'),
-// and the code is (Ev - EMIN) << MBITS plus the rounded quotient, where
-// Ev - EMIN = sh - C + Eb'.  A carry of the rounded quotient into the next
-// binade yields the next code, since codes are monotone in the value.
-template <int ELEM>
-__device__ __forceinline__ uint32_t mx_encode(uint32_t h, int C) {
-  using F = ElemFmt<ELEM>;
-  const uint32_t a = h & 0x7FFFu;
-  const uint32_t sign = ((h >> 15) & 1u) << F::SIGN_SHIFT;
-  if (a == 0) return sign;
-  const uint32_t Eb = a >> 7;
-  const uint32_t sig = Eb ? ((a & 0x7Fu) | 0x80u) : a;
-  const int Ebp = Eb ? (int)Eb : 1;
-  const int L = Eb ? 7 : (31 - __clz(sig));
-  const int sh = max(L - F::MBITS, C - Ebp);
-  uint32_t q;
-  if (sh <= 0) {
-    q = sig << (-sh);
-  } else if (sh > 9) {
-    q = 0;  // sig < 2^8 < half a step
-  } else {
-    const uint32_t qt = sig >> sh;
-    const uint32_t rem = sig & ((1u << sh) - 1u);
-    const uint32_t half = 1u << (sh - 1);
-    q = qt + ((rem > half || (rem == half && (qt & 1u))) ? 1u : 0u);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short short2v __attribute__((ext_vector_type(2)));
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+
+// Element encoding uses the gfx950 conversions v_cvt_scalef32_pk_fp8_bf16 /
+// v_cvt_scalef32_pk_fp4_bf16 (two bf16 -> two codes, divided by a power-of-two
+// fp32 scale).  Measured against the round-to-nearest-even, saturating
+// encoding of x / 2^e for every finite bf16 x and every e in [-127, 127]: FP4
+// matches everywhere (including saturation and signed zero); FP8 matches
+// wherever |x / 2^e| < 464 and returns NaN above, so FP8 inputs are first
+// clamped to the largest code's value 448 * 2^e, which encodes as 0x7E just
+// like every value it replaces (all of them are >= 448 * 2^e).
+__device__ __forceinline__ float pow2f(int e) {  // 2^e for e in [-127, 127], exact
+  return e == -127 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)(e + 127) << 23);
+}
+
+// Loads in flight per lane: each lane issues kBatch independent 16-byte loads
+// (grid-stride apart) before processing them, so that a CU keeps enough bytes
+// in flight to cover HBM latency; the stride is a multiple of 256 chunks, so
+// block-aligned lane groups stay aligned.
+constexpr int kBatch = 4;
+
+// Calls f(v, i) for every chunk i < nchunks of this lane, kBatch loads at a
+// time.  `i < nchunks` is uniform over any lane group whose chunks share a
+// block, because nchunks is a multiple of the group size.
+template <typename F>
+__device__ __forceinline__ void for_chunks(const uint4* __restrict__ x, int64_t nchunks, F&& f) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x; i0 < nchunks; i0 += stride * kBatch) {
+    uint4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t i = i0 + u * stride;
+      v[u] = i < nchunks ? x[i] : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < nchunks) f(v[u], i);
+    }
   }
-  int code = ((sh - C + Ebp) << F::MBITS) + (int)q;
-  code = min(code, F::MAXCODE);
-  return (uint32_t)code | sign;
 }
 
 // One lane = one 16-byte chunk (8 consecutive bf16); four lanes = one
@@ -94,19 +101,15 @@ template <int ELEM>
 __global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__ x, uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales, int64_t nchunks) {
   using F = ElemFmt<ELEM>;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunks; i += stride) {
-    const uint4 v = x[i];
+  for_chunks(x, nchunks, [&](const uint4& v, int64_t i) {
     uint32_t m = chunk_absmax_bits(v);
     m = max(m, quad_swap1(m));
     m = max(m, quad_swap2(m));
 
     uint32_t scale_byte;
-    uint32_t c[8];
-    if (m >= 0x7F80u) {  // NaN or Inf in the block
+    uint32_t lo = 0, hi = 0;  // FP8: codes 0-3, 4-7; FP4: lo = codes 0-7
+    if (m >= 0x7F80u) {  // NaN or Inf in the block: NaN scale, zero codes
       scale_byte = 0xFFu;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) c[j] = 0;
     } else {
       int e;
       if (m == 0) {
@@ -117,27 +120,34 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__
         e = min(max(fl - F::EMAX, -127), 127);
       }
       scale_byte = (uint32_t)(e + 127);
-      const int C = F::EMIN - F::MBITS + 134 + e;
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      const float sc = pow2f(e);
+      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      if constexpr (ELEM == 1) {
+        // |x| <= 448 * 2^e = 1.75 * 2^(e + 8), as bf16 magnitude bits
+        const unsigned short cap = (unsigned short)(((uint32_t)(e + 135) << 7) | 0x60u);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[2 * j] = mx_encode<ELEM>(w[j] & 0xFFFFu, C);
-        c[2 * j + 1] = mx_encode<ELEM>(w[j] >> 16, C);
+        for (int j = 0; j < 4; ++j) {
+          const ushort2v mag = __builtin_bit_cast(ushort2v, w[j] & 0x7FFF7FFFu);
+          const ushort2v cl = __builtin_elementwise_min(mag, ushort2v{cap, cap});
+          w[j] = __builtin_bit_cast(uint32_t, cl) | (w[j] & 0x80008000u);
+        }
+        short2v r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(short2v{0, 0}, __builtin_bit_cast(bf16x2, w[0]), sc, false);
+        r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r0, __builtin_bit_cast(bf16x2, w[1]), sc, true);
+        short2v r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(short2v{0, 0}, __builtin_bit_cast(bf16x2, w[2]), sc, false);
+        r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r1, __builtin_bit_cast(bf16x2, w[3]), sc, true);
+        lo = __builtin_bit_cast(uint32_t, r0);
+        hi = __builtin_bit_cast(uint32_t, r1);
+      } else {
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(lo, __builtin_bit_cast(bf16x2, w[0]), sc, 0);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(lo, __builtin_bit_cast(bf16x2, w[1]), sc, 1);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(lo, __builtin_bit_cast(bf16x2, w[2]), sc, 2);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(lo, __builtin_bit_cast(bf16x2, w[3]), sc, 3);
       }
     }
-    if (ELEM == 1) {
-      uint2 o;
-      o.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-      o.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-      reinterpret_cast<uint2*>(codes)[i] = o;
-    } else {
-      uint32_t o = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o |= c[j] << (4 * j);
-      reinterpret_cast<uint32_t*>(codes)[i] = o;
-    }
+    if (ELEM == 1) reinterpret_cast<uint2*>(codes)[i] = make_uint2(lo, hi);
+    else reinterpret_cast<uint32_t*>(codes)[i] = lo;
     if ((i & 3) == 0) scales[i >> 2] = (uint8_t)scale_byte;
-  }
+  });
 }
 
 // ----------------------------------------------------------------- NVFP4
@@ -155,9 +165,7 @@ __global__ __launch_bounds__(256) void absmax_partials_kernel(const uint4* __res
                                                               uint32_t* __restrict__ partials) {
   __shared__ uint32_t red[4];
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunks; i += stride)
-    m = max(m, chunk_absmax_bits(x[i]));
+  for_chunks(x, nchunks, [&](const uint4& v, int64_t) { m = max(m, chunk_absmax_bits(v)); });
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -227,9 +235,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = ts;
 
   const double ts64 = (double)ts;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunks; i += stride) {
-    const uint4 v = x[i];
+  for_chunks(x, nchunks, [&](const uint4& v, int64_t i) {
     uint32_t b = chunk_absmax_bits(v);
     b = max(b, quad_swap1(b));  // lanes (2t, 2t+1) share a 16-element block
 
@@ -277,7 +283,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
     }
     reinterpret_cast<uint32_t*>(codes)[i] = o;
     if ((i & 1) == 0) scales[i >> 1] = (uint8_t)sc;
-  }
+  });
 }
 
 int grid_for(int64_t nchunks, int64_t cap) {
@@ -293,7 +299,7 @@ hipError_t launch_mx_quant(int elem, const uint16_t* x, int64_t rows, int64_t co
                            uint8_t* scales, hipStream_t stream) {
   const int64_t nchunks = rows * cols / 8;
   if (nchunks == 0) return hipSuccess;
-  const int grid = grid_for(nchunks, 1 << 20);
+  const int grid = grid_for((nchunks + kBatch - 1) / kBatch, 8192);
   if (elem == 1)
     hipLaunchKernelGGL(mx_quant_kernel<1>, dim3(grid), dim3(256), 0, stream, (const uint4*)x, codes, scales, nchunks);
   else
@@ -316,7 +322,7 @@ hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t rows, int64_t cols, uin
   hipLaunchKernelGGL(absmax_partials_kernel, dim3(P), dim3(256), 0, stream, (const uint4*)x, nchunks, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int grid = grid_for(nchunks, 2048);
+  const int grid = grid_for((nchunks + kBatch - 1) / kBatch, 4096);
   hipLaunchKernelGGL(nvfp4_quant_kernel, dim3(grid), dim3(256), 0, stream, (const uint4*)x, nchunks, codes, scales,
                      tensor_scale, (const uint32_t*)partials, P);
   return hipGetLastError();
