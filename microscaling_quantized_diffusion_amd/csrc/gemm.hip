@@ -51,6 +51,8 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 enum Mode { MX8 = 1, MX4 = 2, NV4 = 3, BF16 = 4 };
 
@@ -408,15 +410,21 @@ __device__ __forceinline__ void store_tile_bf16(const v16f (&acc)[TI][TJ], float
     for (int i = 0; i < TI; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        uint32_t hv[4];
+        float fv[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int nb = nw + 32 * i + 8 * g + 4 * q + v;
-          const float bvv = (bias && nb < N) ? bf16_to_f32(bias[nb]) : 0.f;
-          hv[v] = f32_to_bf16_rne(acc[i][j][4 * g + v] * oscale + bvv);
+        for (int v = 0; v < 4; ++v) fv[v] = acc[i][j][4 * g + v] * oscale;
+        if (bias) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int nb = nw + 32 * i + 8 * g + 4 * q + v;
+            if (nb < N) fv[v] += bf16_to_f32(bias[nb]);
+          }
         }
+        // v_cvt_pk_bf16_f32: two nearest-even roundings per instruction
+        const bf16x2 p0 = __builtin_convertvector(f32x2{fv[0], fv[1]}, bf16x2);
+        const bf16x2 p1 = __builtin_convertvector(f32x2{fv[2], fv[3]}, bf16x2);
         *reinterpret_cast<uint2*>(region + r32 * EPI_PITCH + (32 * i + 8 * g + 4 * q) * 2) =
-            make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+            make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
       }
     }
     // the wave reads back what its own lanes wrote
