@@ -879,65 +879,78 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
 }
 
 // ---------------------------------------------------------------- skinny M
-// out[m, n] for M <= MMAX rows of activations: HBM-bound streaming of W.
-// The activations sit in LDS; each wave walks whole W rows, lanes split K in
-// 16-byte chunks, and a wave reduction produces M outputs per row.
-template <int MMAX>
+// out[m, n] for M <= MMAX activation rows: an HBM stream of W, bound by
+// bandwidth (W is read once; 2 FLOP per 2 bytes per activation row).  The
+// activations sit in LDS.  LPR lanes (8, 16 or 32) share one W row and read
+// 16 * LPR contiguous bytes per instruction, so a wave-wide load covers whole
+// lines; each lane keeps U such loads in flight, multiplies bf16 pairs with
+// v_dot2_f32_bf16 (exact products, fp32 accumulation), and the partial sums
+// of a row are combined with DPP lane permutes within each 16-lane row and
+// a lane shuffle across rows.  64 / LPR W rows per wave: finer row groups
+// spread N over the SIMDs more evenly.
+template <int MMAX, int LPR>
 __global__ __launch_bounds__(256) void bf16_skinny_kernel(const uint16_t* __restrict__ A,
                                                           const uint16_t* __restrict__ W,
                                                           const uint16_t* __restrict__ bias,
-                                                          uint16_t* __restrict__ out, int M, int N, int K,
-                                                          int rows_per_wg) {
+                                                          uint16_t* __restrict__ out, int M, int N, int K) {
+  constexpr int U = 8;  // 16-byte W loads in flight per lane
   extern __shared__ uint4 sAv[];  // [M][K/8]
   const int kc = K / 8;
   for (int c = threadIdx.x; c < M * kc; c += 256) sAv[c] = reinterpret_cast<const uint4*>(A)[c];
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n_begin = blockIdx.x * rows_per_wg;
-  const int n_end = min(N, n_begin + rows_per_wg);
-  for (int n = n_begin + wave * 2; n < n_end; n += 8) {
-    const bool two = n + 1 < n_end;
-    float acc0[MMAX], acc1[MMAX];
+  constexpr int RPW = 64 / LPR;                    // W rows per wave
+  const int sub = lane % LPR;                      // lane within its row
+  const int n = (blockIdx.x * 4 + wave) * RPW + lane / LPR;
+  const bool valid = n < N;
+  const uint4* wrow = reinterpret_cast<const uint4*>(W + (size_t)(valid ? n : 0) * K);
+  float acc[MMAX];
 #pragma unroll
-    for (int m = 0; m < MMAX; ++m) acc0[m] = acc1[m] = 0.f;
-    const uint4* w0 = reinterpret_cast<const uint4*>(W + (size_t)n * K);
-    const uint4* w1 = reinterpret_cast<const uint4*>(W + (size_t)(two ? n + 1 : n) * K);
-    for (int c = lane; c < kc; c += 64) {
-      const uint4 x0 = w0[c], x1 = w1[c];
-      const uint32_t wx0[4] = {x0.x, x0.y, x0.z, x0.w}, wx1[4] = {x1.x, x1.y, x1.z, x1.w};
+  for (int m = 0; m < MMAX; ++m) acc[m] = 0.f;
+  auto dot8 = [](const uint4& w, const uint4& a, float c) {
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), __builtin_bit_cast(bf16x2, a.x), c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), __builtin_bit_cast(bf16x2, a.y), c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), __builtin_bit_cast(bf16x2, a.z), c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), __builtin_bit_cast(bf16x2, a.w), c, false);
+    return c;
+  };
+  for (int c0 = sub; c0 < kc; c0 += LPR * U) {
+    uint4 x[U];
 #pragma unroll
-      for (int m = 0; m < MMAX; ++m) {
-        if (m < M) {
-          const uint4 av = sAv[m * kc + c];
-          const uint32_t ax[4] = {av.x, av.y, av.z, av.w};
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float alo = __uint_as_float(ax[t] << 16), ahi = __uint_as_float(ax[t] & 0xFFFF0000u);
-            acc0[m] = fmaf(alo, __uint_as_float(wx0[t] << 16), acc0[m]);
-            acc0[m] = fmaf(ahi, __uint_as_float(wx0[t] & 0xFFFF0000u), acc0[m]);
-            acc1[m] = fmaf(alo, __uint_as_float(wx1[t] << 16), acc1[m]);
-            acc1[m] = fmaf(ahi, __uint_as_float(wx1[t] & 0xFFFF0000u), acc1[m]);
-          }
-        }
-      }
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + LPR * u;
+      x[u] = (valid && c < kc) ? wrow[c] : uint4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int m = 0; m < MMAX; ++m) {
-      if (m < M) {
-        float s0 = acc0[m], s1 = acc1[m];
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + LPR * u;
+      if (c < kc) {
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-          s0 += __shfl_xor(s0, off, 64);
-          s1 += __shfl_xor(s1, off, 64);
-        }
-        if (lane == 0) {
-          const float b0 = bias ? bf16_to_f32(bias[n]) : 0.f;
-          out[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(s0 + b0);
-          if (two) {
-            const float b1 = bias ? bf16_to_f32(bias[n + 1]) : 0.f;
-            out[(size_t)m * N + n + 1] = (uint16_t)f32_to_bf16_rne(s1 + b1);
-          }
-        }
+        for (int m = 0; m < MMAX; ++m)
+          if (m < M) acc[m] = dot8(x[u], sAv[m * kc + c], acc[m]);
+      }
+    }
+  }
+  // sum over the 8 lanes of the row group: xor 1, xor 2 (quad permutes), then
+  // the mirrored quad of the half row
+  auto dpp_add = [](float v, int ctrl) {
+    int o;
+    if (ctrl == 0xB1) o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false);
+    else if (ctrl == 0x4E) o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false);
+    else o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false);
+    return v + __int_as_float(o);
+  };
+#pragma unroll
+  for (int m = 0; m < MMAX; ++m) {
+    if (m < M) {
+      float v = dpp_add(acc[m], 0xB1);
+      v = dpp_add(v, 0x4E);
+      v = dpp_add(v, 0x141);  // now the sum of each 8-lane half row
+      if constexpr (LPR >= 16) v += __shfl_xor(v, 8, 64);
+      if constexpr (LPR >= 32) v += __shfl_xor(v, 16, 64);
+      if (sub == 0 && valid) {
+        const float b = bias ? bf16_to_f32(bias[n]) : 0.f;
+        out[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v + b);
       }
     }
   }
@@ -1016,15 +1029,15 @@ hipError_t launch_bf16_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* a, 
     return hipGetLastError();
   }
   const size_t lds = (size_t)M * K * 2;
-  if (M <= 16 && lds <= 64 * 1024) {
-    const int rows_per_wg = 32;
+#ifndef MXQ_SKINNY_LPR
+#define MXQ_SKINNY_LPR 32
+#endif
+  if (M <= 4 && lds <= 64 * 1024) {
+    constexpr int LPR = MXQ_SKINNY_LPR;
+    const int rows_per_wg = 4 * (64 / LPR);  // 4 waves
     const unsigned grid = (unsigned)((N + rows_per_wg - 1) / rows_per_wg);
-    if (M <= 4)
-      hipLaunchKernelGGL(bf16_skinny_kernel<4>, dim3(grid), dim3(256), lds, stream, a, w, bias, out, (int)M, (int)N,
-                         (int)K, rows_per_wg);
-    else
-      hipLaunchKernelGGL(bf16_skinny_kernel<16>, dim3(grid), dim3(256), lds, stream, a, w, bias, out, (int)M, (int)N,
-                         (int)K, rows_per_wg);
+    hipLaunchKernelGGL((bf16_skinny_kernel<4, LPR>), dim3(grid), dim3(256), lds, stream, a, w, bias, out, (int)M,
+                       (int)N, (int)K);
     return hipGetLastError();
   }
   return launch_tiled<BF16, MXQ_TILE_BF16>(M, N, K, a, nullptr, w, nullptr, nullptr, nullptr, bias, out, stream);
