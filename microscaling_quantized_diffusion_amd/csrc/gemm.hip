@@ -475,12 +475,18 @@ __device__ __forceinline__ void store_tile_bf16(const v16f (&acc)[TI][TJ], float
 //   rows), both measured conflict-free for the operand reads.
 // * Operands.  Lane (r, q) of a 32x32x64 MFMA holds 16-byte chunks 4h + q
 //   and 4h + 2 + q of row r for the 64-byte half h of a slab.  Each wave
-//   streams its W tiles through two register slots: the reads of W tile i+1
-//   are placed ahead of the MFMAs of W tile i (sched_group_barrier) and scale
-//   bytes are read per lane (byte loads), so no VALU work sits between an LDS
-//   read and its MFMA.  Lane q's scale is that of K-block q of the MFMA's 64
-//   K-elements: FP8 block 2c + q of 64-byte chunk c, FP4 blocks 4c + q and
-//   4c + 2 + q for its two MFMAs.
+//   streams its W tiles through two register slots, the reads of the next
+//   MFMA group issued ahead of the current one (see stream_stage).  Lane q's
+//   scale is that of K-block q of the MFMA's 64 K-elements: FP8 block 2c + q
+//   of 64-byte chunk c, FP4 blocks 4c + q and 4c + 2 + q for its two MFMAs.
+// * Measured on gfx950 (s_memtime per wave and stage, FLUX MLP up-projection):
+//   the DMA wait before the stage barrier is ~1% of the loop; the barrier
+//   ~20%, because the older wave of each SIMD wins issue and finishes its
+//   MFMAs first, and the younger one then runs alone on LDS latency.  Wave
+//   priorities (s_setprio around MFMA groups), deeper read pipelines, an L2
+//   prefetch of the next K slab and fewer scale DMAs all left the time
+//   unchanged; removing the LDS operand reads or the DMA does not, so the
+//   loop is bound by LDS traffic (reads + DMA writes) and its latency.
 // * Epilogue.  (+ bias) -> bf16 RNE; each wave stages 32 output rows at a
 //   time through the idle stage buffers (16-byte row pad) and writes whole
 //   256-byte row segments with 16-byte stores, so L2 sees full-line writes.
@@ -522,6 +528,14 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
   const int wm = wave / WN, wn = wave % WN;
   const int q = lane >> 5, r32 = lane & 31;
   auto swz = [](int r) { return SLAB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); };
+  // Every operand row a lane reads is r32 plus a multiple of 32, which leaves
+  // the swizzle unchanged: the lane's chunk offsets depend on (h, chunk) only
+  // and the 32-row steps become immediate offsets of the LDS reads.
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BM % 32 == 0, "swizzle invariant under 32-row steps");
+  const int sw0 = swz(r32);
+  auto choff = [&](int h, int c) { return ((4 * h + 2 * c + q) ^ sw0) << 4; };
+  const int arow = (wm * WTM + r32) * SLAB, wrow = (BM + wn * WTN + r32) * SLAB;
+  const int asrow = (wm * WTM + r32) * 4 * SDW, wsrow = (BM + wn * WTN + r32) * 4 * SDW;
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const uint32_t id = xcd_contiguous_id(blockIdx.x, gridDim.x);
@@ -587,53 +601,65 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
 
-  // One 64-byte half h of stage ks from the stage array `st`.
-  auto stream_half = [&](const auto& st, int ks, int h) {
-    constexpr int NSC = (ELEM == 1) ? 1 : 2;  // scale bytes per row and MFMA group
+  // A stage as one pipeline of H * TI MFMA groups (group g: W tile g % TI of
+  // half g / TI against the TJ A tiles of that half): the LDS reads of group
+  // g + 1 (with the A fragments of a half at its first group) are issued
+  // ahead of the MFMAs of group g, and compiler fences keep that order, so
+  // the reads of the next half overlap the last MFMAs of this one.  Scale
+  // bytes are read per lane (byte loads): no VALU work sits between an LDS
+  // read and its MFMA.
+  auto stream_stage = [&](const auto& st, int ks) {
+    constexpr int D = 1;
+    constexpr int NSC = (ELEM == 1) ? 1 : 2;
+    constexpr int U = H * TI;
     const uint8_t* sb = st + CODE_BYTES;
-    const int c = ks * H + h;                 // 64-byte chunk index along K
-    const int b0 = (ELEM == 1) ? 2 * (c & 1) + q : 4 * h + q;
-    uint4 a[TJ][2], w[2][2];
-    uint32_t sa[TJ][NSC], sw[2][NSC];
+    uint4 a[2][TJ][2], w[D + 1][2];
+    uint32_t sa[2][TJ][NSC], sw[D + 1][NSC];
+    auto read_group = [&](int g) {
+      const int h = g / TI, i = g % TI;
+      const int c = ks * H + h;
+      const int b0 = (ELEM == 1) ? 2 * (c & 1) + q : 4 * h + q;
+      if (i == 0) {
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int row = wm * WTM + 32 * j + r32;
-      const uint8_t* b = st + row * SLAB;
-      a[j][0] = *reinterpret_cast<const uint4*>(b + (((4 * h + q) ^ swz(row)) << 4));
-      a[j][1] = *reinterpret_cast<const uint4*>(b + (((4 * h + 2 + q) ^ swz(row)) << 4));
+        for (int j = 0; j < TJ; ++j) {
+          const int row = wm * WTM + 32 * j + r32;
+          const uint8_t* b = st + arow + 32 * j * SLAB;
+          a[h & 1][j][0] = *reinterpret_cast<const uint4*>(b + choff(h, 0));
+          a[h & 1][j][1] = *reinterpret_cast<const uint4*>(b + choff(h, 1));
 #pragma unroll
-      for (int e = 0; e < NSC; ++e) sa[j][e] = sb[row * 4 * SDW + b0 + 2 * e];
-    }
-    auto read_w = [&](int i, int slot_i) {
+          for (int e = 0; e < NSC; ++e) sa[h & 1][j][e] = sb[asrow + 32 * j * 4 * SDW + b0 + 2 * e];
+        }
+      }
       const int row = BM + wn * WTN + 32 * i + r32;
-      const uint8_t* b = st + row * SLAB;
-      w[slot_i][0] = *reinterpret_cast<const uint4*>(b + (((4 * h + q) ^ swz(row)) << 4));
-      w[slot_i][1] = *reinterpret_cast<const uint4*>(b + (((4 * h + 2 + q) ^ swz(row)) << 4));
+      const uint8_t* b = st + wrow + 32 * i * SLAB;
+      const int sl = g % (D + 1);
+      w[sl][0] = *reinterpret_cast<const uint4*>(b + choff(h, 0));
+      w[sl][1] = *reinterpret_cast<const uint4*>(b + choff(h, 1));
 #pragma unroll
-      for (int e = 0; e < NSC; ++e) sw[slot_i][e] = sb[row * 4 * SDW + b0 + 2 * e];
+      for (int e = 0; e < NSC; ++e) sw[sl][e] = sb[wsrow + 32 * i * 4 * SDW + b0 + 2 * e];
     };
-    read_w(0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, (2 + NSC) * (TJ + 1), 0);
-    static_for<TI>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      if constexpr (i + 1 < TI) read_w(i + 1, (i + 1) & 1);
+    static_for<D>([&](auto gc) { read_group(decltype(gc)::value); });
+    static_for<U>([&](auto uc) {
+      constexpr int g = decltype(uc)::value;
+      if constexpr (g + D < U) read_group(g + D);
+      __builtin_amdgcn_sched_barrier(0);
+      const int h = g / TI, i = g % TI, sl = g % (D + 1);
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         if constexpr (ELEM == 1) {
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              as_v8i(w[i & 1][0], w[i & 1][1]), as_v8i(a[j][0], a[j][1]), acc[i][j], FMT, FMT, 0,
-              (int)sw[i & 1][0], 0, (int)sa[j][0]);
+              as_v8i(w[sl][0], w[sl][1]), as_v8i(a[h & 1][j][0], a[h & 1][j][1]), acc[i][j], FMT, FMT, 0,
+              (int)sw[sl][0], 0, (int)sa[h & 1][j][0]);
         } else {
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              as_v8i_lo(w[i & 1][0]), as_v8i_lo(a[j][0]), acc[i][j], FMT, FMT, 0, (int)sw[i & 1][0], 0,
-              (int)sa[j][0]);
+              as_v8i_lo(w[sl][0]), as_v8i_lo(a[h & 1][j][0]), acc[i][j], FMT, FMT, 0, (int)sw[sl][0], 0,
+              (int)sa[h & 1][j][0]);
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              as_v8i_lo(w[i & 1][1]), as_v8i_lo(a[j][1]), acc[i][j], FMT, FMT, 0, (int)sw[i & 1][1], 0,
-              (int)sa[j][1]);
+              as_v8i_lo(w[sl][1]), as_v8i_lo(a[h & 1][j][1]), acc[i][j], FMT, FMT, 0, (int)sw[sl][1], 0,
+              (int)sa[h & 1][j][1]);
         }
       }
-      if constexpr (i + 1 < TI) __builtin_amdgcn_sched_group_barrier(0x100, 2 + NSC, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, ELEM == 1 ? TJ : 2 * TJ, 0);
+      __builtin_amdgcn_sched_barrier(0);
     });
   };
 
@@ -665,11 +691,7 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
     wait_own(min(NS - 2, nks - ks - 1));
     __builtin_amdgcn_s_barrier();
     if (ks + NS - 1 < nks) issue(slot(std::integral_constant<int, (u + NS - 1) % NS>{}), ks + NS - 1);
-#pragma unroll
-    for (int h = 0; h < H; ++h) {
-      stream_half(slot(u_c), ks, h);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    stream_stage(slot(u_c), ks);
   };
   for (int ks = 0; ks < nks; ks += NS) {
     static_for<NS>([&](auto uc) {
