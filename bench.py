@@ -209,7 +209,7 @@ def main():
         "pct_of_mfma_peak": round(r["pct_peak_fused"], 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": f"mxp_gemm_kernel<{'FP8' if layer.fmt == 'mxfp8' else 'FP4'}, 256x256>",
+            "kernel": f"mxp_gemm_kernel<{'FP8' if layer.fmt == 'mxfp8' else 'FP4'}>",
             "achieved": round(flops / gemm_s / 1e12, 2),
             "peak": PEAK_TFLOPS[layer.fmt],
             "unit": "TFLOP/s",

@@ -394,8 +394,9 @@ __device__ __forceinline__ void store_tile_bf16(const v16f (&acc)[TI][TJ], float
                                                 int M, int N, int mw, int nw, int lane) {
   constexpr int EPI_PITCH = WTN * 2 + 16;
   constexpr int CPRO = WTN * 2 / 16;  // 16-byte chunks per sub-tile row
-  constexpr int RPI = 64 / CPRO;      // rows per wave-wide read
-  static_assert(64 % CPRO == 0 && 32 % RPI == 0, "epilogue read shape");
+  constexpr int RPI = 64 / CPRO;      // rows per wave-wide read (lanes past RPI * CPRO idle)
+  constexpr int NIT = (32 + RPI - 1) / RPI;
+  static_assert(CPRO <= 64, "epilogue read shape");
   const int q = lane >> 5, r32 = lane & 31;
   const bool vec16 = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
   const int cc = lane % CPRO;
@@ -431,8 +432,9 @@ __device__ __forceinline__ void store_tile_bf16(const v16f (&acc)[TI][TJ], float
     wait_lgkmcnt0();
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int it = 0; it < 32 / RPI; ++it) {
+    for (int it = 0; it < NIT; ++it) {
       const int lr = it * RPI + lane / CPRO;
+      if (lr >= 32 || lane >= RPI * CPRO) continue;
       const uint4 val = *reinterpret_cast<const uint4*>(region + lr * EPI_PITCH + 16 * cc);
       const int m = mw + 32 * j + lr;
       if (m >= M) continue;
@@ -708,6 +710,28 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
   const int ea = wave / WPS;
   uint8_t* region = (ea == 0 ? st0 : ea == 1 ? st1 : ea == 2 ? st2 : st3) + (wave % WPS) * EPI_BYTES;
   store_tile_bf16<TI, TJ, WTM, WTN>(acc, 1.0f, region, bias, out, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
+}
+
+// Compute units of the current device (cached per device).
+inline int device_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// 256 x 320 tiles instead of 256 x 256 when ceil(tiles / CUs) * width is
+// smaller (e.g. 4608 x 12288: 864 tiles in 4 rounds vs 702 tiles in 3).
+inline bool mx_prefer_wide_tile(int64_t M, int64_t N, int64_t cus) {
+  const int64_t tm = (M + 255) / 256;
+  const int64_t r256 = (tm * ((N + 255) / 256) + cus - 1) / cus;
+  const int64_t r320 = (tm * ((N + 319) / 320) + cus - 1) / cus;
+  return r320 * 320 < r256 * 256;
 }
 
 template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS>
@@ -1012,13 +1036,16 @@ hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8
   // whole 128-element FP8 K pairs / 256-element FP4 slabs and 4-byte aligned
   // scale rows: the 32x32x64 path with LDS-DMA staging
   const bool scales_aligned = (((uintptr_t)a_scales | (uintptr_t)w_scales) & 3) == 0;
-#ifndef MXQ_MXP
-#define MXQ_MXP 256, 256, 4, 2, 128, 2
-#endif
+  // Tile width 256 or 320 columns (wave tiles 64 x 128 / 64 x 160): with one
+  // workgroup per CU, the time is about (rounds of tiles) x (tile width), so
+  // take the width with the smaller product; ties keep 256.
+  const bool wide = mx_prefer_wide_tile(M, N, device_cu_count());
   if (scales_aligned && elem == 1 && K % 128 == 0)
-    return launch_mxp<1, MXQ_MXP>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+    return wide ? launch_mxp<1, 256, 320, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream)
+                : launch_mxp<1, 256, 256, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
   if (scales_aligned && elem == 2 && K % 256 == 0)
-    return launch_mxp<2, MXQ_MXP>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+    return wide ? launch_mxp<2, 256, 320, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream)
+                : launch_mxp<2, 256, 256, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
   if (elem == 1)
     return launch_tiled<MX8, MXQ_TILE_MX>(M, N, K, a_codes, a_scales, w_codes, w_scales, nullptr, nullptr, bias,
                                              out, stream);

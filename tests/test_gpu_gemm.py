@@ -112,6 +112,28 @@ def test_gemm_bias_and_fused_identity(fmt, dev):
     _gate(bf16_out_to_f64(out2), _oracle_ref(fmt, oqa, oqw, b_bits))
 
 
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_gemm_wide_tiles_ragged(fmt, dev):
+    """A shape whose tiles fill a second round at 256 columns but one round at
+    320 (so the 256 x 320 tile is taken on a 256-CU device), with ragged rows
+    and a ragged last column of tiles, compared in full."""
+    import torch
+
+    from microscaling_quantized_diffusion_amd import mxq
+
+    M, N, K = 250, 65590, 256
+    log_case("gemm wide", fmt, M, N, K)
+    rng = np.random.default_rng(7)
+    a_bits = bf16_bits_from_f32((rng.standard_normal((M, K)) * np.exp(rng.normal(0, 0.5, (M, 1)))).astype(np.float32))
+    w_bits = bf16_bits_from_f32((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    qa = mxq.quantize(fmt, to_dev(a_bits, dev))
+    qw = mxq.quantize(fmt, to_dev(w_bits, dev))
+    out = mxq.gemm(qa, qw)
+    torch.cuda.synchronize()
+    oqa, oqw = _oracle_q(fmt, a_bits), _oracle_q(fmt, w_bits)
+    _gate(bf16_out_to_f64(out), _oracle_ref(fmt, oqa, oqw))
+
+
 def test_identity_weights(dev):
     """W = I reproduces bf16(dequant(A)) exactly (one nonzero product per output)."""
     import torch
@@ -156,8 +178,9 @@ def test_bf16_gemm(M, N, K, dev):
 def _sampled_check(fmt, a_bits, w_bits, out, qa_dev, qw_dev, rng, nsamp=48):
     M, K = a_bits.shape
     N = w_bits.shape[0]
-    rows = np.sort(rng.choice(M, size=min(nsamp, M), replace=False))
-    cols = np.sort(rng.choice(N, size=min(nsamp, N), replace=False))
+    # random rows and columns plus the first and last ones (ragged tile edges)
+    rows = np.union1d(rng.choice(M, size=min(nsamp, M), replace=False), [0, M - 1])
+    cols = np.union1d(rng.choice(N, size=min(nsamp, N), replace=False), [0, N - 1])
     ts_a = ts_w = None
     if fmt == "nvfp4":
         ts_a, ts_w = oracle.nvfp4_tensor_scale(a_bits), oracle.nvfp4_tensor_scale(w_bits)
