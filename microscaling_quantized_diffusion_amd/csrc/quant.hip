@@ -206,7 +206,39 @@ __device__ __forceinline__ uint32_t midpoint_threshold(double T, bool tie_up) {
   return (exact && !tie_up) ? ub + 1u : ub;
 }
 
-// Phase 2: per 16-element block (two lanes), scale and element codes.
+// Threshold from exact fp32 arithmetic: T = a * ts with a = t * dec(sc) exact
+// in fp32 (at most 7 significant bits).  p = RN(T) and the FMA residual
+// e = T - p (exact while T's lowest bit stays a normal fp32, which holds for
+// ts >= 2^-60) decide the smallest float >= T: p when T < p, the next float
+// when T > p, and when T = p either p (tie goes up) or the next float.
+__device__ __forceinline__ uint32_t midpoint_threshold_f32(float a, float ts, bool tie_up) {
+  const float p = a * ts;
+  const float e = __builtin_fmaf(a, ts, -p);
+  const uint32_t pb = __float_as_uint(p);
+  return (e > 0.0f || (e == 0.0f && !tie_up)) ? pb + 1u : pb;
+}
+
+// E2M1 code magnitudes (0..7) of 8 bf16 values against the 7 thresholds,
+// with the sign bit of each input kept, packed 4 bits per element (element j
+// in bits 4j .. 4j + 3).
+__device__ __forceinline__ uint32_t e2m1_codes8(const uint4& v, const uint32_t (&V)[7], bool keep_sign) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t h = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
+    const uint32_t a = (h & 0x7FFFu) << 16;  // |x| as float32 bits
+    uint32_t k = 0;
+#pragma unroll
+    for (int t = 0; t < 7; ++t) k += (a >= V[t]) ? 1u : 0u;
+    if (keep_sign) k |= (h >> 12) & 8u;
+    o |= k << (4 * j);
+  }
+  return o;
+}
+
+// Phase 2: one lane per 16-element block (two 16-byte chunks): block scale,
+// thresholds, element codes.
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restrict__ x, int64_t nchunks,
                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                           float* __restrict__ ts_out,
@@ -233,57 +265,71 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
     ts = (float)((double)bf16_to_f32(g) / 2688.0);
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = ts;
-
   const double ts64 = (double)ts;
-  for_chunks(x, nchunks, [&](const uint4& v, int64_t i) {
-    uint32_t b = chunk_absmax_bits(v);
-    b = max(b, quad_swap1(b));  // lanes (2t, 2t+1) share a 16-element block
+  const bool fast = !nonfinite && ts >= 0x1p-60f;  // uniform
 
-    uint32_t sc;
-    uint32_t V[7];
-    if (nonfinite) {
-      sc = 0x7Fu;
+  const int64_t nblocks = nchunks / 2;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t b0 = (int64_t)blockIdx.x * 256 + threadIdx.x; b0 < nblocks; b0 += stride * kBatch) {
+    uint4 v[kBatch][2];
 #pragma unroll
-      for (int j = 0; j < 7; ++j) V[j] = 0xFFFFFFFFu;
-    } else if (b == 0) {
-      sc = 0;
-#pragma unroll
-      for (int j = 0; j < 7; ++j) V[j] = 0xFFFFFFFFu;
-    } else {
-      // block scale: one rounding of B / (6 ts); operands exact in double and
-      // the division correctly rounded, so the E4M3 rounding sees the exact
-      // quotient's decisions (a non-tie quotient is >= ~2^-32 relative away
-      // from any E4M3 midpoint).
-      const double q = (double)bf16_to_f32(b) / (6.0 * ts64);
-      sc = e4m3_encode_pos(q);
-      if (sc == 0) sc = 1;
-      const double s = e4m3_decode_pos(sc) * ts64;  // <= 28 significant bits: exact
-      // E2M1 midpoints between codes j and j+1; ties go to the even code, i.e.
-      // up for odd j.  t * s has <= 31 significant bits: exact in double.
-      V[0] = midpoint_threshold(0.25 * s, false);
-      V[1] = midpoint_threshold(0.75 * s, true);
-      V[2] = midpoint_threshold(1.25 * s, false);
-      V[3] = midpoint_threshold(1.75 * s, true);
-      V[4] = midpoint_threshold(2.5 * s, false);
-      V[5] = midpoint_threshold(3.5 * s, true);
-      V[6] = midpoint_threshold(5.0 * s, false);
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t b = b0 + u * stride;
+      if (b < nblocks) {
+        v[u][0] = x[2 * b];
+        v[u][1] = x[2 * b + 1];
+      } else {
+        v[u][0] = v[u][1] = uint4{0u, 0u, 0u, 0u};
+      }
     }
-
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t h = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
-      const uint32_t a = (h & 0x7FFFu) << 16;  // |x| as float32 bits
-      uint32_t k = 0;
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t b = b0 + u * stride;
+      if (b >= nblocks) continue;
+      const uint32_t bm = max(chunk_absmax_bits(v[u][0]), chunk_absmax_bits(v[u][1]));
+      uint32_t sc;
+      uint32_t V[7];
+      if (nonfinite || bm == 0) {
+        sc = nonfinite ? 0x7Fu : 0u;
 #pragma unroll
-      for (int t = 0; t < 7; ++t) k += (a >= V[t]) ? 1u : 0u;
-      if (!nonfinite) k |= (h >> 12) & 8u;  // sign bit
-      o |= k << (4 * j);
+        for (int j = 0; j < 7; ++j) V[j] = 0xFFFFFFFFu;
+      } else {
+        // block scale: one rounding of B / (6 ts); operands exact in double and
+        // the division correctly rounded, so the E4M3 rounding sees the exact
+        // quotient's decisions (a non-tie quotient is >= ~2^-32 relative away
+        // from any E4M3 midpoint).
+        const double q = (double)bf16_to_f32(bm) / (6.0 * ts64);
+        sc = e4m3_encode_pos(q);
+        if (sc == 0) sc = 1;
+        // E2M1 midpoints between codes j and j+1 (0.25 .. 5 times the scale);
+        // ties go to the even code, i.e. up after odd codes.
+        if (fast) {
+          const float d = (float)e4m3_decode_pos(sc);  // exact
+          V[0] = midpoint_threshold_f32(0.25f * d, ts, false);
+          V[1] = midpoint_threshold_f32(0.75f * d, ts, true);
+          V[2] = midpoint_threshold_f32(1.25f * d, ts, false);
+          V[3] = midpoint_threshold_f32(1.75f * d, ts, true);
+          V[4] = midpoint_threshold_f32(2.5f * d, ts, false);
+          V[5] = midpoint_threshold_f32(3.5f * d, ts, true);
+          V[6] = midpoint_threshold_f32(5.0f * d, ts, false);
+        } else {
+          const double s = e4m3_decode_pos(sc) * ts64;  // <= 28 significant bits: exact
+          // t * s has <= 31 significant bits: exact in double
+          V[0] = midpoint_threshold(0.25 * s, false);
+          V[1] = midpoint_threshold(0.75 * s, true);
+          V[2] = midpoint_threshold(1.25 * s, false);
+          V[3] = midpoint_threshold(1.75 * s, true);
+          V[4] = midpoint_threshold(2.5 * s, false);
+          V[5] = midpoint_threshold(3.5 * s, true);
+          V[6] = midpoint_threshold(5.0 * s, false);
+        }
+      }
+      const uint32_t lo = e2m1_codes8(v[u][0], V, !nonfinite);
+      const uint32_t hi = e2m1_codes8(v[u][1], V, !nonfinite);
+      reinterpret_cast<uint2*>(codes)[b] = make_uint2(lo, hi);
+      scales[b] = (uint8_t)sc;
     }
-    reinterpret_cast<uint32_t*>(codes)[i] = o;
-    if ((i & 1) == 0) scales[i >> 1] = (uint8_t)sc;
-  });
+  }
 }
 
 int grid_for(int64_t nchunks, int64_t cap) {
@@ -322,7 +368,7 @@ hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t rows, int64_t cols, uin
   hipLaunchKernelGGL(absmax_partials_kernel, dim3(P), dim3(256), 0, stream, (const uint4*)x, nchunks, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int grid = grid_for((nchunks + kBatch - 1) / kBatch, 4096);
+  const int grid = grid_for((nchunks / 2 + kBatch - 1) / kBatch, 4096);
   hipLaunchKernelGGL(nvfp4_quant_kernel, dim3(grid), dim3(256), 0, stream, (const uint4*)x, nchunks, codes, scales,
                      tensor_scale, (const uint32_t*)partials, P);
   return hipGetLastError();

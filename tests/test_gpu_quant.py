@@ -154,8 +154,11 @@ def test_nvfp4_tensor_scale_sweep(dev):
 
 
 def test_nvfp4_block_and_element_sweep(dev):
-    """Block maxima over 12 binades below each tensor-max binade with all element patterns beneath them."""
-    for g_bits in (0x4528, 0x3FC1, 0x1234, 0x7000):
+    """Block maxima over 12 binades below each tensor-max binade with all element patterns beneath them.
+    The tensor maxima put ts on both sides of 2^-60, where the kernel switches
+    between fp32 and double threshold arithmetic (0x2790: ts ~ 2^-59.4,
+    0x2710: ts ~ 2^-60.4), and far on either side."""
+    for g_bits in (0x4528, 0x3FC1, 0x1234, 0x7000, 0x2790, 0x2710):
         sweep = _pinned_sweep(16, 10, 0)
         gval = oracle.decode_bf16(np.array([g_bits], np.uint16))[0]
         vals = oracle.decode_bf16(sweep)
