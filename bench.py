@@ -62,21 +62,28 @@ def _upload(bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def _time_loop(fn, iters, warmup):
-    """Average milliseconds per call, HIP events on torch's current stream (the stream the library launches on)."""
+def _time_loop(fn, iters, warmup, dist=None):
+    """Average milliseconds per call, HIP events on torch's current stream (the stream the library launches on).
+
+    An event is recorded after every call, so ``dist`` (if given) receives the
+    p10 / median / p90 of the per-call times; the average is first to last
+    event over all ``iters`` calls."""
     import torch
 
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    ev[0].record()
     for i in range(iters):
         fn(i)
-    stop.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / iters
+    if dist is not None:
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(iters)])
+        dist.update(p10=float(np.percentile(per, 10)), p50=float(np.percentile(per, 50)),
+                    p90=float(np.percentile(per, 90)))
+    return ev[0].elapsed_time(ev[iters]) / iters
 
 
 def run_layer(layer, dev, steps, warmup, rotate, seed=0):
@@ -109,14 +116,18 @@ def run_layer(layer, dev, steps, warmup, rotate, seed=0):
                   for _ in range(rotate - 1)]
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(mxq.workspace_bytes(fmt, M, K, True), dtype=torch.uint8, device=dev)
-    ms_fused = _time_loop(lambda i: mxq.quant_gemm_fused(As[i % rotate], Ws[i % rotate], None, out, ws), steps, warmup)
+    dist_fused, dist_gemm = {}, {}
+    ms_fused = _time_loop(lambda i: mxq.quant_gemm_fused(As[i % rotate], Ws[i % rotate], None, out, ws), steps, warmup,
+                          dist_fused)
     qa = [mxq.quantize(fmt, a) for a in As]
-    ms_gemm = _time_loop(lambda i: mxq.gemm(qa[i % rotate], Ws[i % rotate], None, out), steps, warmup)
+    ms_gemm = _time_loop(lambda i: mxq.gemm(qa[i % rotate], Ws[i % rotate], None, out), steps, warmup, dist_gemm)
     ms_quant = _time_loop(lambda i: mxq.quantize(fmt, As[i % rotate], qa[i % rotate]), steps, warmup)
     code_b = M * K * (1.0 if fmt == "mxfp8" else 0.5)
     scale_b = M * K / (16 if fmt == "nvfp4" else 32)
     quant_bytes = M * K * 2 + code_b + scale_b
-    res.update(path=fmt, ms=ms_fused, tflops=flops / ms_fused / 1e9, gemm_ms=ms_gemm,
+    res.update(path=fmt, ms=ms_fused, ms_p10=dist_fused["p10"], ms_p50=dist_fused["p50"], ms_p90=dist_fused["p90"],
+               gemm_ms_p10=dist_gemm["p10"], gemm_ms_p50=dist_gemm["p50"], gemm_ms_p90=dist_gemm["p90"],
+               tflops=flops / ms_fused / 1e9, gemm_ms=ms_gemm,
                gemm_tflops=flops / ms_gemm / 1e9, quant_ms=ms_quant, quant_gbs=quant_bytes / ms_quant / 1e6,
                pct_peak_fused=100.0 * flops / ms_fused / 1e9 / PEAK_TFLOPS[fmt],
                pct_peak_gemm=100.0 * flops / ms_gemm / 1e9 / PEAK_TFLOPS[fmt])
@@ -198,6 +209,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(r["ms"], 5),
+        "ms_per_step_p10_p50_p90": [round(r["ms_p10"], 5), round(r["ms_p50"], 5), round(r["ms_p90"], 5)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -218,6 +230,8 @@ def main():
             "algorithmic_bytes": layer.M * layer.K + layer.N * layer.K + (layer.M + layer.N) * layer.K // 32
             + layer.M * layer.N * 2,
             "gemm_ms": round(r["gemm_ms"], 5),
+            "gemm_ms_p10_p50_p90": [round(r["gemm_ms_p10"], 5), round(r["gemm_ms_p50"], 5),
+                                    round(r["gemm_ms_p90"], 5)],
         },
         "quantizer": {"ms": round(r["quant_ms"], 5), "GB/s": round(r["quant_gbs"], 1),
                       "frac_of_hbm": round(r["quant_gbs"] / PEAK_HBM_GBS, 4)},
