@@ -381,84 +381,73 @@ hipError_t launch_tiled(int64_t M, int64_t N, int64_t K, const void* a, const ui
 
 // ------------------------------------------------------------------------
 // Epilogue shared by the 32x32-MFMA kernels: out = acc * oscale (+ bias)
-// rounded to bf16 (nearest even).  The wave's WTM x WTN sub-tile is staged
-// through `region` (its own idle LDS, 16-byte row pad), 32 rows by IP x 32
-// columns at a time, and written back as 16-byte stores covering whole row
-// segments (IP * 64 contiguous bytes per row), so L2 sees full-line writes
-// instead of the accumulator layout's scattered 8-byte pieces.  Lane (r32, q)
-// holds, for the 32 x 32 tile (i, j), output row 32j + r32 and columns
-// 32i + 8g + 4q + v in acc[i][j][4g + v].
-template <int IP>
-constexpr int epi_region_bytes() {
-  return 32 * (IP * 64 + 16);
-}
-template <int TI, int TJ, int WTM, int WTN, int IP = TI>
+// rounded to bf16 (nearest even).  The wave's WTM x WTN sub-tile is staged 32
+// rows at a time through `region` (its own EPI_BYTES of idle LDS, 16-byte row
+// pad) and written back as 16-byte stores covering whole row segments
+// (WTN * 2 contiguous bytes per row), so L2 sees full-line writes instead of
+// the accumulator layout's scattered 8-byte pieces.  Lane (r32, q) holds, for
+// the 32 x 32 tile (i, j), output row 32j + r32 and columns 32i + 8g + 4q + v
+// in acc[i][j][4g + v].
+template <int TI, int TJ, int WTM, int WTN>
 __device__ __forceinline__ void store_tile_bf16(const v16f (&acc)[TI][TJ], float oscale, uint8_t* region,
                                                 const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
                                                 int M, int N, int mw, int nw, int lane) {
-  constexpr int NP = (TI + IP - 1) / IP;  // column passes
+  constexpr int EPI_PITCH = WTN * 2 + 16;
+  constexpr int CPRO = WTN * 2 / 16;  // 16-byte chunks per sub-tile row
+  constexpr int RPI = 64 / CPRO;      // rows per wave-wide read (lanes past RPI * CPRO idle)
+  constexpr int NIT = (32 + RPI - 1) / RPI;
+  static_assert(CPRO <= 64, "epilogue read shape");
   const int q = lane >> 5, r32 = lane & 31;
   const bool vec16 = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+  const int cc = lane % CPRO;
+  const int n = nw + 8 * cc;
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
-    static_for<NP>([&](auto pc) {
-      constexpr int P = decltype(pc)::value;
-      constexpr int I0 = P * IP;
-      constexpr int NI = (TI - I0) < IP ? (TI - I0) : IP;  // tiles in this pass
-      constexpr int PITCH = NI * 64 + 16;
-      constexpr int CPRO = NI * 4;   // 16-byte chunks per row of the pass
-      constexpr int RPI = 64 / CPRO; // rows per wave-wide read (lanes past RPI * CPRO idle)
-      constexpr int NIT = (32 + RPI - 1) / RPI;
-      static_assert(CPRO <= 64, "epilogue read shape");
-      if (j > 0 || P > 0) {  // the previous pass's reads are done before its rows are overwritten
-        wait_lgkmcnt0();
-        __builtin_amdgcn_wave_barrier();
-      }
-#pragma unroll
-      for (int ii = 0; ii < NI; ++ii) {
-        const int i = I0 + ii;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float fv[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) fv[v] = acc[i][j][4 * g + v] * oscale;
-          if (bias) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int nb = nw + 32 * i + 8 * g + 4 * q + v;
-              if (nb < N) fv[v] += bf16_to_f32(bias[nb]);
-            }
-          }
-          // v_cvt_pk_bf16_f32: two nearest-even roundings per instruction
-          const bf16x2 p0 = __builtin_convertvector(f32x2{fv[0], fv[1]}, bf16x2);
-          const bf16x2 p1 = __builtin_convertvector(f32x2{fv[2], fv[3]}, bf16x2);
-          *reinterpret_cast<uint2*>(region + r32 * PITCH + (32 * ii + 8 * g + 4 * q) * 2) =
-              make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
-        }
-      }
-      // the wave reads back what its own lanes wrote
+    if (j > 0) {  // the previous pass's reads are done before its rows are overwritten
       wait_lgkmcnt0();
       __builtin_amdgcn_wave_barrier();
-      const int cc = lane % CPRO;
-      const int n = nw + 32 * I0 + 8 * cc;
+    }
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int lr = it * RPI + lane / CPRO;
-        if (lr >= 32 || lane >= RPI * CPRO) continue;
-        const uint4 val = *reinterpret_cast<const uint4*>(region + lr * PITCH + 16 * cc);
-        const int m = mw + 32 * j + lr;
-        if (m >= M) continue;
-        uint16_t* dst = out + (size_t)m * N + n;
-        if (vec16 && n + 8 <= N) {
-          *reinterpret_cast<uint4*>(dst) = val;
-        } else {
-          const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
+    for (int i = 0; i < TI; ++i) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (n + e < N) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+      for (int g = 0; g < 4; ++g) {
+        float fv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) fv[v] = acc[i][j][4 * g + v] * oscale;
+        if (bias) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int nb = nw + 32 * i + 8 * g + 4 * q + v;
+            if (nb < N) fv[v] += bf16_to_f32(bias[nb]);
+          }
         }
+        // v_cvt_pk_bf16_f32: two nearest-even roundings per instruction
+        const bf16x2 p0 = __builtin_convertvector(f32x2{fv[0], fv[1]}, bf16x2);
+        const bf16x2 p1 = __builtin_convertvector(f32x2{fv[2], fv[3]}, bf16x2);
+        *reinterpret_cast<uint2*>(region + r32 * EPI_PITCH + (32 * i + 8 * g + 4 * q) * 2) =
+            make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
       }
-    });
+    }
+    // the wave reads back what its own lanes wrote
+    wait_lgkmcnt0();
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int lr = it * RPI + lane / CPRO;
+      if (lr >= 32 || lane >= RPI * CPRO) continue;
+      const uint4 val = *reinterpret_cast<const uint4*>(region + lr * EPI_PITCH + 16 * cc);
+      const int m = mw + 32 * j + lr;
+      if (m >= M) continue;
+      uint16_t* dst = out + (size_t)m * N + n;
+      if (vec16 && n + 8 <= N) {
+        *reinterpret_cast<uint4*>(dst) = val;
+      } else {
+        const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < N) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+      }
+    }
   }
 }
 
@@ -712,17 +701,15 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
     });
   }
 
-  // ---- epilogue: (+ bias) -> bf16 RNE -> global, with no workgroup barrier:
-  // the ring slot of stage nks-2 is idle once every wave has passed the last
-  // step's barrier (its reads are done and no DMA targets it), so each wave
-  // stages its outputs there as soon as its own MFMAs are issued, while the
-  // other wave of its SIMD may still be computing.  Column passes of
-  // ceil(TI/2) tiles keep the eight regions within one slot.
-  static_assert(NS == 2, "the barrier-free epilogue uses the idle slot of a two-stage ring");
-  constexpr int IP = (TI + 1) / 2;
-  static_assert(NW * epi_region_bytes<IP>() <= STAGE, "epilogue staging fits one stage buffer");
-  uint8_t* region = ((nks & 1) ? st1 : st0) + wave * epi_region_bytes<IP>();
-  store_tile_bf16<TI, TJ, WTM, WTN, IP>(acc, 1.0f, region, bias, out, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
+  // ---- epilogue: (+ bias) -> bf16 RNE -> global
+  constexpr int EPI_BYTES = 32 * (WTN * 2 + 16);
+  constexpr int WPS = STAGE / EPI_BYTES;       // waves staged per stage array
+  static_assert(WPS >= 1 && WPS * NS >= NW, "epilogue staging fits the stage buffers");
+  // every wave is past its last LDS read and every DMA has landed
+  __builtin_amdgcn_s_barrier();
+  const int ea = wave / WPS;
+  uint8_t* region = (ea == 0 ? st0 : ea == 1 ? st1 : ea == 2 ? st2 : st3) + (wave % WPS) * EPI_BYTES;
+  store_tile_bf16<TI, TJ, WTM, WTN>(acc, 1.0f, region, bias, out, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
 // Compute units of the current device (cached per device).
