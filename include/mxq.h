@@ -33,11 +33,15 @@
  *    stream-ordered and return before the GPU work completes; device faults
  *    surface at the caller's next synchronisation.  Calls on different
  *    streams with disjoint outputs and workspaces may run concurrently.
- *  - Arguments are validated on the host before anything is enqueued; on
- *    any error nothing is launched.  M == 0 or N == 0 (or rows == 0) is a
- *    successful no-op.  K must be a positive multiple of the block size
- *    (32 for MX formats, 16 for NVFP4) wherever K is used.
- *  - No global state: the library keeps nothing between calls.
+ *  - Arguments are validated on the host before anything is enqueued, in
+ *    the order format, sizes, pointers, alignment, workspace; on any error
+ *    nothing is launched.  M == 0 or N == 0 (or rows == 0) is a successful
+ *    no-op, decided right after the sizes, so empty tensors may pass NULL
+ *    pointers (an NVFP4 quantization of zero rows writes no tensor scale).
+ *    K must be a positive multiple of the block size (32 for MX formats, 16
+ *    for NVFP4) wherever K is used.
+ *  - No state between calls beyond a per-device cache of the compute-unit
+ *    count (used to pick the GEMM tile width).
  */
 #ifndef MXQ_H
 #define MXQ_H
@@ -61,7 +65,8 @@ typedef enum {
   MXQ_OK = 0,
   MXQ_ERR_NULL = 1,        /* a required pointer is NULL */
   MXQ_ERR_FORMAT = 2,      /* unknown mxq_format */
-  MXQ_ERR_SHAPE = 3,       /* negative size, or K not a positive multiple of the block */
+  MXQ_ERR_SHAPE = 3,       /* negative size, K not a positive multiple of the block, or a
+                              GEMM beyond K <= 2^22 / M * N <= 2^39 */
   MXQ_ERR_ALIGN = 4,       /* a 16-byte-aligned pointer is misaligned */
   MXQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than mxq_workspace_bytes() */
   MXQ_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
@@ -114,6 +119,9 @@ mxq_status mxq_quantize(mxq_format fmt, const void* x_bf16, int64_t rows, int64_
  *   w_tensor_scale     device float[1] (NVFP4, required); NULL for MX
  *   bias_bf16          device bf16 [N] or NULL
  *   out_bf16           device bf16 [M, N], 16-byte aligned
+ * Sizes: M, N >= 0 with M * N <= 2^39, K a positive multiple of the block and
+ * at most 2^22 (a tile's rows of codes stay within one 32-bit buffer range);
+ * anything else returns MXQ_ERR_SHAPE before any launch.
  */
 mxq_status mxq_gemm(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void* a_codes, const void* a_scales,
                     const float* a_tensor_scale, const void* w_codes, const void* w_scales,
@@ -128,6 +136,7 @@ mxq_status mxq_gemm(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void*
  *   w_*            as in mxq_gemm
  *   workspace      device scratch, at least mxq_workspace_bytes(fmt, M, K, 1)
  *                  bytes, 16-byte aligned; its contents are overwritten
+ * Sizes as in mxq_gemm.
  */
 mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void* a_bf16,
                                 const void* w_codes, const void* w_scales, const float* w_tensor_scale,
@@ -137,7 +146,8 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K,
 /*
  * bf16 GEMM for layers left unquantized by the selective rule:
  *   out[m, n] = sum_k A[m, k] * W[n, k] (+ bias[n]) with bf16 inputs, an fp32
- * accumulator and a nearest-even bf16 result.  K >= 1 (no block constraint).
+ * accumulator and a nearest-even bf16 result.  1 <= K <= 2^22 (no block
+ * constraint), M * N <= 2^39.
  *   a_bf16 [M, K], w_bf16 [N, K], out_bf16 [M, N]: device, 16-byte aligned.
  */
 mxq_status mxq_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* a_bf16, const void* w_bf16,

@@ -21,6 +21,14 @@ bool valid_format(mxq_format fmt) {
 // 32-bit row/column indices.
 bool valid_k(mxq_format fmt, int64_t K) { return K > 0 && K % block_of(fmt) == 0 && K <= (1 << 30); }
 bool valid_dim(int64_t d) { return d >= 0 && d <= (int64_t)1 << 30; }
+// GEMM limits: the kernels address a tile's rows (up to 256 rows of K codes,
+// or 2K bytes of bf16) through one 32-bit buffer range with 32-bit lane
+// offsets, and launch one workgroup per tile (down to 128 x 128 outputs).
+constexpr int64_t kGemmMaxK = (int64_t)1 << 22;
+constexpr int64_t kGemmMaxMN = (int64_t)1 << 39;
+bool valid_gemm(int64_t M, int64_t N, int64_t K) {
+  return valid_dim(M) && valid_dim(N) && K <= kGemmMaxK && M * N <= kGemmMaxMN;
+}
 
 size_t code_bytes(mxq_format fmt, int64_t rows, int64_t K) {
   return (size_t)rows * (size_t)(fmt == MXQ_FMT_MXFP8 ? K : K / 2);
@@ -84,6 +92,7 @@ mxq_status mxq_quantize(mxq_format fmt, const void* x_bf16, int64_t rows, int64_
                         float* tensor_scale, void* workspace, size_t workspace_bytes, void* stream) {
   if (!valid_format(fmt)) return MXQ_ERR_FORMAT;
   if (!valid_dim(rows) || !valid_k(fmt, cols)) return MXQ_ERR_SHAPE;
+  if (rows == 0) return MXQ_OK;  // nothing to read or write, whatever the pointers
   if (!x_bf16 || !codes || !scales) return MXQ_ERR_NULL;
   if (fmt == MXQ_FMT_NVFP4 && !tensor_scale) return MXQ_ERR_NULL;
   if (fmt != MXQ_FMT_NVFP4 && tensor_scale) return MXQ_ERR_UNSUPPORTED;
@@ -91,7 +100,6 @@ mxq_status mxq_quantize(mxq_format fmt, const void* x_bf16, int64_t rows, int64_
   const size_t need = mxq_workspace_bytes(fmt, rows, cols, 0);
   if (need && (!workspace || workspace_bytes < need)) return MXQ_ERR_WORKSPACE;
   if (need && !aligned16(workspace)) return MXQ_ERR_ALIGN;
-  if (rows == 0) return MXQ_OK;
   hipStream_t s = (hipStream_t)stream;
   if (fmt == MXQ_FMT_NVFP4)
     return launch_status(launch_nvfp4_quant((const uint16_t*)x_bf16, rows, cols, (uint8_t*)codes, (uint8_t*)scales,
@@ -104,12 +112,12 @@ mxq_status mxq_gemm(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void*
                     const float* a_tensor_scale, const void* w_codes, const void* w_scales,
                     const float* w_tensor_scale, const void* bias_bf16, void* out_bf16, void* stream) {
   if (!valid_format(fmt)) return MXQ_ERR_FORMAT;
-  if (!valid_dim(M) || !valid_dim(N) || !valid_k(fmt, K)) return MXQ_ERR_SHAPE;
+  if (!valid_k(fmt, K) || !valid_gemm(M, N, K)) return MXQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXQ_OK;  // empty output: nothing to launch, whatever the pointers
   if (!a_codes || !a_scales || !w_codes || !w_scales || !out_bf16) return MXQ_ERR_NULL;
   if (fmt == MXQ_FMT_NVFP4 && (!a_tensor_scale || !w_tensor_scale)) return MXQ_ERR_NULL;
   if (fmt != MXQ_FMT_NVFP4 && (a_tensor_scale || w_tensor_scale)) return MXQ_ERR_UNSUPPORTED;
   if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
-  if (M == 0 || N == 0) return MXQ_OK;
   hipStream_t s = (hipStream_t)stream;
   if (fmt == MXQ_FMT_NVFP4)
     return launch_status(launch_nvfp4_gemm(M, N, K, (const uint8_t*)a_codes, (const uint8_t*)a_scales, a_tensor_scale,
@@ -125,7 +133,8 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K,
                                 const void* bias_bf16, void* out_bf16, void* workspace, size_t workspace_bytes,
                                 void* stream) {
   if (!valid_format(fmt)) return MXQ_ERR_FORMAT;
-  if (!valid_dim(M) || !valid_dim(N) || !valid_k(fmt, K)) return MXQ_ERR_SHAPE;
+  if (!valid_k(fmt, K) || !valid_gemm(M, N, K)) return MXQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXQ_OK;  // empty output: nothing to launch, whatever the pointers
   if (!a_bf16 || !w_codes || !w_scales || !out_bf16) return MXQ_ERR_NULL;
   if (fmt == MXQ_FMT_NVFP4 && !w_tensor_scale) return MXQ_ERR_NULL;
   if (fmt != MXQ_FMT_NVFP4 && w_tensor_scale) return MXQ_ERR_UNSUPPORTED;
@@ -133,7 +142,6 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K,
   const FusedLayout L = fused_layout(fmt, M, K);
   if (!workspace || workspace_bytes < L.total) return MXQ_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MXQ_ERR_ALIGN;
-  if (M == 0 || N == 0) return MXQ_OK;
   hipStream_t s = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
   uint8_t* a_codes = ws + L.codes;
@@ -156,10 +164,10 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K,
 
 mxq_status mxq_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* a_bf16, const void* w_bf16,
                          const void* bias_bf16, void* out_bf16, void* stream) {
-  if (!valid_dim(M) || !valid_dim(N) || K <= 0 || K > (1 << 30)) return MXQ_ERR_SHAPE;
+  if (K <= 0 || !valid_gemm(M, N, K)) return MXQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXQ_OK;  // empty output: nothing to launch, whatever the pointers
   if (!a_bf16 || !w_bf16 || !out_bf16) return MXQ_ERR_NULL;
   if (!aligned16(a_bf16) || !aligned16(w_bf16) || !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
-  if (M == 0 || N == 0) return MXQ_OK;
   return launch_status(launch_bf16_gemm(M, N, K, (const uint16_t*)a_bf16, (const uint16_t*)w_bf16,
                                         (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, (hipStream_t)stream));
 }

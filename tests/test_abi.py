@@ -103,3 +103,19 @@ def test_bf16_argument_errors(lib):
     assert b(4, 4, 8, None, P, None, P, None) == 1
     assert b(4, 4, 8, P, P + 1, None, P, None) == 4
     assert b(0, 4, 8, P, P, None, P, None) == 0
+
+
+def test_gemm_size_limits(lib):
+    """GEMMs beyond K = 2^22 or M * N = 2^39 are rejected before any launch (the
+    tile's rows of codes must stay within one 32-bit buffer range)."""
+    g, f, b = lib.mxq_gemm, lib.mxq_quant_gemm_fused, lib.mxq_gemm_bf16
+    big_k = (1 << 22) + 32
+    assert g(1, 4, 4, big_k, P, P, None, P, P, None, None, P, None) == 3
+    assert g(3, 4, 4, big_k, P, P, P, P, P, P, None, P, None) == 3
+    assert g(1, 1 << 20, (1 << 19) + 1, 32, P, P, None, P, P, None, None, P, None) == 3
+    assert f(1, 4, 4, big_k, P, P, P, None, None, P, P, 1 << 40, None) == 3
+    assert b(4, 4, (1 << 22) + 1, P, P, None, P, None) == 3
+    assert b(1 << 20, (1 << 19) + 1, 8, P, P, None, P, None) == 3
+    # the limits themselves are valid shapes: the call proceeds to the pointer checks
+    assert g(1, 1 << 20, 1 << 19, 1 << 22, None, P, None, P, P, None, None, P, None) == 1
+    assert b(1 << 20, 1 << 19, 1 << 22, None, P, None, P, None) == 1
