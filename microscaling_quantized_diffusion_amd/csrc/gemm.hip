@@ -1,42 +1,24 @@
-// Tiled GEMMs on the gfx950 matrix cores, one kernel template for four
-// operand modes:
-//   MX8  : MXFP8 (E4M3 codes, E8M0 scale per 32 K)  -> scaled MFMA, FP8
-//   MX4  : MXFP4 (E2M1 codes, E8M0 scale per 32 K)  -> scaled MFMA, FP4
-//   NV4  : NVFP4 (E2M1 codes, E4M3 scale per 16 K, fp32 tensor scales)
-//          -> codes dequantized in registers to f16 (exact) -> f16 MFMA
-//   BF16 : unquantized bf16 operands                 -> bf16 MFMA
-// computing out[m, n] = sum_k deq(A)[m, k] * deq(W)[n, k] (+ bias[n]) with
-// an fp32 accumulator and a nearest-even bf16 result.  This is the GEMM of
-// the aitrends.kr MXFP8/NVFP4 article ("Section details": quantized weights
-// times dynamically quantized activations; second "Evidence" block: small
-// layers stay in bf16).
-//
-// Data flow per workgroup (one BM x BN output tile):
-//   global --buffer_load_dwordx4 ... lds (LDS DMA, no VGPR staging)--> LDS
-//   (two stages; every row holds one 128-byte K slab; 16-byte chunks are
-//   XOR-swizzled by row) --ds_read_b128--> MFMA operands.  The loads of K
-//   step k+1 are in flight while step k computes.  The buffer resource spans
-//   the tile's rows only, so rows past M / N and the K tail read as zeros.
-//   Per-lane scale bytes are read from global memory one K step ahead.
-//
-// Operand layouts (measured on gfx950):
-//   scaled 16x16x128: lane l serves row l % 16 and K-quarter q = l / 16;
-//     FP8 operand bytes 0-15 = K [16q, 16q+16), bytes 16-31 = K [64+16q, +16);
-//     FP4 operand bytes 0-15 = K [32q, 32q+32), low nibble first;
-//     the scale byte of lane l is that of K-block q of row l % 16.
-//   bf16/f16 16x16x32: lane l holds 8 K-values of row l % 16; any K order
-//     works as long as both operands use the same one.
-// Every mode therefore reads 16-byte chunks q and 4+q of each 128-byte row
-// slab.  Weights are the MFMA "A" operand and activations the "B" operand,
-// so the accumulators of lane l are 4 consecutive output columns of one
-// output row (8-byte stores in the epilogue).
-//
-// NV4 dequantization: the E4M3 scale is not a power of two, so it cannot
-// ride on the E8M0 scale port; e2m1 * e4m3 needs at most 6 significant
-// bits and lies in [2^-10, 2688], so it is exact in f16.  Each dword of
-// codes (8 elements, inside one 16-element block) is widened with
-// v_cvt_scalef32_pk_f16_fp4 (unit scale) and multiplied by the block scale
-// with v_pk_mul_f16; the tensor scales multiply the fp32 result.
+// GEMMs on the gfx950 matrix cores for the block-scaled formats and bf16,
+// computing out[m, n] = sum_k deq(A)[m, k] * deq(W)[n, k] (+ bias[n]) with an
+// fp32 accumulator and a nearest-even bf16 result.  This is the GEMM of the
+// aitrends.kr MXFP8/NVFP4 article ("Section details": quantized weights times
+// dynamically quantized activations; second "Evidence" block: small layers
+// stay in bf16).  Kernels:
+//   mxp_gemm_kernel   MXFP8 / MXFP4 main path: 256x256 or 256x320 tiles,
+//                     scaled 32x32x64 MFMA (hardware E8M0 block scales),
+//                     two-stage LDS-DMA ring of 128-byte K slabs.
+//   nv4_gemm_kernel   NVFP4 main path: the same tile and ring; codes widened
+//                     to f16 with the E4M3 block scale applied (exact), f16
+//                     32x32x16 MFMA, tensor scales in the epilogue.
+//   gemm_kernel       generic 16x16 path for every mode (MX8 / MX4 / NV4 /
+//                     BF16) and shape: K not a multiple of the main paths'
+//                     slab, unaligned scale rows, and the bf16 MFMA GEMM.
+//   bf16_skinny_kernel / bf16_generic_kernel   bf16 fallback for a few
+//                     activation rows (an HBM stream of W) and for K % 8 != 0.
+// Weights are the MFMA "A" operand and activations the "B" operand, so a
+// lane's accumulators are consecutive output columns of one output row.
+// Every kernel's buffer resources span only the tile's rows, so rows past
+// M / N and the K tail read as zeros.
 #include <utility>
 
 #include "mxq_internal.h"
@@ -136,6 +118,27 @@ __device__ __forceinline__ void wait_vmcnt() {
 // s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (0x7 << 4)); }
 
+// Generic path.  Data flow per workgroup (one BM x BN output tile):
+//   global --buffer_load_dwordx4 ... lds (LDS DMA, no VGPR staging)--> LDS
+//   (two stages; every row holds one 128-byte K slab; 16-byte chunks are
+//   XOR-swizzled by row) --ds_read_b128--> MFMA operands.  The loads of K
+//   step k+1 are in flight while step k computes.  Per-lane scale bytes are
+//   read from global memory one K step ahead.
+// Operand layouts (measured on gfx950):
+//   scaled 16x16x128: lane l serves row l % 16 and K-quarter q = l / 16;
+//     FP8 operand bytes 0-15 = K [16q, 16q+16), bytes 16-31 = K [64+16q, +16);
+//     FP4 operand bytes 0-15 = K [32q, 32q+32), low nibble first;
+//     the scale byte of lane l is that of K-block q of row l % 16.
+//   bf16/f16 16x16x32: lane l holds 8 K-values of row l % 16; any K order
+//     works as long as both operands use the same one.
+// Every mode therefore reads 16-byte chunks q and 4+q of each 128-byte row
+// slab, and the accumulators of lane l are 4 consecutive output columns of
+// one output row (8-byte stores in the epilogue).  NV4 codes (one dword = 8
+// elements inside one 16-element block) are widened with
+// v_cvt_scalef32_pk_f16_fp4 at unit scale and multiplied by the E4M3 block
+// scale with v_pk_mul_f16 (e2m1 * e4m3 needs at most 6 significant bits and
+// lies in [2^-10, 2688]: exact in f16); the tensor scales multiply the fp32
+// result.
 template <int MODE, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
