@@ -136,6 +136,31 @@ def run_layer(layer, dev, steps, warmup, rotate, seed=0):
     return res
 
 
+def run_sequence(workload, dev, steps, warmup):
+    """One DiT block's linears back to back (selective rule included): eager calls vs one HIP-graph replay."""
+    import torch
+
+    from microscaling_quantized_diffusion_amd import mxq
+    from microscaling_quantized_diffusion_amd.inputs import WORKLOADS, make_layer_inputs
+
+    layers, inputs = [], []
+    for i, ly in enumerate(WORKLOADS[workload].layers):
+        a_bits, w_bits = make_layer_inputs(ly, seed=i)
+        layers.append(mxq.QuantLinear.from_weight(ly.fmt, _upload(w_bits, dev)))
+        inputs.append(_upload(a_bits, dev))
+    seq = mxq.LinearSequence(layers, inputs)
+    ms_eager = _time_loop(lambda i: seq(), steps, warmup)
+    graphed = mxq.GraphedCall(seq)
+    ms_graph = _time_loop(lambda i: graphed(), steps, warmup)
+    flops = sum(2.0 * ly.M * ly.N * ly.K for ly in WORKLOADS[workload].layers)
+    res = {"workload": workload, "sequence": [ly.name for ly in WORKLOADS[workload].layers],
+           "ms_eager": ms_eager, "ms_graph": ms_graph, "tflops_eager": flops / ms_eager / 1e9,
+           "tflops_graph": flops / ms_graph / 1e9}
+    del seq, graphed, layers, inputs
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(layer, sample_rows):
     """Time the CPU oracle (quantize A, dequantize both operands, fp64 GEMM) on a row sample of the workload."""
     import oracle
@@ -245,6 +270,11 @@ def main():
                 e["workload"] = name
                 extra.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in e.items()})
         line["extra"] = extra
+        line["block_sequences"] = []
+        for name in ("flux_double_block_b1", "flux_double_block_b4"):
+            print(f"# timing the {name} linear sequence, eager and graphed", file=sys.stderr, flush=True)
+            e = run_sequence(name, dev, max(10, args.steps // 2), 3)
+            line["block_sequences"].append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in e.items()})
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

@@ -13,7 +13,7 @@ from __future__ import annotations
 import ctypes
 import os
 from dataclasses import dataclass
-from typing import Optional
+from typing import Callable, List, Optional
 
 import torch
 
@@ -223,3 +223,51 @@ class QuantLinear:
         if self.weight_bf16 is None:
             raise ValueError("layer falls back to bf16 but holds no bf16 weight")
         return gemm_bf16(x, self.weight_bf16, self.bias, out)
+
+
+class LinearSequence:
+    """A fixed sequence of linears over static input tensors (one DiT block's
+    linears, say), with every output and fused-call workspace preallocated, so
+    that calling it allocates nothing and it can be captured into one HIP graph.
+    Each layer applies the selective rule as QuantLinear does."""
+
+    def __init__(self, layers: List[QuantLinear], inputs: List[torch.Tensor]):
+        if len(layers) != len(inputs):
+            raise ValueError("one input per layer")
+        self.layers, self.inputs = list(layers), list(inputs)
+        self.outs: List[torch.Tensor] = []
+        self.workspaces: List[Optional[torch.Tensor]] = []
+        for lin, x in zip(self.layers, self.inputs):
+            M, K = x.shape
+            N = lin.qweight.rows if lin.qweight is not None else lin.weight_bf16.shape[0]
+            self.outs.append(torch.empty((M, N), dtype=torch.bfloat16, device=x.device))
+            quantized = lin.qweight is not None and should_quantize(M, K, N)
+            need = workspace_bytes(lin.fmt, M, K, True) if quantized else 0
+            self.workspaces.append(torch.empty(max(need, 1), dtype=torch.uint8, device=x.device) if quantized else None)
+
+    def __call__(self) -> List[torch.Tensor]:
+        for lin, x, out, ws in zip(self.layers, self.inputs, self.outs, self.workspaces):
+            lin(x, out, ws)
+        return self.outs
+
+
+class GraphedCall:
+    """Captures `fn` (library calls on static tensors, issued on torch's current
+    stream) into one HIP graph and replays it with a single launch.  `fn` runs
+    `warmup` times on a side stream of default priority before capture; the
+    library itself allocates, synchronises and memsets nothing, so every entry
+    point can be captured.  Replays read the static inputs' current contents."""
+
+    def __init__(self, fn: Callable[[], object], warmup: int = 1):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            fn()
+
+    def __call__(self) -> None:
+        self.graph.replay()
