@@ -34,7 +34,8 @@ formats  closed-form decode of bf16 / E4M3 / E2M1 / E8M0 and the
 exact    scalar reference in exact rational arithmetic (fractions.Fraction)
          used to pin the vectorized code on small and exhaustive cases.
 quant    MXFP8 / MXFP4 / NVFP4 quantizers and dequantizers (numpy, fp64).
-gemm     fp64 GEMM references and the normwise error metric.
+gemm     fp64 GEMM references, the normwise error metric and the GELU
+         (tanh form) applied before an epilogue's requantization.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, exhaustive brute force, library decoders and hand-
@@ -66,6 +67,7 @@ from .quant import (  # noqa: F401
 from .gemm import (  # noqa: F401
     bf16_half_ulp,
     bf16_round,
+    gelu_tanh,
     gemm_error,
     rounding_mismatch_rate,
     gemm_bf16_ref,

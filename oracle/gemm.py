@@ -41,6 +41,19 @@ def gemm_nvfp4_ref(a_codes, a_scales, a_ts, w_codes, w_scales, w_ts, bias=None) 
     return _matmul_t(dequant_nvfp4(a_codes, a_scales, a_ts), dequant_nvfp4(w_codes, w_scales, w_ts), bias)
 
 
+def gelu_tanh(x: np.ndarray) -> np.ndarray:
+    """GELU in its tanh form, 0.5 x (1 + tanh(sqrt(2 / pi) (x + 0.044715 x^3))), in fp64.
+
+    The activation between a DiT MLP's up- and down-projections (wavespeed.ai
+    "WaveSpeedAI X DataCrunch: FLUX real-time image inference on B200", model
+    overview: the MLP of each transformer block); the tanh form is a reading,
+    the one FLUX's MLP uses.  Applied to the fp64 GEMM reference when checking
+    the GEMM epilogue that quantizes act(y) for the next layer.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x * x * x)))
+
+
 def gemm_bf16_ref(a_bits, w_bits, bias=None) -> np.ndarray:
     """fp64 reference of the bf16 GEMM (inputs as bf16 bit patterns)."""
     return _matmul_t(decode_bf16(a_bits), decode_bf16(w_bits), bias)

@@ -22,6 +22,7 @@ from oracle import (
     quantize_mx,
     quantize_nvfp4,
     unpack_fp4,
+    gelu_tanh,
 )
 from oracle import exact
 from microscaling_quantized_diffusion_amd.inputs import bf16_bits_from_f32
@@ -189,3 +190,28 @@ def test_gemm_error_separates_output_rounding():
     # truncation toward zero instead of rounding shows up as mismatches
     trunc = np.sign(r) * np.floor(np.abs(r) / (2 * bf16_half_ulp(r))) * (2 * bf16_half_ulp(r))
     assert rounding_mismatch_rate(trunc, r) > 0.3
+
+
+def test_gelu_tanh_odd_identity_and_limits():
+    """The tanh form satisfies gelu(x) - gelu(-x) = x exactly (its odd part is x/2), vanishes at 0,
+    and tends to x / 0 for large positive / negative x."""
+    x = np.linspace(-9, 9, 3601)
+    np.testing.assert_allclose(gelu_tanh(x) - gelu_tanh(-x), x, rtol=0, atol=1e-12)
+    assert gelu_tanh(np.array([0.0]))[0] == 0.0
+    assert abs(gelu_tanh(np.array([10.0]))[0] - 10.0) < 1e-12
+    assert abs(gelu_tanh(np.array([-10.0]))[0]) < 1e-12
+
+
+def test_gelu_tanh_close_to_erf_gelu():
+    """Against GELU's defining form x * Phi(x) (math.erf): the tanh form deviates by well under 1e-3,
+    while dropping its cubic term, or changing a constant by 1%, deviates by more."""
+    import math
+
+    x = np.linspace(-6, 6, 4801)
+    exact = np.array([v * 0.5 * (1.0 + math.erf(v / math.sqrt(2.0))) for v in x])
+    dev = np.max(np.abs(gelu_tanh(x) - exact))
+    assert dev < 5e-4, dev
+    no_cubic = 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * x))
+    assert np.max(np.abs(no_cubic - exact)) > 5e-3
+    off = 0.5 * x * (1.0 + np.tanh(1.01 * np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+    assert np.max(np.abs(off - exact)) > 1e-3
