@@ -161,6 +161,45 @@ def run_sequence(workload, dev, steps, warmup):
     return res
 
 
+def run_producer_fused(dev, steps, warmup, rotate):
+    """FLUX MLP at 1024x1024 (4608 tokens, 3072 -> 12288 -> 3072, MXFP8): the up-projection's output
+    quantized for the down-projection by a separate quantizer pass vs inside the GEMM epilogue."""
+    import torch
+
+    from microscaling_quantized_diffusion_amd import mxq
+    from microscaling_quantized_diffusion_amd.inputs import WORKLOADS, make_layer_inputs
+
+    up = WORKLOADS["flux_mlp_up_mxfp8"].layers[0]
+    M, D, H = up.M, up.K, up.N
+    a_bits, w_bits = make_layer_inputs(up, seed=0)
+    _, wd_bits = make_layer_inputs(up, seed=1, N=D, K=H)
+    xs = [_upload(a_bits, dev)] + [None] * (rotate - 1)
+    for i in range(1, rotate):
+        xs[i] = xs[0].clone()
+    qxs = [mxq.quantize("mxfp8", x) for x in xs]
+    w_up = mxq.quantize("mxfp8", _upload(w_bits, dev))
+    w_dn = mxq.quantize("mxfp8", _upload(wd_bits, dev))
+    h = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    qh = mxq.QTensor("mxfp8", torch.empty((M, H), dtype=torch.uint8, device=dev),
+                     torch.empty((M, H // 32), dtype=torch.uint8, device=dev), None, H)
+    y = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    up_sep = _time_loop(lambda i: (mxq.gemm(qxs[i % rotate], w_up, None, h), mxq.quantize("mxfp8", h, qh)), steps,
+                        warmup)
+    up_fused = _time_loop(lambda i: mxq.gemm_requant(qxs[i % rotate], w_up, "mxfp8", None, "none", qh), steps,
+                          warmup)
+    up_fused_gelu = _time_loop(lambda i: mxq.gemm_requant(qxs[i % rotate], w_up, "mxfp8", None, "gelu_tanh", qh),
+                               steps, warmup)
+    chain_sep = _time_loop(lambda i: (mxq.gemm(qxs[i % rotate], w_up, None, h), mxq.quantize("mxfp8", h, qh),
+                                      mxq.gemm(qh, w_dn, None, y)), steps, warmup)
+    chain_fused = _time_loop(lambda i: (mxq.gemm_requant(qxs[i % rotate], w_up, "mxfp8", None, "gelu_tanh", qh),
+                                        mxq.gemm(qh, w_dn, None, y)), steps, warmup)
+    del xs, qxs, w_up, w_dn, h, qh, y
+    torch.cuda.empty_cache()
+    return {"shape": f"{M}x{D} -> {H} -> {D}", "up_gemm_then_quantize_ms": up_sep, "up_requant_gemm_ms": up_fused,
+            "up_requant_gemm_gelu_ms": up_fused_gelu, "mlp_chain_separate_quantizer_ms": chain_sep,
+            "mlp_chain_producer_fused_gelu_ms": chain_fused}
+
+
 def cpu_baseline(layer, sample_rows):
     """Time the CPU oracle (quantize A, dequantize both operands, fp64 GEMM) on a row sample of the workload."""
     import oracle
@@ -270,6 +309,9 @@ def main():
                 e["workload"] = name
                 extra.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in e.items()})
         line["extra"] = extra
+        print("# timing producer-fused quantization on the FLUX MLP", file=sys.stderr, flush=True)
+        pf = run_producer_fused(dev, max(10, args.steps // 2), 3, min(args.rotate, 4))
+        line["producer_fused"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in pf.items()}
         line["block_sequences"] = []
         for name in ("flux_double_block_b1", "flux_double_block_b4"):
             print(f"# timing the {name} linear sequence, eager and graphed", file=sys.stderr, flush=True)

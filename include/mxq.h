@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 1
+#define MXQ_ABI_VERSION 2
 
 typedef enum {
   MXQ_FMT_MXFP8 = 1, /* E4M3 codes, E8M0 scale per 32 K-elements */
@@ -142,6 +142,33 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K,
                                 const void* w_codes, const void* w_scales, const float* w_tensor_scale,
                                 const void* bias_bf16, void* out_bf16, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/*
+ * Block-scaled GEMM whose epilogue emits the next layer's MX-quantized
+ * activations (producer-fused quantization; the devin.kr article on FLUX
+ * image generation accelerated 4.45x on Blackwell, "Compute efficiency and
+ * acceleration": fused activation kernels around the low-precision GEMMs):
+ *   y = act(deq(A) deq(W)^T + bias) formed in fp32 and rounded to bf16
+ *   (nearest even), then quantized along N in 32-column blocks exactly as
+ *   mxq_quantize(out_fmt, y) would, so the codes feed the next mxq_gemm as
+ *   its A operand without y passing through memory as bf16.
+ *   act: 0 = none, 1 = GELU in its tanh form,
+ *        0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))).
+ *
+ *   fmt, M, N, K, a_*, w_*, bias_bf16   as in mxq_gemm (MX formats only)
+ *   out_fmt        MXQ_FMT_MXFP8 or MXQ_FMT_MXFP4
+ *   out_bf16       device bf16 [M, N], 16-byte aligned, or NULL: also store y
+ *   out_codes      device, out: uint8 [M, N] (MXFP8) or [M, N/2] (MXFP4),
+ *                  16-byte aligned
+ *   out_scales     device, out: uint8 [M, N/32] E8M0
+ * Supported where N % 32 == 0, K % 128 == 0 (MXFP8 operands) or K % 256 == 0
+ * (MXFP4 operands), and the scale rows are 4-byte aligned; other shapes
+ * return MXQ_ERR_UNSUPPORTED.  Sizes otherwise as in mxq_gemm.
+ */
+mxq_status mxq_gemm_requant(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void* a_codes,
+                            const void* a_scales, const void* w_codes, const void* w_scales, const void* bias_bf16,
+                            int act, mxq_format out_fmt, void* out_bf16, void* out_codes, void* out_scales,
+                            void* stream);
 
 /*
  * bf16 GEMM for layers left unquantized by the selective rule:

@@ -21,6 +21,7 @@
 // M / N and the K tail read as zeros.
 #include <utility>
 
+#include "mx_encode.h"
 #include "mxq_internal.h"
 
 namespace mxq {
@@ -391,7 +392,47 @@ hipError_t launch_tiled(int64_t M, int64_t N, int64_t K, const void* a, const ui
 // the accumulator layout's scattered 8-byte pieces.  Lane (r32, q) holds, for
 // the 32 x 32 tile (i, j), output row 32j + r32 and columns 32i + 8g + 4q + v
 // in acc[i][j][4g + v].
-template <int TI, int TJ, int WTM, int WTN>
+// Output activations applied in fp32 before the bf16 rounding.
+enum Act { ACT_NONE = 0, ACT_GELU_TANH = 1 };
+
+// GELU in its tanh form, 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), the
+// activation between a DiT MLP's up- and down-projections (wavespeed.ai FLUX
+// article, model overview: the MLP of each transformer block).  Evaluated as
+// x / (1 + exp(-2u)), the same function (0.5 (1 + tanh u) = 1 / (1 + e^-2u)),
+// with the hardware exp2 and reciprocal: measured within 1.5 fp32 ulp of the
+// fp64 function wherever |GELU(x)| >= 0.25, at a fraction of tanhf's cost.
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float u = 0.7978845608028654f * (x + 0.044715f * x * x * x);
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
+}
+
+// Four outputs of lane (r32, q) for the 32 x 32 tile (i, j) and column group g
+// (columns nw + 32i + 8g + 4q + v): acc * oscale (+ bias), then the
+// activation, rounded to bf16 (nearest even, v_cvt_pk_bf16_f32), packed two
+// per dword.
+template <int ACT, int TI, int TJ>
+__device__ __forceinline__ uint2 epi_bf16x4(const v16f (&acc)[TI][TJ], int i, int j, int g, float oscale,
+                                          const uint16_t* __restrict__ bias, int N, int nw, int q) {
+  float fv[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) fv[v] = acc[i][j][4 * g + v] * oscale;
+  if (bias) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int nb = nw + 32 * i + 8 * g + 4 * q + v;
+      if (nb < N) fv[v] += bf16_to_f32(bias[nb]);
+    }
+  }
+  if constexpr (ACT == ACT_GELU_TANH) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) fv[v] = gelu_tanh(fv[v]);
+  }
+  const bf16x2 p0 = __builtin_convertvector(f32x2{fv[0], fv[1]}, bf16x2);
+  const bf16x2 p1 = __builtin_convertvector(f32x2{fv[2], fv[3]}, bf16x2);
+  return make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
+}
+
+template <int TI, int TJ, int WTM, int WTN, int ACT = ACT_NONE>
 __device__ __forceinline__ void store_tile_bf16(const v16f (&acc)[TI][TJ], float oscale, uint8_t* region,
                                                 const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
                                                 int M, int N, int mw, int nw, int lane) {
@@ -411,26 +452,11 @@ __device__ __forceinline__ void store_tile_bf16(const v16f (&acc)[TI][TJ], float
       __builtin_amdgcn_wave_barrier();
     }
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float fv[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) fv[v] = acc[i][j][4 * g + v] * oscale;
-        if (bias) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int nb = nw + 32 * i + 8 * g + 4 * q + v;
-            if (nb < N) fv[v] += bf16_to_f32(bias[nb]);
-          }
-        }
-        // v_cvt_pk_bf16_f32: two nearest-even roundings per instruction
-        const bf16x2 p0 = __builtin_convertvector(f32x2{fv[0], fv[1]}, bf16x2);
-        const bf16x2 p1 = __builtin_convertvector(f32x2{fv[2], fv[3]}, bf16x2);
+      for (int g = 0; g < 4; ++g)
         *reinterpret_cast<uint2*>(region + r32 * EPI_PITCH + (32 * i + 8 * g + 4 * q) * 2) =
-            make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
-      }
-    }
+            epi_bf16x4<ACT>(acc, i, j, g, oscale, bias, N, nw, q);
     // the wave reads back what its own lanes wrote
     wait_lgkmcnt0();
     __builtin_amdgcn_wave_barrier();
@@ -450,6 +476,84 @@ __device__ __forceinline__ void store_tile_bf16(const v16f (&acc)[TI][TJ], float
         for (int e = 0; e < 8; ++e)
           if (n + e < N) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
       }
+    }
+  }
+}
+
+// Epilogue that emits the next layer's MX-quantized activations instead of
+// (or beside) bf16: the outputs are formed and rounded to bf16 exactly as
+// store_tile_bf16 does, then each row's 32-column block is encoded with the
+// activation quantizer's arithmetic (mx_encode.h), so the codes and scales
+// equal those of quantizing the bf16 output.  Lanes r32 and r32 + 32 hold the
+// two 16-column halves of a row's block; their maxima meet through one
+// v_permlane32_swap.  Codes are staged through `region` and written as whole
+// row segments; requires N % 32 == 0 (whole blocks).  OELEM: 1 = E4M3 codes
+// [M, N], 2 = E2M1 codes [M, N/2]; scales E8M0 [M, N/32].
+template <int TI, int TJ, int WTM, int WTN, int OELEM, int ACT>
+__device__ __forceinline__ void store_tile_requant(const v16f (&acc)[TI][TJ], float oscale, uint8_t* region,
+                                                   const uint16_t* __restrict__ bias, uint8_t* __restrict__ qcodes,
+                                                   uint8_t* __restrict__ qscales, int M, int N, int mw, int nw,
+                                                   int lane) {
+  constexpr int CB = OELEM == 1 ? 32 : 16;  // code bytes per row and 32-column block
+  constexpr int RB = TI * CB;               // code bytes per row of the wave's segment
+  constexpr int PITCH = RB + 16;
+  constexpr int CPR = RB / 16;              // 16-byte chunks per row segment
+  constexpr int RPI = 64 / CPR;
+  constexpr int NIT = (32 + RPI - 1) / RPI;
+  constexpr int COLS_PER_CHUNK = 16 * 32 / CB;
+  static_assert(TI <= 4 && CPR <= 64, "requant epilogue shape");
+  const int q = lane >> 5, r32 = lane & 31;
+  const size_t crow = OELEM == 1 ? (size_t)N : (size_t)N / 2;  // code bytes per output row
+  const int nsb = N / 32;                                      // scale bytes per output row
+  const int cc = lane % CPR;
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    if (j > 0) {
+      wait_lgkmcnt0();
+      __builtin_amdgcn_wave_barrier();
+    }
+    uint32_t sword = 0;  // scale bytes of blocks i = 0 .. TI-1 of this lane's row
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      uint2 v[4];
+      uint32_t m = 0;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        v[g] = epi_bf16x4<ACT>(acc, i, j, g, oscale, bias, N, nw, q);
+        m = max(m, mx_absmax_bits4(v[g].x, v[g].y));
+      }
+      const auto sw = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+      m = max(sw[0], sw[1]);
+      const bool nonfinite = m >= 0x7F80u;  // NaN or Inf in the block: NaN scale, zero codes
+      const int e = nonfinite ? 0 : mx_shared_exponent<OELEM>(m);
+      sword |= (nonfinite ? 0xFFu : (uint32_t)(e + 127)) << (8 * i);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if constexpr (OELEM == 1) {
+          const uint32_t c = nonfinite ? 0u : mx_encode_fp8x4(v[g].x, v[g].y, e);
+          *reinterpret_cast<uint32_t*>(region + r32 * PITCH + 32 * i + 8 * g + 4 * q) = c;
+        } else {
+          const uint32_t c = nonfinite ? 0u : mx_encode_fp4x4<0>(0u, v[g].x, v[g].y, e);
+          *reinterpret_cast<uint16_t*>(region + r32 * PITCH + 16 * i + 4 * g + 2 * q) = (uint16_t)c;
+        }
+      }
+    }
+    const int mrow = mw + 32 * j + r32;
+    if (q == 0 && mrow < M) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        if (nw + 32 * i < N) qscales[(size_t)mrow * nsb + nw / 32 + i] = (uint8_t)(sword >> (8 * i));
+    }
+    wait_lgkmcnt0();
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int lr = it * RPI + lane / CPR;
+      if (lr >= 32 || lane >= RPI * CPR) continue;
+      const int mr = mw + 32 * j + lr;
+      if (mr >= M || nw + cc * COLS_PER_CHUNK >= N) continue;  // whole blocks: a chunk is inside or outside N
+      const uint4 val = *reinterpret_cast<const uint4*>(region + lr * PITCH + 16 * cc);
+      *reinterpret_cast<uint4*>(qcodes + (size_t)mr * crow + (size_t)nw * CB / 32 + 16 * cc) = val;
     }
   }
 }
@@ -498,11 +602,14 @@ __device__ __forceinline__ void store_tile_bf16(const v16f (&acc)[TI][TJ], float
 // Requires K % (2 * SLAB) == 0 (FP8: 128-element K pairs) or K % (2 * SLAB)
 // == 0 in elements for FP4 (K % 256 at SLAB = 128), and 4-byte aligned scale
 // rows.
-template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS>
+// REQ: 0 = bf16 output; 1 / 2 = the output MX-quantized to E4M3 / E2M1 codes
+// and E8M0 scales (qcodes, qscales), with the bf16 output also written when
+// `out` is not null.  ACT: activation applied before the bf16 rounding.
+template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS, int REQ = 0, int ACT = ACT_NONE>
 __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1) void mxp_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
     const uint8_t* __restrict__ Ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N,
-    int K) {
+    int K, uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TJ = WTM / 32, TI = WTN / 32;  // 32 x 32 tiles per wave (M, N)
@@ -712,7 +819,18 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
   __builtin_amdgcn_s_barrier();
   const int ea = wave / WPS;
   uint8_t* region = (ea == 0 ? st0 : ea == 1 ? st1 : ea == 2 ? st2 : st3) + (wave % WPS) * EPI_BYTES;
-  store_tile_bf16<TI, TJ, WTM, WTN>(acc, 1.0f, region, bias, out, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
+  if constexpr (REQ == 0) {
+    store_tile_bf16<TI, TJ, WTM, WTN, ACT>(acc, 1.0f, region, bias, out, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
+  } else {
+    store_tile_requant<TI, TJ, WTM, WTN, REQ, ACT>(acc, 1.0f, region, bias, qcodes, qscales, M, N, m0 + wm * WTM,
+                                                   n0 + wn * WTN, lane);
+    if (out) {
+      wait_lgkmcnt0();
+      __builtin_amdgcn_wave_barrier();
+      store_tile_bf16<TI, TJ, WTM, WTN, ACT>(acc, 1.0f, region, bias, out, M, N, m0 + wm * WTM, n0 + wn * WTN,
+                                             lane);
+    }
+  }
 }
 
 // Compute units of the current device (cached per device).
@@ -737,12 +855,13 @@ inline bool mx_prefer_wide_tile(int64_t M, int64_t N, int64_t cus) {
   return r320 * 320 < r256 * 256;
 }
 
-template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS>
+template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS, int REQ = 0, int ACT = ACT_NONE>
 hipError_t launch_mxp(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as, const uint8_t* w,
-                      const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream) {
+                      const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream,
+                      uint8_t* qcodes = nullptr, uint8_t* qscales = nullptr) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((mxp_gemm_kernel<ELEM, BM, BN, WM, WN, SLAB, NS>), dim3((unsigned)tiles), dim3(64 * WM * WN),
-                     0, stream, a, as, w, ws, bias, out, (int)M, (int)N, (int)K);
+  hipLaunchKernelGGL((mxp_gemm_kernel<ELEM, BM, BN, WM, WN, SLAB, NS, REQ, ACT>), dim3((unsigned)tiles),
+                     dim3(64 * WM * WN), 0, stream, a, as, w, ws, bias, out, (int)M, (int)N, (int)K, qcodes, qscales);
   return hipGetLastError();
 }
 
@@ -1054,6 +1173,39 @@ hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8
                                              out, stream);
   return launch_tiled<MX4, MXQ_TILE_MX>(M, N, K, a_codes, a_scales, w_codes, w_scales, nullptr, nullptr, bias, out,
                                            stream);
+}
+
+bool mx_requant_supported(int elem, int64_t N, int64_t K, const uint8_t* a_scales, const uint8_t* w_scales) {
+  const bool scales_aligned = (((uintptr_t)a_scales | (uintptr_t)w_scales) & 3) == 0;
+  return scales_aligned && N % 32 == 0 && (elem == 1 ? K % 128 == 0 : K % 256 == 0);
+}
+
+template <int ELEM, int OELEM>
+hipError_t launch_requant_act(int act, int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
+                              const uint8_t* w, const uint8_t* ws, const uint16_t* bias, uint16_t* out,
+                              uint8_t* qcodes, uint8_t* qscales, hipStream_t stream) {
+  if (act == ACT_GELU_TANH)
+    return launch_mxp<ELEM, 256, 256, 4, 2, 128, 2, OELEM, ACT_GELU_TANH>(M, N, K, a, as, w, ws, bias, out, stream,
+                                                                          qcodes, qscales);
+  return launch_mxp<ELEM, 256, 256, 4, 2, 128, 2, OELEM, ACT_NONE>(M, N, K, a, as, w, ws, bias, out, stream, qcodes,
+                                                                   qscales);
+}
+
+hipError_t launch_mx_gemm_requant(int elem, int out_elem, int act, int64_t M, int64_t N, int64_t K,
+                                  const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
+                                  const uint8_t* w_scales, const uint16_t* bias, uint16_t* out_bf16,
+                                  uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream) {
+  if (elem == 1 && out_elem == 1)
+    return launch_requant_act<1, 1>(act, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16, out_codes,
+                                    out_scales, stream);
+  if (elem == 1)
+    return launch_requant_act<1, 2>(act, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16, out_codes,
+                                    out_scales, stream);
+  if (out_elem == 1)
+    return launch_requant_act<2, 1>(act, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16, out_codes,
+                                    out_scales, stream);
+  return launch_requant_act<2, 2>(act, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16, out_codes,
+                                  out_scales, stream);
 }
 
 hipError_t launch_nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,

@@ -162,6 +162,26 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K,
   return launch_status(e);
 }
 
+mxq_status mxq_gemm_requant(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void* a_codes,
+                            const void* a_scales, const void* w_codes, const void* w_scales, const void* bias_bf16,
+                            int act, mxq_format out_fmt, void* out_bf16, void* out_codes, void* out_scales,
+                            void* stream) {
+  if (!valid_format(fmt) || !valid_format(out_fmt)) return MXQ_ERR_FORMAT;
+  if (!valid_k(fmt, K) || !valid_gemm(M, N, K) || N % 32 != 0) return MXQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXQ_OK;  // empty output: nothing to launch, whatever the pointers
+  if (!a_codes || !a_scales || !w_codes || !w_scales || !out_codes || !out_scales) return MXQ_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned16(out_codes)) return MXQ_ERR_ALIGN;
+  if (out_bf16 && !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
+  if (fmt == MXQ_FMT_NVFP4 || out_fmt == MXQ_FMT_NVFP4 || (act != 0 && act != 1)) return MXQ_ERR_UNSUPPORTED;
+  if (!mx_requant_supported(elem_of(fmt), N, K, (const uint8_t*)a_scales, (const uint8_t*)w_scales))
+    return MXQ_ERR_UNSUPPORTED;
+  return launch_status(launch_mx_gemm_requant(elem_of(fmt), elem_of(out_fmt), act, M, N, K, (const uint8_t*)a_codes,
+                                              (const uint8_t*)a_scales, (const uint8_t*)w_codes,
+                                              (const uint8_t*)w_scales, (const uint16_t*)bias_bf16,
+                                              (uint16_t*)out_bf16, (uint8_t*)out_codes, (uint8_t*)out_scales,
+                                              (hipStream_t)stream));
+}
+
 mxq_status mxq_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* a_bf16, const void* w_bf16,
                          const void* bias_bf16, void* out_bf16, void* stream) {
   if (K <= 0 || !valid_gemm(M, N, K)) return MXQ_ERR_SHAPE;

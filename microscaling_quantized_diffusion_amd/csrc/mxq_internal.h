@@ -28,6 +28,16 @@ hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8
                           const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
                           const uint16_t* bias, uint16_t* out, hipStream_t stream);
 
+// MX GEMM whose epilogue emits the output MX-quantized (out_elem: 1 = E4M3,
+// 2 = E2M1; E8M0 scales per 32 output columns), after an optional activation
+// (act: 0 none, 1 GELU tanh form); out_bf16 (nullable) also receives the bf16
+// values that were quantized.  Only where mx_requant_supported() holds.
+bool mx_requant_supported(int elem, int64_t N, int64_t K, const uint8_t* a_scales, const uint8_t* w_scales);
+hipError_t launch_mx_gemm_requant(int elem, int out_elem, int act, int64_t M, int64_t N, int64_t K,
+                                  const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
+                                  const uint8_t* w_scales, const uint16_t* bias, uint16_t* out_bf16,
+                                  uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream);
+
 // NVFP4 GEMM.
 hipError_t launch_nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                              const float* a_ts, const uint8_t* w_codes, const uint8_t* w_scales,

@@ -16,22 +16,11 @@
 // measured equal to the definition for every input (FP8 after a clamp, see
 // below); NVFP4 codes, whose divisor is not a power of two, from exact
 // comparisons against per-block thresholds.
+#include "mx_encode.h"
 #include "mxq_internal.h"
 
 namespace mxq {
 namespace {
-
-// emax: exponent of the element format's largest power of two
-template <int ELEM>
-struct ElemFmt;
-template <>
-struct ElemFmt<1> {  // E4M3: max 448 = 1.75 * 2^8
-  static constexpr int EMAX = 8;
-};
-template <>
-struct ElemFmt<2> {  // E2M1: max 6 = 1.5 * 2^2
-  static constexpr int EMAX = 2;
-};
 
 __device__ __forceinline__ uint32_t quad_swap1(uint32_t v) {  // lanes 0<->1, 2<->3 of each quad
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
@@ -41,30 +30,8 @@ __device__ __forceinline__ uint32_t quad_swap2(uint32_t v) {  // lanes 0<->2, 1<
 }
 
 // Largest |x| (as bf16 magnitude bits) of the 8 elements in a 16-byte chunk.
-// For finite values the magnitude order equals the integer order of the bits;
-// NaN and Inf compare above every finite value (>= 0x7F80).
 __device__ __forceinline__ uint32_t chunk_absmax_bits(const uint4& v) {
-  uint32_t m0 = max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu);
-  uint32_t m1 = max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu);
-  uint32_t m2 = max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu);
-  uint32_t m3 = max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu);
-  return max(max(m0, m1), max(m2, m3));
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short short2v __attribute__((ext_vector_type(2)));
-typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
-
-// Element encoding uses the gfx950 conversions v_cvt_scalef32_pk_fp8_bf16 /
-// v_cvt_scalef32_pk_fp4_bf16 (two bf16 -> two codes, divided by a power-of-two
-// fp32 scale).  Measured against the round-to-nearest-even, saturating
-// encoding of x / 2^e for every finite bf16 x and every e in [-127, 127]: FP4
-// matches everywhere (including saturation and signed zero); FP8 matches
-// wherever |x / 2^e| < 464 and returns NaN above, so FP8 inputs are first
-// clamped to the largest code's value 448 * 2^e, which encodes as 0x7E just
-// like every value it replaces (all of them are >= 448 * 2^e).
-__device__ __forceinline__ float pow2f(int e) {  // 2^e for e in [-127, 127], exact
-  return e == -127 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)(e + 127) << 23);
+  return max(mx_absmax_bits4(v.x, v.y), mx_absmax_bits4(v.z, v.w));
 }
 
 // Loads in flight per lane: each lane issues kBatch independent 16-byte loads
@@ -100,7 +67,6 @@ __device__ __forceinline__ void for_chunks(const uint4* __restrict__ x, int64_t 
 template <int ELEM>
 __global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__ x, uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales, int64_t nchunks) {
-  using F = ElemFmt<ELEM>;
   for_chunks(x, nchunks, [&](const uint4& v, int64_t i) {
     uint32_t m = chunk_absmax_bits(v);
     m = max(m, quad_swap1(m));
@@ -111,37 +77,14 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__
     if (m >= 0x7F80u) {  // NaN or Inf in the block: NaN scale, zero codes
       scale_byte = 0xFFu;
     } else {
-      int e;
-      if (m == 0) {
-        e = -127;
-      } else {
-        const int Eb = (int)(m >> 7);
-        const int fl = Eb ? Eb - 127 : (31 - __clz(m)) - 133;  // floor(log2 amax)
-        e = min(max(fl - F::EMAX, -127), 127);
-      }
+      const int e = mx_shared_exponent<ELEM>(m);
       scale_byte = (uint32_t)(e + 127);
-      const float sc = pow2f(e);
-      uint32_t w[4] = {v.x, v.y, v.z, v.w};
       if constexpr (ELEM == 1) {
-        // |x| <= 448 * 2^e = 1.75 * 2^(e + 8), as bf16 magnitude bits
-        const unsigned short cap = (unsigned short)(((uint32_t)(e + 135) << 7) | 0x60u);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const ushort2v mag = __builtin_bit_cast(ushort2v, w[j] & 0x7FFF7FFFu);
-          const ushort2v cl = __builtin_elementwise_min(mag, ushort2v{cap, cap});
-          w[j] = __builtin_bit_cast(uint32_t, cl) | (w[j] & 0x80008000u);
-        }
-        short2v r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(short2v{0, 0}, __builtin_bit_cast(bf16x2, w[0]), sc, false);
-        r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r0, __builtin_bit_cast(bf16x2, w[1]), sc, true);
-        short2v r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(short2v{0, 0}, __builtin_bit_cast(bf16x2, w[2]), sc, false);
-        r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r1, __builtin_bit_cast(bf16x2, w[3]), sc, true);
-        lo = __builtin_bit_cast(uint32_t, r0);
-        hi = __builtin_bit_cast(uint32_t, r1);
+        lo = mx_encode_fp8x4(v.x, v.y, e);
+        hi = mx_encode_fp8x4(v.z, v.w, e);
       } else {
-        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(lo, __builtin_bit_cast(bf16x2, w[0]), sc, 0);
-        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(lo, __builtin_bit_cast(bf16x2, w[1]), sc, 1);
-        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(lo, __builtin_bit_cast(bf16x2, w[2]), sc, 2);
-        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(lo, __builtin_bit_cast(bf16x2, w[3]), sc, 3);
+        lo = mx_encode_fp4x4<0>(0u, v.x, v.y, e);
+        lo = mx_encode_fp4x4<2>(lo, v.z, v.w, e);
       }
     }
     if (ELEM == 1) reinterpret_cast<uint2*>(codes)[i] = make_uint2(lo, hi);

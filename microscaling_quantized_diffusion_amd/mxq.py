@@ -41,6 +41,7 @@ SIGNATURES = {
     "mxq_quantize": (_I, [_I, _VP, _I64, _I64, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "mxq_gemm": (_I, [_I, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "mxq_quant_gemm_fused": (_I, [_I, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "mxq_gemm_requant": (_I, [_I, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _I, _I, _VP, _VP, _VP, _VP]),
     "mxq_gemm_bf16": (_I, [_I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
     "mxq_workspace_bytes": (_SZ, [_I, _I64, _I64, _I]),
     "mxq_should_quantize": (_I, [_I64, _I64, _I64]),
@@ -179,6 +180,30 @@ def quant_gemm_fused(a: torch.Tensor, w: QTensor, bias: Optional[torch.Tensor] =
     _check("mxq_quant_gemm_fused",
            lib().mxq_quant_gemm_fused(_fmt(w.fmt), M, N, K, _ptr(a), _ptr(w.codes), _ptr(w.scales),
                                       _ptr(w.tensor_scale), _ptr(bias), _ptr(out), _ptr(workspace), wsz, _stream(a)))
+    return out
+
+
+ACTS = {"none": 0, "gelu_tanh": 1}
+
+
+def gemm_requant(a: QTensor, w: QTensor, out_fmt: str, bias: Optional[torch.Tensor] = None, act: str = "none",
+                 out: Optional[QTensor] = None, out_bf16: Optional[torch.Tensor] = None) -> QTensor:
+    """mxq_gemm_requant: quantized A [M, K] x quantized W [N, K]^T -> act(.) as the next layer's quantized
+    activation, a QTensor [M, N] in `out_fmt` (MXFP8 / MXFP4).  `out_bf16` (optional) also receives the bf16
+    values that were quantized."""
+    if a.fmt != w.fmt or a.K != w.K:
+        raise ValueError("A and W must share format and K")
+    if act not in ACTS:
+        raise ValueError(f"unknown activation {act!r}")
+    M, N = a.rows, w.rows
+    dev = a.codes.device
+    if out is None:
+        out = QTensor(out_fmt, torch.empty((M, code_cols(out_fmt, N)), dtype=torch.uint8, device=dev),
+                      torch.empty((M, N // 32), dtype=torch.uint8, device=dev), None, N)
+    _check("mxq_gemm_requant",
+           lib().mxq_gemm_requant(_fmt(a.fmt), M, N, a.K, _ptr(a.codes), _ptr(a.scales), _ptr(w.codes),
+                                  _ptr(w.scales), _ptr(bias), ACTS[act], _fmt(out_fmt), _ptr(out_bf16),
+                                  _ptr(out.codes), _ptr(out.scales), _stream(a.codes)))
     return out
 
 

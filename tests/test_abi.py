@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert mxq.abi_version() == 1
+    assert mxq.abi_version() == 2
     for s in range(8):
         assert lib.mxq_status_string(s)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -119,3 +119,19 @@ def test_gemm_size_limits(lib):
     # the limits themselves are valid shapes: the call proceeds to the pointer checks
     assert g(1, 1 << 20, 1 << 19, 1 << 22, None, P, None, P, P, None, None, P, None) == 1
     assert b(1 << 20, 1 << 19, 1 << 22, None, P, None, P, None) == 1
+
+
+def test_requant_argument_errors(lib):
+    r = lib.mxq_gemm_requant
+    # fmt, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, act, out_fmt, out_bf16, out_codes, out_scales, stream
+    assert r(9, 4, 64, 128, P, P, P, P, None, 0, 1, None, P, P, None) == 2  # format
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 7, None, P, P, None) == 2  # output format
+    assert r(1, 4, 48, 128, P, P, P, P, None, 0, 1, None, P, P, None) == 3  # N not whole 32-column blocks
+    assert r(1, 0, 64, 128, None, None, None, None, None, 0, 1, None, None, None, None) == 0  # empty
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 1, None, None, P, None) == 1  # null codes
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 1, P + 2, P, P, None) == 4  # misaligned bf16 copy
+    assert r(1, 4, 64, 96, P, P, P, P, None, 0, 1, None, P, P, None) == 6  # K not a multiple of 128 (FP8)
+    assert r(2, 4, 64, 128, P, P, P, P, None, 0, 1, None, P, P, None) == 6  # K not a multiple of 256 (FP4)
+    assert r(3, 4, 64, 128, P, P, P, P, None, 0, 1, None, P, P, None) == 6  # NVFP4 operands
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 3, None, P, P, None) == 6  # NVFP4 output
+    assert r(1, 4, 64, 128, P, P, P, P, None, 5, 1, None, P, P, None) == 6  # unknown activation
