@@ -86,19 +86,35 @@ def _floor_log2(a: Fraction) -> int:
     return e
 
 
-def mx_block(bits: Sequence[int], elem: str) -> Tuple[int, List[int]]:
+def _ceil_log2(q: Fraction) -> int:
+    """ceil(log2 q) for a positive rational q, exactly."""
+    f = _floor_log2(q)
+    return f if q == Fraction(2) ** f else f + 1
+
+
+def mx_block(bits: Sequence[int], elem: str, rule: str = "floor") -> Tuple[int, List[int]]:
     """Quantize one block of finite bf16 bit patterns to (E8M0 scale byte, element codes).
 
-    Shared exponent (OCP MX v1.0): e = floor(log2 amax) - emax_elem, clamped to
-    [-127, 127]; an all-zero block uses e = -127.  Elements are x / 2**e encoded
-    round-to-nearest-even with saturation.
+    Shared exponent, clamped to [-127, 127], an all-zero block using e = -127:
+      "floor" (OCP MX v1.0): e = floor(log2 amax) - emax_elem;
+      "rceil": e = ceil(log2(amax / max_elem)), the smallest power of two that
+               brings the block maximum within the element format's range.
+    Elements are x / 2**e encoded round-to-nearest-even with saturation.
     """
     emax = 8 if elem == "e4m3" else 2
+    max_elem = Fraction(448) if elem == "e4m3" else Fraction(6)
     enc = e4m3_encode if elem == "e4m3" else e2m1_encode
     vals = [bf16_value(b) for b in bits]
     negs = [bool((b >> 15) & 1) for b in bits]
     amax = max(abs(v) for v in vals)
-    e = -127 if amax == 0 else max(-127, min(127, _floor_log2(amax) - emax))
+    if amax == 0:
+        e = -127
+    elif rule == "floor":
+        e = max(-127, min(127, _floor_log2(amax) - emax))
+    elif rule == "rceil":
+        e = max(-127, min(127, _ceil_log2(amax / max_elem)))
+    else:
+        raise ValueError(f"unknown scale rule {rule!r}")
     scale = Fraction(2) ** e
     return e + 127, [enc(v / scale, n) for v, n in zip(vals, negs)]
 

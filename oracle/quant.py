@@ -73,22 +73,39 @@ def _check_bits(bits: np.ndarray, block: int) -> np.ndarray:
     return b
 
 
-def quantize_mx(bits: np.ndarray, scheme: Scheme):
-    """MX quantization of a bf16 matrix along K (OCP MX v1.0 shared-exponent rule).
+SCALE_RULES = ("floor", "rceil")
+
+
+def quantize_mx(bits: np.ndarray, scheme: Scheme, rule: str = "floor"):
+    """MX quantization of a bf16 matrix along K.
 
     For each row and each block of 32 consecutive K elements:
       1. if any element is NaN or Inf: scale byte 0xFF, codes 0;
       2. amax = max |x|;
-      3. e = floor(log2 amax) - emax_elem, clamped to [-127, 127]
-         (e = -127 for an all-zero block);
+      3. shared exponent e, clamped to [-127, 127] (e = -127 for an all-zero
+         block):
+         * rule "floor" (the OCP MX v1.0 rule): e = floor(log2 amax) - emax_elem.
+           The block maximum can exceed the element format's largest value
+           (up to 2x) and then saturates;
+         * rule "rceil": e = the smallest integer with amax <= max_elem * 2**e,
+           i.e. ceil(log2(amax / max_elem)), so no element saturates.  It is
+           the floor exponent, plus one when amax > max_elem * 2**e_floor;
       4. scale byte = e + 127;
       5. code = RNE-saturating encode of x / 2**e (a power-of-two division,
          exact in float64);
       6. E2M1 codes are packed two per byte.
     Returns (codes uint8, scales uint8).
+
+    The pages fix the format family only by name (aitrends.kr MXFP8/NVFP4
+    article, Glossary "Microscaling Formats": one shared scale per short
+    block keeps a wide range at low bit depth; "MXFP8": the OCP standard).
+    "floor" is that standard's rule; "rceil" is the variant that rounds the
+    shared scale up instead, offered as an option beside it.
     """
     if scheme.block != 32:
         raise ValueError("MX schemes use 32-element blocks")
+    if rule not in SCALE_RULES:
+        raise ValueError(f"unknown scale rule {rule!r}")
     b = _check_bits(bits, 32)
     rows, K = b.shape
     x = decode_bf16(b).reshape(rows, K // 32, 32)
@@ -96,6 +113,9 @@ def quantize_mx(bits: np.ndarray, scheme: Scheme):
     xf = np.where(finite[..., None], x, 0.0)
     amax = np.abs(xf).max(axis=-1)
     e = np.where(amax == 0, -127, floor_log2(np.where(amax == 0, 1.0, amax)) - scheme.elem.emax)
+    if rule == "rceil":
+        # both sides exact in float64: amax is a bf16 value, the product a power-of-two multiple of max_elem
+        e = e + (amax > np.ldexp(scheme.elem.max_value, e)).astype(np.int64)
     e = np.clip(e, -127, 127)
     scaled = np.ldexp(xf, -e[..., None])
     codes = encode(scheme.elem, scaled)

@@ -106,18 +106,79 @@ def _random_blocks(rng, n_blocks, block):
     return np.stack(out)
 
 
+@pytest.mark.parametrize("rule", ["floor", "rceil"])
 @pytest.mark.parametrize("scheme", [MXFP8, MXFP4], ids=["mxfp8", "mxfp4"])
-def test_mx_matches_exact_reference(scheme):
+def test_mx_matches_exact_reference(scheme, rule):
     rng = np.random.default_rng(7)
     blocks = _random_blocks(rng, 120, 32)
-    codes, scales = quantize_mx(blocks.reshape(4, -1), scheme)
+    codes, scales = quantize_mx(blocks.reshape(4, -1), scheme, rule)
     codes = unpack_fp4(codes) if scheme.packed else codes
     codes = codes.reshape(120, 32)
     scales = scales.reshape(120)
     for i in range(120):
-        sc, ec = exact.mx_block([int(v) for v in blocks[i]], scheme.elem.name)
+        sc, ec = exact.mx_block([int(v) for v in blocks[i]], scheme.elem.name, rule)
         assert int(scales[i]) == sc, i
         assert list(codes[i].astype(int)) == ec, i
+
+
+def test_mx_rceil_worked_blocks(golden_dir):
+    blocks, _ = _parse_blocks(os.path.join(golden_dir, "mx_rceil_blocks.txt"), 32)
+    assert len(blocks) == 7
+    for b in blocks:
+        scheme = MXFP8 if b["scheme"] == "mxfp8" else MXFP4
+        codes, scales = quantize_mx(np.array([b["bits"]], dtype=np.uint16), scheme, "rceil")
+        if scheme.packed:
+            codes = unpack_fp4(codes)
+        assert int(scales[0, 0]) == b["scale"], b
+        assert list(codes[0].astype(int)) == b["codes"], b
+        sc, ec = exact.mx_block(b["bits"], scheme.elem.name, "rceil")
+        assert sc == b["scale"] and ec == b["codes"]
+
+
+@pytest.mark.parametrize("scheme", [MXFP8, MXFP4], ids=["mxfp8", "mxfp4"])
+def test_mx_rceil_exponent_brute_force(scheme):
+    """Every positive finite bf16 value as a block maximum: the scale byte is 127 plus the first e in
+    -127..127 (searched one by one) with amax <= max_elem * 2**e."""
+    mags = np.arange(1, 0x7F80, dtype=np.uint16)
+    bits = np.zeros((mags.size, 32), dtype=np.uint16)
+    bits[:, 5] = mags
+    _, scales = quantize_mx(bits, scheme, "rceil")
+    amax = decode_bf16(mags)
+    want = np.full(mags.size, 127, dtype=np.int64)
+    found = np.zeros(mags.size, dtype=bool)
+    for e in range(-127, 128):
+        hit = ~found & (amax <= scheme.elem.max_value * 2.0 ** e)
+        want[hit] = e
+        found |= hit
+    assert found.all()
+    assert np.array_equal(scales[:, 0].astype(np.int64) - 127, want)
+
+
+@pytest.mark.parametrize("scheme", [MXFP8, MXFP4], ids=["mxfp8", "mxfp4"])
+def test_mx_rceil_no_saturation_and_tight(scheme):
+    """Under the round-up rule the block maximum never exceeds the element format's range, the
+    next smaller exponent would overflow it, and the exponent is the floor rule's or one above."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((64, 1024)) * 2.0 ** rng.integers(-60, 60, (64, 32)).repeat(32, 1)
+    bits = bf16_bits_from_f32(x.astype(np.float32))
+    _, s_floor = quantize_mx(bits, scheme, "floor")
+    codes, s_ceil = quantize_mx(bits, scheme, "rceil")
+    amax = np.abs(decode_bf16(bits)).reshape(64, 32, 32).max(-1)
+    e = s_ceil.astype(np.int64) - 127
+    d = e - (s_floor.astype(np.int64) - 127)
+    assert set(np.unique(d)) <= {0, 1} and d.any() and not d.all()
+    unclamped = (e > -127) & (e < 127) & (amax > 0)
+    q = np.ldexp(amax, -e)
+    assert np.all(q[unclamped] <= scheme.elem.max_value)
+    assert np.all(q[unclamped] > scheme.elem.max_value / 2)
+    # the block maximum's code is never the saturated result of a larger value
+    deq = np.abs(dequant_mx(codes, s_ceil, scheme)).reshape(64, 32, 32).max(-1)
+    assert np.all(np.abs(deq - amax)[unclamped] <= amax[unclamped] * (2.0 ** -3 if scheme is MXFP8 else 0.25))
+
+
+def test_mx_unknown_rule():
+    with pytest.raises(ValueError):
+        quantize_mx(np.zeros((1, 32), np.uint16), MXFP8, "ceil")
 
 
 @pytest.mark.parametrize("scheme", [MXFP8, MXFP4], ids=["mxfp8", "mxfp4"])
