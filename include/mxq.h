@@ -53,13 +53,30 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 2
+#define MXQ_ABI_VERSION 3
 
 typedef enum {
   MXQ_FMT_MXFP8 = 1, /* E4M3 codes, E8M0 scale per 32 K-elements */
   MXQ_FMT_MXFP4 = 2, /* E2M1 codes, E8M0 scale per 32 K-elements */
   MXQ_FMT_NVFP4 = 3  /* E2M1 codes, E4M3 scale per 16 K-elements, fp32 per-tensor scale */
 } mxq_format;
+
+/*
+ * Shared-scale rule flag, OR-ed into the format argument of a call that
+ * quantizes to an MX format: mxq_quantize, mxq_quant_gemm_fused, and the
+ * out_fmt of mxq_gemm_requant.
+ *   without it        e = floor(log2 amax) - emax (the OCP MX v1.0 rule the
+ *                     aitrends.kr article's Glossary entry "MXFP8" names); a
+ *                     block maximum above the element range saturates;
+ *   MXQ_SCALE_RCEIL   e = ceil(log2(amax / max_elem)), max_elem = 448 (E4M3)
+ *                     or 6 (E2M1): the smallest power of two that keeps the
+ *                     block maximum in range, so no element saturates.
+ * Either way e is clamped to [-127, 127].  The rule does not change the code
+ * or scale formats: mxq_gemm and the input format of mxq_gemm_requant accept
+ * and ignore the flag, and mxq_workspace_bytes ignores it.  With
+ * MXQ_FMT_NVFP4, or with any other bit set, a call returns MXQ_ERR_FORMAT.
+ */
+#define MXQ_SCALE_RCEIL 0x100
 
 typedef enum {
   MXQ_OK = 0,
@@ -83,7 +100,8 @@ typedef enum {
  * 2 (E2M1), e = -127 for an all-zero block; scale byte = e + 127; codes are
  * x / 2^e rounded to nearest-even with saturation at +-448 / +-6 (never NaN);
  * signed zeros keep their sign.  A block holding NaN/Inf gets scale 0xFF and
- * zero codes.
+ * zero codes.  With MXQ_SCALE_RCEIL, e = clamp(ceil(log2(amax / max_elem)),
+ * -127, 127) instead.
  *
  * NVFP4: ts = RN_fp32(G / 2688) with G = max|x| over the whole tensor
  * (G = 0 gives ts = 1); per block of 16 with amax B, the E4M3 scale is the
@@ -92,7 +110,7 @@ typedef enum {
  * encoding of x / (dec(scale) * ts), each quotient rounded once.  Any NaN/Inf
  * in the tensor gives ts = NaN, scales 0x7F and zero codes.
  *
- *   fmt            MXQ_FMT_*
+ *   fmt            MXQ_FMT_*, MX formats optionally | MXQ_SCALE_RCEIL
  *   x_bf16         device, bf16 [rows, cols], 16-byte aligned
  *   rows, cols     rows >= 0; cols a positive multiple of the block size
  *   codes          device, out: uint8 [rows, cols] (MXFP8) or [rows, cols/2]
@@ -130,7 +148,8 @@ mxq_status mxq_gemm(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void*
 /*
  * Dynamic activation quantization followed by the block-scaled GEMM, in one
  * call: A (bf16) is quantized once into `workspace`, then multiplied with the
- * pre-quantized W.  Results are identical to mxq_quantize + mxq_gemm.
+ * pre-quantized W.  Results are identical to mxq_quantize + mxq_gemm with the
+ * same fmt (an MXQ_SCALE_RCEIL flag selects A's scale rule).
  *
  *   a_bf16         device bf16 [M, K], 16-byte aligned
  *   w_*            as in mxq_gemm
@@ -156,7 +175,7 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K,
  *        0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))).
  *
  *   fmt, M, N, K, a_*, w_*, bias_bf16   as in mxq_gemm (MX formats only)
- *   out_fmt        MXQ_FMT_MXFP8 or MXQ_FMT_MXFP4
+ *   out_fmt        MXQ_FMT_MXFP8 or MXQ_FMT_MXFP4, optionally | MXQ_SCALE_RCEIL
  *   out_bf16       device bf16 [M, N], 16-byte aligned, or NULL: also store y
  *   out_codes      device, out: uint8 [M, N] (MXFP8) or [M, N/2] (MXFP4),
  *                  16-byte aligned

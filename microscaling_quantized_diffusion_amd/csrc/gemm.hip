@@ -493,7 +493,7 @@ template <int TI, int TJ, int WTM, int WTN, int OELEM, int ACT>
 __device__ __forceinline__ void store_tile_requant(const v16f (&acc)[TI][TJ], float oscale, uint8_t* region,
                                                    const uint16_t* __restrict__ bias, uint8_t* __restrict__ qcodes,
                                                    uint8_t* __restrict__ qscales, int M, int N, int mw, int nw,
-                                                   int lane) {
+                                                   int lane, int rceil) {
   constexpr int CB = OELEM == 1 ? 32 : 16;  // code bytes per row and 32-column block
   constexpr int RB = TI * CB;               // code bytes per row of the wave's segment
   constexpr int PITCH = RB + 16;
@@ -525,7 +525,7 @@ __device__ __forceinline__ void store_tile_requant(const v16f (&acc)[TI][TJ], fl
       const auto sw = __builtin_amdgcn_permlane32_swap(m, m, false, false);
       m = max(sw[0], sw[1]);
       const bool nonfinite = m >= 0x7F80u;  // NaN or Inf in the block: NaN scale, zero codes
-      const int e = nonfinite ? 0 : mx_shared_exponent<OELEM>(m);
+      const int e = nonfinite ? 0 : mx_shared_exponent<OELEM>(m, rceil);
       sword |= (nonfinite ? 0xFFu : (uint32_t)(e + 127)) << (8 * i);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -603,13 +603,14 @@ __device__ __forceinline__ void store_tile_requant(const v16f (&acc)[TI][TJ], fl
 // == 0 in elements for FP4 (K % 256 at SLAB = 128), and 4-byte aligned scale
 // rows.
 // REQ: 0 = bf16 output; 1 / 2 = the output MX-quantized to E4M3 / E2M1 codes
-// and E8M0 scales (qcodes, qscales), with the bf16 output also written when
-// `out` is not null.  ACT: activation applied before the bf16 rounding.
+// and E8M0 scales (qcodes, qscales; rceil selects the round-up shared-exponent
+// rule), with the bf16 output also written when `out` is not null.  ACT:
+// activation applied before the bf16 rounding.
 template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS, int REQ = 0, int ACT = ACT_NONE>
 __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1) void mxp_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
     const uint8_t* __restrict__ Ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N,
-    int K, uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales) {
+    int K, uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales, int rceil) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TJ = WTM / 32, TI = WTN / 32;  // 32 x 32 tiles per wave (M, N)
@@ -823,7 +824,7 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
     store_tile_bf16<TI, TJ, WTM, WTN, ACT>(acc, 1.0f, region, bias, out, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
   } else {
     store_tile_requant<TI, TJ, WTM, WTN, REQ, ACT>(acc, 1.0f, region, bias, qcodes, qscales, M, N, m0 + wm * WTM,
-                                                   n0 + wn * WTN, lane);
+                                                   n0 + wn * WTN, lane, rceil);
     if (out) {
       wait_lgkmcnt0();
       __builtin_amdgcn_wave_barrier();
@@ -858,10 +859,11 @@ inline bool mx_prefer_wide_tile(int64_t M, int64_t N, int64_t cus) {
 template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS, int REQ = 0, int ACT = ACT_NONE>
 hipError_t launch_mxp(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as, const uint8_t* w,
                       const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream,
-                      uint8_t* qcodes = nullptr, uint8_t* qscales = nullptr) {
+                      uint8_t* qcodes = nullptr, uint8_t* qscales = nullptr, int rceil = 0) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   hipLaunchKernelGGL((mxp_gemm_kernel<ELEM, BM, BN, WM, WN, SLAB, NS, REQ, ACT>), dim3((unsigned)tiles),
-                     dim3(64 * WM * WN), 0, stream, a, as, w, ws, bias, out, (int)M, (int)N, (int)K, qcodes, qscales);
+                     dim3(64 * WM * WN), 0, stream, a, as, w, ws, bias, out, (int)M, (int)N, (int)K, qcodes, qscales,
+                     rceil);
   return hipGetLastError();
 }
 
@@ -1181,31 +1183,31 @@ bool mx_requant_supported(int elem, int64_t N, int64_t K, const uint8_t* a_scale
 }
 
 template <int ELEM, int OELEM>
-hipError_t launch_requant_act(int act, int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
-                              const uint8_t* w, const uint8_t* ws, const uint16_t* bias, uint16_t* out,
-                              uint8_t* qcodes, uint8_t* qscales, hipStream_t stream) {
+hipError_t launch_requant_act(int act, int rceil, int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                              const uint8_t* as, const uint8_t* w, const uint8_t* ws, const uint16_t* bias,
+                              uint16_t* out, uint8_t* qcodes, uint8_t* qscales, hipStream_t stream) {
   if (act == ACT_GELU_TANH)
     return launch_mxp<ELEM, 256, 256, 4, 2, 128, 2, OELEM, ACT_GELU_TANH>(M, N, K, a, as, w, ws, bias, out, stream,
-                                                                          qcodes, qscales);
+                                                                          qcodes, qscales, rceil);
   return launch_mxp<ELEM, 256, 256, 4, 2, 128, 2, OELEM, ACT_NONE>(M, N, K, a, as, w, ws, bias, out, stream, qcodes,
-                                                                   qscales);
+                                                                   qscales, rceil);
 }
 
-hipError_t launch_mx_gemm_requant(int elem, int out_elem, int act, int64_t M, int64_t N, int64_t K,
+hipError_t launch_mx_gemm_requant(int elem, int out_elem, int out_rceil, int act, int64_t M, int64_t N, int64_t K,
                                   const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
                                   const uint8_t* w_scales, const uint16_t* bias, uint16_t* out_bf16,
                                   uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream) {
   if (elem == 1 && out_elem == 1)
-    return launch_requant_act<1, 1>(act, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16, out_codes,
-                                    out_scales, stream);
+    return launch_requant_act<1, 1>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16,
+                                    out_codes, out_scales, stream);
   if (elem == 1)
-    return launch_requant_act<1, 2>(act, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16, out_codes,
-                                    out_scales, stream);
+    return launch_requant_act<1, 2>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16,
+                                    out_codes, out_scales, stream);
   if (out_elem == 1)
-    return launch_requant_act<2, 1>(act, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16, out_codes,
-                                    out_scales, stream);
-  return launch_requant_act<2, 2>(act, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16, out_codes,
-                                  out_scales, stream);
+    return launch_requant_act<2, 1>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16,
+                                    out_codes, out_scales, stream);
+  return launch_requant_act<2, 2>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16,
+                                  out_codes, out_scales, stream);
 }
 
 hipError_t launch_nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,

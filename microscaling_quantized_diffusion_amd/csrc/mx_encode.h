@@ -5,7 +5,9 @@
 // MXFP8/NVFP4 article (Glossary "Microscaling Formats", "MXFP8"): shared
 // exponent e = floor(log2(amax)) - emax clamped to [-127, 127] (stored as
 // e + 127), elements encoded round-to-nearest-even with saturation, a block
-// holding NaN or Inf gets the NaN scale 0xFF and zero codes.
+// holding NaN or Inf gets the NaN scale 0xFF and zero codes.  Optional
+// round-up rule: e = ceil(log2(amax / max_elem)), the smallest power of two
+// that keeps the block maximum within the element range (no saturation).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,14 +33,34 @@ __device__ __forceinline__ uint32_t mx_absmax_bits4(uint32_t w0, uint32_t w1) {
   return max(max(w0 & 0x7FFFu, (w0 >> 16) & 0x7FFFu), max(w1 & 0x7FFFu, (w1 >> 16) & 0x7FFFu));
 }
 
-// Shared exponent of a finite block from its largest magnitude bit pattern m
-// (m < 0x7F80): floor(log2(amax)) - emax, clamped; m == 0 gives -127.
+// bf16 fraction bits of the element format's largest value's significand
+// (448 = 1.75 * 2^8 -> 0x60; 6 = 1.5 * 2^2 -> 0x40).
 template <int ELEM>
-__device__ __forceinline__ int mx_shared_exponent(uint32_t m) {
+constexpr uint32_t mx_max_fraction() {
+  return ELEM == 1 ? 0x60u : 0x40u;
+}
+
+// Shared exponent of a finite block from its largest magnitude bit pattern m
+// (m < 0x7F80), clamped to [-127, 127]; m == 0 gives -127.
+//   rceil == 0: floor(log2(amax)) - emax;
+//   rceil == 1: ceil(log2(amax / max_elem)), which is the floor exponent plus
+//               one exactly when amax's significand exceeds max_elem's.
+template <int ELEM>
+__device__ __forceinline__ int mx_shared_exponent(uint32_t m, int rceil) {
   if (m == 0) return -127;
   const int Eb = (int)(m >> 7);
-  const int fl = Eb ? Eb - 127 : (31 - __clz(m)) - 133;  // subnormal bf16: position of the top bit
-  return min(max(fl - mx_emax<ELEM>(), -127), 127);
+  int fl;
+  uint32_t frac;  // 7 fraction bits of amax's significand
+  if (Eb) {
+    fl = Eb - 127;
+    frac = m & 0x7Fu;
+  } else {  // subnormal bf16: the top set bit p carries the leading one
+    const int p = 31 - __clz(m);
+    fl = p - 133;
+    frac = (m << (7 - p)) & 0x7Fu;
+  }
+  const int e = fl - mx_emax<ELEM>() + (rceil & (int)(frac > mx_max_fraction<ELEM>()));
+  return min(max(e, -127), 127);
 }
 
 __device__ __forceinline__ float mx_pow2f(int e) {  // 2^e for e in [-127, 127], exact

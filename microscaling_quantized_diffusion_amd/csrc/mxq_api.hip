@@ -17,6 +17,16 @@ bool valid_format(mxq_format fmt) {
   return fmt == MXQ_FMT_MXFP8 || fmt == MXQ_FMT_MXFP4 || fmt == MXQ_FMT_NVFP4;
 }
 
+// A format argument is a base format, optionally OR-ed with MXQ_SCALE_RCEIL
+// (MX formats only).  Splits it; false for anything else.
+bool split_format(mxq_format arg, mxq_format* base, int* rceil) {
+  const int v = (int)arg;
+  *base = (mxq_format)(v & 0xFF);
+  *rceil = (v & MXQ_SCALE_RCEIL) ? 1 : 0;
+  if ((v & ~0xFF & ~MXQ_SCALE_RCEIL) != 0 || !valid_format(*base)) return false;
+  return !(*rceil && *base == MXQ_FMT_NVFP4);
+}
+
 // K must be a positive multiple of the block; sizes must fit the kernels'
 // 32-bit row/column indices.
 bool valid_k(mxq_format fmt, int64_t K) { return K > 0 && K % block_of(fmt) == 0 && K <= (1 << 30); }
@@ -81,16 +91,20 @@ int mxq_should_quantize(int64_t M, int64_t K, int64_t N) {
   return mn >= 1024 ? 1 : 0;
 }
 
-size_t mxq_workspace_bytes(mxq_format fmt, int64_t M, int64_t K, int fused) {
-  if (!valid_format(fmt) || !valid_dim(M) || !valid_k(fmt, K)) return 0;
+size_t mxq_workspace_bytes(mxq_format fmt_arg, int64_t M, int64_t K, int fused) {
+  mxq_format fmt;
+  int rceil;
+  if (!split_format(fmt_arg, &fmt, &rceil) || !valid_dim(M) || !valid_k(fmt, K)) return 0;
   if (fused) return fused_layout(fmt, M, K).total;
   if (fmt == MXQ_FMT_NVFP4) return round256((size_t)nvfp4_partials_count(M * K) * 4);
   return 0;
 }
 
-mxq_status mxq_quantize(mxq_format fmt, const void* x_bf16, int64_t rows, int64_t cols, void* codes, void* scales,
-                        float* tensor_scale, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!valid_format(fmt)) return MXQ_ERR_FORMAT;
+mxq_status mxq_quantize(mxq_format fmt_arg, const void* x_bf16, int64_t rows, int64_t cols, void* codes,
+                        void* scales, float* tensor_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  mxq_format fmt;
+  int rceil;
+  if (!split_format(fmt_arg, &fmt, &rceil)) return MXQ_ERR_FORMAT;
   if (!valid_dim(rows) || !valid_k(fmt, cols)) return MXQ_ERR_SHAPE;
   if (rows == 0) return MXQ_OK;  // nothing to read or write, whatever the pointers
   if (!x_bf16 || !codes || !scales) return MXQ_ERR_NULL;
@@ -104,14 +118,16 @@ mxq_status mxq_quantize(mxq_format fmt, const void* x_bf16, int64_t rows, int64_
   if (fmt == MXQ_FMT_NVFP4)
     return launch_status(launch_nvfp4_quant((const uint16_t*)x_bf16, rows, cols, (uint8_t*)codes, (uint8_t*)scales,
                                             tensor_scale, (uint32_t*)workspace, s));
-  return launch_status(
-      launch_mx_quant(elem_of(fmt), (const uint16_t*)x_bf16, rows, cols, (uint8_t*)codes, (uint8_t*)scales, s));
+  return launch_status(launch_mx_quant(elem_of(fmt), rceil, (const uint16_t*)x_bf16, rows, cols, (uint8_t*)codes,
+                                       (uint8_t*)scales, s));
 }
 
-mxq_status mxq_gemm(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void* a_codes, const void* a_scales,
+mxq_status mxq_gemm(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K, const void* a_codes, const void* a_scales,
                     const float* a_tensor_scale, const void* w_codes, const void* w_scales,
                     const float* w_tensor_scale, const void* bias_bf16, void* out_bf16, void* stream) {
-  if (!valid_format(fmt)) return MXQ_ERR_FORMAT;
+  mxq_format fmt;
+  int rceil;  // quantizes nothing: the scale rule does not apply
+  if (!split_format(fmt_arg, &fmt, &rceil)) return MXQ_ERR_FORMAT;
   if (!valid_k(fmt, K) || !valid_gemm(M, N, K)) return MXQ_ERR_SHAPE;
   if (M == 0 || N == 0) return MXQ_OK;  // empty output: nothing to launch, whatever the pointers
   if (!a_codes || !a_scales || !w_codes || !w_scales || !out_bf16) return MXQ_ERR_NULL;
@@ -128,11 +144,13 @@ mxq_status mxq_gemm(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void*
                                       (uint16_t*)out_bf16, s));
 }
 
-mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void* a_bf16,
+mxq_status mxq_quant_gemm_fused(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K, const void* a_bf16,
                                 const void* w_codes, const void* w_scales, const float* w_tensor_scale,
                                 const void* bias_bf16, void* out_bf16, void* workspace, size_t workspace_bytes,
                                 void* stream) {
-  if (!valid_format(fmt)) return MXQ_ERR_FORMAT;
+  mxq_format fmt;
+  int rceil;
+  if (!split_format(fmt_arg, &fmt, &rceil)) return MXQ_ERR_FORMAT;
   if (!valid_k(fmt, K) || !valid_gemm(M, N, K)) return MXQ_ERR_SHAPE;
   if (M == 0 || N == 0) return MXQ_OK;  // empty output: nothing to launch, whatever the pointers
   if (!a_bf16 || !w_codes || !w_scales || !out_bf16) return MXQ_ERR_NULL;
@@ -155,18 +173,21 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K,
                           w_tensor_scale, (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s);
     return launch_status(e);
   }
-  e = launch_mx_quant(elem_of(fmt), (const uint16_t*)a_bf16, M, K, a_codes, a_scales, s);
+  e = launch_mx_quant(elem_of(fmt), rceil, (const uint16_t*)a_bf16, M, K, a_codes, a_scales, s);
   if (e != hipSuccess) return MXQ_ERR_LAUNCH;
   e = launch_mx_gemm(elem_of(fmt), M, N, K, a_codes, a_scales, (const uint8_t*)w_codes, (const uint8_t*)w_scales,
                      (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s);
   return launch_status(e);
 }
 
-mxq_status mxq_gemm_requant(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void* a_codes,
+mxq_status mxq_gemm_requant(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K, const void* a_codes,
                             const void* a_scales, const void* w_codes, const void* w_scales, const void* bias_bf16,
-                            int act, mxq_format out_fmt, void* out_bf16, void* out_codes, void* out_scales,
+                            int act, mxq_format out_fmt_arg, void* out_bf16, void* out_codes, void* out_scales,
                             void* stream) {
-  if (!valid_format(fmt) || !valid_format(out_fmt)) return MXQ_ERR_FORMAT;
+  mxq_format fmt, out_fmt;
+  int in_rceil, rceil;  // the input operands are already quantized: only out_fmt's rule applies
+  if (!split_format(fmt_arg, &fmt, &in_rceil) || !split_format(out_fmt_arg, &out_fmt, &rceil))
+    return MXQ_ERR_FORMAT;
   if (!valid_k(fmt, K) || !valid_gemm(M, N, K) || N % 32 != 0) return MXQ_ERR_SHAPE;
   if (M == 0 || N == 0) return MXQ_OK;  // empty output: nothing to launch, whatever the pointers
   if (!a_codes || !a_scales || !w_codes || !w_scales || !out_codes || !out_scales) return MXQ_ERR_NULL;
@@ -175,7 +196,8 @@ mxq_status mxq_gemm_requant(mxq_format fmt, int64_t M, int64_t N, int64_t K, con
   if (fmt == MXQ_FMT_NVFP4 || out_fmt == MXQ_FMT_NVFP4 || (act != 0 && act != 1)) return MXQ_ERR_UNSUPPORTED;
   if (!mx_requant_supported(elem_of(fmt), N, K, (const uint8_t*)a_scales, (const uint8_t*)w_scales))
     return MXQ_ERR_UNSUPPORTED;
-  return launch_status(launch_mx_gemm_requant(elem_of(fmt), elem_of(out_fmt), act, M, N, K, (const uint8_t*)a_codes,
+  return launch_status(launch_mx_gemm_requant(elem_of(fmt), elem_of(out_fmt), rceil, act, M, N, K,
+                                              (const uint8_t*)a_codes,
                                               (const uint8_t*)a_scales, (const uint8_t*)w_codes,
                                               (const uint8_t*)w_scales, (const uint16_t*)bias_bf16,
                                               (uint16_t*)out_bf16, (uint8_t*)out_codes, (uint8_t*)out_scales,

@@ -13,8 +13,9 @@ namespace mxq {
 // Each launcher enqueues its kernels on `stream` and returns the HIP error of
 // the launch (hipSuccess when nothing failed).  Shapes are already validated.
 
-// MX quantizer: x bf16 [rows, cols] -> codes / E8M0 scales.  elem: 1 = E4M3, 2 = E2M1.
-hipError_t launch_mx_quant(int elem, const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
+// MX quantizer: x bf16 [rows, cols] -> codes / E8M0 scales.  elem: 1 = E4M3,
+// 2 = E2M1; rceil: 0 = floor shared-exponent rule, 1 = round-up rule.
+hipError_t launch_mx_quant(int elem, int rceil, const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, hipStream_t stream);
 
 // NVFP4 quantizer (two kernels: global-amax partials, then block quantization).
@@ -29,11 +30,12 @@ hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8
                           const uint16_t* bias, uint16_t* out, hipStream_t stream);
 
 // MX GEMM whose epilogue emits the output MX-quantized (out_elem: 1 = E4M3,
-// 2 = E2M1; E8M0 scales per 32 output columns), after an optional activation
-// (act: 0 none, 1 GELU tanh form); out_bf16 (nullable) also receives the bf16
-// values that were quantized.  Only where mx_requant_supported() holds.
+// 2 = E2M1; E8M0 scales per 32 output columns, shared-exponent rule as in
+// launch_mx_quant), after an optional activation (act: 0 none, 1 GELU tanh
+// form); out_bf16 (nullable) also receives the bf16 values that were
+// quantized.  Only where mx_requant_supported() holds.
 bool mx_requant_supported(int elem, int64_t N, int64_t K, const uint8_t* a_scales, const uint8_t* w_scales);
-hipError_t launch_mx_gemm_requant(int elem, int out_elem, int act, int64_t M, int64_t N, int64_t K,
+hipError_t launch_mx_gemm_requant(int elem, int out_elem, int out_rceil, int act, int64_t M, int64_t N, int64_t K,
                                   const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
                                   const uint8_t* w_scales, const uint16_t* bias, uint16_t* out_bf16,
                                   uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream);

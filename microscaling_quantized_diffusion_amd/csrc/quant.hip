@@ -66,7 +66,8 @@ __device__ __forceinline__ void for_chunks(const uint4* __restrict__ x, int64_t 
 // starts on a block boundary, so the whole quad is active together.
 template <int ELEM>
 __global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__ x, uint8_t* __restrict__ codes,
-                                                       uint8_t* __restrict__ scales, int64_t nchunks) {
+                                                       uint8_t* __restrict__ scales, int64_t nchunks,
+                                                       int rceil) {
   for_chunks(x, nchunks, [&](const uint4& v, int64_t i) {
     uint32_t m = chunk_absmax_bits(v);
     m = max(m, quad_swap1(m));
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__
     if (m >= 0x7F80u) {  // NaN or Inf in the block: NaN scale, zero codes
       scale_byte = 0xFFu;
     } else {
-      const int e = mx_shared_exponent<ELEM>(m);
+      const int e = mx_shared_exponent<ELEM>(m, rceil);
       scale_byte = (uint32_t)(e + 127);
       if constexpr (ELEM == 1) {
         lo = mx_encode_fp8x4(v.x, v.y, e);
@@ -284,15 +285,17 @@ int grid_for(int64_t nchunks, int64_t cap) {
 
 }  // namespace
 
-hipError_t launch_mx_quant(int elem, const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
+hipError_t launch_mx_quant(int elem, int rceil, const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, hipStream_t stream) {
   const int64_t nchunks = rows * cols / 8;
   if (nchunks == 0) return hipSuccess;
   const int grid = grid_for((nchunks + kBatch - 1) / kBatch, 8192);
   if (elem == 1)
-    hipLaunchKernelGGL(mx_quant_kernel<1>, dim3(grid), dim3(256), 0, stream, (const uint4*)x, codes, scales, nchunks);
+    hipLaunchKernelGGL(mx_quant_kernel<1>, dim3(grid), dim3(256), 0, stream, (const uint4*)x, codes, scales, nchunks,
+                       rceil);
   else
-    hipLaunchKernelGGL(mx_quant_kernel<2>, dim3(grid), dim3(256), 0, stream, (const uint4*)x, codes, scales, nchunks);
+    hipLaunchKernelGGL(mx_quant_kernel<2>, dim3(grid), dim3(256), 0, stream, (const uint4*)x, codes, scales, nchunks,
+                       rceil);
   return hipGetLastError();
 }
 

@@ -5,7 +5,9 @@ torch is used here only to allocate device memory and to name the current
 HIP stream.  If the library is not built, every call raises: there is no
 fallback implementation.
 
-Names mirror include/mxq.h.  Formats: "mxfp8", "mxfp4", "nvfp4".
+Names mirror include/mxq.h.  Formats: "mxfp8", "mxfp4", "nvfp4".  Calls
+that quantize to an MX format take ``scale_rule``: "floor" (the OCP rule,
+default) or "rceil" (round the shared scale up, MXQ_SCALE_RCEIL).
 """
 
 from __future__ import annotations
@@ -21,6 +23,7 @@ _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libmxq.so")
 
 FORMATS = {"mxfp8": 1, "mxfp4": 2, "nvfp4": 3}
+SCALE_RULES = {"floor": 0, "rceil": 0x100}  # MXQ_SCALE_RCEIL, OR-ed into the format argument
 BLOCK = {"mxfp8": 32, "mxfp4": 32, "nvfp4": 16}
 
 MXQ_OK = 0
@@ -86,10 +89,12 @@ def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _fmt(fmt: str) -> int:
+def _fmt(fmt: str, scale_rule: str = "floor") -> int:
     if fmt not in FORMATS:
         raise ValueError(f"unknown format {fmt!r}")
-    return FORMATS[fmt]
+    if scale_rule not in SCALE_RULES:
+        raise ValueError(f"unknown scale rule {scale_rule!r}")
+    return FORMATS[fmt] | SCALE_RULES[scale_rule]
 
 
 def _require(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
@@ -129,11 +134,11 @@ def workspace_bytes(fmt: str, M: int, K: int, fused: bool) -> int:
 
 
 def quantize(fmt: str, x: torch.Tensor, out: Optional[QTensor] = None,
-             workspace: Optional[torch.Tensor] = None) -> QTensor:
+             workspace: Optional[torch.Tensor] = None, scale_rule: str = "floor") -> QTensor:
     """mxq_quantize: bf16 [rows, K] -> QTensor (codes, scales, tensor scale)."""
     _require(x, torch.bfloat16, "x")
     rows, K = x.shape
-    f = _fmt(fmt)
+    f = _fmt(fmt, scale_rule)
     dev = x.device
     if out is None:
         codes = torch.empty((rows, code_cols(fmt, K)), dtype=torch.uint8, device=dev)
@@ -164,7 +169,8 @@ def gemm(a: QTensor, w: QTensor, bias: Optional[torch.Tensor] = None,
 
 
 def quant_gemm_fused(a: torch.Tensor, w: QTensor, bias: Optional[torch.Tensor] = None,
-                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     scale_rule: str = "floor") -> torch.Tensor:
     """mxq_quant_gemm_fused: bf16 A [M, K] quantized on the fly, times quantized W [N, K]^T -> bf16 [M, N]."""
     _require(a, torch.bfloat16, "a")
     M, K = a.shape
@@ -178,7 +184,7 @@ def quant_gemm_fused(a: torch.Tensor, w: QTensor, bias: Optional[torch.Tensor] =
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=a.device)
     wsz = workspace.numel() * workspace.element_size()
     _check("mxq_quant_gemm_fused",
-           lib().mxq_quant_gemm_fused(_fmt(w.fmt), M, N, K, _ptr(a), _ptr(w.codes), _ptr(w.scales),
+           lib().mxq_quant_gemm_fused(_fmt(w.fmt, scale_rule), M, N, K, _ptr(a), _ptr(w.codes), _ptr(w.scales),
                                       _ptr(w.tensor_scale), _ptr(bias), _ptr(out), _ptr(workspace), wsz, _stream(a)))
     return out
 
@@ -187,7 +193,8 @@ ACTS = {"none": 0, "gelu_tanh": 1}
 
 
 def gemm_requant(a: QTensor, w: QTensor, out_fmt: str, bias: Optional[torch.Tensor] = None, act: str = "none",
-                 out: Optional[QTensor] = None, out_bf16: Optional[torch.Tensor] = None) -> QTensor:
+                 out: Optional[QTensor] = None, out_bf16: Optional[torch.Tensor] = None,
+                 scale_rule: str = "floor") -> QTensor:
     """mxq_gemm_requant: quantized A [M, K] x quantized W [N, K]^T -> act(.) as the next layer's quantized
     activation, a QTensor [M, N] in `out_fmt` (MXFP8 / MXFP4).  `out_bf16` (optional) also receives the bf16
     values that were quantized."""
@@ -202,7 +209,7 @@ def gemm_requant(a: QTensor, w: QTensor, out_fmt: str, bias: Optional[torch.Tens
                       torch.empty((M, N // 32), dtype=torch.uint8, device=dev), None, N)
     _check("mxq_gemm_requant",
            lib().mxq_gemm_requant(_fmt(a.fmt), M, N, a.K, _ptr(a.codes), _ptr(a.scales), _ptr(w.codes),
-                                  _ptr(w.scales), _ptr(bias), ACTS[act], _fmt(out_fmt), _ptr(out_bf16),
+                                  _ptr(w.scales), _ptr(bias), ACTS[act], _fmt(out_fmt, scale_rule), _ptr(out_bf16),
                                   _ptr(out.codes), _ptr(out.scales), _stream(a.codes)))
     return out
 

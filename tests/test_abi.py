@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert mxq.abi_version() == 2
+    assert mxq.abi_version() == 3
     for s in range(8):
         assert lib.mxq_status_string(s)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -135,3 +135,26 @@ def test_requant_argument_errors(lib):
     assert r(3, 4, 64, 128, P, P, P, P, None, 0, 1, None, P, P, None) == 6  # NVFP4 operands
     assert r(1, 4, 64, 128, P, P, P, P, None, 0, 3, None, P, P, None) == 6  # NVFP4 output
     assert r(1, 4, 64, 128, P, P, P, P, None, 5, 1, None, P, P, None) == 6  # unknown activation
+
+
+RCEIL = 0x100  # MXQ_SCALE_RCEIL
+
+
+def test_scale_rule_flag(lib):
+    """The round-up scale-rule flag is accepted with MX formats wherever a format is taken, and rejected
+    with NVFP4 or next to unknown bits, before any pointer is looked at."""
+    q, g, f, r = lib.mxq_quantize, lib.mxq_gemm, lib.mxq_quant_gemm_fused, lib.mxq_gemm_requant
+    assert q(1 | RCEIL, P, 0, 32, P, P, None, None, 0, None) == 0  # empty: accepted format, no-op
+    assert q(2 | RCEIL, None, 4, 32, P, P, None, None, 0, None) == 1  # passes the format check
+    assert q(3 | RCEIL, P, 4, 32, P, P, P, P, 1 << 20, None) == 2  # NVFP4 has no such rule
+    assert q(1 | 0x200, P, 4, 32, P, P, None, None, 0, None) == 2  # unknown flag bit
+    assert q(RCEIL, P, 4, 32, P, P, None, None, 0, None) == 2  # flag without a format
+    assert g(1 | RCEIL, 4, 4, 32, None, P, None, P, P, None, None, P, None) == 1  # accepted and ignored
+    assert f(2 | RCEIL, 64, 64, 64, P, P, P, None, None, P, None, 0, None) == 5  # passes to the workspace check
+    assert f(3 | RCEIL, 64, 64, 64, P, P, P, None, None, P, P, 1 << 20, None) == 2
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 2 | RCEIL, None, None, P, None) == 1  # output rule accepted
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 3 | RCEIL, None, P, P, None) == 2
+    assert lib.mxq_workspace_bytes(1 | RCEIL, 64, 64, 1) == lib.mxq_workspace_bytes(1, 64, 64, 1)
+    assert lib.mxq_workspace_bytes(3 | RCEIL, 64, 64, 1) == 0
+    with pytest.raises(ValueError):
+        mxq._fmt("mxfp8", "ceil")
