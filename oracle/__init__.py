@@ -21,6 +21,10 @@ What it computes, and where the pages define it:
   TorchAO configuration shown under "Section details") is read as E2M1
   elements with one E4M3 scale per 16 elements and one fp32 per-tensor scale
   derived from the global absolute maximum.
+* Attention in 8-bit floating point with per-token correction of the
+  quantization error (devin.kr article on FLUX image generation accelerated
+  on Blackwell, "Compute efficiency and acceleration"); the steps are
+  readings, stated in ``attention``.
 * Dynamic activation quantization followed by a low-precision GEMM against
   pre-quantized weights (same page, "Section details": the NVFP4 dynamic-
   activation / NVFP4-weight configuration), with layers whose smallest GEMM
@@ -36,6 +40,9 @@ exact    scalar reference in exact rational arithmetic (fractions.Fraction)
 quant    MXFP8 / MXFP4 / NVFP4 quantizers and dequantizers (numpy, fp64).
 gemm     fp64 GEMM references, the normwise error metric and the GELU
          (tanh form) applied before an epilogue's requantization.
+attention  block-scaled FP8 attention (MXFP8 Q, K along the head dimension,
+         V along tokens, online softmax over key tiles with P in E4M3 at a
+         fixed 2^8 scale) and textbook softmax attention, in float64.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, exhaustive brute force, library decoders and hand-

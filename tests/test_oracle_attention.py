@@ -1,0 +1,118 @@
+"""Pins for the oracle's block-scaled FP8 attention.
+
+Pinned by: the textbook softmax attention (online bookkeeping with P
+unquantized, several tile sizes, a ragged last tile), a closed form (equal
+scores give the mean of V), an exact power-of-two scaling invariant of V, a
+direct single-tile formula whose P encoding is an argmin over the E4M3 code
+table (the exact reference's encoder), the token axis of V's block scales, and
+the size of the quantization error against unquantized attention.
+"""
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import attention as att
+from oracle import exact
+from oracle.formats import decode_bf16
+from microscaling_quantized_diffusion_amd.inputs import bf16_bits_from_f32
+
+
+def _bits(x):
+    return bf16_bits_from_f32(np.asarray(x, dtype=np.float32))
+
+
+def _qkv(rng, S, D=128, spread=1.0):
+    q = _bits(rng.standard_normal((S, D)) * spread)
+    k = _bits(rng.standard_normal((S, D)) * spread)
+    v = _bits(rng.standard_normal((S, D)))
+    return q, k, v
+
+
+@pytest.mark.parametrize("tile", [16, 64, 100])
+def test_online_softmax_equals_textbook(tile):
+    """With P unquantized, the online algorithm is exact algebra: any tile size (100 leaves a ragged
+    last tile) reproduces softmax(q k^T / sqrt(D)) v to float64 rounding."""
+    rng = np.random.default_rng(1)
+    q, k, v = (rng.standard_normal((300, 64)) * s for s in (2.0, 2.0, 1.0))
+    got = att.online_attention(q, k, v, kv_tile=tile, quantize_probs=False)
+    want = att.attention_ref(q, k, v)
+    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+
+
+def test_equal_scores_give_the_mean_of_v():
+    """K = 0: every score is 0, p = 1 encodes exactly (256 = 2^8 is an E4M3 value), so the output is
+    the mean of the dequantized V rows, whatever the tiles."""
+    rng = np.random.default_rng(2)
+    S, D = 192, 128
+    q = _bits(rng.standard_normal((S, D)))
+    k = np.zeros((S, D), dtype=np.uint16)
+    v = _bits(rng.standard_normal((S, D)))
+    out = att.attention_fp8_ref(q, k, v)
+    vhat = att.quantize_qkv(q, k, v)["v"]
+    assert np.allclose(out, np.broadcast_to(vhat.mean(axis=0), out.shape), rtol=0, atol=1e-15)
+
+
+def test_v_power_of_two_scaling_is_exact():
+    """Scaling V by 2^j scales every block scale of V by 2^j and leaves its codes, so the output
+    scales by exactly 2^j."""
+    rng = np.random.default_rng(3)
+    q, k, v = _qkv(rng, 128)
+    v8 = _bits(decode_bf16(v) * 2.0 ** 8)
+    a = att.attention_fp8_ref(q, k, v)
+    b = att.attention_fp8_ref(q, k, v8)
+    assert np.array_equal(b, a * 256.0)
+
+
+def test_single_tile_direct_formula():
+    """One key tile: O = sum_j p^_j v_j / sum_j p_j with p = exp(s - max s) and p^ the nearest E4M3
+    value of p * 2^8 (argmin over the code table, ties to the even code) divided by 2^8."""
+    rng = np.random.default_rng(4)
+    S, D = 64, 128
+    q, k, v = _qkv(rng, S, spread=1.5)
+    t = att.quantize_qkv(q, k, v)
+    s = t["q"] @ t["k"].T / math.sqrt(D)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    ph = np.empty_like(p)
+    for idx, val in np.ndenumerate(p):
+        code = exact.e4m3_encode(Fraction(float(val)) * 256, False)
+        ph[idx] = float(dict(exact.e4m3_table())[code]) / 256.0
+    want = (ph @ t["v"]) / p.sum(axis=1, keepdims=True)
+    got = att.attention_fp8_ref(q, k, v, kv_tile=64)
+    assert np.max(np.abs(got - want)) <= 1e-13 * np.max(np.abs(want))
+
+
+def test_v_scales_run_along_tokens():
+    """V's blocks are 32 consecutive tokens of one channel: a large value at token 40, channel 5
+    coarsens tokens 32-63 of channel 5 only."""
+    rng = np.random.default_rng(5)
+    q, k, v = _qkv(rng, 96)
+    v2 = v.copy()
+    v2[40, 5] = _bits([[1000.0]])[0, 0]
+    a, b = att.quantize_qkv(q, k, v)["v"], att.quantize_qkv(q, k, v2)["v"]
+    changed = a != b
+    changed[40, 5] = False
+    rows, cols = np.nonzero(changed)
+    assert rows.size > 0 and set(cols) == {5} and rows.min() >= 32 and rows.max() <= 63
+
+
+def test_quantization_error_size():
+    """The FP8 result is near unquantized attention of the same bf16 inputs, and measurably different
+    from it.  E4M3 keeps 3 mantissa bits (relative step 2^-4 .. 2^-3); with diffuse attention over
+    random V the output averages hundreds of values, so it is small next to V's per-element
+    quantization noise and the normwise error is several per cent."""
+    rng = np.random.default_rng(6)
+    q, k, v = _qkv(rng, 256)
+    got = att.attention_fp8_ref(q, k, v)
+    ref = att.attention_ref(decode_bf16(q), decode_bf16(k), decode_bf16(v))
+    err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
+    assert 1e-3 < err < 0.1, err
+
+
+def test_p_encoding_is_e4m3_rne():
+    """quantize_p against hand-worked values: 1 -> 1; 0.5 -> 0.5; 127/256 (p * 256 = 127 lies
+    between 120 and 128, step 8) -> 128/256; 0.3 (76.8: step 8 in [64, 128) -> 80) -> 80/256."""
+    got = att.quantize_p(np.array([1.0, 0.5, 127 / 256, 0.3]))
+    assert list(got) == [1.0, 0.5, 0.5, 80 / 256]
