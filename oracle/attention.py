@@ -97,3 +97,84 @@ def attention_fp8_ref(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray
     t = quantize_qkv(q_bits, k_bits, v_bits)
     q = t["q"] if rows is None else t["q"][np.asarray(rows)]
     return online_attention(q, t["k"], t["v"], kv_tile, True)
+
+
+# E4M3 values >= 0 in increasing order (for the neighbours of a midpoint)
+_E4M3_GRID = np.unique(decode_e4m3(np.arange(0x7F)))
+
+
+def p_code_slack(q: np.ndarray, k: np.ndarray, v: np.ndarray, score_eta: float, exp_eta: float = 2.0 ** -20,
+                 kv_tile: int = 64, forced=None):
+    """Bound of what a valid other rounding of near-midpoint P codes can change in the output.
+
+    Step 5 rounds p * 2^8 to E4M3, a decision taken from floating-point scores.
+    A kernel that forms each score in a float accumulator of unit roundoff u
+    over D products errs by at most gamma_D sum_d |q_d k_d| with gamma_D about
+    D u (the recursive-summation bound), in the score itself and in the row's
+    running maximum.  `score_eta` is that relative bound (D * 2^-24 for fp32
+    and D = 128); `exp_eta` covers the exponential and the scaling.  For each
+    key whose p * 2^8 lies within the resulting relative distance of an E4M3
+    midpoint, either neighbour is a correct code; the returned slack [Sq, D]
+    sums, per output, one E4M3 step (divided by 2^8) times |v_j| rescaled to
+    the final maximum and divided by the final row sum, over those keys.
+
+    `forced` (optional, for checking the bound): a set of (row, key) pairs
+    whose code is taken as the other neighbour of the nearest midpoint; the
+    function then also returns the output computed with those codes.
+    Returns (slack, out_forced or None)."""
+    Sq, D = q.shape
+    Skv = k.shape[0]
+    c = 1.0 / math.sqrt(D)
+    A = np.abs(q) @ np.abs(k).T
+    tol = c * score_eta * 2.0 * A.max(axis=1) + exp_eta  # relative bound on p, per row
+    mids = (_E4M3_GRID[1:] + _E4M3_GRID[:-1]) / 2
+    m = np.full(Sq, -np.inf)
+    l = np.zeros(Sq)
+    contrib = np.zeros((Sq, v.shape[1]))
+    acc = np.zeros((Sq, v.shape[1]))
+    for t0 in range(0, Skv, kv_tile):
+        s = (q @ k[t0:t0 + kv_tile].T) * c
+        m_new = np.maximum(m, s.max(axis=1))
+        alpha = np.exp(m - m_new)
+        p = np.exp(s - m_new[:, None])
+        x = np.ldexp(p, P_SCALE_EXP)
+        i = np.clip(np.searchsorted(mids, x), 1, len(mids) - 1)
+        near_mid = np.where(np.abs(mids[i - 1] - x) < np.abs(mids[i] - x), mids[i - 1], mids[i])
+        idx = np.searchsorted(_E4M3_GRID, near_mid)
+        step = _E4M3_GRID[idx] - _E4M3_GRID[idx - 1]
+        near = np.abs(x - near_mid) <= x * tol[:, None]
+        contrib = contrib * alpha[:, None] + (near * step * 2.0 ** -P_SCALE_EXP) @ np.abs(v[t0:t0 + kv_tile])
+        ph = quantize_p(p)
+        if forced:
+            for (r, j) in forced:
+                if t0 <= j < t0 + kv_tile:
+                    jj = j - t0
+                    lo, hi = _E4M3_GRID[idx[r, jj] - 1], _E4M3_GRID[idx[r, jj]]
+                    cur = ph[r, jj] * 2.0 ** P_SCALE_EXP
+                    ph[r, jj] = (hi if cur == lo else lo) * 2.0 ** -P_SCALE_EXP
+        acc = acc * alpha[:, None] + ph @ v[t0:t0 + kv_tile]
+        l = l * alpha + p.sum(axis=1)
+        m = m_new
+    slack = contrib / l[:, None]
+    return slack, (acc / l[:, None] if forced else None)
+
+
+def near_midpoint_keys(q: np.ndarray, k: np.ndarray, score_eta: float, exp_eta: float = 2.0 ** -20,
+                       kv_tile: int = 64):
+    """The (row, key) pairs whose P code p_code_slack treats as ambiguous."""
+    Sq, D = q.shape
+    c = 1.0 / math.sqrt(D)
+    A = np.abs(q) @ np.abs(k).T
+    tol = c * score_eta * 2.0 * A.max(axis=1) + exp_eta
+    mids = (_E4M3_GRID[1:] + _E4M3_GRID[:-1]) / 2
+    out = []
+    m = np.full(Sq, -np.inf)
+    for t0 in range(0, k.shape[0], kv_tile):
+        s = (q @ k[t0:t0 + kv_tile].T) * c
+        m = np.maximum(m, s.max(axis=1))
+        x = np.ldexp(np.exp(s - m[:, None]), P_SCALE_EXP)
+        i = np.clip(np.searchsorted(mids, x), 1, len(mids) - 1)
+        d = np.minimum(np.abs(mids[i - 1] - x), np.abs(mids[i] - x))
+        for r, j in zip(*np.nonzero(d <= x * tol[:, None])):
+            out.append((int(r), int(t0 + j)))
+    return out

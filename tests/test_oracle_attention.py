@@ -116,3 +116,29 @@ def test_p_encoding_is_e4m3_rne():
     between 120 and 128, step 8) -> 128/256; 0.3 (76.8: step 8 in [64, 128) -> 80) -> 80/256."""
     got = att.quantize_p(np.array([1.0, 0.5, 127 / 256, 0.3]))
     assert list(got) == [1.0, 0.5, 0.5, 80 / 256]
+
+
+def test_p_code_slack_zero_without_error_bound():
+    rng = np.random.default_rng(7)
+    q, k, v = _qkv(rng, 128)
+    t = att.quantize_qkv(q, k, v)
+    slack, _ = att.p_code_slack(t["q"], t["k"], t["v"], score_eta=0.0, exp_eta=0.0)
+    assert not slack.any()
+
+
+def test_p_code_slack_covers_each_other_rounding():
+    """Brute force: taking each ambiguous code as the other neighbour of its midpoint moves the output
+    by no more than the slack (and by a nonzero amount, so the keys found are real decisions)."""
+    rng = np.random.default_rng(8)
+    q, k, v = _qkv(rng, 192)
+    t = att.quantize_qkv(q, k, v)
+    eta = 128 * 2.0 ** -24 * 8  # a wide bound, so that several keys are ambiguous
+    keys = att.near_midpoint_keys(t["q"], t["k"], eta)
+    assert 5 <= len(keys) <= 0.05 * 192 * 192
+    slack, _ = att.p_code_slack(t["q"], t["k"], t["v"], eta)
+    base = att.online_attention(t["q"], t["k"], t["v"])
+    for rk in keys[:40]:
+        _, forced = att.p_code_slack(t["q"], t["k"], t["v"], eta, forced={rk})
+        d = np.abs(forced - base)
+        assert d[rk[0]].max() > 0
+        assert np.all(d <= slack * (1 + 1e-9) + 1e-15)
