@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 3
+#define MXQ_ABI_VERSION 4
 
 typedef enum {
   MXQ_FMT_MXFP8 = 1, /* E4M3 codes, E8M0 scale per 32 K-elements */
@@ -198,6 +198,42 @@ mxq_status mxq_gemm_requant(mxq_format fmt, int64_t M, int64_t N, int64_t K, con
  */
 mxq_status mxq_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* a_bf16, const void* w_bf16,
                          const void* bias_bf16, void* out_bf16, void* stream);
+
+/*
+ * Block-scaled FP8 attention, for each of the B * H heads independently:
+ *   out = softmax(Q K^T / sqrt(D)) V computed in 8-bit floating point, the
+ * FP8 attention with per-token error correction of the devin.kr article on
+ * FLUX image generation accelerated on Blackwell ("Compute efficiency and
+ * acceleration"), read as follows (the pages give no steps):
+ *   - Q and K are MXFP8-quantized along D (E4M3 codes, one E8M0 scale per 32
+ *     channels of each token, the rule of mxq_quantize); V is
+ *     MXFP8-quantized along the token axis (one scale per 32 tokens of each
+ *     channel);
+ *   - scores come from the dequantized codes with an fp32 accumulator; the
+ *     softmax runs online over key tiles of 64 in key order: running max m,
+ *     p = exp(s - m) <= 1 encoded as E4M3 at the fixed scale 2^8, the output
+ *     accumulator and the row sum (of the unquantized p) rescaled by
+ *     exp(m_old - m_new) at each tile; out = acc / sum, rounded to bf16
+ *     (nearest-even).
+ * All the quantization happens inside the call, into `workspace`.
+ *
+ *   B, H, S, D     batch, heads, tokens (queries = keys), head dimension
+ *   q_bf16, k_bf16, v_bf16   device bf16 [B, H, S, D], 16-byte aligned
+ *   out_bf16       device bf16 [B, H, S, D], 16-byte aligned
+ *   workspace      device scratch of mxq_attention_workspace_bytes(B, H, S, D)
+ *                  bytes, 16-byte aligned; its contents are overwritten
+ * Sizes: B, H, S >= 0, D > 0, S <= 2^24, B * H <= 65535, else MXQ_ERR_SHAPE.
+ * This build implements D == 128 with S a multiple of 64; other valid sizes
+ * return MXQ_ERR_UNSUPPORTED.  B * H == 0 or S == 0 is a successful no-op.
+ * Inputs are expected finite (a NaN or Inf makes its head's output
+ * meaningless).
+ */
+mxq_status mxq_attention_fp8(int64_t B, int64_t H, int64_t S, int64_t D, const void* q_bf16, const void* k_bf16,
+                             const void* v_bf16, void* out_bf16, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Workspace bytes needed by mxq_attention_fp8; 0 for sizes it rejects. */
+size_t mxq_attention_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D);
 
 /*
  * Workspace bytes needed by mxq_quantize (fused = 0) or mxq_quant_gemm_fused

@@ -1,0 +1,356 @@
+// Block-scaled FP8 attention for gfx950 (one head dimension: 128).
+//
+// Method: the devin.kr article on FLUX image generation accelerated on
+// Blackwell ("Compute efficiency and acceleration") runs attention in 8-bit
+// floating point with a per-token correction of the quantization error.  The
+// pages give no steps; this path computes, per head:
+//   * Q and K MXFP8-quantized along the head dimension (E4M3 codes, one E8M0
+//     scale per 32 channels of each token), V MXFP8-quantized along the token
+//     axis (one E8M0 scale per 32 tokens of each channel), the microscaling
+//     formats of the aitrends.kr MXFP8/NVFP4 article (Glossary "Microscaling
+//     Formats", "MXFP8");
+//   * scores from the dequantized codes (scaled MFMA, fp32 accumulate), an
+//     online softmax over 64-key tiles in key order, P = exp(s - running max)
+//     encoded as E4M3 at the fixed scale 2^8, O += P V with V's block scales,
+//     the row sum taken over the unquantized P; out = O / l in bf16.
+//
+// Kernels
+//   vt_quant_kernel   V [S, 128] bf16 -> V^T codes [128, S] and scales
+//                     [128, S/32]: a workgroup stages 64 tokens x 128
+//                     channels in LDS; each thread encodes one 32-token block
+//                     of one channel with the quantizer's block encoding.
+//   attn_fp8_kernel   one workgroup = 128 queries of one head (four waves of
+//                     32); key tiles of 64 double-buffered in LDS through
+//                     registers (K rows and V^T rows XOR-swizzled by 16-byte
+//                     chunk, as in the GEMM staging).  Per tile and wave:
+//       S^T = K Q^T    four 32x32x64 scaled MFMAs (K rows are the A operand
+//                      from LDS, the wave's 32 queries the B operand, held in
+//                      registers for the whole loop);
+//       softmax        in the log2 domain: each lane holds 32 scores of one
+//                      query (16 of each 32-key tile), the running max is
+//                      combined with the other lane half by permlane32 swap;
+//                      P codes from v_cvt_scalef32_pk_fp8_f32 at scale 2^-8;
+//       P -> operand   the 32x32 accumulator gives lane half h keys 8i + 4h
+//                      + (0..3); the MFMA's B operand wants keys 16h .. 16h
+//                      + 15 of each 32-key tile, so each tile swaps two
+//                      dwords of codes across the lane halves;
+//       O^T += V^T P^T four scaled MFMAs (V^T rows from LDS with their E8M0
+//                      scales, P with the constant scale 2^-8).
+#include "mx_encode.h"
+#include "mxq_internal.h"
+
+namespace mxq {
+namespace {
+
+typedef int att_v8i __attribute__((ext_vector_type(8)));
+typedef float att_v16f __attribute__((ext_vector_type(16)));
+typedef float att_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 att_bf16x2 __attribute__((ext_vector_type(2)));
+typedef short att_short2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;   // head dimension
+constexpr int kBQ = 128;  // queries per workgroup (4 waves x 32)
+constexpr int kBK = 64;   // keys per tile
+constexpr int kKOff = 0;                       // K tile: 64 rows x 128 code bytes
+constexpr int kVOff = kBK * kD;                // V^T tile: 128 rows x 64 code bytes
+constexpr int kKsOff = kVOff + kD * kBK;       // K scales: 64 rows x 4 bytes
+constexpr int kVsOff = kKsOff + kBK * 4;       // V^T scales: 128 rows x 2 bytes
+constexpr int kStage = kVsOff + kD * 2;        // 16896 bytes
+constexpr int kPScale = 127 - 8;               // E8M0 byte of 2^-8, the scale of the P codes
+
+__device__ __forceinline__ att_v8i att_as_v8i(const uint4& lo, const uint4& hi) {
+  return att_v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// The value lane l ^ 32 passed in `send`.  permlane32_swap exchanges one
+// operand's upper lane half with the other operand's lower half; with the same
+// value in both operands, one result holds the lane's own value and the other
+// its partner's, so the one that differs from `send` is the partner's (and
+// when none differs the two values are equal).
+__device__ __forceinline__ uint32_t xchg_half(uint32_t send) {
+  const auto r = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+  return r[0] != send ? r[0] : r[1];
+}
+__device__ __forceinline__ float max_half(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_half(float v) {  // own + partner: one result is each
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Four fp32 values in [0, 1] -> four E4M3 codes of p * 2^8 (one dword, value k in byte k).
+__device__ __forceinline__ uint32_t p_codes4(float p0, float p1, float p2, float p3) {
+  constexpr float kInv = 0x1p-8f;  // the conversion divides by its scale operand
+  att_short2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(att_short2{0, 0}, p0, p1, kInv, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, p2, p3, kInv, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// V [S, 128] bf16 of head blockIdx.y -> V^T codes [128, S] and scales [128, S/32].
+// Workgroup: tokens 64 * blockIdx.x .. + 63; thread t: channel t % 128, 32-token block t / 128.
+__global__ __launch_bounds__(256) void vt_quant_kernel(const uint16_t* __restrict__ v, uint8_t* __restrict__ vt_codes,
+                                                       uint8_t* __restrict__ vt_scales, int S) {
+  constexpr int kPitch = kD + 2;  // u16 per LDS row: a 4-byte pad keeps column reads spread over banks
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kPitch];
+  const int bh = blockIdx.y;
+  const int t0 = blockIdx.x * 64;
+  const uint16_t* src = v + ((size_t)bh * S + t0) * kD;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {  // 64 rows x 16 chunks of 16 bytes
+    const int g = threadIdx.x + 256 * u;
+    const int row = g >> 4, col = (g & 15) * 8;
+    const uint4 val = *reinterpret_cast<const uint4*>(src + (size_t)row * kD + col);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(tile + row * kPitch + col);
+    dst[0] = val.x;
+    dst[1] = val.y;
+    dst[2] = val.z;
+    dst[3] = val.w;
+  }
+  __syncthreads();
+  const int c = threadIdx.x & (kD - 1), blk = threadIdx.x >> 7;
+  uint32_t w[16];  // tokens 32 blk + 2j (low half) and + 2j + 1 (high half) of channel c
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t lo = tile[(32 * blk + 2 * j) * kPitch + c];
+    const uint32_t hi = tile[(32 * blk + 2 * j + 1) * kPitch + c];
+    w[j] = lo | (hi << 16);
+    m = max(m, max(lo & 0x7FFFu, hi & 0x7FFFu));
+  }
+  uint32_t code[8];
+  uint32_t sbyte;
+  if (m >= 0x7F80u) {  // NaN or Inf in the block: NaN scale, zero codes
+    sbyte = 0xFFu;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) code[k] = 0;
+  } else {
+    const int e = mx_shared_exponent<1>(m, 0);
+    sbyte = (uint32_t)(e + 127);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) code[k] = mx_encode_fp8x4(w[2 * k], w[2 * k + 1], e);
+  }
+  uint8_t* dst = vt_codes + ((size_t)bh * kD + c) * S + t0 + 32 * blk;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(code[0], code[1], code[2], code[3]);
+  *reinterpret_cast<uint4*>(dst + 16) = make_uint4(code[4], code[5], code[6], code[7]);
+  vt_scales[((size_t)bh * kD + c) * (S / 32) + t0 / 32 + blk] = (uint8_t)sbyte;
+}
+
+// Attention of 128 queries of head blockIdx.y.  Q, K: codes [BH*S, 128] and
+// scales [BH*S, 4]; V^T: codes [BH*128, S] and scales [BH*128, S/32]; out
+// bf16 [BH*S, 128].  S is a multiple of 64; c_log2 = log2(e) / sqrt(128).
+__global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restrict__ qc,
+                                                          const uint8_t* __restrict__ qs,
+                                                          const uint8_t* __restrict__ kc,
+                                                          const uint8_t* __restrict__ ks,
+                                                          const uint8_t* __restrict__ vtc,
+                                                          const uint8_t* __restrict__ vts,
+                                                          uint16_t* __restrict__ out, int S, float c_log2) {
+  __shared__ __attribute__((aligned(16))) uint8_t st[2][kStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 5, r32 = lane & 31;
+  const int bh = blockIdx.y;
+  const int qrow = blockIdx.x * kBQ + wave * 32 + r32;
+  const bool qvalid = qrow < S;
+  const int qr = qvalid ? qrow : S - 1;  // rows past S compute on a valid row and store nothing
+
+  // B operand of S^T: this lane's query, channels 64 s + (16 q .. 16 q + 15) and 64 s + 32 + (16 q ..)
+  const uint8_t* qp = qc + ((size_t)bh * S + qr) * kD;
+  uint4 qa[2][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    qa[s][0] = *reinterpret_cast<const uint4*>(qp + 64 * s + 16 * q);
+    qa[s][1] = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 + 16 * q);
+  }
+  const uint32_t qsw = *reinterpret_cast<const uint32_t*>(qs + ((size_t)bh * S + qr) * 4);
+  const int qsc0 = (int)((qsw >> (8 * q)) & 0xFFu);        // channel block q of the first 64
+  const int qsc1 = (int)((qsw >> (8 * (2 + q))) & 0xFFu);  // block 2 + q
+
+  const uint8_t* kbase = kc + (size_t)bh * S * kD;
+  const uint8_t* ksbase = ks + (size_t)bh * S * 4;
+  const uint8_t* vbase = vtc + (size_t)bh * kD * S;
+  const uint8_t* vsbase = vts + (size_t)bh * kD * (S / 32);
+  const int nsb = S / 32;
+
+  // global -> registers (issued a tile ahead) -> LDS
+  uint4 pk[2], pv[2];
+  uint32_t psc = 0;
+  auto load = [&](int kv0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int g = tid + 256 * u;
+      pk[u] = *reinterpret_cast<const uint4*>(kbase + (size_t)(kv0 + (g >> 3)) * kD + 16 * (g & 7));
+      pv[u] = *reinterpret_cast<const uint4*>(vbase + (size_t)(g >> 2) * S + kv0 + 16 * (g & 3));
+    }
+    if (tid < kBK)
+      psc = *reinterpret_cast<const uint32_t*>(ksbase + (size_t)(kv0 + tid) * 4);
+    else if (tid < kBK + kD)
+      psc = *reinterpret_cast<const uint16_t*>(vsbase + (size_t)(tid - kBK) * nsb + kv0 / 32);
+  };
+  auto store = [&](uint8_t* b) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int g = tid + 256 * u;
+      const int kr = g >> 3, kcol = g & 7;
+      *reinterpret_cast<uint4*>(b + kKOff + kr * kD + ((kcol ^ ((kr >> 1) & 7)) << 4)) = pk[u];
+      const int vr = g >> 2, vcol = g & 3;
+      *reinterpret_cast<uint4*>(b + kVOff + vr * kBK + ((vcol ^ ((vr >> 2) & 3)) << 4)) = pv[u];
+    }
+    if (tid < kBK)
+      *reinterpret_cast<uint32_t*>(b + kKsOff + tid * 4) = psc;
+    else if (tid < kBK + kD)
+      *reinterpret_cast<uint16_t*>(b + kVsOff + (tid - kBK) * 2) = (uint16_t)psc;
+  };
+
+  att_v16f acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = att_v16f{};
+  float m = -INFINITY, l = 0.0f;
+  const int ksw = (r32 >> 1) & 7;  // K row swizzle (invariant under 32-row steps)
+  const int vsw = (r32 >> 2) & 3;  // V^T row swizzle
+  const int ntiles = S / kBK;
+
+  load(0);
+  store(st[0]);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const uint8_t* b = st[t & 1];
+    if (t + 1 < ntiles) load((t + 1) * kBK);
+
+    // S^T tiles: keys 32 tt + (0..31) x the wave's 32 queries
+    att_v16f sacc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sacc[tt] = att_v16f{};
+      const int krow = 32 * tt + r32;
+      const uint8_t* kr = b + kKOff + krow * kD;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint4 a0 = *reinterpret_cast<const uint4*>(kr + (((4 * s + q) ^ ksw) << 4));
+        const uint4 a1 = *reinterpret_cast<const uint4*>(kr + (((4 * s + 2 + q) ^ ksw) << 4));
+        const int ksc = b[kKsOff + krow * 4 + 2 * s + q];
+        sacc[tt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(att_as_v8i(a0, a1),
+                                                                   att_as_v8i(qa[s][0], qa[s][1]), sacc[tt], 0, 0,
+                                                                   0, ksc, 0, s == 0 ? qsc0 : qsc1);
+      }
+    }
+
+    // online softmax (log2 domain)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sacc[tt][r] *= c_log2;
+        mx = fmaxf(mx, sacc[tt][r]);
+      }
+    mx = max_half(mx);
+    const float m_new = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 at the first tile
+    float ls = 0.0f;
+    uint32_t d[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          p[u] = __builtin_amdgcn_exp2f(sacc[tt][4 * i + u] - m_new);
+          ls += p[u];
+        }
+        d[tt][i] = p_codes4(p[0], p[1], p[2], p[3]);
+      }
+    l = l * alpha + ls;
+    m = m_new;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[c][r] *= alpha;
+
+    // P codes into the B-operand layout: lane half q holds keys 16 q .. 16 q + 15 of each tile
+    uint32_t pw[8];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const uint32_t r0 = xchg_half(q ? d[tt][0] : d[tt][2]);
+      const uint32_t r1 = xchg_half(q ? d[tt][1] : d[tt][3]);
+      pw[4 * tt + 0] = q ? r0 : d[tt][0];
+      pw[4 * tt + 1] = q ? d[tt][2] : r0;
+      pw[4 * tt + 2] = q ? r1 : d[tt][1];
+      pw[4 * tt + 3] = q ? d[tt][3] : r1;
+    }
+    const att_v8i pop = att_v8i{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
+                                (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+
+    // O^T += V^T P^T: channels 32 c + (0..31) x the wave's 32 queries
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int vrow = 32 * c + r32;
+      const uint8_t* vr = b + kVOff + vrow * kBK;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(vr + ((q ^ vsw) << 4));
+      const uint4 a1 = *reinterpret_cast<const uint4*>(vr + (((2 + q) ^ vsw) << 4));
+      const int vsc = b[kVsOff + vrow * 2 + q];
+      acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(att_as_v8i(a0, a1), pop, acc[c], 0, 0, 0, vsc, 0,
+                                                               kPScale);
+    }
+
+    if (t + 1 < ntiles) store(st[(t + 1) & 1]);
+    __syncthreads();
+  }
+
+  // out = O / l: lane (query, q) holds channels 32 c + 8 i + 4 q + (0..3)
+  const float inv = 1.0f / sum_half(l);
+  if (qvalid) {
+    uint16_t* orow = out + ((size_t)bh * S + qrow) * kD;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const att_bf16x2 lo = __builtin_convertvector(att_f32x2{acc[c][4 * i] * inv, acc[c][4 * i + 1] * inv},
+                                                      att_bf16x2);
+        const att_bf16x2 hi = __builtin_convertvector(
+            att_f32x2{acc[c][4 * i + 2] * inv, acc[c][4 * i + 3] * inv}, att_bf16x2);
+        *reinterpret_cast<uint2*>(orow + 32 * c + 8 * i + 4 * q) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+      }
+  }
+}
+
+}  // namespace
+
+AttentionLayout attention_layout(int64_t BH, int64_t S) {
+  auto r256 = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  AttentionLayout L{};
+  const size_t codes = (size_t)BH * (size_t)S * kD, scales = codes / 32;
+  L.q_codes = 0;
+  L.q_scales = L.q_codes + r256(codes);
+  L.k_codes = L.q_scales + r256(scales);
+  L.k_scales = L.k_codes + r256(codes);
+  L.vt_codes = L.k_scales + r256(scales);
+  L.vt_scales = L.vt_codes + r256(codes);
+  L.total = L.vt_scales + r256(scales);
+  return L;
+}
+
+hipError_t launch_attention_fp8(int64_t BH, int64_t S, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                uint16_t* out, uint8_t* ws, hipStream_t stream) {
+  const AttentionLayout L = attention_layout(BH, S);
+  hipError_t e = launch_mx_quant(1, 0, q, BH * S, kD, ws + L.q_codes, ws + L.q_scales, stream);
+  if (e != hipSuccess) return e;
+  e = launch_mx_quant(1, 0, k, BH * S, kD, ws + L.k_codes, ws + L.k_scales, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(vt_quant_kernel, dim3((unsigned)(S / 64), (unsigned)BH), dim3(256), 0, stream, v,
+                     ws + L.vt_codes, ws + L.vt_scales, (int)S);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const float c_log2 = 1.4426950408889634f / 11.313708498984761f;  // log2(e) / sqrt(128)
+  hipLaunchKernelGGL(attn_fp8_kernel, dim3((unsigned)((S + kBQ - 1) / kBQ), (unsigned)BH), dim3(256), 0, stream,
+                     ws + L.q_codes, ws + L.q_scales, ws + L.k_codes, ws + L.k_scales, ws + L.vt_codes,
+                     ws + L.vt_scales, out, (int)S, c_log2);
+  return hipGetLastError();
+}
+
+}  // namespace mxq

@@ -204,6 +204,40 @@ mxq_status mxq_gemm_requant(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K,
                                               (hipStream_t)stream));
 }
 
+namespace {
+constexpr int64_t kAttnHeadDim = 128;
+constexpr int64_t kAttnMaxBH = 65535;         // one grid row per (batch, head)
+constexpr int64_t kAttnMaxS = (int64_t)1 << 24;
+// shape status of an attention call: sizes, then what this build implements
+mxq_status attention_shape(int64_t B, int64_t H, int64_t S, int64_t D) {
+  if (B < 0 || H < 0 || S < 0 || D <= 0 || S > kAttnMaxS || (B > 0 && H > kAttnMaxBH / B)) return MXQ_ERR_SHAPE;
+  if (D != kAttnHeadDim || S % 64 != 0) return MXQ_ERR_UNSUPPORTED;
+  return MXQ_OK;
+}
+}  // namespace
+
+size_t mxq_attention_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D) {
+  if (attention_shape(B, H, S, D) != MXQ_OK) return 0;
+  return attention_layout(B * H, S).total;
+}
+
+mxq_status mxq_attention_fp8(int64_t B, int64_t H, int64_t S, int64_t D, const void* q_bf16, const void* k_bf16,
+                             const void* v_bf16, void* out_bf16, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  const mxq_status sh = attention_shape(B, H, S, D);
+  if (sh == MXQ_ERR_SHAPE) return sh;
+  if (B * H == 0 || S == 0) return MXQ_OK;  // empty: nothing to launch, whatever the pointers
+  if (sh != MXQ_OK) return sh;
+  if (!q_bf16 || !k_bf16 || !v_bf16 || !out_bf16) return MXQ_ERR_NULL;
+  if (!aligned16(q_bf16) || !aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
+  const size_t need = attention_layout(B * H, S).total;
+  if (!workspace || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MXQ_ERR_ALIGN;
+  return launch_status(launch_attention_fp8(B * H, S, (const uint16_t*)q_bf16, (const uint16_t*)k_bf16,
+                                            (const uint16_t*)v_bf16, (uint16_t*)out_bf16, (uint8_t*)workspace,
+                                            (hipStream_t)stream));
+}
+
 mxq_status mxq_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* a_bf16, const void* w_bf16,
                          const void* bias_bf16, void* out_bf16, void* stream) {
   if (K <= 0 || !valid_gemm(M, N, K)) return MXQ_ERR_SHAPE;

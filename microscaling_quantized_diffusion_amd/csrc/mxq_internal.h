@@ -45,6 +45,17 @@ hipError_t launch_nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_c
                              const float* a_ts, const uint8_t* w_codes, const uint8_t* w_scales,
                              const float* w_ts, const uint16_t* bias, uint16_t* out, hipStream_t stream);
 
+// Block-scaled FP8 attention, head dimension 128, S a multiple of 64.  The
+// workspace holds the MXFP8 Q and K (codes [BH*S, 128], scales [BH*S, 4]) and
+// V^T (codes [BH*128, S], scales [BH*128, S/32]), each section 256-byte
+// aligned; q, k, v, out are bf16 [BH, S, 128].
+struct AttentionLayout {
+  size_t q_codes, q_scales, k_codes, k_scales, vt_codes, vt_scales, total;
+};
+AttentionLayout attention_layout(int64_t BH, int64_t S);
+hipError_t launch_attention_fp8(int64_t BH, int64_t S, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                uint16_t* out, uint8_t* workspace, hipStream_t stream);
+
 // bf16 GEMM.
 hipError_t launch_bf16_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* a, const uint16_t* w,
                             const uint16_t* bias, uint16_t* out, hipStream_t stream);

@@ -46,6 +46,8 @@ SIGNATURES = {
     "mxq_quant_gemm_fused": (_I, [_I, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "mxq_gemm_requant": (_I, [_I, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _I, _I, _VP, _VP, _VP, _VP]),
     "mxq_gemm_bf16": (_I, [_I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
+    "mxq_attention_fp8": (_I, [_I64, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "mxq_attention_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
     "mxq_workspace_bytes": (_SZ, [_I, _I64, _I64, _I]),
     "mxq_should_quantize": (_I, [_I64, _I64, _I64]),
     "mxq_status_string": (ctypes.c_char_p, [_I]),
@@ -224,6 +226,29 @@ def gemm_bf16(a: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = N
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     _check("mxq_gemm_bf16", lib().mxq_gemm_bf16(M, N, K, _ptr(a), _ptr(w), _ptr(bias), _ptr(out), _stream(a)))
+    return out
+
+
+def attention_workspace_bytes(B: int, H: int, S: int, D: int) -> int:
+    return int(lib().mxq_attention_workspace_bytes(B, H, S, D))
+
+
+def attention_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mxq_attention_fp8: block-scaled FP8 attention of bf16 q, k, v [B, H, S, D] -> bf16 [B, H, S, D]."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, torch.bfloat16, n)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, S, D] shape")
+    B, H, S, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    need = attention_workspace_bytes(B, H, S, D)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    wsz = workspace.numel() * workspace.element_size()
+    _check("mxq_attention_fp8", lib().mxq_attention_fp8(B, H, S, D, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                                         _ptr(workspace), wsz, _stream(q)))
     return out
 
 

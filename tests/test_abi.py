@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert mxq.abi_version() == 3
+    assert mxq.abi_version() == 4
     for s in range(8):
         assert lib.mxq_status_string(s)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -158,3 +158,20 @@ def test_scale_rule_flag(lib):
     assert lib.mxq_workspace_bytes(3 | RCEIL, 64, 64, 1) == 0
     with pytest.raises(ValueError):
         mxq._fmt("mxfp8", "ceil")
+
+
+def test_attention_argument_errors(lib):
+    a, wb = lib.mxq_attention_fp8, lib.mxq_attention_workspace_bytes
+    need = wb(1, 2, 256, 128)
+    assert need >= 3 * 2 * 256 * 128
+    assert wb(1, 2, 256, 64) == 0 and wb(1, 2, 96, 128) == 0 and wb(-1, 2, 256, 128) == 0
+    # B, H, S, D, q, k, v, out, workspace, bytes, stream
+    assert a(1, 2, -64, 128, P, P, P, P, P, need, None) == 3  # negative size
+    assert a(1, 70000, 64, 128, P, P, P, P, P, need, None) == 3  # B * H beyond one grid dimension
+    assert a(0, 2, 256, 128, None, None, None, None, None, 0, None) == 0  # empty
+    assert a(1, 2, 256, 64, P, P, P, P, P, need, None) == 6  # head dimension other than 128
+    assert a(1, 2, 96, 128, P, P, P, P, P, need, None) == 6  # S not a multiple of 64
+    assert a(1, 2, 256, 128, P, None, P, P, P, need, None) == 1
+    assert a(1, 2, 256, 128, P, P, P, P + 8, P, need, None) == 4
+    assert a(1, 2, 256, 128, P, P, P, P, P, need - 1, None) == 5
+    assert a(1, 2, 256, 128, P, P, P, P, None, need, None) == 5
