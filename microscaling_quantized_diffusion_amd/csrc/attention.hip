@@ -20,9 +20,11 @@
 //                     channels in LDS; each thread encodes one 32-token block
 //                     of one channel with the quantizer's block encoding.
 //   attn_fp8_kernel   one workgroup = 128 queries of one head (four waves of
-//                     32); key tiles of 64 double-buffered in LDS through
-//                     registers (K rows and V^T rows XOR-swizzled by 16-byte
-//                     chunk, as in the GEMM staging).  Per tile and wave:
+//                     32); key tiles of 64 double-buffered in LDS, filled by
+//                     LDS DMA one tile ahead (K rows and V^T rows XOR-swizzled
+//                     by 16-byte chunk through the DMA source offsets, as in
+//                     the GEMM staging; every wave issues five DMAs per tile).
+//                     Per tile and wave:
 //       S^T = K Q^T    four 32x32x64 scaled MFMAs (K rows are the A operand
 //                      from LDS, the wave's 32 queries the B operand, held in
 //                      registers for the whole loop);
@@ -36,6 +38,7 @@
 //                      dwords of codes across the lane halves;
 //       O^T += V^T P^T four scaled MFMAs (V^T rows from LDS with their E8M0
 //                      scales, P with the constant scale 2^-8).
+#include "lds_dma.h"
 #include "mx_encode.h"
 #include "mxq_internal.h"
 
@@ -55,7 +58,8 @@ constexpr int kKOff = 0;                       // K tile: 64 rows x 128 code byt
 constexpr int kVOff = kBK * kD;                // V^T tile: 128 rows x 64 code bytes
 constexpr int kKsOff = kVOff + kD * kBK;       // K scales: 64 rows x 4 bytes
 constexpr int kVsOff = kKsOff + kBK * 4;       // V^T scales: 128 rows x 2 bytes
-constexpr int kStage = kVsOff + kD * 2;        // 16896 bytes
+constexpr int kSinkOff = kVsOff + kD * 2;      // landing area of the two idle scale DMAs
+constexpr int kStage = kSinkOff + 512;         // 17408 bytes
 constexpr int kPScale = 127 - 8;               // E8M0 byte of 2^-8, the scale of the P codes
 
 __device__ __forceinline__ att_v8i att_as_v8i(const uint4& lo, const uint4& hi) {
@@ -88,7 +92,9 @@ __device__ __forceinline__ uint32_t p_codes4(float p0, float p1, float p2, float
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// V [S, 128] bf16 of head blockIdx.y -> V^T codes [128, S] and scales [128, S/32].
+// V [S, 128] bf16 of head blockIdx.y -> V^T codes [128, S] and scales, the
+// scales tile-major ([S/64][128 channels][2 blocks]) so that each 64-key
+// tile's 256 scale bytes are contiguous for the attention kernel's DMA.
 // Workgroup: tokens 64 * blockIdx.x .. + 63; thread t: channel t % 128, 32-token block t / 128.
 __global__ __launch_bounds__(256) void vt_quant_kernel(const uint16_t* __restrict__ v, uint8_t* __restrict__ vt_codes,
                                                        uint8_t* __restrict__ vt_scales, int S) {
@@ -134,12 +140,13 @@ __global__ __launch_bounds__(256) void vt_quant_kernel(const uint16_t* __restric
   uint8_t* dst = vt_codes + ((size_t)bh * kD + c) * S + t0 + 32 * blk;
   *reinterpret_cast<uint4*>(dst) = make_uint4(code[0], code[1], code[2], code[3]);
   *reinterpret_cast<uint4*>(dst + 16) = make_uint4(code[4], code[5], code[6], code[7]);
-  vt_scales[((size_t)bh * kD + c) * (S / 32) + t0 / 32 + blk] = (uint8_t)sbyte;
+  vt_scales[((size_t)bh * (S / 64) + blockIdx.x) * (2 * kD) + 2 * c + blk] = (uint8_t)sbyte;
 }
 
 // Attention of 128 queries of head blockIdx.y.  Q, K: codes [BH*S, 128] and
-// scales [BH*S, 4]; V^T: codes [BH*128, S] and scales [BH*128, S/32]; out
-// bf16 [BH*S, 128].  S is a multiple of 64; c_log2 = log2(e) / sqrt(128).
+// scales [BH*S, 4]; V^T: codes [BH*128, S] and tile-major scales
+// [BH][S/64][128][2]; out bf16 [BH*S, 128].  S is a multiple of 64;
+// c_log2 = log2(e) / sqrt(128).
 __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restrict__ qc,
                                                           const uint8_t* __restrict__ qs,
                                                           const uint8_t* __restrict__ kc,
@@ -147,7 +154,10 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
                                                           const uint8_t* __restrict__ vtc,
                                                           const uint8_t* __restrict__ vts,
                                                           uint16_t* __restrict__ out, int S, float c_log2) {
-  __shared__ __attribute__((aligned(16))) uint8_t st[2][kStage];
+  // one __shared__ array per stage, each named at compile time in the
+  // unrolled loop, so the compiler waits only on the stage being read
+  __shared__ __attribute__((aligned(16))) uint8_t st0[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -169,40 +179,36 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
   const int qsc0 = (int)((qsw >> (8 * q)) & 0xFFu);        // channel block q of the first 64
   const int qsc1 = (int)((qsw >> (8 * (2 + q))) & 0xFFu);  // block 2 + q
 
-  const uint8_t* kbase = kc + (size_t)bh * S * kD;
-  const uint8_t* ksbase = ks + (size_t)bh * S * 4;
-  const uint8_t* vbase = vtc + (size_t)bh * kD * S;
-  const uint8_t* vsbase = vts + (size_t)bh * kD * (S / 32);
-  const int nsb = S / 32;
-
-  // global -> registers (issued a tile ahead) -> LDS
-  uint4 pk[2], pv[2];
-  uint32_t psc = 0;
-  auto load = [&](int kv0) {
+  // DMA sources: this head's K codes, K scales, V^T codes and V^T scales
+  const uint32_t head_bytes = (uint32_t)S * kD;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + (size_t)bh * head_bytes, head_bytes);
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(ks + (size_t)bh * S * 4, (uint32_t)S * 4);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vtc + (size_t)bh * head_bytes, head_bytes);
+  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vts + (size_t)bh * (S / 64) * (2 * kD), (uint32_t)(S / 64) * (2 * kD));
+  // Per-lane source offsets without the tile term.  A wave-wide 16-byte DMA
+  // fills 1 KiB of LDS in lane order: K rows 8 g .. 8 g + 7 (g = 2 wave + u),
+  // V^T rows 16 g .. 16 g + 15; each lane fetches the chunk whose swizzled
+  // position is its own.  Scales: wave 0 the tile's K scales, wave 1 its V^T
+  // scales (256 bytes each), waves 2 and 3 nothing (out of range, into the sink).
+  uint32_t koff[2], voff[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int g = 2 * wave + u;
+    const int kr = 8 * g + (lane >> 3), kp = lane & 7;
+    koff[u] = (uint32_t)kr * kD + (uint32_t)((kp ^ ((kr >> 1) & 7)) << 4);
+    const int vr = 16 * g + (lane >> 2), vp = lane & 3;
+    voff[u] = (uint32_t)vr * (uint32_t)S + (uint32_t)((vp ^ ((vr >> 2) & 3)) << 4);
+  }
+  const uint32_t soff = wave < 2 ? (uint32_t)lane * 4 : kOutOfRange;
+  const __amdgpu_buffer_rsrc_t rsc = wave == 1 ? rvs : rks;
+  auto issue = [&](auto& st, int kv0) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int g = tid + 256 * u;
-      pk[u] = *reinterpret_cast<const uint4*>(kbase + (size_t)(kv0 + (g >> 3)) * kD + 16 * (g & 7));
-      pv[u] = *reinterpret_cast<const uint4*>(vbase + (size_t)(g >> 2) * S + kv0 + 16 * (g & 3));
+      lds_dma16(rk, &st[kKOff + 1024 * (2 * wave + u)], koff[u], (uint32_t)kv0 * kD);
+      lds_dma16(rv, &st[kVOff + 1024 * (2 * wave + u)], voff[u], (uint32_t)kv0);
     }
-    if (tid < kBK)
-      psc = *reinterpret_cast<const uint32_t*>(ksbase + (size_t)(kv0 + tid) * 4);
-    else if (tid < kBK + kD)
-      psc = *reinterpret_cast<const uint16_t*>(vsbase + (size_t)(tid - kBK) * nsb + kv0 / 32);
-  };
-  auto store = [&](uint8_t* b) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int g = tid + 256 * u;
-      const int kr = g >> 3, kcol = g & 7;
-      *reinterpret_cast<uint4*>(b + kKOff + kr * kD + ((kcol ^ ((kr >> 1) & 7)) << 4)) = pk[u];
-      const int vr = g >> 2, vcol = g & 3;
-      *reinterpret_cast<uint4*>(b + kVOff + vr * kBK + ((vcol ^ ((vr >> 2) & 3)) << 4)) = pv[u];
-    }
-    if (tid < kBK)
-      *reinterpret_cast<uint32_t*>(b + kKsOff + tid * 4) = psc;
-    else if (tid < kBK + kD)
-      *reinterpret_cast<uint16_t*>(b + kVsOff + (tid - kBK) * 2) = (uint16_t)psc;
+    // tile kv0 / 64 of either scale array starts at byte 4 kv0
+    lds_dma4(rsc, &st[kKsOff + 256 * wave], soff, (uint32_t)kv0 * 4);
   };
 
   att_v16f acc[4];
@@ -213,22 +219,26 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
   const int vsw = (r32 >> 2) & 3;  // V^T row swizzle
   const int ntiles = S / kBK;
 
-  load(0);
-  store(st[0]);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const uint8_t* b = st[t & 1];
-    if (t + 1 < ntiles) load((t + 1) * kBK);
+  // One tile: its DMA has landed in `cur` (own wait, then the barrier for
+  // everyone's); the next tile's DMA goes into `nxt`, which every wave has
+  // finished reading (the last tile reloads itself, so the issue is
+  // unconditional); then scores, softmax and P V from `cur`.
+  auto step = [&](auto& cur, auto& nxt, int t) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    issue(nxt, (t + 1 < ntiles ? t + 1 : t) * kBK);
+    const uint8_t* b = cur;
 
     // S^T tiles: keys 32 tt + (0..31) x the wave's 32 queries
     att_v16f sacc[2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      sacc[tt] = att_v16f{};
-      const int krow = 32 * tt + r32;
-      const uint8_t* kr = b + kKOff + krow * kD;
+    for (int tt = 0; tt < 2; ++tt) sacc[tt] = att_v16f{};
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int krow = 32 * tt + r32;
+        const uint8_t* kr = b + kKOff + krow * kD;
         const uint4 a0 = *reinterpret_cast<const uint4*>(kr + (((4 * s + q) ^ ksw) << 4));
         const uint4 a1 = *reinterpret_cast<const uint4*>(kr + (((4 * s + 2 + q) ^ ksw) << 4));
         const int ksc = b[kKsOff + krow * 4 + 2 * s + q];
@@ -236,19 +246,17 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
                                                                    att_as_v8i(qa[s][0], qa[s][1]), sacc[tt], 0, 0,
                                                                    0, ksc, 0, s == 0 ? qsc0 : qsc1);
       }
-    }
 
-    // online softmax (log2 domain)
+    // online softmax in the log2 domain: the maximum is taken over the raw
+    // scores (the scale c_log2 is positive) and p = exp2(s c_log2 - m) is one
+    // fused multiply-add and one exponential per score
     float mx = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sacc[tt][r] *= c_log2;
-        mx = fmaxf(mx, sacc[tt][r]);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[tt][r]);
     mx = max_half(mx);
-    const float m_new = fmaxf(m, mx);
+    const float m_new = fmaxf(m, mx * c_log2);
     const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 at the first tile
     float ls = 0.0f;
     uint32_t d[2][4];
@@ -259,17 +267,21 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
         float p[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          p[u] = __builtin_amdgcn_exp2f(sacc[tt][4 * i + u] - m_new);
+          p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tt][4 * i + u], c_log2, -m_new));
           ls += p[u];
         }
         d[tt][i] = p_codes4(p[0], p[1], p[2], p[3]);
       }
     l = l * alpha + ls;
     m = m_new;
+    // once the running maxima settle, alpha is exactly 1 in every lane and the
+    // rescale is skipped (a wave-uniform branch; multiplying by 1 is exact)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[c][r] *= alpha;
+        for (int r = 0; r < 16; ++r) acc[c][r] *= alpha;
+    }
 
     // P codes into the B-operand layout: lane half q holds keys 16 q .. 16 q + 15 of each tile
     uint32_t pw[8];
@@ -296,10 +308,16 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
       acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(att_as_v8i(a0, a1), pop, acc[c], 0, 0, 0, vsc, 0,
                                                                kPScale);
     }
+  };
 
-    if (t + 1 < ntiles) store(st[(t + 1) & 1]);
-    __syncthreads();
+  issue(st0, 0);
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(st0, st1, t);
+    step(st1, st0, t + 1);
   }
+  if (t < ntiles) step(st0, st1, t);
+  wait_vmcnt<0>();  // the last (redundant) DMA lands before the workgroup's LDS is released
 
   // out = O / l: lane (query, q) holds channels 32 c + 8 i + 4 q + (0..3)
   const float inv = 1.0f / sum_half(l);

@@ -47,8 +47,9 @@ hipError_t launch_nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_c
 
 // Block-scaled FP8 attention, head dimension 128, S a multiple of 64.  The
 // workspace holds the MXFP8 Q and K (codes [BH*S, 128], scales [BH*S, 4]) and
-// V^T (codes [BH*128, S], scales [BH*128, S/32]), each section 256-byte
-// aligned; q, k, v, out are bf16 [BH, S, 128].
+// V^T (codes [BH*128, S]; scales tile-major [BH][S/64][128][2], one 256-byte
+// run per 64-key tile), each section 256-byte aligned; q, k, v, out are bf16
+// [BH, S, 128].
 struct AttentionLayout {
   size_t q_codes, q_scales, k_codes, k_scales, vt_codes, vt_scales, total;
 };
