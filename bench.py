@@ -9,7 +9,11 @@ resident copies so the working set exceeds the 256 MB Infinity Cache.
 
 Prints ONE JSON line.  ``--all`` adds the other FLUX-shaped workloads
 (MXFP4 single-stream linears, NVFP4 at 2048x2048, one double-stream block
-with selective bf16 fallback) under "extra".
+with selective bf16 fallback) under "extra", and the widened paths:
+producer-fused quantization ("producer_fused"), a block's linears eager vs
+HIP-graphed ("block_sequences"), block-scaled FP8 attention at the FLUX
+shape beside torch's bf16 attention ("attention") and the quantizer under
+both shared-scale rules ("scale_rules").
 """
 
 from __future__ import annotations
@@ -204,6 +208,55 @@ def run_producer_fused(dev, steps, warmup, rotate):
             "mlp_chain_producer_fused_ms": chain_fused, "mlp_chain_producer_fused_gelu_ms": chain_fused_gelu}
 
 
+def run_attention(dev, steps, warmup, B=1, H=24, S=4608, D=128):
+    """Block-scaled FP8 attention at the FLUX-dev 1024 x 1024 shape (24 heads, 4608 tokens = 4096 image +
+    512 text, head dimension 128), one mxq_attention_fp8 call per step (Q, K, V quantization included);
+    torch's bf16 scaled_dot_product_attention on the same inputs is timed beside it as context."""
+    import torch
+    import torch.nn.functional as F
+
+    from microscaling_quantized_diffusion_amd import mxq
+
+    g = torch.Generator(device=dev).manual_seed(0)
+    q, k, v = (torch.randn((B, H, S, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(3))
+    out = torch.empty_like(q)
+    ws = torch.empty(mxq.attention_workspace_bytes(B, H, S, D), dtype=torch.uint8, device=dev)
+    flops = 4.0 * B * H * S * S * D
+    dist = {}
+    ms = _time_loop(lambda i: mxq.attention_fp8(q, k, v, out, ws), steps, warmup, dist)
+    ms_sdpa = _time_loop(lambda i: F.scaled_dot_product_attention(q, k, v), steps, warmup)
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return {"shape": f"B={B} H={H} S={S} D={D}", "ms": ms, "ms_p10_p50_p90": [dist["p10"], dist["p50"], dist["p90"]],
+            "tflops": flops / ms / 1e9, "frac_of_fp8_mfma_peak": flops / ms / 1e9 / PEAK_TFLOPS["mxfp8"],
+            "sdpa_bf16_ms": ms_sdpa, "sdpa_bf16_tflops": flops / ms_sdpa / 1e9, "speedup_vs_sdpa_bf16": ms_sdpa / ms}
+
+
+def run_scale_rules(dev, steps, warmup, rotate):
+    """The MXFP8 quantizer on the FLUX MLP activation (4608 x 3072) with the OCP floor rule and the
+    round-up rule."""
+    import torch
+
+    from microscaling_quantized_diffusion_amd import mxq
+    from microscaling_quantized_diffusion_amd.inputs import WORKLOADS, make_layer_inputs
+
+    layer = WORKLOADS["flux_mlp_up_mxfp8"].layers[0]
+    a_bits, _ = make_layer_inputs(layer, seed=0)
+    xs = [_upload(a_bits, dev)]
+    xs += [xs[0].clone() for _ in range(rotate - 1)]
+    qs = [mxq.quantize("mxfp8", x) for x in xs]
+    res = {"shape": f"{layer.M}x{layer.K}"}
+    nbytes = layer.M * layer.K * (2 + 1 + 1 / 32)
+    for rule in ("floor", "rceil"):
+        ms = _time_loop(lambda i: mxq.quantize("mxfp8", xs[i % rotate], qs[i % rotate], scale_rule=rule), steps,
+                        warmup)
+        res[f"{rule}_ms"] = ms
+        res[f"{rule}_GB/s"] = nbytes / ms / 1e6
+    del xs, qs
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(layer, sample_rows):
     """Time the CPU oracle (quantize A, dequantize both operands, fp64 GEMM) on a row sample of the workload."""
     import oracle
@@ -321,6 +374,13 @@ def main():
             print(f"# timing the {name} linear sequence, eager and graphed", file=sys.stderr, flush=True)
             e = run_sequence(name, dev, max(10, args.steps // 2), 3)
             line["block_sequences"].append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in e.items()})
+        print("# timing FP8 attention at the FLUX shape", file=sys.stderr, flush=True)
+        at = run_attention(dev, max(10, args.steps // 2), 3)
+        line["attention"] = {k: (round(v, 4) if isinstance(v, float) else
+                                 [round(x, 4) for x in v] if isinstance(v, list) else v) for k, v in at.items()}
+        print("# timing the MXFP8 quantizer with both scale rules", file=sys.stderr, flush=True)
+        sr = run_scale_rules(dev, max(10, args.steps // 2), 3, min(args.rotate, 4))
+        line["scale_rules"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in sr.items()}
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
