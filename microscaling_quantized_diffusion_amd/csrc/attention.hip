@@ -34,8 +34,8 @@
 //                      P codes from v_cvt_scalef32_pk_fp8_f32 at scale 2^-8;
 //       P -> operand   the 32x32 accumulator gives lane half h keys 8i + 4h
 //                      + (0..3); the MFMA's B operand wants keys 16h .. 16h
-//                      + 15 of each 32-key tile, so each tile swaps two
-//                      dwords of codes across the lane halves;
+//                      + 15 of each 32-key tile, which two permlane32 swaps
+//                      per tile produce directly;
 //       O^T += V^T P^T four scaled MFMAs (V^T rows from LDS with their E8M0
 //                      scales, P with the constant scale 2^-8).
 #include "lds_dma.h"
@@ -66,20 +66,26 @@ __device__ __forceinline__ att_v8i att_as_v8i(const uint4& lo, const uint4& hi) 
   return att_v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// The value lane l ^ 32 passed in `send`.  permlane32_swap exchanges one
-// operand's upper lane half with the other operand's lower half; with the same
-// value in both operands, one result holds the lane's own value and the other
-// its partner's, so the one that differs from `send` is the partner's (and
-// when none differs the two values are equal).
-__device__ __forceinline__ uint32_t xchg_half(uint32_t send) {
-  const auto r = __builtin_amdgcn_permlane32_swap(send, send, false, false);
-  return r[0] != send ? r[0] : r[1];
+// v_permlane32_swap(x, y), measured on gfx950: result 0 is x in lanes 0-31
+// and y of lane l - 32 in lanes 32-63; result 1 is x of lane l + 32 in lanes
+// 0-31 and y in lanes 32-63.  For the P codes of a 32-key accumulator tile
+// (dword i of lane half h = keys 8 i + 4 h + 0..3), swap(d0, d2) gives every
+// lane its keys 16 h + 0..7 and swap(d1, d3) its keys 16 h + 8..15, in order.
+__device__ __forceinline__ void p_regroup(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3, uint32_t* pw) {
+  const auto r0 = __builtin_amdgcn_permlane32_swap(d0, d2, false, false);
+  const auto r1 = __builtin_amdgcn_permlane32_swap(d1, d3, false, false);
+  pw[0] = r0[0];
+  pw[1] = r0[1];
+  pw[2] = r1[0];
+  pw[3] = r1[1];
 }
+// max / sum of the lane's value and that of lane l ^ 32 (one result of the
+// swap is each, in either lane half)
 __device__ __forceinline__ float max_half(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float sum_half(float v) {  // own + partner: one result is each
+__device__ __forceinline__ float sum_half(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
@@ -286,14 +292,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
     // P codes into the B-operand layout: lane half q holds keys 16 q .. 16 q + 15 of each tile
     uint32_t pw[8];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const uint32_t r0 = xchg_half(q ? d[tt][0] : d[tt][2]);
-      const uint32_t r1 = xchg_half(q ? d[tt][1] : d[tt][3]);
-      pw[4 * tt + 0] = q ? r0 : d[tt][0];
-      pw[4 * tt + 1] = q ? d[tt][2] : r0;
-      pw[4 * tt + 2] = q ? r1 : d[tt][1];
-      pw[4 * tt + 3] = q ? d[tt][3] : r1;
-    }
+    for (int tt = 0; tt < 2; ++tt) p_regroup(d[tt][0], d[tt][1], d[tt][2], d[tt][3], pw + 4 * tt);
     const att_v8i pop = att_v8i{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
                                 (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
 
