@@ -12,8 +12,10 @@ Prints ONE JSON line.  ``--all`` adds the other FLUX-shaped workloads
 with selective bf16 fallback) under "extra", and the widened paths:
 producer-fused quantization ("producer_fused"), a block's linears eager vs
 HIP-graphed ("block_sequences"), block-scaled FP8 attention at the FLUX
-shape beside torch's bf16 attention ("attention") and the quantizer under
-both shared-scale rules ("scale_rules").
+shape beside torch's bf16 attention ("attention"), the single-stream
+block's concatenated linear2 input built by the producers' epilogues
+("single_block_concat") and the quantizer under both shared-scale rules
+("scale_rules").
 """
 
 from __future__ import annotations
@@ -232,6 +234,43 @@ def run_attention(dev, steps, warmup, B=1, H=24, S=4608, D=128):
             "sdpa_bf16_ms": ms_sdpa, "sdpa_bf16_tflops": flops / ms_sdpa / 1e9, "speedup_vs_sdpa_bf16": ms_sdpa / ms}
 
 
+def run_single_block_concat(dev, steps, warmup, H=24, S=4608, F=12288):
+    """FLUX single-stream block at 1024 x 1024, MXFP4: the input of linear2 is [attention output (3072) |
+    GELU of linear1's MLP part (12288)] for 4608 tokens.  Unfused: bf16 attention, the bf16 MLP GEMM and the
+    standalone quantizer over the concatenation (the bf16 concatenation itself counted as free).  Fused:
+    the attention and the MLP GEMM emit their MXFP4 codes straight into the concatenated matrix."""
+    import torch
+
+    from microscaling_quantized_diffusion_amd import mxq
+
+    D = H * 128
+    g = torch.Generator(device=dev).manual_seed(0)
+    q, k, v = (torch.randn((1, H, S, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(3))
+    x = mxq.quantize("mxfp4", torch.randn((S, D), generator=g, device=dev).to(torch.bfloat16))
+    w = mxq.quantize("mxfp4", (torch.randn((F, D), generator=g, device=dev) * 0.02).to(torch.bfloat16))
+    ws = torch.empty(mxq.attention_workspace_bytes(1, H, S, 128), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    h = torch.empty((S, F), dtype=torch.bfloat16, device=dev)
+    cat_bf16 = torch.zeros((S, D + F), dtype=torch.bfloat16, device=dev)
+    cat = mxq.quantize("mxfp4", cat_bf16)
+    att_part = mxq.QTensor("mxfp4", cat.codes[:, :D // 2], cat.scales[:, :D // 32], None, D)
+    mlp_part = mxq.QTensor("mxfp4", cat.codes[:, D // 2:], cat.scales[:, D // 32:], None, F)
+    t_att = _time_loop(lambda i: mxq.attention_fp8(q, k, v, o, ws), steps, warmup)
+    t_mlp = _time_loop(lambda i: mxq.gemm(x, w, None, h), steps, warmup)
+    t_quant = _time_loop(lambda i: mxq.quantize("mxfp4", cat_bf16, cat), steps, warmup)
+    t_att_rq = _time_loop(lambda i: mxq.attention_fp8_requant(q, k, v, "mxfp4", att_part, ws), steps, warmup)
+    t_mlp_rq = _time_loop(lambda i: mxq.gemm_requant(x, w, "mxfp4", None, "gelu_tanh", mlp_part), steps, warmup)
+    unfused = _time_loop(lambda i: (mxq.attention_fp8(q, k, v, o, ws), mxq.gemm(x, w, None, h),
+                                    mxq.quantize("mxfp4", cat_bf16, cat)), steps, warmup)
+    fused = _time_loop(lambda i: (mxq.attention_fp8_requant(q, k, v, "mxfp4", att_part, ws),
+                                  mxq.gemm_requant(x, w, "mxfp4", None, "gelu_tanh", mlp_part)), steps, warmup)
+    del q, k, v, x, w, ws, o, h, cat_bf16, cat
+    torch.cuda.empty_cache()
+    return {"shape": f"{S} tokens, [{D} | {F}] -> MXFP4", "attention_bf16_ms": t_att, "mlp_gemm_bf16_ms": t_mlp,
+            "concat_quantizer_ms": t_quant, "attention_requant_ms": t_att_rq, "mlp_gemm_gelu_requant_ms": t_mlp_rq,
+            "unfused_ms": unfused, "producer_fused_ms": fused}
+
+
 def run_scale_rules(dev, steps, warmup, rotate):
     """The MXFP8 quantizer on the FLUX MLP activation (4608 x 3072) with the OCP floor rule and the
     round-up rule."""
@@ -378,6 +417,9 @@ def main():
         at = run_attention(dev, max(10, args.steps // 2), 3)
         line["attention"] = {k: (round(v, 4) if isinstance(v, float) else
                                  [round(x, 4) for x in v] if isinstance(v, list) else v) for k, v in at.items()}
+        print("# timing the single-stream block's concatenated linear2 input", file=sys.stderr, flush=True)
+        sb = run_single_block_concat(dev, max(10, args.steps // 2), 3)
+        line["single_block_concat"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in sb.items()}
         print("# timing the MXFP8 quantizer with both scale rules", file=sys.stderr, flush=True)
         sr = run_scale_rules(dev, max(10, args.steps // 2), 3, min(args.rotate, 4))
         line["scale_rules"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in sr.items()}

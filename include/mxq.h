@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 4
+#define MXQ_ABI_VERSION 5
 
 typedef enum {
   MXQ_FMT_MXFP8 = 1, /* E4M3 codes, E8M0 scale per 32 K-elements */
@@ -178,8 +178,15 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K,
  *   out_fmt        MXQ_FMT_MXFP8 or MXQ_FMT_MXFP4, optionally | MXQ_SCALE_RCEIL
  *   out_bf16       device bf16 [M, N], 16-byte aligned, or NULL: also store y
  *   out_codes      device, out: uint8 [M, N] (MXFP8) or [M, N/2] (MXFP4),
- *                  16-byte aligned
- *   out_scales     device, out: uint8 [M, N/32] E8M0
+ *                  rows out_codes_ld bytes apart, 16-byte aligned
+ *   out_scales     device, out: uint8 [M, N/32] E8M0, rows out_scales_ld
+ *                  bytes apart
+ *   out_codes_ld, out_scales_ld   row strides in bytes, 0 for dense rows;
+ *                  otherwise at least a dense row, the codes' a multiple of
+ *                  16 (MXQ_ERR_SHAPE / MXQ_ERR_ALIGN).  With them the GEMM
+ *                  writes a column range of a wider quantized matrix (pass
+ *                  pointers offset to its first column, a multiple of 32
+ *                  elements), e.g. one part of a concatenated activation.
  * Supported where N % 32 == 0, K % 128 == 0 (MXFP8 operands) or K % 256 == 0
  * (MXFP4 operands), and the scale rows are 4-byte aligned; other shapes
  * return MXQ_ERR_UNSUPPORTED.  Sizes otherwise as in mxq_gemm.
@@ -187,7 +194,7 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K,
 mxq_status mxq_gemm_requant(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void* a_codes,
                             const void* a_scales, const void* w_codes, const void* w_scales, const void* bias_bf16,
                             int act, mxq_format out_fmt, void* out_bf16, void* out_codes, void* out_scales,
-                            void* stream);
+                            int64_t out_codes_ld, int64_t out_scales_ld, void* stream);
 
 /*
  * bf16 GEMM for layers left unquantized by the selective rule:
@@ -231,6 +238,31 @@ mxq_status mxq_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* a_bf16, co
 mxq_status mxq_attention_fp8(int64_t B, int64_t H, int64_t S, int64_t D, const void* q_bf16, const void* k_bf16,
                              const void* v_bf16, void* out_bf16, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * mxq_attention_fp8 with the output MX-quantized for the next layer instead
+ * of stored as bf16, so that no bf16 attention output passes through memory
+ * on its way to a quantized linear: the bf16 values mxq_attention_fp8 would
+ * store are quantized as mxq_quantize(out_fmt) would quantize them, laid out
+ * token-major with the heads side by side, the layout a DiT's output
+ * projection reads:
+ *   row b * S + s, column h * D + d  (B * S rows, H * D columns).
+ *
+ *   B, H, S, D, q_bf16, k_bf16, v_bf16, workspace   as in mxq_attention_fp8
+ *   out_fmt        MXQ_FMT_MXFP8 or MXQ_FMT_MXFP4, optionally | MXQ_SCALE_RCEIL
+ *   out_codes      device, out: uint8 rows of H * D (MXFP8) or H * D / 2 (MXFP4)
+ *                  bytes, out_codes_ld bytes apart, 16-byte aligned
+ *   out_scales     device, out: uint8 rows of H * D / 32 E8M0 bytes,
+ *                  out_scales_ld bytes apart
+ *   out_codes_ld, out_scales_ld   row strides in bytes, 0 for dense rows, as
+ *                  in mxq_gemm_requant (so the codes can land in a column
+ *                  range of a wider matrix, e.g. a concatenated activation)
+ * Errors as in mxq_attention_fp8; NVFP4 output is MXQ_ERR_UNSUPPORTED.
+ */
+mxq_status mxq_attention_fp8_requant(int64_t B, int64_t H, int64_t S, int64_t D, const void* q_bf16,
+                                     const void* k_bf16, const void* v_bf16, mxq_format out_fmt,
+                                     void* out_codes, void* out_scales, int64_t out_codes_ld,
+                                     int64_t out_scales_ld, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes needed by mxq_attention_fp8; 0 for sizes it rejects. */
 size_t mxq_attention_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D);

@@ -151,15 +151,23 @@ __global__ __launch_bounds__(256) void vt_quant_kernel(const uint16_t* __restric
 
 // Attention of 128 queries of head blockIdx.y.  Q, K: codes [BH*S, 128] and
 // scales [BH*S, 4]; V^T: codes [BH*128, S] and tile-major scales
-// [BH][S/64][128][2]; out bf16 [BH*S, 128].  S is a multiple of 64;
-// c_log2 = log2(e) / sqrt(128).
+// [BH][S/64][128][2].  S is a multiple of 64; c_log2 = log2(e) / sqrt(128).
+// Output: REQ 0: bf16 [BH*S, 128] in `out`.  REQ 1 / 2: MX-quantized (E4M3 /
+// E2M1 codes, E8M0 scales per 32 channels, rceil selecting the round-up rule)
+// token-major, heads side by side: row b*S + s, columns h*128 + d, rows qld
+// code bytes and sld scale bytes apart; the bf16 values quantized are those
+// REQ 0 would store.
+template <int REQ>
 __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restrict__ qc,
                                                           const uint8_t* __restrict__ qs,
                                                           const uint8_t* __restrict__ kc,
                                                           const uint8_t* __restrict__ ks,
                                                           const uint8_t* __restrict__ vtc,
                                                           const uint8_t* __restrict__ vts,
-                                                          uint16_t* __restrict__ out, int S, float c_log2) {
+                                                          uint16_t* __restrict__ out, int S, float c_log2,
+                                                          uint8_t* __restrict__ qcodes,
+                                                          uint8_t* __restrict__ qscales, int64_t qld, int64_t sld,
+                                                          int H, int rceil) {
   // one __shared__ array per stage, each named at compile time in the
   // unrolled loop, so the compiler waits only on the stage being read
   __shared__ __attribute__((aligned(16))) uint8_t st0[kStage];
@@ -320,19 +328,61 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
 
   // out = O / l: lane (query, q) holds channels 32 c + 8 i + 4 q + (0..3)
   const float inv = 1.0f / sum_half(l);
-  if (qvalid) {
-    uint16_t* orow = out + ((size_t)bh * S + qrow) * kD;
+  if constexpr (REQ == 0) {
+    if (qvalid) {
+      uint16_t* orow = out + ((size_t)bh * S + qrow) * kD;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const att_bf16x2 lo = __builtin_convertvector(att_f32x2{acc[c][4 * i] * inv, acc[c][4 * i + 1] * inv},
+                                                        att_bf16x2);
+          const att_bf16x2 hi = __builtin_convertvector(
+              att_f32x2{acc[c][4 * i + 2] * inv, acc[c][4 * i + 3] * inv}, att_bf16x2);
+          *reinterpret_cast<uint2*>(orow + 32 * c + 8 * i + 4 * q) =
+              make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+        }
+    }
+  } else {
+    // The same bf16 values, MX-quantized per 32 channels: a block is this
+    // lane's 16 values and the other lane half's 16 (the amax is exchanged
+    // with one swap); codes and scale as the standalone quantizer makes them.
+    const int b = bh / H, h = bh % H;
+    const size_t orow = (size_t)b * S + qrow;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t w[8];  // bf16 pairs: channels 8 i + 4 q + (0, 1) and (2, 3)
+      uint32_t m = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const att_bf16x2 lo = __builtin_convertvector(att_f32x2{acc[c][4 * i] * inv, acc[c][4 * i + 1] * inv},
                                                       att_bf16x2);
-        const att_bf16x2 hi = __builtin_convertvector(
-            att_f32x2{acc[c][4 * i + 2] * inv, acc[c][4 * i + 3] * inv}, att_bf16x2);
-        *reinterpret_cast<uint2*>(orow + 32 * c + 8 * i + 4 * q) =
-            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+        const att_bf16x2 hi = __builtin_convertvector(att_f32x2{acc[c][4 * i + 2] * inv, acc[c][4 * i + 3] * inv},
+                                                      att_bf16x2);
+        w[2 * i] = __builtin_bit_cast(uint32_t, lo);
+        w[2 * i + 1] = __builtin_bit_cast(uint32_t, hi);
+        m = max(m, mx_absmax_bits4(w[2 * i], w[2 * i + 1]));
       }
+      const auto sw = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+      m = max(sw[0], sw[1]);
+      const bool nonfinite = m >= 0x7F80u;  // NaN or Inf in the block: NaN scale, zero codes
+      const int e = nonfinite ? 0 : mx_shared_exponent<REQ>(m, rceil);
+      if (qvalid) {
+        const int col = h * kD + 32 * c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ch = col + 8 * i + 4 * q;
+          if constexpr (REQ == 1) {
+            const uint32_t code = nonfinite ? 0u : mx_encode_fp8x4(w[2 * i], w[2 * i + 1], e);
+            *reinterpret_cast<uint32_t*>(qcodes + orow * (size_t)qld + ch) = code;
+          } else {
+            const uint32_t code = nonfinite ? 0u : mx_encode_fp4x4<0>(0u, w[2 * i], w[2 * i + 1], e);
+            *reinterpret_cast<uint16_t*>(qcodes + orow * (size_t)qld + ch / 2) = (uint16_t)code;
+          }
+        }
+        if (q == 0) qscales[orow * (size_t)sld + col / 32] = nonfinite ? 0xFFu : (uint8_t)(e + 127);
+      }
+    }
   }
 }
 
@@ -353,7 +403,8 @@ AttentionLayout attention_layout(int64_t BH, int64_t S) {
 }
 
 hipError_t launch_attention_fp8(int64_t BH, int64_t S, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                uint16_t* out, uint8_t* ws, hipStream_t stream) {
+                                uint16_t* out, uint8_t* ws, hipStream_t stream, int out_elem, int rceil, int64_t H,
+                                uint8_t* qcodes, uint8_t* qscales, int64_t qld, int64_t sld) {
   const AttentionLayout L = attention_layout(BH, S);
   hipError_t e = launch_mx_quant(1, 0, q, BH * S, kD, ws + L.q_codes, ws + L.q_scales, stream);
   if (e != hipSuccess) return e;
@@ -364,9 +415,19 @@ hipError_t launch_attention_fp8(int64_t BH, int64_t S, const uint16_t* q, const 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float c_log2 = 1.4426950408889634f / 11.313708498984761f;  // log2(e) / sqrt(128)
-  hipLaunchKernelGGL(attn_fp8_kernel, dim3((unsigned)((S + kBQ - 1) / kBQ), (unsigned)BH), dim3(256), 0, stream,
-                     ws + L.q_codes, ws + L.q_scales, ws + L.k_codes, ws + L.k_scales, ws + L.vt_codes,
-                     ws + L.vt_scales, out, (int)S, c_log2);
+  const dim3 grid((unsigned)((S + kBQ - 1) / kBQ), (unsigned)BH);
+  if (out_elem == 0)
+    hipLaunchKernelGGL(attn_fp8_kernel<0>, grid, dim3(256), 0, stream, ws + L.q_codes, ws + L.q_scales,
+                       ws + L.k_codes, ws + L.k_scales, ws + L.vt_codes, ws + L.vt_scales, out, (int)S, c_log2,
+                       nullptr, nullptr, (int64_t)0, (int64_t)0, (int)H, 0);
+  else if (out_elem == 1)
+    hipLaunchKernelGGL(attn_fp8_kernel<1>, grid, dim3(256), 0, stream, ws + L.q_codes, ws + L.q_scales,
+                       ws + L.k_codes, ws + L.k_scales, ws + L.vt_codes, ws + L.vt_scales, nullptr, (int)S, c_log2,
+                       qcodes, qscales, qld, sld, (int)H, rceil);
+  else
+    hipLaunchKernelGGL(attn_fp8_kernel<2>, grid, dim3(256), 0, stream, ws + L.q_codes, ws + L.q_scales,
+                       ws + L.k_codes, ws + L.k_scales, ws + L.vt_codes, ws + L.vt_scales, nullptr, (int)S, c_log2,
+                       qcodes, qscales, qld, sld, (int)H, rceil);
   return hipGetLastError();
 }
 

@@ -461,7 +461,7 @@ template <int TI, int TJ, int WTM, int WTN, int OELEM, int ACT>
 __device__ __forceinline__ void store_tile_requant(const v16f (&acc)[TI][TJ], float oscale, uint8_t* region,
                                                    const uint16_t* __restrict__ bias, uint8_t* __restrict__ qcodes,
                                                    uint8_t* __restrict__ qscales, int M, int N, int mw, int nw,
-                                                   int lane, int rceil) {
+                                                   int lane, int rceil, int64_t qld, int64_t sld) {
   constexpr int CB = OELEM == 1 ? 32 : 16;  // code bytes per row and 32-column block
   constexpr int RB = TI * CB;               // code bytes per row of the wave's segment
   constexpr int PITCH = RB + 16;
@@ -469,10 +469,10 @@ __device__ __forceinline__ void store_tile_requant(const v16f (&acc)[TI][TJ], fl
   constexpr int RPI = 64 / CPR;
   constexpr int NIT = (32 + RPI - 1) / RPI;
   constexpr int COLS_PER_CHUNK = 16 * 32 / CB;
-  static_assert(TI <= 4 && CPR <= 64, "requant epilogue shape");
+  static_assert(TI <= 8 && CPR <= 64, "requant epilogue shape");
   const int q = lane >> 5, r32 = lane & 31;
-  const size_t crow = OELEM == 1 ? (size_t)N : (size_t)N / 2;  // code bytes per output row
-  const int nsb = N / 32;                                      // scale bytes per output row
+  const size_t crow = (size_t)qld;  // code bytes between output rows
+  const size_t nsb = (size_t)sld;   // scale bytes between output rows
   const int cc = lane % CPR;
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
@@ -480,7 +480,7 @@ __device__ __forceinline__ void store_tile_requant(const v16f (&acc)[TI][TJ], fl
       wait_lgkmcnt0();
       __builtin_amdgcn_wave_barrier();
     }
-    uint32_t sword = 0;  // scale bytes of blocks i = 0 .. TI-1 of this lane's row
+    uint64_t sword = 0;  // scale bytes of blocks i = 0 .. TI-1 of this lane's row
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       uint2 v[4];
@@ -494,7 +494,7 @@ __device__ __forceinline__ void store_tile_requant(const v16f (&acc)[TI][TJ], fl
       m = max(sw[0], sw[1]);
       const bool nonfinite = m >= 0x7F80u;  // NaN or Inf in the block: NaN scale, zero codes
       const int e = nonfinite ? 0 : mx_shared_exponent<OELEM>(m, rceil);
-      sword |= (nonfinite ? 0xFFu : (uint32_t)(e + 127)) << (8 * i);
+      sword |= (uint64_t)(nonfinite ? 0xFFu : (uint32_t)(e + 127)) << (8 * i);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         if constexpr (OELEM == 1) {
@@ -510,7 +510,7 @@ __device__ __forceinline__ void store_tile_requant(const v16f (&acc)[TI][TJ], fl
     if (q == 0 && mrow < M) {
 #pragma unroll
       for (int i = 0; i < TI; ++i)
-        if (nw + 32 * i < N) qscales[(size_t)mrow * nsb + nw / 32 + i] = (uint8_t)(sword >> (8 * i));
+        if (nw + 32 * i < N) qscales[(size_t)mrow * nsb + (size_t)(nw / 32 + i)] = (uint8_t)(sword >> (8 * i));
     }
     wait_lgkmcnt0();
     __builtin_amdgcn_wave_barrier();
@@ -578,7 +578,7 @@ template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS, int REQ = 
 __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1) void mxp_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
     const uint8_t* __restrict__ Ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N,
-    int K, uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales, int rceil) {
+    int K, uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales, int rceil, int64_t qld, int64_t sld) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TJ = WTM / 32, TI = WTN / 32;  // 32 x 32 tiles per wave (M, N)
@@ -792,7 +792,7 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
     store_tile_bf16<TI, TJ, WTM, WTN, ACT>(acc, 1.0f, region, bias, out, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
   } else {
     store_tile_requant<TI, TJ, WTM, WTN, REQ, ACT>(acc, 1.0f, region, bias, qcodes, qscales, M, N, m0 + wm * WTM,
-                                                   n0 + wn * WTN, lane, rceil);
+                                                   n0 + wn * WTN, lane, rceil, qld, sld);
     if (out) {
       wait_lgkmcnt0();
       __builtin_amdgcn_wave_barrier();
@@ -827,11 +827,12 @@ inline bool mx_prefer_wide_tile(int64_t M, int64_t N, int64_t cus) {
 template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS, int REQ = 0, int ACT = ACT_NONE>
 hipError_t launch_mxp(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as, const uint8_t* w,
                       const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream,
-                      uint8_t* qcodes = nullptr, uint8_t* qscales = nullptr, int rceil = 0) {
+                      uint8_t* qcodes = nullptr, uint8_t* qscales = nullptr, int rceil = 0, int64_t qld = 0,
+                      int64_t sld = 0) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   hipLaunchKernelGGL((mxp_gemm_kernel<ELEM, BM, BN, WM, WN, SLAB, NS, REQ, ACT>), dim3((unsigned)tiles),
                      dim3(64 * WM * WN), 0, stream, a, as, w, ws, bias, out, (int)M, (int)N, (int)K, qcodes, qscales,
-                     rceil);
+                     rceil, qld, sld);
   return hipGetLastError();
 }
 
@@ -1153,29 +1154,41 @@ bool mx_requant_supported(int elem, int64_t N, int64_t K, const uint8_t* a_scale
 template <int ELEM, int OELEM>
 hipError_t launch_requant_act(int act, int rceil, int64_t M, int64_t N, int64_t K, const uint8_t* a,
                               const uint8_t* as, const uint8_t* w, const uint8_t* ws, const uint16_t* bias,
-                              uint16_t* out, uint8_t* qcodes, uint8_t* qscales, hipStream_t stream) {
+                              uint16_t* out, uint8_t* qcodes, uint8_t* qscales, int64_t qld, int64_t sld,
+                              hipStream_t stream) {
+  // tile width as for the bf16-output GEMM (256 or 320 columns)
+  const bool wide = mx_prefer_wide_tile(M, N, device_cu_count());
   if (act == ACT_GELU_TANH)
-    return launch_mxp<ELEM, 256, 256, 4, 2, 128, 2, OELEM, ACT_GELU_TANH>(M, N, K, a, as, w, ws, bias, out, stream,
-                                                                          qcodes, qscales, rceil);
-  return launch_mxp<ELEM, 256, 256, 4, 2, 128, 2, OELEM, ACT_NONE>(M, N, K, a, as, w, ws, bias, out, stream, qcodes,
-                                                                   qscales, rceil);
+    return wide ? launch_mxp<ELEM, 256, 320, 4, 2, 128, 2, OELEM, ACT_GELU_TANH>(M, N, K, a, as, w, ws, bias, out,
+                                                                                 stream, qcodes, qscales, rceil, qld,
+                                                                                 sld)
+                : launch_mxp<ELEM, 256, 256, 4, 2, 128, 2, OELEM, ACT_GELU_TANH>(M, N, K, a, as, w, ws, bias, out,
+                                                                                 stream, qcodes, qscales, rceil, qld,
+                                                                                 sld);
+  return wide ? launch_mxp<ELEM, 256, 320, 4, 2, 128, 2, OELEM, ACT_NONE>(M, N, K, a, as, w, ws, bias, out, stream,
+                                                                          qcodes, qscales, rceil, qld, sld)
+              : launch_mxp<ELEM, 256, 256, 4, 2, 128, 2, OELEM, ACT_NONE>(M, N, K, a, as, w, ws, bias, out, stream,
+                                                                          qcodes, qscales, rceil, qld, sld);
 }
 
 hipError_t launch_mx_gemm_requant(int elem, int out_elem, int out_rceil, int act, int64_t M, int64_t N, int64_t K,
                                   const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
                                   const uint8_t* w_scales, const uint16_t* bias, uint16_t* out_bf16,
-                                  uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream) {
+                                  uint8_t* out_codes, uint8_t* out_scales, int64_t codes_ld, int64_t scales_ld,
+                                  hipStream_t stream) {
+  const int64_t qld = codes_ld ? codes_ld : (out_elem == 1 ? N : N / 2);
+  const int64_t sld = scales_ld ? scales_ld : N / 32;
   if (elem == 1 && out_elem == 1)
     return launch_requant_act<1, 1>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16,
-                                    out_codes, out_scales, stream);
+                                    out_codes, out_scales, qld, sld, stream);
   if (elem == 1)
     return launch_requant_act<1, 2>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16,
-                                    out_codes, out_scales, stream);
+                                    out_codes, out_scales, qld, sld, stream);
   if (out_elem == 1)
     return launch_requant_act<2, 1>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16,
-                                    out_codes, out_scales, stream);
+                                    out_codes, out_scales, qld, sld, stream);
   return launch_requant_act<2, 2>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16,
-                                  out_codes, out_scales, stream);
+                                  out_codes, out_scales, qld, sld, stream);
 }
 
 hipError_t launch_nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,

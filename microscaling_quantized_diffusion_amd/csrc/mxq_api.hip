@@ -180,18 +180,33 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt_arg, int64_t M, int64_t N, int64_
   return launch_status(e);
 }
 
+namespace {
+// Row strides of a quantized output (bytes; 0 = dense): the codes' a multiple
+// of 16 (16-byte row stores) and at least a dense row, the scales' at least
+// a dense row.
+mxq_status check_out_strides(int elem, int64_t cols, int64_t codes_ld, int64_t scales_ld) {
+  const int64_t dense = elem == 1 ? cols : cols / 2;
+  if (codes_ld < 0 || scales_ld < 0 || (codes_ld && codes_ld < dense) || (scales_ld && scales_ld < cols / 32))
+    return MXQ_ERR_SHAPE;
+  if (codes_ld % 16 != 0) return MXQ_ERR_ALIGN;
+  return MXQ_OK;
+}
+}  // namespace
+
 mxq_status mxq_gemm_requant(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K, const void* a_codes,
                             const void* a_scales, const void* w_codes, const void* w_scales, const void* bias_bf16,
                             int act, mxq_format out_fmt_arg, void* out_bf16, void* out_codes, void* out_scales,
-                            void* stream) {
+                            int64_t out_codes_ld, int64_t out_scales_ld, void* stream) {
   mxq_format fmt, out_fmt;
   int in_rceil, rceil;  // the input operands are already quantized: only out_fmt's rule applies
   if (!split_format(fmt_arg, &fmt, &in_rceil) || !split_format(out_fmt_arg, &out_fmt, &rceil))
     return MXQ_ERR_FORMAT;
   if (!valid_k(fmt, K) || !valid_gemm(M, N, K) || N % 32 != 0) return MXQ_ERR_SHAPE;
+  const mxq_status st = check_out_strides(elem_of(out_fmt), N, out_codes_ld, out_scales_ld);
+  if (st == MXQ_ERR_SHAPE) return st;
   if (M == 0 || N == 0) return MXQ_OK;  // empty output: nothing to launch, whatever the pointers
   if (!a_codes || !a_scales || !w_codes || !w_scales || !out_codes || !out_scales) return MXQ_ERR_NULL;
-  if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned16(out_codes)) return MXQ_ERR_ALIGN;
+  if (st != MXQ_OK || !aligned16(a_codes) || !aligned16(w_codes) || !aligned16(out_codes)) return MXQ_ERR_ALIGN;
   if (out_bf16 && !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
   if (fmt == MXQ_FMT_NVFP4 || out_fmt == MXQ_FMT_NVFP4 || (act != 0 && act != 1)) return MXQ_ERR_UNSUPPORTED;
   if (!mx_requant_supported(elem_of(fmt), N, K, (const uint8_t*)a_scales, (const uint8_t*)w_scales))
@@ -201,7 +216,7 @@ mxq_status mxq_gemm_requant(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K,
                                               (const uint8_t*)a_scales, (const uint8_t*)w_codes,
                                               (const uint8_t*)w_scales, (const uint16_t*)bias_bf16,
                                               (uint16_t*)out_bf16, (uint8_t*)out_codes, (uint8_t*)out_scales,
-                                              (hipStream_t)stream));
+                                              out_codes_ld, out_scales_ld, (hipStream_t)stream));
 }
 
 namespace {
@@ -236,6 +251,34 @@ mxq_status mxq_attention_fp8(int64_t B, int64_t H, int64_t S, int64_t D, const v
   return launch_status(launch_attention_fp8(B * H, S, (const uint16_t*)q_bf16, (const uint16_t*)k_bf16,
                                             (const uint16_t*)v_bf16, (uint16_t*)out_bf16, (uint8_t*)workspace,
                                             (hipStream_t)stream));
+}
+
+mxq_status mxq_attention_fp8_requant(int64_t B, int64_t H, int64_t S, int64_t D, const void* q_bf16,
+                                     const void* k_bf16, const void* v_bf16, mxq_format out_fmt_arg,
+                                     void* out_codes, void* out_scales, int64_t out_codes_ld,
+                                     int64_t out_scales_ld, void* workspace, size_t workspace_bytes, void* stream) {
+  mxq_format out_fmt;
+  int rceil;
+  if (!split_format(out_fmt_arg, &out_fmt, &rceil)) return MXQ_ERR_FORMAT;
+  const mxq_status sh = attention_shape(B, H, S, D);
+  if (sh == MXQ_ERR_SHAPE) return sh;
+  const mxq_status st = check_out_strides(elem_of(out_fmt), H * D, out_codes_ld, out_scales_ld);
+  if (st == MXQ_ERR_SHAPE) return st;
+  if (B * H == 0 || S == 0) return MXQ_OK;  // empty: nothing to launch, whatever the pointers
+  if (sh != MXQ_OK || out_fmt == MXQ_FMT_NVFP4) return MXQ_ERR_UNSUPPORTED;
+  if (!q_bf16 || !k_bf16 || !v_bf16 || !out_codes || !out_scales) return MXQ_ERR_NULL;
+  if (st != MXQ_OK || !aligned16(q_bf16) || !aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(out_codes))
+    return MXQ_ERR_ALIGN;
+  const size_t need = attention_layout(B * H, S).total;
+  if (!workspace || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MXQ_ERR_ALIGN;
+  const int elem = elem_of(out_fmt);
+  const int64_t qld = out_codes_ld ? out_codes_ld : (elem == 1 ? H * D : H * D / 2);
+  const int64_t sld = out_scales_ld ? out_scales_ld : H * D / 32;
+  return launch_status(launch_attention_fp8(B * H, S, (const uint16_t*)q_bf16, (const uint16_t*)k_bf16,
+                                            (const uint16_t*)v_bf16, nullptr, (uint8_t*)workspace,
+                                            (hipStream_t)stream, elem, rceil, H, (uint8_t*)out_codes,
+                                            (uint8_t*)out_scales, qld, sld));
 }
 
 mxq_status mxq_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* a_bf16, const void* w_bf16,

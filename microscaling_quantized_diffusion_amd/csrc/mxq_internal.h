@@ -33,12 +33,15 @@ hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8
 // 2 = E2M1; E8M0 scales per 32 output columns, shared-exponent rule as in
 // launch_mx_quant), after an optional activation (act: 0 none, 1 GELU tanh
 // form); out_bf16 (nullable) also receives the bf16 values that were
-// quantized.  Only where mx_requant_supported() holds.
+// quantized.  codes_ld / scales_ld: bytes between output rows of the codes
+// and scales (0 = dense, N or N/2 and N/32).  Only where
+// mx_requant_supported() holds.
 bool mx_requant_supported(int elem, int64_t N, int64_t K, const uint8_t* a_scales, const uint8_t* w_scales);
 hipError_t launch_mx_gemm_requant(int elem, int out_elem, int out_rceil, int act, int64_t M, int64_t N, int64_t K,
                                   const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
                                   const uint8_t* w_scales, const uint16_t* bias, uint16_t* out_bf16,
-                                  uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream);
+                                  uint8_t* out_codes, uint8_t* out_scales, int64_t codes_ld, int64_t scales_ld,
+                                  hipStream_t stream);
 
 // NVFP4 GEMM.
 hipError_t launch_nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
@@ -53,9 +56,15 @@ hipError_t launch_nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_c
 struct AttentionLayout {
   size_t q_codes, q_scales, k_codes, k_scales, vt_codes, vt_scales, total;
 };
+// out_elem 0: bf16 output `out` [BH, S, 128].  out_elem 1 / 2: the same
+// values MX-quantized (E4M3 / E2M1, rceil selecting the scale rule) into
+// qcodes / qscales token-major: row b*S + s, columns h*128 + d (H heads per
+// batch), rows qld and sld bytes apart.
 AttentionLayout attention_layout(int64_t BH, int64_t S);
 hipError_t launch_attention_fp8(int64_t BH, int64_t S, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                uint16_t* out, uint8_t* workspace, hipStream_t stream);
+                                uint16_t* out, uint8_t* workspace, hipStream_t stream, int out_elem = 0,
+                                int rceil = 0, int64_t H = 1, uint8_t* qcodes = nullptr, uint8_t* qscales = nullptr,
+                                int64_t qld = 0, int64_t sld = 0);
 
 // bf16 GEMM.
 hipError_t launch_bf16_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* a, const uint16_t* w,

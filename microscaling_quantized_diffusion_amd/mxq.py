@@ -44,7 +44,10 @@ SIGNATURES = {
     "mxq_quantize": (_I, [_I, _VP, _I64, _I64, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "mxq_gemm": (_I, [_I, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "mxq_quant_gemm_fused": (_I, [_I, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
-    "mxq_gemm_requant": (_I, [_I, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _I, _I, _VP, _VP, _VP, _VP]),
+    "mxq_gemm_requant": (_I, [_I, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _I, _I, _VP, _VP, _VP, _I64, _I64,
+                              _VP]),
+    "mxq_attention_fp8_requant": (_I, [_I64, _I64, _I64, _I64, _VP, _VP, _VP, _I, _VP, _VP, _I64, _I64, _VP, _SZ,
+                                       _VP]),
     "mxq_gemm_bf16": (_I, [_I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
     "mxq_attention_fp8": (_I, [_I64, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "mxq_attention_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
@@ -194,12 +197,21 @@ def quant_gemm_fused(a: torch.Tensor, w: QTensor, bias: Optional[torch.Tensor] =
 ACTS = {"none": 0, "gelu_tanh": 1}
 
 
+def _row_strides(q: QTensor):
+    """Row strides (bytes) of a quantized output; the codes and scales may be column slices of wider
+    matrices (views whose rows are contiguous), e.g. one part of a concatenated activation."""
+    for t, n in ((q.codes, "codes"), (q.scales, "scales")):
+        if t.dtype != torch.uint8 or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+            raise ValueError(f"{n} must be a uint8 [rows, cols] tensor with contiguous rows")
+    return q.codes.stride(0), q.scales.stride(0)
+
+
 def gemm_requant(a: QTensor, w: QTensor, out_fmt: str, bias: Optional[torch.Tensor] = None, act: str = "none",
                  out: Optional[QTensor] = None, out_bf16: Optional[torch.Tensor] = None,
                  scale_rule: str = "floor") -> QTensor:
     """mxq_gemm_requant: quantized A [M, K] x quantized W [N, K]^T -> act(.) as the next layer's quantized
     activation, a QTensor [M, N] in `out_fmt` (MXFP8 / MXFP4).  `out_bf16` (optional) also receives the bf16
-    values that were quantized."""
+    values that were quantized.  `out` may hold column slices of wider code / scale matrices."""
     if a.fmt != w.fmt or a.K != w.K:
         raise ValueError("A and W must share format and K")
     if act not in ACTS:
@@ -209,10 +221,11 @@ def gemm_requant(a: QTensor, w: QTensor, out_fmt: str, bias: Optional[torch.Tens
     if out is None:
         out = QTensor(out_fmt, torch.empty((M, code_cols(out_fmt, N)), dtype=torch.uint8, device=dev),
                       torch.empty((M, N // 32), dtype=torch.uint8, device=dev), None, N)
+    qld, sld = _row_strides(out)
     _check("mxq_gemm_requant",
            lib().mxq_gemm_requant(_fmt(a.fmt), M, N, a.K, _ptr(a.codes), _ptr(a.scales), _ptr(w.codes),
                                   _ptr(w.scales), _ptr(bias), ACTS[act], _fmt(out_fmt, scale_rule), _ptr(out_bf16),
-                                  _ptr(out.codes), _ptr(out.scales), _stream(a.codes)))
+                                  _ptr(out.codes), _ptr(out.scales), qld, sld, _stream(a.codes)))
     return out
 
 
@@ -249,6 +262,32 @@ def attention_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Option
     wsz = workspace.numel() * workspace.element_size()
     _check("mxq_attention_fp8", lib().mxq_attention_fp8(B, H, S, D, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                                          _ptr(workspace), wsz, _stream(q)))
+    return out
+
+
+def attention_fp8_requant(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out_fmt: str,
+                          out: Optional[QTensor] = None, workspace: Optional[torch.Tensor] = None,
+                          scale_rule: str = "floor") -> QTensor:
+    """mxq_attention_fp8_requant: the attention output of bf16 q, k, v [B, H, S, D] MX-quantized for the next
+    layer, token-major with the heads side by side: a QTensor [B * S, H * D] in `out_fmt`.  `out` may hold
+    column slices of wider code / scale matrices (e.g. the attention part of a concatenated activation)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, torch.bfloat16, n)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, S, D] shape")
+    B, H, S, D = q.shape
+    if out is None:
+        out = QTensor(out_fmt, torch.empty((B * S, code_cols(out_fmt, H * D)), dtype=torch.uint8, device=q.device),
+                      torch.empty((B * S, H * D // 32), dtype=torch.uint8, device=q.device), None, H * D)
+    qld, sld = _row_strides(out)
+    need = attention_workspace_bytes(B, H, S, D)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    wsz = workspace.numel() * workspace.element_size()
+    _check("mxq_attention_fp8_requant",
+           lib().mxq_attention_fp8_requant(B, H, S, D, _ptr(q), _ptr(k), _ptr(v), _fmt(out_fmt, scale_rule),
+                                           _ptr(out.codes), _ptr(out.scales), qld, sld, _ptr(workspace), wsz,
+                                           _stream(q)))
     return out
 
 

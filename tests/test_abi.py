@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert mxq.abi_version() == 4
+    assert mxq.abi_version() == 5
     for s in range(8):
         assert lib.mxq_status_string(s)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -123,18 +123,19 @@ def test_gemm_size_limits(lib):
 
 def test_requant_argument_errors(lib):
     r = lib.mxq_gemm_requant
-    # fmt, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, act, out_fmt, out_bf16, out_codes, out_scales, stream
-    assert r(9, 4, 64, 128, P, P, P, P, None, 0, 1, None, P, P, None) == 2  # format
-    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 7, None, P, P, None) == 2  # output format
-    assert r(1, 4, 48, 128, P, P, P, P, None, 0, 1, None, P, P, None) == 3  # N not whole 32-column blocks
-    assert r(1, 0, 64, 128, None, None, None, None, None, 0, 1, None, None, None, None) == 0  # empty
-    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 1, None, None, P, None) == 1  # null codes
-    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 1, P + 2, P, P, None) == 4  # misaligned bf16 copy
-    assert r(1, 4, 64, 96, P, P, P, P, None, 0, 1, None, P, P, None) == 6  # K not a multiple of 128 (FP8)
-    assert r(2, 4, 64, 128, P, P, P, P, None, 0, 1, None, P, P, None) == 6  # K not a multiple of 256 (FP4)
-    assert r(3, 4, 64, 128, P, P, P, P, None, 0, 1, None, P, P, None) == 6  # NVFP4 operands
-    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 3, None, P, P, None) == 6  # NVFP4 output
-    assert r(1, 4, 64, 128, P, P, P, P, None, 5, 1, None, P, P, None) == 6  # unknown activation
+    # fmt, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, act, out_fmt, out_bf16, out_codes, out_scales,
+    # out_codes_ld, out_scales_ld, stream
+    assert r(9, 4, 64, 128, P, P, P, P, None, 0, 1, None, P, P, 0, 0, None) == 2  # format
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 7, None, P, P, 0, 0, None) == 2  # output format
+    assert r(1, 4, 48, 128, P, P, P, P, None, 0, 1, None, P, P, 0, 0, None) == 3  # N not whole 32-column blocks
+    assert r(1, 0, 64, 128, None, None, None, None, None, 0, 1, None, None, None, 0, 0, None) == 0  # empty
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 1, None, None, P, 0, 0, None) == 1  # null codes
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 1, P + 2, P, P, 0, 0, None) == 4  # misaligned bf16 copy
+    assert r(1, 4, 64, 96, P, P, P, P, None, 0, 1, None, P, P, 0, 0, None) == 6  # K not a multiple of 128 (FP8)
+    assert r(2, 4, 64, 128, P, P, P, P, None, 0, 1, None, P, P, 0, 0, None) == 6  # K not a multiple of 256 (FP4)
+    assert r(3, 4, 64, 128, P, P, P, P, None, 0, 1, None, P, P, 0, 0, None) == 6  # NVFP4 operands
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 3, None, P, P, 0, 0, None) == 6  # NVFP4 output
+    assert r(1, 4, 64, 128, P, P, P, P, None, 5, 1, None, P, P, 0, 0, None) == 6  # unknown activation
 
 
 RCEIL = 0x100  # MXQ_SCALE_RCEIL
@@ -152,8 +153,8 @@ def test_scale_rule_flag(lib):
     assert g(1 | RCEIL, 4, 4, 32, None, P, None, P, P, None, None, P, None) == 1  # accepted and ignored
     assert f(2 | RCEIL, 64, 64, 64, P, P, P, None, None, P, None, 0, None) == 5  # passes to the workspace check
     assert f(3 | RCEIL, 64, 64, 64, P, P, P, None, None, P, P, 1 << 20, None) == 2
-    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 2 | RCEIL, None, None, P, None) == 1  # output rule accepted
-    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 3 | RCEIL, None, P, P, None) == 2
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 2 | RCEIL, None, None, P, 0, 0, None) == 1  # output rule accepted
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 3 | RCEIL, None, P, P, 0, 0, None) == 2
     assert lib.mxq_workspace_bytes(1 | RCEIL, 64, 64, 1) == lib.mxq_workspace_bytes(1, 64, 64, 1)
     assert lib.mxq_workspace_bytes(3 | RCEIL, 64, 64, 1) == 0
     with pytest.raises(ValueError):
@@ -175,3 +176,22 @@ def test_attention_argument_errors(lib):
     assert a(1, 2, 256, 128, P, P, P, P + 8, P, need, None) == 4
     assert a(1, 2, 256, 128, P, P, P, P, P, need - 1, None) == 5
     assert a(1, 2, 256, 128, P, P, P, P, None, need, None) == 5
+
+
+def test_requant_output_strides(lib):
+    r, ar = lib.mxq_gemm_requant, lib.mxq_attention_fp8_requant
+    # fmt, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, act, out_fmt, out_bf16, out_codes, out_scales,
+    # out_codes_ld, out_scales_ld, stream
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 1, None, P, P, 48, 0, None) == 3  # code rows shorter than N
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 2, None, P, P, 0, 1, None) == 3  # scale rows shorter than N/32
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 1, None, P, P, 72, 0, None) == 4  # code stride not 16-aligned
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 1, None, None, P, 128, 8, None) == 1  # valid strides
+    need = lib.mxq_attention_workspace_bytes(1, 2, 256, 128)
+    # B, H, S, D, q, k, v, out_fmt, out_codes, out_scales, codes_ld, scales_ld, workspace, bytes, stream
+    assert ar(1, 2, 256, 128, P, P, P, 3, P, P, 0, 0, P, need, None) == 6  # NVFP4 output
+    assert ar(1, 2, 256, 128, P, P, P, 9, P, P, 0, 0, P, need, None) == 2
+    assert ar(1, 2, 256, 128, P, P, P, 2, P, P, 64, 0, P, need, None) == 3  # FP4 rows of 128 bytes
+    assert ar(1, 2, 256, 128, P, P, P, 1, P, P, 264, 0, P, need, None) == 4
+    assert ar(1, 2, 256, 128, P, P, P, 1, None, P, 0, 0, P, need, None) == 1
+    assert ar(1, 2, 256, 128, P, P, P, 1, P, P, 0, 0, P, need - 1, None) == 5
+    assert ar(0, 2, 256, 128, None, None, None, 1, None, None, 0, 0, None, 0, None) == 0
