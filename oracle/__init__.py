@@ -16,7 +16,8 @@ What it computes, and where the pages define it:
 * MXFP8 is the OCP-standard 8-bit microscaling format (same page, Glossary
   "MXFP8"); its element and scale encodings (E4M3, E8M0) and the shared-
   exponent rule are taken from the public OCP Microscaling Formats (MX) v1.0
-  specification, which that entry names.
+  specification, which that entry names.  The same specification's 6-bit
+  formats (MXFP6: E2M3, E3M2) are offered beside MXFP8 and MXFP4.
 * NVFP4 (same page, Glossary "NVFP4"; dynamic per-tensor scale in the
   TorchAO configuration shown under "Section details") is read as E2M1
   elements with one E4M3 scale per 16 elements and one fp32 per-tensor scale
@@ -61,6 +62,8 @@ from .formats import (  # noqa: F401
 )
 from .quant import (  # noqa: F401
     MXFP4,
+    MXFP6_E2M3,
+    MXFP6_E3M2,
     MXFP8,
     NVFP4,
     dequant_mx,
@@ -69,7 +72,9 @@ from .quant import (  # noqa: F401
     quantize_mx,
     quantize_nvfp4,
     should_quantize,
+    pack_fp6,
     unpack_fp4,
+    unpack_fp6,
 )
 from .gemm import (  # noqa: F401
     bf16_half_ulp,

@@ -43,6 +43,18 @@ def e2m1_table() -> Tuple[Tuple[int, Fraction], ...]:
     return tuple((c, _minifloat_value(c, 2, 1, 1)) for c in range(8))
 
 
+@lru_cache(maxsize=None)
+def e2m3_table() -> Tuple[Tuple[int, Fraction], ...]:
+    """All non-negative E2M3 codes with their exact values (0x00 .. 0x1F)."""
+    return tuple((c, _minifloat_value(c, 2, 3, 1)) for c in range(32))
+
+
+@lru_cache(maxsize=None)
+def e3m2_table() -> Tuple[Tuple[int, Fraction], ...]:
+    """All non-negative E3M2 codes with their exact values (0x00 .. 0x1F)."""
+    return tuple((c, _minifloat_value(c, 3, 2, 3)) for c in range(32))
+
+
 def bf16_value(bits: int) -> Fraction:
     """Exact value of a finite bf16 bit pattern."""
     s = (bits >> 15) & 1
@@ -76,6 +88,14 @@ def e2m1_encode(v: Fraction, negative: bool) -> int:
     return encode_argmin(e2m1_table(), v, negative, 0x8)
 
 
+def e2m3_encode(v: Fraction, negative: bool) -> int:
+    return encode_argmin(e2m3_table(), v, negative, 0x20)
+
+
+def e3m2_encode(v: Fraction, negative: bool) -> int:
+    return encode_argmin(e3m2_table(), v, negative, 0x20)
+
+
 def _floor_log2(a: Fraction) -> int:
     """floor(log2 a) for a > 0, by exact comparison."""
     e = a.numerator.bit_length() - a.denominator.bit_length()
@@ -101,9 +121,12 @@ def mx_block(bits: Sequence[int], elem: str, rule: str = "floor") -> Tuple[int, 
                brings the block maximum within the element format's range.
     Elements are x / 2**e encoded round-to-nearest-even with saturation.
     """
-    emax = 8 if elem == "e4m3" else 2
-    max_elem = Fraction(448) if elem == "e4m3" else Fraction(6)
-    enc = e4m3_encode if elem == "e4m3" else e2m1_encode
+    emax, max_elem, enc = {
+        "e4m3": (8, Fraction(448), e4m3_encode),
+        "e2m1": (2, Fraction(6), e2m1_encode),
+        "e2m3": (2, Fraction(15, 2), e2m3_encode),
+        "e3m2": (4, Fraction(28), e3m2_encode),
+    }[elem]
     vals = [bf16_value(b) for b in bits]
     negs = [bool((b >> 15) & 1) for b in bits]
     amax = max(abs(v) for v in vals)

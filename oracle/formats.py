@@ -47,6 +47,9 @@ class ElemFormat:
 
 E4M3 = ElemFormat("e4m3", ebits=4, mbits=3, bias=7, max_value=448.0, max_code=0x7E, emax=8)
 E2M1 = ElemFormat("e2m1", ebits=2, mbits=1, bias=1, max_value=6.0, max_code=0x7, emax=2)
+# the two 6-bit element formats of the OCP MX v1.0 specification (MXFP6)
+E2M3 = ElemFormat("e2m3", ebits=2, mbits=3, bias=1, max_value=7.5, max_code=0x1F, emax=2)
+E3M2 = ElemFormat("e3m2", ebits=3, mbits=2, bias=3, max_value=28.0, max_code=0x1F, emax=4)
 
 
 def _decode_minifloat(fmt: ElemFormat, codes: np.ndarray) -> np.ndarray:
@@ -73,6 +76,16 @@ def decode_e2m1(codes: np.ndarray) -> np.ndarray:
     """Decode 4-bit E2M1 codes (low nibble of each value)."""
     c = np.asarray(codes).astype(np.int64) & 0xF
     return _decode_minifloat(E2M1, c)
+
+
+def decode_e2m3(codes: np.ndarray) -> np.ndarray:
+    """Decode 6-bit E2M3 codes (no NaN or Inf)."""
+    return _decode_minifloat(E2M3, np.asarray(codes).astype(np.int64) & 0x3F)
+
+
+def decode_e3m2(codes: np.ndarray) -> np.ndarray:
+    """Decode 6-bit E3M2 codes (no NaN or Inf)."""
+    return _decode_minifloat(E3M2, np.asarray(codes).astype(np.int64) & 0x3F)
 
 
 def decode_e8m0(codes: np.ndarray) -> np.ndarray:

@@ -4,7 +4,9 @@ Inputs are bf16 bit patterns (uint16 arrays, row-major [rows, K], blocks run
 along K).  Outputs use the layouts of the library:
 
 * MX codes: uint8 [rows, K] (E4M3) or uint8 [rows, K/2] (E2M1, element 2j in
-  the low nibble of byte j, element 2j+1 in the high nibble);
+  the low nibble of byte j, element 2j+1 in the high nibble) or uint8
+  [rows, 3K/4] (E2M3 / E3M2: each 32-element block is 24 bytes, element j at
+  bits 6j .. 6j+5 of the block's little-endian 192-bit integer);
 * MX scales: uint8 [rows, K/32] E8M0, row-major;
 * NVFP4: uint8 [rows, K/2] packed E2M1, uint8 [rows, K/16] E4M3 block scales
   and one float32 per-tensor scale.
@@ -23,7 +25,8 @@ from fractions import Fraction
 
 import numpy as np
 
-from .formats import E2M1, E4M3, ElemFormat, decode_bf16, decode_e2m1, decode_e4m3, decode_e8m0, encode, floor_log2
+from .formats import (E2M1, E2M3, E3M2, E4M3, ElemFormat, decode_bf16, decode_e2m1, decode_e2m3, decode_e3m2,
+                      decode_e4m3, decode_e8m0, encode, floor_log2)
 
 
 @dataclass(frozen=True)
@@ -32,11 +35,15 @@ class Scheme:
     elem: ElemFormat
     block: int
     packed: bool  # two 4-bit codes per byte
+    fp6: bool = False  # four 6-bit codes per three bytes
 
 
 MXFP8 = Scheme("mxfp8", E4M3, 32, False)
 MXFP4 = Scheme("mxfp4", E2M1, 32, True)
 NVFP4 = Scheme("nvfp4", E2M1, 16, True)
+# MXFP6 (OCP MX v1.0), the 6-bit formats of the same family as MXFP8 and MXFP4
+MXFP6_E2M3 = Scheme("mxfp6_e2m3", E2M3, 32, False, True)
+MXFP6_E3M2 = Scheme("mxfp6_e3m2", E3M2, 32, False, True)
 
 
 def should_quantize(M: int, K: int, N: int) -> bool:
@@ -62,6 +69,39 @@ def unpack_fp4(packed: np.ndarray) -> np.ndarray:
     out[..., 0::2] = p & 0xF
     out[..., 1::2] = p >> 4
     return out
+
+
+def pack_fp6(codes: np.ndarray) -> np.ndarray:
+    """[rows, K] 6-bit codes -> [rows, 3K/4] bytes: each 32-element block becomes the 24 little-endian
+    bytes of sum_j code_j * 2**(6 j)."""
+    c = np.asarray(codes).astype(np.uint64) & np.uint64(0x3F)
+    rows, K = c.shape
+    c = c.reshape(rows, K // 32, 32)
+    words = np.zeros((rows, K // 32, 3), dtype=np.uint64)
+    for j in range(32):
+        bit = 6 * j
+        w, off = bit // 64, bit % 64
+        words[..., w] |= (c[..., j] << np.uint64(off)) & np.uint64(0xFFFFFFFFFFFFFFFF)
+        if off > 58:  # the code straddles two 64-bit words
+            words[..., w + 1] |= c[..., j] >> np.uint64(64 - off)
+    return words.astype("<u8").view(np.uint8).reshape(rows, K // 32 * 24)
+
+
+def unpack_fp6(packed: np.ndarray) -> np.ndarray:
+    """[rows, 3K/4] bytes -> [rows, K] 6-bit codes."""
+    p = np.ascontiguousarray(np.asarray(packed, dtype=np.uint8))
+    rows = p.shape[0]
+    nb = p.shape[1] // 24
+    words = p.reshape(rows, nb, 24).view("<u8").astype(np.uint64)  # [rows, nb, 3]
+    out = np.empty((rows, nb, 32), dtype=np.uint8)
+    for j in range(32):
+        bit = 6 * j
+        w, off = bit // 64, bit % 64
+        v = words[..., w] >> np.uint64(off)
+        if off > 58:
+            v |= words[..., w + 1] << np.uint64(64 - off)
+        out[..., j] = (v & np.uint64(0x3F)).astype(np.uint8)
+    return out.reshape(rows, nb * 32)
 
 
 def _check_bits(bits: np.ndarray, block: int) -> np.ndarray:
@@ -123,6 +163,8 @@ def quantize_mx(bits: np.ndarray, scheme: Scheme, rule: str = "floor"):
     scales = np.where(finite, e + 127, 0xFF).astype(np.uint8)
     if scheme.packed:
         return pack_fp4(codes), scales
+    if scheme.fp6:
+        return pack_fp6(codes), scales
     return codes.astype(np.uint8), scales
 
 
@@ -191,8 +233,8 @@ def quantize_nvfp4(bits: np.ndarray, ts=None):
 
 def dequant_mx(codes: np.ndarray, scales: np.ndarray, scheme: Scheme) -> np.ndarray:
     """value = dec_elem(code) * 2**(scale - 127), float64 [rows, K] (exact)."""
-    c = unpack_fp4(codes) if scheme.packed else np.asarray(codes)
-    dec = decode_e2m1 if scheme.elem is E2M1 else decode_e4m3
+    c = unpack_fp4(codes) if scheme.packed else unpack_fp6(codes) if scheme.fp6 else np.asarray(codes)
+    dec = {"e2m1": decode_e2m1, "e4m3": decode_e4m3, "e2m3": decode_e2m3, "e3m2": decode_e3m2}[scheme.elem.name]
     v = dec(c)
     rows, K = v.shape
     s = decode_e8m0(scales).reshape(rows, K // 32, 1)

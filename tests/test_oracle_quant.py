@@ -14,6 +14,8 @@ import pytest
 
 from oracle import (
     MXFP4,
+    MXFP6_E2M3,
+    MXFP6_E3M2,
     MXFP8,
     decode_bf16,
     decode_e2m1,
@@ -24,10 +26,21 @@ from oracle import (
     quantize_mx,
     quantize_nvfp4,
     should_quantize,
+    pack_fp6,
     unpack_fp4,
+    unpack_fp6,
 )
+from oracle.formats import decode_e2m3, decode_e3m2
 from oracle import exact
 from microscaling_quantized_diffusion_amd.inputs import bf16_bits_from_f32
+
+
+MX_SCHEMES = [MXFP8, MXFP4, MXFP6_E2M3, MXFP6_E3M2]
+MX_IDS = ["mxfp8", "mxfp4", "mxfp6_e2m3", "mxfp6_e3m2"]
+
+
+def _unpack(codes, scheme):
+    return unpack_fp4(codes) if scheme.packed else unpack_fp6(codes) if scheme.fp6 else codes
 
 
 def _parse_blocks(path, block_len):
@@ -107,12 +120,12 @@ def _random_blocks(rng, n_blocks, block):
 
 
 @pytest.mark.parametrize("rule", ["floor", "rceil"])
-@pytest.mark.parametrize("scheme", [MXFP8, MXFP4], ids=["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("scheme", MX_SCHEMES, ids=MX_IDS)
 def test_mx_matches_exact_reference(scheme, rule):
     rng = np.random.default_rng(7)
     blocks = _random_blocks(rng, 120, 32)
     codes, scales = quantize_mx(blocks.reshape(4, -1), scheme, rule)
-    codes = unpack_fp4(codes) if scheme.packed else codes
+    codes = _unpack(codes, scheme)
     codes = codes.reshape(120, 32)
     scales = scales.reshape(120)
     for i in range(120):
@@ -135,7 +148,7 @@ def test_mx_rceil_worked_blocks(golden_dir):
         assert sc == b["scale"] and ec == b["codes"]
 
 
-@pytest.mark.parametrize("scheme", [MXFP8, MXFP4], ids=["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("scheme", MX_SCHEMES, ids=MX_IDS)
 def test_mx_rceil_exponent_brute_force(scheme):
     """Every positive finite bf16 value as a block maximum: the scale byte is 127 plus the first e in
     -127..127 (searched one by one) with amax <= max_elem * 2**e."""
@@ -154,7 +167,7 @@ def test_mx_rceil_exponent_brute_force(scheme):
     assert np.array_equal(scales[:, 0].astype(np.int64) - 127, want)
 
 
-@pytest.mark.parametrize("scheme", [MXFP8, MXFP4], ids=["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("scheme", MX_SCHEMES, ids=MX_IDS)
 def test_mx_rceil_no_saturation_and_tight(scheme):
     """Under the round-up rule the block maximum never exceeds the element format's range, the
     next smaller exponent would overflow it, and the exponent is the floor rule's or one above."""
@@ -173,7 +186,7 @@ def test_mx_rceil_no_saturation_and_tight(scheme):
     assert np.all(q[unclamped] > scheme.elem.max_value / 2)
     # the block maximum's code is never the saturated result of a larger value
     deq = np.abs(dequant_mx(codes, s_ceil, scheme)).reshape(64, 32, 32).max(-1)
-    assert np.all(np.abs(deq - amax)[unclamped] <= amax[unclamped] * (2.0 ** -3 if scheme is MXFP8 else 0.25))
+    assert np.all(np.abs(deq - amax)[unclamped] <= amax[unclamped] * 2.0 ** -(scheme.elem.mbits + 1) * 2)
 
 
 def test_mx_unknown_rule():
@@ -181,13 +194,13 @@ def test_mx_unknown_rule():
         quantize_mx(np.zeros((1, 32), np.uint16), MXFP8, "ceil")
 
 
-@pytest.mark.parametrize("scheme", [MXFP8, MXFP4], ids=["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("scheme", MX_SCHEMES, ids=MX_IDS)
 def test_mx_scale_bracketing_and_block_max(scheme):
     rng = np.random.default_rng(11)
     x = rng.standard_normal((64, 1024)) * np.exp(rng.normal(0, 3, size=(64, 1))) * 2.0 ** rng.integers(-60, 60, (64, 32)).repeat(32, 1)
     bits = bf16_bits_from_f32(x.astype(np.float32))
     codes, scales = quantize_mx(bits, scheme)
-    codes = unpack_fp4(codes) if scheme.packed else codes
+    codes = _unpack(codes, scheme)
     v = np.abs(decode_bf16(bits)).reshape(64, 32, 32)
     amax = v.max(-1)
     e = scales.astype(np.int64) - 127
@@ -196,13 +209,13 @@ def test_mx_scale_bracketing_and_block_max(scheme):
     lo = np.ldexp(1.0, e + emax)
     assert np.all(lo[unclamped] <= amax[unclamped])
     assert np.all(amax[unclamped] < 2 * lo[unclamped])
-    mag = codes.reshape(64, 32, 32).astype(np.int64) & (0x7F if not scheme.packed else 0x7)
-    dec = decode_e4m3 if not scheme.packed else decode_e2m1
+    sign = 1 << (scheme.elem.ebits + scheme.elem.mbits)
+    mag = codes.reshape(64, 32, 32).astype(np.int64) & (sign - 1)
+    dec = {"e4m3": decode_e4m3, "e2m1": decode_e2m1, "e2m3": decode_e2m3, "e3m2": decode_e3m2}[scheme.elem.name]
     maxval = dec(mag).max(-1)
-    if scheme is MXFP8:
-        assert np.all((maxval[unclamped] >= 256) & (maxval[unclamped] <= 448))
-    else:
-        assert np.all(np.isin(maxval[unclamped], [4.0, 6.0]))
+    # the block maximum lies in the top binade [2^emax, 2^(emax+1)), saturating at max_value
+    lo_b, hi_b = 2.0 ** scheme.elem.emax, scheme.elem.max_value
+    assert np.all((maxval[unclamped] >= lo_b) & (maxval[unclamped] <= hi_b))
 
 
 @pytest.mark.parametrize("scheme", [MXFP8, MXFP4], ids=["mxfp8", "mxfp4"])
@@ -348,3 +361,58 @@ def test_should_quantize_rule():
     assert not should_quantize(1023, 4096, 4096)
     assert not should_quantize(1, 3072, 18432)
     assert should_quantize(4608, 3072, 12288)
+
+
+def test_fp6_packing_worked_bytes():
+    """Codes 1, 2, 3, 4 at bits 0, 6, 12, 18: 1 + 2*64 + 3*4096 + 4*262144 = 0x103081 -> bytes 81 30 10;
+    a code straddling the first 64-bit word (element 10, bits 60..65) lands in bytes 7 and 8."""
+    c = np.zeros((1, 32), dtype=np.uint8)
+    c[0, :4] = [1, 2, 3, 4]
+    assert pack_fp6(c)[0, :4].tolist() == [0x81, 0x30, 0x10, 0x00]
+    c = np.zeros((1, 32), dtype=np.uint8)
+    c[0, 10] = 0x3F  # bits 60..65
+    b = pack_fp6(c)[0]
+    assert b[7] == 0xF0 and b[8] == 0x03 and int(b.sum()) == 0xF0 + 0x03
+
+
+def test_fp6_pack_round_trip():
+    rng = np.random.default_rng(13)
+    c = rng.integers(0, 64, size=(7, 160)).astype(np.uint8)
+    assert np.array_equal(unpack_fp6(pack_fp6(c)), c)
+
+
+def test_mx_fp6_worked_blocks(golden_dir):
+    blocks, _ = _parse_blocks(os.path.join(golden_dir, "mx_fp6_blocks.txt"), 32)
+    assert len(blocks) == 2
+    for b in blocks:
+        scheme = {"mxfp6_e2m3": MXFP6_E2M3, "mxfp6_e3m2": MXFP6_E3M2}[b["scheme"]]
+        codes, scales = quantize_mx(np.array([b["bits"]], dtype=np.uint16), scheme)
+        assert int(scales[0, 0]) == b["scale"], b
+        assert list(unpack_fp6(codes)[0].astype(int)) == b["codes"], b
+        sc, ec = exact.mx_block(b["bits"], scheme.elem.name)
+        assert sc == b["scale"] and ec == b["codes"]
+
+
+@pytest.mark.parametrize("scheme", [MXFP6_E2M3, MXFP6_E3M2], ids=["e2m3", "e3m2"])
+def test_fp6_exhaustive_element_codes(scheme):
+    """Every finite bf16 value times a unit-scale block (a block maximum fixing e = 0): each element's code
+    equals the exact reference's argmin over the code table."""
+    top = bf16_bits_from_f32(np.array([2.0 ** scheme.elem.emax], np.float32))[0]
+    vals = np.arange(0, 0x7F80, 7, dtype=np.uint16)  # every 7th positive finite pattern, both signs
+    vals = vals[np.abs(decode_bf16(vals)) < 2.0 ** scheme.elem.emax]
+    vals = np.concatenate([vals, vals | 0x8000])
+    n = (len(vals) + 30) // 31
+    bits = np.zeros((n, 32), dtype=np.uint16)
+    bits[:, 0] = top
+    flat = np.zeros(n * 31, dtype=np.uint16)
+    flat[: len(vals)] = vals
+    bits[:, 1:] = flat.reshape(n, 31)
+    codes, scales = quantize_mx(bits, scheme)
+    assert (scales == 127).all()
+    codes = unpack_fp6(codes)
+    enc = exact.e2m3_encode if scheme.elem.name == "e2m3" else exact.e3m2_encode
+    for r in range(0, n, 9):
+        for j in range(1, 32):
+            b = int(bits[r, j])
+            want = enc(abs(exact.bf16_value(b)), bool(b >> 15))
+            assert int(codes[r, j]) == want, (hex(b), int(codes[r, j]), want)
