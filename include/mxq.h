@@ -25,7 +25,14 @@
  *                                        byte j; scales uint8 [rows, K/32] E8M0;
  *      NVFP4 codes  uint8 [rows, K/2]   E2M1 (same packing), scales uint8
  *                                        [rows, K/16] E4M3, plus one float32
- *                                        per-tensor scale in device memory.
+ *                                        per-tensor scale in device memory;
+ *      MXFP6 codes  uint8 [rows, 3K/4]  E2M3 or E3M2: each 32-element block is
+ *                                        24 bytes, element j at bits 6j..6j+5
+ *                                        of the block's little-endian 192-bit
+ *                                        integer; scales uint8 [rows, K/32]
+ *                                        E8M0.  The MXFP6 GEMM needs K % 64 == 0
+ *                                        (MXQ_ERR_UNSUPPORTED otherwise) and is
+ *                                        not a requantization target.
  *  - Every pointer is caller-owned DEVICE memory (the library never
  *    allocates or frees).  Base pointers of A, W, codes, out and workspace
  *    must be 16-byte aligned; scale and bias pointers need no alignment.
@@ -53,12 +60,14 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 5
+#define MXQ_ABI_VERSION 6
 
 typedef enum {
   MXQ_FMT_MXFP8 = 1, /* E4M3 codes, E8M0 scale per 32 K-elements */
   MXQ_FMT_MXFP4 = 2, /* E2M1 codes, E8M0 scale per 32 K-elements */
-  MXQ_FMT_NVFP4 = 3  /* E2M1 codes, E4M3 scale per 16 K-elements, fp32 per-tensor scale */
+  MXQ_FMT_NVFP4 = 3, /* E2M1 codes, E4M3 scale per 16 K-elements, fp32 per-tensor scale */
+  MXQ_FMT_MXFP6_E2M3 = 4, /* E2M3 codes, E8M0 scale per 32 K-elements */
+  MXQ_FMT_MXFP6_E3M2 = 5  /* E3M2 codes, E8M0 scale per 32 K-elements */
 } mxq_format;
 
 /*

@@ -20,10 +20,11 @@ typedef short mx_short2 __attribute__((ext_vector_type(2)));
 typedef unsigned short mx_ushort2 __attribute__((ext_vector_type(2)));
 
 // emax: exponent of the element format's largest power of two
-// (E4M3: 448 = 1.75 * 2^8; E2M1: 6 = 1.5 * 2^2).  elem: 1 = E4M3, 2 = E2M1.
+// (E4M3: 448 = 1.75 * 2^8; E2M1: 6 = 1.5 * 2^2; E2M3: 7.5 = 1.875 * 2^2;
+// E3M2: 28 = 1.75 * 2^4).  elem: 1 = E4M3, 2 = E2M1, 3 = E2M3, 4 = E3M2.
 template <int ELEM>
 constexpr int mx_emax() {
-  return ELEM == 1 ? 8 : 2;
+  return ELEM == 1 ? 8 : ELEM == 4 ? 4 : 2;
 }
 
 // Largest bf16 magnitude bit pattern of the 4 values in two dwords.  For
@@ -34,10 +35,11 @@ __device__ __forceinline__ uint32_t mx_absmax_bits4(uint32_t w0, uint32_t w1) {
 }
 
 // bf16 fraction bits of the element format's largest value's significand
-// (448 = 1.75 * 2^8 -> 0x60; 6 = 1.5 * 2^2 -> 0x40).
+// (448 = 1.75 * 2^8 -> 0x60; 6 = 1.5 * 2^2 -> 0x40; 7.5 = 1.875 * 2^2 ->
+// 0x70; 28 = 1.75 * 2^4 -> 0x60).
 template <int ELEM>
 constexpr uint32_t mx_max_fraction() {
-  return ELEM == 1 ? 0x60u : 0x40u;
+  return ELEM == 1 ? 0x60u : ELEM == 2 ? 0x40u : ELEM == 3 ? 0x70u : 0x60u;
 }
 
 // Shared exponent of a finite block from its largest magnitude bit pattern m

@@ -14,8 +14,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int block_of(mxq_format fmt) { return fmt == MXQ_FMT_NVFP4 ? 16 : 32; }
 
 bool valid_format(mxq_format fmt) {
-  return fmt == MXQ_FMT_MXFP8 || fmt == MXQ_FMT_MXFP4 || fmt == MXQ_FMT_NVFP4;
+  return fmt == MXQ_FMT_MXFP8 || fmt == MXQ_FMT_MXFP4 || fmt == MXQ_FMT_NVFP4 || fmt == MXQ_FMT_MXFP6_E2M3 ||
+         fmt == MXQ_FMT_MXFP6_E3M2;
 }
+bool is_fp6(mxq_format fmt) { return fmt == MXQ_FMT_MXFP6_E2M3 || fmt == MXQ_FMT_MXFP6_E3M2; }
 
 // A format argument is a base format, optionally OR-ed with MXQ_SCALE_RCEIL
 // (MX formats only).  Splits it; false for anything else.
@@ -41,7 +43,7 @@ bool valid_gemm(int64_t M, int64_t N, int64_t K) {
 }
 
 size_t code_bytes(mxq_format fmt, int64_t rows, int64_t K) {
-  return (size_t)rows * (size_t)(fmt == MXQ_FMT_MXFP8 ? K : K / 2);
+  return (size_t)rows * (size_t)(fmt == MXQ_FMT_MXFP8 ? K : is_fp6(fmt) ? K / 32 * 24 : K / 2);
 }
 size_t scale_bytes(mxq_format fmt, int64_t rows, int64_t K) { return (size_t)rows * (size_t)(K / block_of(fmt)); }
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -63,7 +65,10 @@ FusedLayout fused_layout(mxq_format fmt, int64_t M, int64_t K) {
 
 mxq_status launch_status(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_ERR_LAUNCH; }
 
-int elem_of(mxq_format fmt) { return fmt == MXQ_FMT_MXFP8 ? 1 : 2; }
+// element format of an MX format: 1 = E4M3, 2 = E2M1, 3 = E2M3, 4 = E3M2
+int elem_of(mxq_format fmt) {
+  return fmt == MXQ_FMT_MXFP8 ? 1 : fmt == MXQ_FMT_MXFP6_E2M3 ? 3 : fmt == MXQ_FMT_MXFP6_E3M2 ? 4 : 2;
+}
 
 }  // namespace
 
@@ -118,6 +123,9 @@ mxq_status mxq_quantize(mxq_format fmt_arg, const void* x_bf16, int64_t rows, in
   if (fmt == MXQ_FMT_NVFP4)
     return launch_status(launch_nvfp4_quant((const uint16_t*)x_bf16, rows, cols, (uint8_t*)codes, (uint8_t*)scales,
                                             tensor_scale, (uint32_t*)workspace, s));
+  if (is_fp6(fmt))
+    return launch_status(launch_mx6_quant(elem_of(fmt), rceil, (const uint16_t*)x_bf16, rows, cols, (uint8_t*)codes,
+                                          (uint8_t*)scales, s));
   return launch_status(launch_mx_quant(elem_of(fmt), rceil, (const uint16_t*)x_bf16, rows, cols, (uint8_t*)codes,
                                        (uint8_t*)scales, s));
 }
@@ -134,7 +142,12 @@ mxq_status mxq_gemm(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K, const v
   if (fmt == MXQ_FMT_NVFP4 && (!a_tensor_scale || !w_tensor_scale)) return MXQ_ERR_NULL;
   if (fmt != MXQ_FMT_NVFP4 && (a_tensor_scale || w_tensor_scale)) return MXQ_ERR_UNSUPPORTED;
   if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
+  if (is_fp6(fmt) && K % 64 != 0) return MXQ_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
+  if (is_fp6(fmt))
+    return launch_status(launch_mx6_gemm(elem_of(fmt), M, N, K, (const uint8_t*)a_codes, (const uint8_t*)a_scales,
+                                         (const uint8_t*)w_codes, (const uint8_t*)w_scales,
+                                         (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s));
   if (fmt == MXQ_FMT_NVFP4)
     return launch_status(launch_nvfp4_gemm(M, N, K, (const uint8_t*)a_codes, (const uint8_t*)a_scales, a_tensor_scale,
                                            (const uint8_t*)w_codes, (const uint8_t*)w_scales, w_tensor_scale,
@@ -157,6 +170,7 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt_arg, int64_t M, int64_t N, int64_
   if (fmt == MXQ_FMT_NVFP4 && !w_tensor_scale) return MXQ_ERR_NULL;
   if (fmt != MXQ_FMT_NVFP4 && w_tensor_scale) return MXQ_ERR_UNSUPPORTED;
   if (!aligned16(a_bf16) || !aligned16(w_codes) || !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
+  if (is_fp6(fmt) && K % 64 != 0) return MXQ_ERR_UNSUPPORTED;
   const FusedLayout L = fused_layout(fmt, M, K);
   if (!workspace || workspace_bytes < L.total) return MXQ_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MXQ_ERR_ALIGN;
@@ -172,6 +186,13 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt_arg, int64_t M, int64_t N, int64_
     e = launch_nvfp4_gemm(M, N, K, a_codes, a_scales, a_ts, (const uint8_t*)w_codes, (const uint8_t*)w_scales,
                           w_tensor_scale, (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s);
     return launch_status(e);
+  }
+  if (is_fp6(fmt)) {
+    e = launch_mx6_quant(elem_of(fmt), rceil, (const uint16_t*)a_bf16, M, K, a_codes, a_scales, s);
+    if (e != hipSuccess) return MXQ_ERR_LAUNCH;
+    return launch_status(launch_mx6_gemm(elem_of(fmt), M, N, K, a_codes, a_scales, (const uint8_t*)w_codes,
+                                         (const uint8_t*)w_scales, (const uint16_t*)bias_bf16, (uint16_t*)out_bf16,
+                                         s));
   }
   e = launch_mx_quant(elem_of(fmt), rceil, (const uint16_t*)a_bf16, M, K, a_codes, a_scales, s);
   if (e != hipSuccess) return MXQ_ERR_LAUNCH;
@@ -208,7 +229,8 @@ mxq_status mxq_gemm_requant(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K,
   if (!a_codes || !a_scales || !w_codes || !w_scales || !out_codes || !out_scales) return MXQ_ERR_NULL;
   if (st != MXQ_OK || !aligned16(a_codes) || !aligned16(w_codes) || !aligned16(out_codes)) return MXQ_ERR_ALIGN;
   if (out_bf16 && !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
-  if (fmt == MXQ_FMT_NVFP4 || out_fmt == MXQ_FMT_NVFP4 || (act != 0 && act != 1)) return MXQ_ERR_UNSUPPORTED;
+  if (fmt == MXQ_FMT_NVFP4 || out_fmt == MXQ_FMT_NVFP4 || is_fp6(fmt) || is_fp6(out_fmt) || (act != 0 && act != 1))
+    return MXQ_ERR_UNSUPPORTED;
   if (!mx_requant_supported(elem_of(fmt), N, K, (const uint8_t*)a_scales, (const uint8_t*)w_scales))
     return MXQ_ERR_UNSUPPORTED;
   return launch_status(launch_mx_gemm_requant(elem_of(fmt), elem_of(out_fmt), rceil, act, M, N, K,
@@ -265,7 +287,7 @@ mxq_status mxq_attention_fp8_requant(int64_t B, int64_t H, int64_t S, int64_t D,
   const mxq_status st = check_out_strides(elem_of(out_fmt), H * D, out_codes_ld, out_scales_ld);
   if (st == MXQ_ERR_SHAPE) return st;
   if (B * H == 0 || S == 0) return MXQ_OK;  // empty: nothing to launch, whatever the pointers
-  if (sh != MXQ_OK || out_fmt == MXQ_FMT_NVFP4) return MXQ_ERR_UNSUPPORTED;
+  if (sh != MXQ_OK || out_fmt == MXQ_FMT_NVFP4 || is_fp6(out_fmt)) return MXQ_ERR_UNSUPPORTED;
   if (!q_bf16 || !k_bf16 || !v_bf16 || !out_codes || !out_scales) return MXQ_ERR_NULL;
   if (st != MXQ_OK || !aligned16(q_bf16) || !aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(out_codes))
     return MXQ_ERR_ALIGN;

@@ -18,6 +18,15 @@ namespace mxq {
 hipError_t launch_mx_quant(int elem, int rceil, const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, hipStream_t stream);
 
+// MXFP6 quantizer and GEMM (elem 3 = E2M3, 4 = E3M2; codes: 24 bytes per
+// 32-element block, element j at bits 6j of the block's little-endian 192-bit
+// integer).  The GEMM needs K % 64 == 0.
+hipError_t launch_mx6_quant(int elem, int rceil, const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
+                            uint8_t* scales, hipStream_t stream);
+hipError_t launch_mx6_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                           const uint8_t* w_codes, const uint8_t* w_scales, const uint16_t* bias, uint16_t* out,
+                           hipStream_t stream);
+
 // NVFP4 quantizer (two kernels: global-amax partials, then block quantization).
 // `partials` holds nvfp4_partials_count(rows*cols) uint32 values.
 int64_t nvfp4_partials_count(int64_t n_elems);

@@ -5,7 +5,8 @@ torch is used here only to allocate device memory and to name the current
 HIP stream.  If the library is not built, every call raises: there is no
 fallback implementation.
 
-Names mirror include/mxq.h.  Formats: "mxfp8", "mxfp4", "nvfp4".  Calls
+Names mirror include/mxq.h.  Formats: "mxfp8", "mxfp4", "nvfp4", "mxfp6_e2m3",
+"mxfp6_e3m2".  Calls
 that quantize to an MX format take ``scale_rule``: "floor" (the OCP rule,
 default) or "rceil" (round the shared scale up, MXQ_SCALE_RCEIL).
 """
@@ -22,9 +23,9 @@ import torch
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libmxq.so")
 
-FORMATS = {"mxfp8": 1, "mxfp4": 2, "nvfp4": 3}
+FORMATS = {"mxfp8": 1, "mxfp4": 2, "nvfp4": 3, "mxfp6_e2m3": 4, "mxfp6_e3m2": 5}
 SCALE_RULES = {"floor": 0, "rceil": 0x100}  # MXQ_SCALE_RCEIL, OR-ed into the format argument
-BLOCK = {"mxfp8": 32, "mxfp4": 32, "nvfp4": 16}
+BLOCK = {"mxfp8": 32, "mxfp4": 32, "nvfp4": 16, "mxfp6_e2m3": 32, "mxfp6_e3m2": 32}
 
 MXQ_OK = 0
 STATUS_NAMES = {
@@ -108,7 +109,11 @@ def _require(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
 
 
 def code_cols(fmt: str, K: int) -> int:
-    return K if fmt == "mxfp8" else K // 2
+    if fmt == "mxfp8":
+        return K
+    if fmt.startswith("mxfp6"):
+        return K // 32 * 24
+    return K // 2
 
 
 @dataclass
