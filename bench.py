@@ -34,7 +34,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "block-scaled GEMM TFLOP/s at FLUX DiT shapes (MXFP8/MXFP4); % of MFMA peak"
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
-PEAK_TFLOPS = {"mxfp8": 5000.0, "mxfp4": 10100.0, "nvfp4": 2500.0, "bf16": 2500.0}
+PEAK_TFLOPS = {"mxfp8": 5000.0, "mxfp4": 10100.0, "mxfp6_e2m3": 10100.0, "mxfp6_e3m2": 10100.0, "nvfp4": 2500.0,
+               "bf16": 2500.0}
 PEAK_HBM_GBS = 8000.0
 GEMM_SRC = os.path.join(ROOT, "microscaling_quantized_diffusion_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mxfp8_flux_mlp_up_traffic.txt")
@@ -128,7 +129,7 @@ def run_layer(layer, dev, steps, warmup, rotate, seed=0):
     qa = [mxq.quantize(fmt, a) for a in As]
     ms_gemm = _time_loop(lambda i: mxq.gemm(qa[i % rotate], Ws[i % rotate], None, out), steps, warmup, dist_gemm)
     ms_quant = _time_loop(lambda i: mxq.quantize(fmt, As[i % rotate], qa[i % rotate]), steps, warmup)
-    code_b = M * K * (1.0 if fmt == "mxfp8" else 0.5)
+    code_b = M * K * (1.0 if fmt == "mxfp8" else 0.75 if fmt.startswith("mxfp6") else 0.5)
     scale_b = M * K / (16 if fmt == "nvfp4" else 32)
     quant_bytes = M * K * 2 + code_b + scale_b
     res.update(path=fmt, ms=ms_fused, ms_p10=dist_fused["p10"], ms_p50=dist_fused["p50"], ms_p90=dist_fused["p90"],
@@ -398,7 +399,8 @@ def main():
     }
     if args.all:
         extra = []
-        for name in ("flux_single_mxfp4", "flux_2048_nvfp4", "flux_double_block_b1", "flux_double_block_b4"):
+        for name in ("flux_single_mxfp4", "flux_mlp_up_mxfp6", "flux_2048_nvfp4", "flux_double_block_b1",
+                     "flux_double_block_b4"):
             for i, ly in enumerate(WORKLOADS[name].layers):
                 print(f"# timing {name}/{ly.name}", file=sys.stderr, flush=True)
                 e = run_layer(ly, dev, max(10, args.steps // 2), 3, min(args.rotate, 4), seed=i)

@@ -17,11 +17,12 @@
 //                     exponent bits, rintf of the scaled value), 24 bytes out.
 //   mx6_gemm_kernel   a 128 x 128 output tile per workgroup, four waves of
 //                     64 x 64 (2 x 2 scaled 32x32x64 MFMAs with the FP6
-//                     format code), one 64-element K step (48 code bytes per
-//                     row) staged in LDS per iteration, double-buffered
-//                     through registers; bf16 epilogue with optional bias.
-//                     A plain design, not tuned: the MX GEMM's LDS-DMA ring
-//                     is built around 16-byte chunks of 128-byte slabs.
+//                     format code); 128 K-elements (96 code bytes per row)
+//                     staged in LDS per iteration, the next stage's loads in
+//                     flight in registers meanwhile; bf16 epilogue with
+//                     optional bias.  A plain design: the MX GEMM's LDS-DMA
+//                     ring is built around 16-byte chunks of 128-byte slabs,
+//                     which 24-byte blocks do not fit.
 #include "mx_encode.h"
 #include "mxq_internal.h"
 
@@ -91,61 +92,84 @@ __global__ __launch_bounds__(256) void mx6_quant_kernel(const uint4* __restrict_
   }
 }
 
-constexpr int kT = 128;     // output tile rows and columns
-constexpr int kRowB = 48;   // code bytes per row and 64-element K step (two blocks)
-constexpr int kPitch = 56;  // LDS bytes per staged row (8-byte aligned, spreads the banks)
+constexpr int kT = 128;          // output tile rows and columns
+constexpr int kStageBlocks = 4;  // 32-element blocks per row and stage (128 K-elements, 2 MFMA steps)
+constexpr int kRowB = kStageBlocks * 24;  // 96 code bytes per row and stage
+constexpr int kPitch = 104;      // LDS bytes per staged row: 8-byte aligned, 26 dwords (spreads the banks)
+constexpr int kChunks = kT * kRowB / 16;  // 16-byte chunks per operand and stage (768, 3 per thread)
 
 template <int ELEM>
-__global__ __launch_bounds__(256) void mx6_gemm_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
+__global__ __launch_bounds__(256, 2) void mx6_gemm_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
                                                        const uint8_t* __restrict__ W, const uint8_t* __restrict__ Ws,
                                                        const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
                                                        int M, int N, int K, int tiles_n) {
   constexpr int FMT = ELEM == 3 ? 2 : 3;  // MFMA operand format: 2 = E2M3, 3 = E3M2
-  __shared__ __attribute__((aligned(16))) uint8_t sa[2][kT * kPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t sw[2][kT * kPitch];
+  constexpr int CPT = kChunks / 256;      // chunks per thread and operand
+  __shared__ __attribute__((aligned(16))) uint8_t sa[kT * kPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t sw[kT * kPitch];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 5, r32 = lane & 31;
   const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves of 64 x 64 outputs
-  const int m0 = (int)(blockIdx.x / (unsigned)tiles_n) * kT, n0 = (int)(blockIdx.x % (unsigned)tiles_n) * kT;
-  const size_t KB = (size_t)K / 32 * 24;  // code bytes per row
-  const int SK = K / 32;                  // scale bytes per row
-  const int nsteps = K / 64;
+  // tile order as in the MX GEMM: each XCD takes a contiguous range of ids, and ids walk groups of 8
+  // tile rows column by column, so that concurrent tiles share A and W rows in one L2
+  const int tiles_m = (M + kT - 1) / kT;
+  const uint32_t id = xcd_contiguous_id(blockIdx.x, gridDim.x);
+  constexpr int GROUP = 8;
+  const int group = (int)(id / (uint32_t)(GROUP * tiles_n));
+  const int gsz = min(tiles_m - group * GROUP, GROUP);
+  const int m0 = (group * GROUP + (int)(id % (uint32_t)gsz)) * kT;
+  const int n0 = (int)((id % (uint32_t)(GROUP * tiles_n)) / (uint32_t)gsz) * kT;
+  const int SK = K / 32;                  // blocks (and scale bytes) per row
+  const size_t KB = (size_t)SK * 24;      // code bytes per row
+  const int nstages = (SK + kStageBlocks - 1) / kStageBlocks;
 
-  // 128 rows x 48 bytes per operand and step = 384 chunks of 16 bytes: chunk c = row c / 3, part c % 3
-  uint4 ra[2], rw[2];
-  auto load = [&](int ks) {
+  // scale of block b of a row; rows past M / N and blocks past K hold zero codes (any scale)
+  auto scale = [&](const uint8_t* S, int grow, int rows, int b) {
+    return (grow < rows && b < SK) ? (int)S[(size_t)grow * SK + b] : 127;
+  };
+  // stage s of an operand: rows x 96 bytes; chunk c = row c / 6, byte 16 (c % 6) of the row's
+  // stage; blocks past K (the last stage of a K that is not a multiple of 128) load as zeros
+  uint4 ra[CPT], rw[CPT];
+  // scale bytes of the lane's rows for a stage: [tile][MFMA step], fetched a stage ahead with the codes
+  int nsa[2][kStageBlocks / 2], nsw[2][kStageBlocks / 2];
+  auto load = [&](int st) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < CPT; ++u) {
       const int c = tid + 256 * u;
-      const int row = c / 3, part = c - 3 * (c / 3);
+      const int row = c / 6, off = 16 * (c - 6 * (c / 6));
+      const size_t kb = (size_t)st * kRowB + off;  // byte within the row
       ra[u] = uint4{0u, 0u, 0u, 0u};
       rw[u] = uint4{0u, 0u, 0u, 0u};
-      if (c < 384 && m0 + row < M)
-        ra[u] = *reinterpret_cast<const uint4*>(A + (size_t)(m0 + row) * KB + (size_t)ks * kRowB + 16 * part);
-      if (c < 384 && n0 + row < N)
-        rw[u] = *reinterpret_cast<const uint4*>(W + (size_t)(n0 + row) * KB + (size_t)ks * kRowB + 16 * part);
+      if (kb < KB && m0 + row < M) ra[u] = *reinterpret_cast<const uint4*>(A + (size_t)(m0 + row) * KB + kb);
+      if (kb < KB && n0 + row < N) rw[u] = *reinterpret_cast<const uint4*>(W + (size_t)(n0 + row) * KB + kb);
     }
-  };
-  auto store = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = tid + 256 * u;
-      if (c < 384) {
-        const int row = c / 3, part = c - 3 * (c / 3);
-        uint2* da = reinterpret_cast<uint2*>(&sa[buf][row * kPitch + 16 * part]);
-        uint2* dw = reinterpret_cast<uint2*>(&sw[buf][row * kPitch + 16 * part]);
-        da[0] = make_uint2(ra[u].x, ra[u].y);
-        da[1] = make_uint2(ra[u].z, ra[u].w);
-        dw[0] = make_uint2(rw[u].x, rw[u].y);
-        dw[1] = make_uint2(rw[u].z, rw[u].w);
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int kk = 0; kk < kStageBlocks / 2; ++kk) {
+        const int b = st * kStageBlocks + 2 * kk + q;
+        nsa[t][kk] = scale(As, m0 + wm * 64 + 32 * t + r32, M, b);
+        nsw[t][kk] = scale(Ws, n0 + wn * 64 + 32 * t + r32, N, b);
       }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + 256 * u;
+      const int row = c / 6, off = 16 * (c - 6 * (c / 6));
+      uint2* da = reinterpret_cast<uint2*>(&sa[row * kPitch + off]);
+      uint2* dw = reinterpret_cast<uint2*>(&sw[row * kPitch + off]);
+      da[0] = make_uint2(ra[u].x, ra[u].y);
+      da[1] = make_uint2(ra[u].z, ra[u].w);
+      dw[0] = make_uint2(rw[u].x, rw[u].y);
+      dw[1] = make_uint2(rw[u].z, rw[u].w);
     }
   };
-  // lane (r, q) of an operand tile: block q of the step, 24 bytes as three 8-byte LDS reads
-  auto operand = [&](const uint8_t* s, int row) {
-    const uint2* p = reinterpret_cast<const uint2*>(s + row * kPitch + 24 * q);
+  // lane (r, q) of an operand tile at MFMA step kk of the stage: block 2 kk + q, 24 bytes
+  auto operand = [&](const uint8_t* s, int row, int kk) {
+    const uint2* p = reinterpret_cast<const uint2*>(s + row * kPitch + 24 * (2 * kk + q));
     const uint2 x0 = p[0], x1 = p[1], x2 = p[2];
     return m6_v8i{(int)x0.x, (int)x0.y, (int)x1.x, (int)x1.y, (int)x2.x, (int)x2.y, 0, 0};
   };
@@ -157,30 +181,39 @@ __global__ __launch_bounds__(256) void mx6_gemm_kernel(const uint8_t* __restrict
     for (int j = 0; j < 2; ++j) acc[i][j] = m6_v16f{};
 
   load(0);
-  store(0);
-  __syncthreads();
-  for (int ks = 0; ks < nsteps; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nsteps) load(ks + 1);
-    m6_v8i wop[2], aop[2];
-    int wsc[2], asc[2];
+  for (int st = 0; st < nstages; ++st) {
+    __syncthreads();  // every wave is done reading the previous stage
+    store();
+    int csa[2][kStageBlocks / 2], csw[2][kStageBlocks / 2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int arow = wm * 64 + 32 * t + r32, wrow = wn * 64 + 32 * t + r32;
-      aop[t] = operand(sa[buf], arow);
-      wop[t] = operand(sw[buf], wrow);
-      // scale of block 2 ks + q of the row; rows past M / N hold zero codes (any scale)
-      asc[t] = m0 + arow < M ? As[(size_t)(m0 + arow) * SK + 2 * ks + q] : 127;
-      wsc[t] = n0 + wrow < N ? Ws[(size_t)(n0 + wrow) * SK + 2 * ks + q] : 127;
-    }
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop[i], aop[j], acc[i][j], FMT, FMT, 0,
-                                                                    wsc[i], 0, asc[j]);
-    if (ks + 1 < nsteps) store(buf ^ 1);
+      for (int kk = 0; kk < kStageBlocks / 2; ++kk) {
+        csa[t][kk] = nsa[t][kk];
+        csw[t][kk] = nsw[t][kk];
+      }
     __syncthreads();
+    if (st + 1 < nstages) load(st + 1);  // in flight while this stage computes
+#pragma unroll
+    for (int kk = 0; kk < kStageBlocks / 2; ++kk) {
+      m6_v8i wop[2], aop[2];
+      int wsc[2], asc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        aop[t] = operand(sa, wm * 64 + 32 * t + r32, kk);
+        wop[t] = operand(sw, wn * 64 + 32 * t + r32, kk);
+        asc[t] = csa[t][kk];
+        wsc[t] = csw[t][kk];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop[i], aop[j], acc[i][j], FMT, FMT, 0,
+                                                                      wsc[i], 0, asc[j]);
+      // one step's operands live at a time (keeps the kernel at two waves per SIMD)
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // epilogue: lane (r32, q) of tile (i, j) holds output row m = m0 + wm 64 + 32 j + r32 and columns

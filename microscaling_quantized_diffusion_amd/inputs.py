@@ -70,7 +70,7 @@ class Linear:
     M: int
     K: int
     N: int
-    fmt: str  # "mxfp8" | "mxfp4" | "nvfp4" | "bf16" (selective dispatch decides at run time)
+    fmt: str  # "mxfp8" | "mxfp4" | "mxfp6_e2m3" | "mxfp6_e3m2" | "nvfp4" (bf16 when the selective rule says so)
     act: str
 
 
@@ -107,6 +107,14 @@ WORKLOADS: Dict[str, Workload] = {
         "flux_mlp_up_mxfp8",
         [Linear("mlp_up", 4608, 3072, 12288, "mxfp8", "outlier")],
         "FLUX-dev MLP up-projection at 1024x1024 (4096 image + 512 text tokens), MXFP8",
+    ),
+    "flux_mlp_up_mxfp6": Workload(
+        "flux_mlp_up_mxfp6",
+        [
+            Linear("mlp_up_e2m3", 4608, 3072, 12288, "mxfp6_e2m3", "outlier"),
+            Linear("mlp_up_e3m2", 4608, 3072, 12288, "mxfp6_e3m2", "outlier"),
+        ],
+        "FLUX-dev MLP up-projection at 1024x1024 in the two MXFP6 element formats",
     ),
     "flux_single_mxfp4": Workload(
         "flux_single_mxfp4",
