@@ -5,8 +5,9 @@ along K).  Outputs use the layouts of the library:
 
 * MX codes: uint8 [rows, K] (E4M3) or uint8 [rows, K/2] (E2M1, element 2j in
   the low nibble of byte j, element 2j+1 in the high nibble) or uint8
-  [rows, 3K/4] (E2M3 / E3M2: each 32-element block is 24 bytes, element j at
-  bits 6j .. 6j+5 of the block's little-endian 192-bit integer);
+  [rows, K] (E2M3 / E3M2: each 32-element block occupies a 32-byte slot, the
+  24 little-endian bytes of its 192-bit integer, element j at bits 6j ..
+  6j+5, then 8 zero bytes);
 * MX scales: uint8 [rows, K/32] E8M0, row-major;
 * NVFP4: uint8 [rows, K/2] packed E2M1, uint8 [rows, K/16] E4M3 block scales
   and one float32 per-tensor scale.
@@ -35,7 +36,7 @@ class Scheme:
     elem: ElemFormat
     block: int
     packed: bool  # two 4-bit codes per byte
-    fp6: bool = False  # four 6-bit codes per three bytes
+    fp6: bool = False  # 6-bit codes, one 32-byte slot per 32-element block
 
 
 MXFP8 = Scheme("mxfp8", E4M3, 32, False)
@@ -72,8 +73,8 @@ def unpack_fp4(packed: np.ndarray) -> np.ndarray:
 
 
 def pack_fp6(codes: np.ndarray) -> np.ndarray:
-    """[rows, K] 6-bit codes -> [rows, 3K/4] bytes: each 32-element block becomes the 24 little-endian
-    bytes of sum_j code_j * 2**(6 j)."""
+    """[rows, K] 6-bit codes -> [rows, K] bytes: each 32-element block becomes a 32-byte slot holding the
+    24 little-endian bytes of sum_j code_j * 2**(6 j), then 8 zero bytes."""
     c = np.asarray(codes).astype(np.uint64) & np.uint64(0x3F)
     rows, K = c.shape
     c = c.reshape(rows, K // 32, 32)
@@ -84,15 +85,17 @@ def pack_fp6(codes: np.ndarray) -> np.ndarray:
         words[..., w] |= (c[..., j] << np.uint64(off)) & np.uint64(0xFFFFFFFFFFFFFFFF)
         if off > 58:  # the code straddles two 64-bit words
             words[..., w + 1] |= c[..., j] >> np.uint64(64 - off)
-    return words.astype("<u8").view(np.uint8).reshape(rows, K // 32 * 24)
+    slots = np.zeros((rows, K // 32, 4), dtype="<u8")
+    slots[..., :3] = words
+    return slots.view(np.uint8).reshape(rows, K)
 
 
 def unpack_fp6(packed: np.ndarray) -> np.ndarray:
-    """[rows, 3K/4] bytes -> [rows, K] 6-bit codes."""
+    """[rows, K] bytes (32-byte slots) -> [rows, K] 6-bit codes; the slots' last 8 bytes are ignored."""
     p = np.ascontiguousarray(np.asarray(packed, dtype=np.uint8))
     rows = p.shape[0]
-    nb = p.shape[1] // 24
-    words = p.reshape(rows, nb, 24).view("<u8").astype(np.uint64)  # [rows, nb, 3]
+    nb = p.shape[1] // 32
+    words = p.reshape(rows, nb, 32).view("<u8").astype(np.uint64)[..., :3]  # [rows, nb, 3]
     out = np.empty((rows, nb, 32), dtype=np.uint8)
     for j in range(32):
         bit = 6 * j

@@ -365,14 +365,20 @@ def test_should_quantize_rule():
 
 def test_fp6_packing_worked_bytes():
     """Codes 1, 2, 3, 4 at bits 0, 6, 12, 18: 1 + 2*64 + 3*4096 + 4*262144 = 0x103081 -> bytes 81 30 10;
-    a code straddling the first 64-bit word (element 10, bits 60..65) lands in bytes 7 and 8."""
-    c = np.zeros((1, 32), dtype=np.uint8)
+    a code straddling the first 64-bit word (element 10, bits 60..65) lands in bytes 7 and 8; the last
+    element (bits 186..191) fills the top of byte 23; each block is a 32-byte slot whose last 8 bytes
+    are zero, so the second block starts at byte 32."""
+    c = np.zeros((1, 64), dtype=np.uint8)
     c[0, :4] = [1, 2, 3, 4]
-    assert pack_fp6(c)[0, :4].tolist() == [0x81, 0x30, 0x10, 0x00]
+    c[0, 32] = 0x05
+    b = pack_fp6(c)[0]
+    assert b.shape == (64,)
+    assert b[:4].tolist() == [0x81, 0x30, 0x10, 0x00] and b[32] == 0x05 and not b[24:32].any()
     c = np.zeros((1, 32), dtype=np.uint8)
     c[0, 10] = 0x3F  # bits 60..65
+    c[0, 31] = 0x3F  # bits 186..191
     b = pack_fp6(c)[0]
-    assert b[7] == 0xF0 and b[8] == 0x03 and int(b.sum()) == 0xF0 + 0x03
+    assert b[7] == 0xF0 and b[8] == 0x03 and b[23] == 0xFC and int(b.sum()) == 0xF0 + 0x03 + 0xFC
 
 
 def test_fp6_pack_round_trip():
