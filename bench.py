@@ -129,7 +129,8 @@ def run_layer(layer, dev, steps, warmup, rotate, seed=0):
     qa = [mxq.quantize(fmt, a) for a in As]
     ms_gemm = _time_loop(lambda i: mxq.gemm(qa[i % rotate], Ws[i % rotate], None, out), steps, warmup, dist_gemm)
     ms_quant = _time_loop(lambda i: mxq.quantize(fmt, As[i % rotate], qa[i % rotate]), steps, warmup)
-    code_b = M * K * (1.0 if fmt == "mxfp8" else 0.75 if fmt.startswith("mxfp6") else 0.5)
+    # bytes the quantizer writes: MXFP6 stores each 24-byte block in a 32-byte slot
+    code_b = M * K * (1.0 if fmt == "mxfp8" or fmt.startswith("mxfp6") else 0.5)
     scale_b = M * K / (16 if fmt == "nvfp4" else 32)
     quant_bytes = M * K * 2 + code_b + scale_b
     res.update(path=fmt, ms=ms_fused, ms_p10=dist_fused["p10"], ms_p50=dist_fused["p50"], ms_p90=dist_fused["p90"],

@@ -26,16 +26,20 @@
  *      NVFP4 codes  uint8 [rows, K/2]   E2M1 (same packing), scales uint8
  *                                        [rows, K/16] E4M3, plus one float32
  *                                        per-tensor scale in device memory;
- *      MXFP6 codes  uint8 [rows, 3K/4]  E2M3 or E3M2: each 32-element block is
- *                                        24 bytes, element j at bits 6j..6j+5
- *                                        of the block's little-endian 192-bit
- *                                        integer; scales uint8 [rows, K/32]
- *                                        E8M0.  The MXFP6 GEMM needs K % 64 == 0
- *                                        (MXQ_ERR_UNSUPPORTED otherwise) and is
- *                                        not a requantization target.
+ *      MXFP6 codes  uint8 [rows, K]     E2M3 or E3M2: each 32-element block
+ *                                        takes a 32-byte slot, the 24 bytes of
+ *                                        its little-endian 192-bit integer
+ *                                        (element j at bits 6j..6j+5), then 8
+ *                                        zero bytes; scales uint8 [rows, K/32]
+ *                                        E8M0.  The MXFP6 GEMM needs K % 128
+ *                                        == 0 (MXQ_ERR_UNSUPPORTED otherwise)
+ *                                        and 4-byte aligned scale pointers
+ *                                        (MXQ_ERR_ALIGN); MXFP6 is not a
+ *                                        requantization format.
  *  - Every pointer is caller-owned DEVICE memory (the library never
  *    allocates or frees).  Base pointers of A, W, codes, out and workspace
- *    must be 16-byte aligned; scale and bias pointers need no alignment.
+ *    must be 16-byte aligned; scale and bias pointers need no alignment
+ *    (except the MXFP6 GEMM's scales, above).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *    stream-ordered and return before the GPU work completes; device faults
  *    surface at the caller's next synchronisation.  Calls on different
@@ -60,7 +64,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 6
+#define MXQ_ABI_VERSION 7
 
 typedef enum {
   MXQ_FMT_MXFP8 = 1, /* E4M3 codes, E8M0 scale per 32 K-elements */

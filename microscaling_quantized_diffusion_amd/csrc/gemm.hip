@@ -4,7 +4,7 @@
 // aitrends.kr MXFP8/NVFP4 article ("Section details": quantized weights times
 // dynamically quantized activations; second "Evidence" block: small layers
 // stay in bf16).  Kernels:
-//   mxp_gemm_kernel   MXFP8 / MXFP4 main path: 256x256 or 256x320 tiles,
+//   mxp_gemm_kernel   MXFP8 / MXFP6 / MXFP4 main path: 256x256 or 256x320 tiles,
 //                     scaled 32x32x64 MFMA (hardware E8M0 block scales),
 //                     two-stage LDS-DMA ring of 128-byte K slabs.
 //   nv4_gemm_kernel   NVFP4 main path: the same tile and ring; codes widened
@@ -530,8 +530,10 @@ __device__ __forceinline__ void store_tile_requant(const v16f (&acc)[TI][TJ], fl
 // MX main path.  One BM x BN output tile per workgroup (default 256 x 256,
 // eight waves as 4 x 2, each 64 x 128 outputs in fp32 accumulators), 32x32x64
 // scaled MFMA, and an NS-stage LDS ring of SLAB-byte K slabs (SLAB = 128:
-// 128 FP8 / 256 FP4 elements per row; SLAB = 64: half that) filled by LDS DMA
-// NS-1 stages ahead of use.
+// 128 FP8 / FP6 or 256 FP4 elements per row; SLAB = 64: half that) filled by
+// LDS DMA NS-1 stages ahead of use.  An FP6 row stores each 32-element block
+// in a 32-byte slot (24 code bytes, 8 zero bytes), so it stages exactly like
+// an FP8 row.
 //
 // * Staging.  Measured on gfx950, L2 -> LDS DMA throughput tracks the
 //   contiguous bytes each instruction reads per row (32 B: 8, 64 B: 16,
@@ -545,17 +547,19 @@ __device__ __forceinline__ void store_tile_requant(const v16f (&acc)[TI][TJ], fl
 //   visibility: wait for the wave's own DMA (vmcnt through the builtin, which
 //   the compiler's bookkeeping sees), then s_barrier.
 // * Scales ride with the codes of each stage: per row one dword of E8M0
-//   bytes (FP8: K-blocks 4p .. 4p+3 of the stage's 256-byte K pair, fetched
-//   again by the second 64-byte stage of the pair; FP4: SLAB/64 dwords).
+//   bytes (FP8 / FP6: K-blocks 4p .. 4p+3 of the stage's 128 K-elements;
+//   FP4: SLAB/64 dwords).
 // * LDS layout.  Row r's SLAB bytes at r * SLAB, its 16-byte chunks
 //   XOR-swizzled by (r >> 1) & 7 (128-byte rows) or (r >> 2) & 3 (64-byte
 //   rows), both measured conflict-free for the operand reads.
 // * Operands.  Lane (r, q) of a 32x32x64 MFMA holds 16-byte chunks 4h + q
-//   and 4h + 2 + q of row r for the 64-byte half h of a slab.  Each wave
+//   and 4h + 2 + q of row r for the 64-byte half h of a slab (FP8, FP4), or
+//   chunks 4h + 2q and 4h + 2q + 1, the slot of K-block q, whose six code
+//   dwords the FP6 MFMA reads and whose two zero dwords it ignores.  Each wave
 //   streams its W tiles through two register slots, the reads of the next
 //   MFMA group issued ahead of the current one (see stream_stage).  Lane q's
-//   scale is that of K-block q of the MFMA's 64 K-elements: FP8 block 2c + q
-//   of 64-byte chunk c, FP4 blocks 4c + q and 4c + 2 + q for its two MFMAs.
+//   scale is that of K-block q of the MFMA's 64 K-elements: FP8 / FP6 block
+//   2h + q of the stage, FP4 blocks 4h + q and 4h + 2 + q for its two MFMAs.
 // * Measured on gfx950 (s_memtime per wave and stage, FLUX MLP up-projection):
 //   the DMA wait before the stage barrier is ~1% of the loop; the barrier
 //   ~20%, because the older wave of each SIMD wins issue and finishes its
@@ -567,9 +571,8 @@ __device__ __forceinline__ void store_tile_requant(const v16f (&acc)[TI][TJ], fl
 // * Epilogue.  (+ bias) -> bf16 RNE; each wave stages 32 output rows at a
 //   time through the idle stage buffers (16-byte row pad) and writes whole
 //   256-byte row segments with 16-byte stores, so L2 sees full-line writes.
-// Requires K % (2 * SLAB) == 0 (FP8: 128-element K pairs) or K % (2 * SLAB)
-// == 0 in elements for FP4 (K % 256 at SLAB = 128), and 4-byte aligned scale
-// rows.
+// Requires whole stages (K % 128 == 0 for FP8 and FP6, K % 256 == 0 for FP4
+// at SLAB = 128) and 4-byte aligned scale rows.
 // REQ: 0 = bf16 output; 1 / 2 = the output MX-quantized to E4M3 / E2M1 codes
 // and E8M0 scales (qcodes, qscales; rceil selects the round-up shared-exponent
 // rule), with the bf16 output also written when `out` is not null.  ACT:
@@ -587,7 +590,8 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
   constexpr int CPR = SLAB / 16;               // 16-byte chunks per row
   constexpr int RPG = 64 / CPR;                // rows per wave-wide code DMA
   constexpr int CODE_BYTES = ROWS * SLAB;
-  constexpr int SDW = (ELEM == 1) ? 1 : H;     // scale dwords per row and stage
+  constexpr bool FP4 = ELEM == 2;              // two codes per byte; else one code byte or FP6 slot byte per element
+  constexpr int SDW = FP4 ? H : 1;             // scale dwords per row and stage
   constexpr int SGROUPS = ((ROWS * SDW + 63) / 64 + NW - 1) / NW * NW;  // wave-wide 4-byte scale DMAs per stage
   constexpr int STAGE = CODE_BYTES + SGROUPS * 256;
   constexpr int CGROUPS = CODE_BYTES / 1024;   // wave-wide 16-byte code DMAs per stage
@@ -597,7 +601,7 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
   static_assert(BM % RPG == 0 && (BM * SDW) % 64 == 0, "a DMA group never straddles the A/W boundary");
   constexpr int CPW = CGROUPS / NW, SPW = SGROUPS / NW;
   constexpr int PER_WAVE = CPW + SPW;          // VMEM instructions per wave and stage
-  constexpr int FMT = (ELEM == 1) ? 0 : 4;
+  constexpr int FMT = ELEM == 1 ? 0 : ELEM == 2 ? 4 : ELEM == 3 ? 2 : 3;  // E4M3, E2M1, E2M3, E3M2
 
   __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
@@ -614,7 +618,8 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
   // and the 32-row steps become immediate offsets of the LDS reads.
   static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BM % 32 == 0, "swizzle invariant under 32-row steps");
   const int sw0 = swz(r32);
-  auto choff = [&](int h, int c) { return ((4 * h + 2 * c + q) ^ sw0) << 4; };
+  // FP8 / FP4: chunks 4h + q and 4h + 2 + q; FP6: the two chunks of 32-byte slot 2h + q (one K-block)
+  auto choff = [&](int h, int c) { return ((ELEM >= 3 ? 4 * h + 2 * q + c : 4 * h + 2 * c + q) ^ sw0) << 4; };
   const int arow = (wm * WTM + r32) * SLAB, wrow = (BM + wn * WTN + r32) * SLAB;
   const int asrow = (wm * WTM + r32) * 4 * SDW, wsrow = (BM + wn * WTN + r32) * 4 * SDW;
 
@@ -628,7 +633,7 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
   const int tn = (int)((id % (uint32_t)(GROUP * tiles_n)) / (uint32_t)gsz);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  const int KB = (ELEM == 1) ? K : K / 2;
+  const int KB = FP4 ? K / 2 : K;
   const int SK = K / 32;
   const int nks = KB / SLAB;
   const uint32_t rows_a = (uint32_t)min(BM, M - m0), rows_w = (uint32_t)min(BN, N - n0);
@@ -667,7 +672,7 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
     }
     // scale bytes of stage ks: FP8 the dword of its 128-element K pair, FP4
     // the SDW dwords of its 64-byte halves
-    const uint32_t sk = (ELEM == 1) ? (uint32_t)(4 * ((ks * SLAB) / 128)) : (uint32_t)(4 * SDW * ks);
+    const uint32_t sk = FP4 ? (uint32_t)(4 * SDW * ks) : (uint32_t)(4 * ((ks * SLAB) / 128));
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
       const int gi = wave * SPW + u;
@@ -691,7 +696,7 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
   // read and its MFMA.
   auto stream_stage = [&](const auto& st, int ks) {
     constexpr int D = 1;
-    constexpr int NSC = (ELEM == 1) ? 1 : 2;
+    constexpr int NSC = FP4 ? 2 : 1;
     constexpr int U = H * TI;
     const uint8_t* sb = st + CODE_BYTES;
     uint4 a[2][TJ][2], w[D + 1][2];
@@ -699,7 +704,7 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
     auto read_group = [&](int g) {
       const int h = g / TI, i = g % TI;
       const int c = ks * H + h;
-      const int b0 = (ELEM == 1) ? 2 * (c & 1) + q : 4 * h + q;
+      const int b0 = FP4 ? 4 * h + q : 2 * (c & 1) + q;
       if (i == 0) {
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
@@ -727,7 +732,7 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
       const int h = g / TI, i = g % TI, sl = g % (D + 1);
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        if constexpr (ELEM == 1) {
+        if constexpr (!FP4) {
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               as_v8i(w[sl][0], w[sl][1]), as_v8i(a[h & 1][j][0], a[h & 1][j][1]), acc[i][j], FMT, FMT, 0,
               (int)sw[sl][0], 0, (int)sa[h & 1][j][0]);
@@ -1126,8 +1131,8 @@ __global__ __launch_bounds__(256) void bf16_generic_kernel(const uint16_t* __res
 hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                           const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
                           const uint16_t* bias, uint16_t* out, hipStream_t stream) {
-  // whole 128-element FP8 K pairs / 256-element FP4 slabs and 4-byte aligned
-  // scale rows: the 32x32x64 path with LDS-DMA staging
+  // whole 128-element FP8 / FP6 stages or 256-element FP4 stages and 4-byte
+  // aligned scale rows: the 32x32x64 path with LDS-DMA staging
   const bool scales_aligned = (((uintptr_t)a_scales | (uintptr_t)w_scales) & 3) == 0;
   // Tile width 256 or 320 columns (wave tiles 64 x 128 / 64 x 160): with one
   // workgroup per CU, the time is about (rounds of tiles) x (tile width), so
@@ -1139,6 +1144,13 @@ hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8
   if (scales_aligned && elem == 2 && K % 256 == 0)
     return wide ? launch_mxp<2, 256, 320, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream)
                 : launch_mxp<2, 256, 256, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+  if (scales_aligned && elem == 3 && K % 128 == 0)
+    return wide ? launch_mxp<3, 256, 320, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream)
+                : launch_mxp<3, 256, 256, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+  if (scales_aligned && elem == 4 && K % 128 == 0)
+    return wide ? launch_mxp<4, 256, 320, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream)
+                : launch_mxp<4, 256, 256, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+  if (elem >= 3) return hipErrorInvalidValue;  // FP6 has no generic path: callers check the shape first
   if (elem == 1)
     return launch_tiled<MX8, MXQ_TILE_MX>(M, N, K, a_codes, a_scales, w_codes, w_scales, nullptr, nullptr, bias,
                                              out, stream);

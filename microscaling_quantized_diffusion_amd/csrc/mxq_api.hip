@@ -10,6 +10,7 @@ using namespace mxq;
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* a, const void* b) { return (((uintptr_t)a | (uintptr_t)b) & 3u) == 0; }
 
 int block_of(mxq_format fmt) { return fmt == MXQ_FMT_NVFP4 ? 16 : 32; }
 
@@ -43,7 +44,7 @@ bool valid_gemm(int64_t M, int64_t N, int64_t K) {
 }
 
 size_t code_bytes(mxq_format fmt, int64_t rows, int64_t K) {
-  return (size_t)rows * (size_t)(fmt == MXQ_FMT_MXFP8 ? K : is_fp6(fmt) ? K / 32 * 24 : K / 2);
+  return (size_t)rows * (size_t)(fmt == MXQ_FMT_MXFP8 || is_fp6(fmt) ? K : K / 2);
 }
 size_t scale_bytes(mxq_format fmt, int64_t rows, int64_t K) { return (size_t)rows * (size_t)(K / block_of(fmt)); }
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -142,12 +143,9 @@ mxq_status mxq_gemm(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K, const v
   if (fmt == MXQ_FMT_NVFP4 && (!a_tensor_scale || !w_tensor_scale)) return MXQ_ERR_NULL;
   if (fmt != MXQ_FMT_NVFP4 && (a_tensor_scale || w_tensor_scale)) return MXQ_ERR_UNSUPPORTED;
   if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
-  if (is_fp6(fmt) && K % 64 != 0) return MXQ_ERR_UNSUPPORTED;
+  if (is_fp6(fmt) && K % 128 != 0) return MXQ_ERR_UNSUPPORTED;
+  if (is_fp6(fmt) && !aligned4(a_scales, w_scales)) return MXQ_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
-  if (is_fp6(fmt))
-    return launch_status(launch_mx6_gemm(elem_of(fmt), M, N, K, (const uint8_t*)a_codes, (const uint8_t*)a_scales,
-                                         (const uint8_t*)w_codes, (const uint8_t*)w_scales,
-                                         (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s));
   if (fmt == MXQ_FMT_NVFP4)
     return launch_status(launch_nvfp4_gemm(M, N, K, (const uint8_t*)a_codes, (const uint8_t*)a_scales, a_tensor_scale,
                                            (const uint8_t*)w_codes, (const uint8_t*)w_scales, w_tensor_scale,
@@ -170,7 +168,8 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt_arg, int64_t M, int64_t N, int64_
   if (fmt == MXQ_FMT_NVFP4 && !w_tensor_scale) return MXQ_ERR_NULL;
   if (fmt != MXQ_FMT_NVFP4 && w_tensor_scale) return MXQ_ERR_UNSUPPORTED;
   if (!aligned16(a_bf16) || !aligned16(w_codes) || !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
-  if (is_fp6(fmt) && K % 64 != 0) return MXQ_ERR_UNSUPPORTED;
+  if (is_fp6(fmt) && K % 128 != 0) return MXQ_ERR_UNSUPPORTED;
+  if (is_fp6(fmt) && !aligned4(w_scales, w_scales)) return MXQ_ERR_ALIGN;  // the activation scales are in the workspace
   const FusedLayout L = fused_layout(fmt, M, K);
   if (!workspace || workspace_bytes < L.total) return MXQ_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MXQ_ERR_ALIGN;
@@ -187,14 +186,8 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt_arg, int64_t M, int64_t N, int64_
                           w_tensor_scale, (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s);
     return launch_status(e);
   }
-  if (is_fp6(fmt)) {
-    e = launch_mx6_quant(elem_of(fmt), rceil, (const uint16_t*)a_bf16, M, K, a_codes, a_scales, s);
-    if (e != hipSuccess) return MXQ_ERR_LAUNCH;
-    return launch_status(launch_mx6_gemm(elem_of(fmt), M, N, K, a_codes, a_scales, (const uint8_t*)w_codes,
-                                         (const uint8_t*)w_scales, (const uint16_t*)bias_bf16, (uint16_t*)out_bf16,
-                                         s));
-  }
-  e = launch_mx_quant(elem_of(fmt), rceil, (const uint16_t*)a_bf16, M, K, a_codes, a_scales, s);
+  e = is_fp6(fmt) ? launch_mx6_quant(elem_of(fmt), rceil, (const uint16_t*)a_bf16, M, K, a_codes, a_scales, s)
+                  : launch_mx_quant(elem_of(fmt), rceil, (const uint16_t*)a_bf16, M, K, a_codes, a_scales, s);
   if (e != hipSuccess) return MXQ_ERR_LAUNCH;
   e = launch_mx_gemm(elem_of(fmt), M, N, K, a_codes, a_scales, (const uint8_t*)w_codes, (const uint8_t*)w_scales,
                      (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s);

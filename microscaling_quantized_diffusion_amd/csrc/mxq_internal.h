@@ -18,14 +18,11 @@ namespace mxq {
 hipError_t launch_mx_quant(int elem, int rceil, const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, hipStream_t stream);
 
-// MXFP6 quantizer and GEMM (elem 3 = E2M3, 4 = E3M2; codes: 24 bytes per
-// 32-element block, element j at bits 6j of the block's little-endian 192-bit
-// integer).  The GEMM needs K % 64 == 0.
+// MXFP6 quantizer (elem 3 = E2M3, 4 = E3M2; codes: a 32-byte slot per
+// 32-element block, element j at bits 6j of the slot's little-endian 192-bit
+// integer, then 8 zero bytes).
 hipError_t launch_mx6_quant(int elem, int rceil, const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
                             uint8_t* scales, hipStream_t stream);
-hipError_t launch_mx6_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
-                           const uint8_t* w_codes, const uint8_t* w_scales, const uint16_t* bias, uint16_t* out,
-                           hipStream_t stream);
 
 // NVFP4 quantizer (two kernels: global-amax partials, then block quantization).
 // `partials` holds nvfp4_partials_count(rows*cols) uint32 values.
@@ -33,7 +30,8 @@ int64_t nvfp4_partials_count(int64_t n_elems);
 hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                               float* tensor_scale, uint32_t* partials, hipStream_t stream);
 
-// MX GEMM (elem: 1 = E4M3, 2 = E2M1).
+// MX GEMM (elem: 1 = E4M3, 2 = E2M1, 3 = E2M3, 4 = E3M2; the FP6 formats
+// need K % 128 == 0 and 4-byte aligned scale rows, else hipErrorInvalidValue).
 hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                           const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
                           const uint16_t* bias, uint16_t* out, hipStream_t stream);

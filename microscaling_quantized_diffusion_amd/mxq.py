@@ -109,10 +109,9 @@ def _require(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
 
 
 def code_cols(fmt: str, K: int) -> int:
-    if fmt == "mxfp8":
+    """Code bytes per row: MXFP8 one per element, MXFP6 a 32-byte slot per 32-element block, FP4 two codes per byte."""
+    if fmt == "mxfp8" or fmt.startswith("mxfp6"):
         return K
-    if fmt.startswith("mxfp6"):
-        return K // 32 * 24
     return K // 2
 
 

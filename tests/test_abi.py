@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert mxq.abi_version() == 6
+    assert mxq.abi_version() == 7
     for s in range(8):
         assert lib.mxq_status_string(s)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -85,6 +85,9 @@ def test_gemm_argument_errors(lib):
     assert g(1, 4, 4, 32, P, P, None, P, P, None, None, P + 8, None) == 4
     assert g(1, 0, 4, 32, P, P, None, P, P, None, None, P, None) == 0
     assert g(1, 4, 0, 32, P, P, None, P, P, None, None, P, None) == 0
+    assert g(4, 4, 4, 192, P, P, None, P, P, None, None, P, None) == 6  # MXFP6 K not a multiple of 128
+    assert g(5, 4, 4, 128, P, P + 1, None, P, P, None, None, P, None) == 4  # MXFP6 scales not 4-byte aligned
+    assert lib.mxq_workspace_bytes(4, 64, 256, 1) >= 64 * 256 + 64 * 8  # MXFP6 codes: one byte per element
 
 
 def test_fused_argument_errors(lib):

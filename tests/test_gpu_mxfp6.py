@@ -1,7 +1,7 @@
 """GPU parity of MXFP6 (E2M3 / E3M2 codes, E8M0 scale per 32): the quantizer byte for byte against the
 oracle (every bf16 bit pattern, both shared-scale rules, ragged shapes), the GEMM within the GEMM gate
-(ragged M and N, K a multiple of 64, with bias), the fused call equal to quantize + GEMM, and sampled
-rows of the FLUX MLP up-projection."""
+(ragged M and N, K a multiple of 128, with bias), the fused call equal to quantize + GEMM, the
+slots' zero padding ignored by the MFMA, and sampled rows of the FLUX MLP up-projection."""
 
 import numpy as np
 import pytest
@@ -57,9 +57,10 @@ def test_ragged_and_activation_shapes(fmt, rows, K, dev):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M,N,K", [(300, 203, 256), (129, 384, 192), (64, 64, 64)])
+@pytest.mark.parametrize("M,N,K", [(300, 203, 256), (129, 384, 384), (64, 64, 128), (513, 1100, 640)])
 def test_gemm_matches_oracle(fmt, M, N, K, dev):
-    """Ragged M and N (N = 203 also takes the element-wise store path), bias on the first case."""
+    """Ragged M and N over several 256-row tiles, an odd number of 128-element K stages, bias with
+    N = 203."""
     import torch
 
     from microscaling_quantized_diffusion_amd import mxq
@@ -86,11 +87,36 @@ def test_gemm_matches_oracle(fmt, M, N, K, dev):
     assert mis <= 0.01, mis
 
 
-def test_gemm_k_not_multiple_of_64_is_unsupported(dev):
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_ignores_slot_padding(fmt, dev):
+    """Bytes 24..31 of every 32-byte slot are outside the codes: filling them with ones in both
+    operands leaves the GEMM's output bit for bit unchanged."""
+    import torch
+
     from microscaling_quantized_diffusion_amd import mxq
 
-    log_case("mxfp6 K % 64")
-    a = to_dev(bf16_bits_from_f32(np.ones((64, 96), np.float32)), dev)
+    M, N, K = 256, 256, 256
+    log_case("mxfp6 slot padding", fmt, M, N, K)
+    rng = np.random.default_rng(62)
+    qa = mxq.quantize(fmt, to_dev(bf16_bits_from_f32(rng.standard_normal((M, K)).astype(np.float32)), dev))
+    qw = mxq.quantize(fmt, to_dev(bf16_bits_from_f32((rng.standard_normal((N, K)) * 0.05).astype(np.float32)), dev))
+    y = mxq.gemm(qa, qw)
+    pad = torch.zeros(K, dtype=torch.bool, device=dev).view(K // 32, 32)
+    pad[:, 24:] = True
+    pad = pad.view(K)
+    assert not bool(qa.codes[:, pad].any()) and not bool(qw.codes[:, pad].any())
+    qa.codes[:, pad] = 0xFF
+    qw.codes[:, pad] = 0xFF
+    y2 = mxq.gemm(qa, qw)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+def test_gemm_k_not_multiple_of_128_is_unsupported(dev):
+    from microscaling_quantized_diffusion_amd import mxq
+
+    log_case("mxfp6 K % 128")
+    a = to_dev(bf16_bits_from_f32(np.ones((64, 192), np.float32)), dev)
     qa = mxq.quantize("mxfp6_e2m3", a)
     with pytest.raises(mxq.MxqError) as e:
         mxq.gemm(qa, qa)
