@@ -18,6 +18,11 @@ namespace mxq {
 typedef __bf16 mx_bf16x2 __attribute__((ext_vector_type(2)));
 typedef short mx_short2 __attribute__((ext_vector_type(2)));
 typedef unsigned short mx_ushort2 __attribute__((ext_vector_type(2)));
+typedef __bf16 mx_bf16x32 __attribute__((ext_vector_type(32)));
+typedef uint32_t mx_u32x16 __attribute__((ext_vector_type(16)));
+// Six dwords in registers.  Its in-memory size is padded to 32 bytes: never
+// load or store it as a whole, only its elements.
+typedef uint32_t mx_u32x6 __attribute__((ext_vector_type(6)));
 
 // emax: exponent of the element format's largest power of two
 // (E4M3: 448 = 1.75 * 2^8; E2M1: 6 = 1.5 * 2^2; E2M3: 7.5 = 1.875 * 2^2;
@@ -98,6 +103,26 @@ __device__ __forceinline__ uint32_t mx_encode_fp4x4(uint32_t into, uint32_t w0, 
   into = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(into, __builtin_bit_cast(mx_bf16x2, w0), sc, BYTE);
   into = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(into, __builtin_bit_cast(mx_bf16x2, w1), sc, BYTE + 1);
   return into;
+}
+
+// Eight bf16 values (four dwords, element order low half first) -> eight
+// E2M3 (ELEM 3) / E3M2 (ELEM 4) codes of x / 2^e, element j at bits 6j of the
+// 48-bit result (lo: bits 0..31, hi: bits 32..47).  The gfx950 conversions
+// v_cvt_scalef32_pk32_fp6_bf16 / _bf6_bf16 (32 elements, element j at bits 6j
+// of six dwords, dividing by the scale operand) were measured equal to the
+// RNE-saturating encoding for every finite bf16 and every e in [-127, 127],
+// with the sign of zero kept.  The 24 unused inputs are zeros (code 0).
+template <int ELEM>
+__device__ __forceinline__ void mx_encode_fp6x8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, int e,
+                                                uint32_t& lo, uint32_t& hi) {
+  static_assert(ELEM == 3 || ELEM == 4, "FP6 element");
+  const mx_u32x16 in = {w0, w1, w2, w3, 0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  const mx_bf16x32 xv = __builtin_bit_cast(mx_bf16x32, in);
+  mx_u32x6 r;
+  if constexpr (ELEM == 3) r = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(xv, mx_pow2f(e));
+  else r = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(xv, mx_pow2f(e));
+  lo = r[0];
+  hi = r[1] & 0xFFFFu;
 }
 
 }  // namespace mxq

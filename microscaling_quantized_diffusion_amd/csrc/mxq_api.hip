@@ -124,9 +124,6 @@ mxq_status mxq_quantize(mxq_format fmt_arg, const void* x_bf16, int64_t rows, in
   if (fmt == MXQ_FMT_NVFP4)
     return launch_status(launch_nvfp4_quant((const uint16_t*)x_bf16, rows, cols, (uint8_t*)codes, (uint8_t*)scales,
                                             tensor_scale, (uint32_t*)workspace, s));
-  if (is_fp6(fmt))
-    return launch_status(launch_mx6_quant(elem_of(fmt), rceil, (const uint16_t*)x_bf16, rows, cols, (uint8_t*)codes,
-                                          (uint8_t*)scales, s));
   return launch_status(launch_mx_quant(elem_of(fmt), rceil, (const uint16_t*)x_bf16, rows, cols, (uint8_t*)codes,
                                        (uint8_t*)scales, s));
 }
@@ -186,8 +183,7 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt_arg, int64_t M, int64_t N, int64_
                           w_tensor_scale, (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s);
     return launch_status(e);
   }
-  e = is_fp6(fmt) ? launch_mx6_quant(elem_of(fmt), rceil, (const uint16_t*)a_bf16, M, K, a_codes, a_scales, s)
-                  : launch_mx_quant(elem_of(fmt), rceil, (const uint16_t*)a_bf16, M, K, a_codes, a_scales, s);
+  e = launch_mx_quant(elem_of(fmt), rceil, (const uint16_t*)a_bf16, M, K, a_codes, a_scales, s);
   if (e != hipSuccess) return MXQ_ERR_LAUNCH;
   e = launch_mx_gemm(elem_of(fmt), M, N, K, a_codes, a_scales, (const uint8_t*)w_codes, (const uint8_t*)w_scales,
                      (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s);

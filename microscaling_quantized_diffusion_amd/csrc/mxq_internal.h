@@ -14,15 +14,12 @@ namespace mxq {
 // the launch (hipSuccess when nothing failed).  Shapes are already validated.
 
 // MX quantizer: x bf16 [rows, cols] -> codes / E8M0 scales.  elem: 1 = E4M3,
-// 2 = E2M1; rceil: 0 = floor shared-exponent rule, 1 = round-up rule.
+// 2 = E2M1, 3 = E2M3, 4 = E3M2 (FP6 codes: a 32-byte slot per 32-element
+// block, element j at bits 6j of the slot's little-endian 192-bit integer,
+// then 8 zero bytes); rceil: 0 = floor shared-exponent rule, 1 = round-up
+// rule.
 hipError_t launch_mx_quant(int elem, int rceil, const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, hipStream_t stream);
-
-// MXFP6 quantizer (elem 3 = E2M3, 4 = E3M2; codes: a 32-byte slot per
-// 32-element block, element j at bits 6j of the slot's little-endian 192-bit
-// integer, then 8 zero bytes).
-hipError_t launch_mx6_quant(int elem, int rceil, const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
-                            uint8_t* scales, hipStream_t stream);
 
 // NVFP4 quantizer (two kernels: global-amax partials, then block quantization).
 // `partials` holds nvfp4_partials_count(rows*cols) uint32 values.

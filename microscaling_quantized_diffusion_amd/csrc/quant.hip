@@ -1,10 +1,11 @@
-// Dynamic block-scaled quantizers for gfx950: MXFP8 / MXFP4 (E8M0 scale per
-// 32 elements) and NVFP4-style (E4M3 scale per 16 elements + fp32 tensor
-// scale).  Method: aitrends.kr "Accelerating diffusion-model inference with
+// Dynamic block-scaled quantizers for gfx950: MXFP8 / MXFP6 / MXFP4 (E8M0
+// scale per 32 elements) and NVFP4-style (E4M3 scale per 16 elements + fp32
+// tensor scale).  Method: aitrends.kr "Accelerating diffusion-model inference with
 // MXFP8 and NVFP4 quantization on NVIDIA B200", Glossary ("Microscaling
 // Formats", "MXFP8", "NVFP4") and "Section details" (dynamic activation
 // quantization, dynamic per-tensor scale); encodings and the shared-exponent
-// rule of the OCP Microscaling Formats v1.0 specification.
+// rule of the OCP Microscaling Formats v1.0 specification (which also defines
+// the 6-bit E2M3 and E3M2 elements).
 //
 // Both quantizers are HBM-streaming kernels: every lane owns one 16-byte
 // chunk (8 bf16) per iteration, loaded with one 128-bit load, so a wave reads
@@ -14,8 +15,9 @@
 // comes from integer arithmetic on the bf16 bit patterns; MX element codes
 // from the hardware bf16 -> FP8 / FP4 conversions, whose rounding was
 // measured equal to the definition for every input (FP8 after a clamp, see
-// below); NVFP4 codes, whose divisor is not a power of two, from exact
-// comparisons against per-block thresholds.
+// below) and the bf16 -> FP6 conversions (measured exact, see
+// mx_encode_fp6x8); NVFP4 codes, whose divisor is not a power of two, from
+// exact comparisons against per-block thresholds.
 #include "mx_encode.h"
 #include "mxq_internal.h"
 
@@ -27,6 +29,9 @@ __device__ __forceinline__ uint32_t quad_swap1(uint32_t v) {  // lanes 0<->1, 2<
 }
 __device__ __forceinline__ uint32_t quad_swap2(uint32_t v) {  // lanes 0<->2, 1<->3 of each quad
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t quad_next(uint32_t v) {  // lane t of each quad gets lane min(t + 1, 3)
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xF9, 0xF, 0xF, false);
 }
 
 // Largest |x| (as bf16 magnitude bits) of the 8 elements in a 16-byte chunk.
@@ -91,6 +96,38 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__
     if (ELEM == 1) reinterpret_cast<uint2*>(codes)[i] = make_uint2(lo, hi);
     else reinterpret_cast<uint32_t*>(codes)[i] = lo;
     if ((i & 3) == 0) scales[i >> 2] = (uint8_t)scale_byte;
+  });
+}
+
+
+// ----------------------------------------------------------------- MXFP6
+// MXFP6 codes: each 32-element block is a 32-byte slot holding its 192-bit
+// code integer (element j at bits 6j, little-endian) and 8 zero bytes.  Lane
+// t of a quad encodes elements 8t .. 8t+7, i.e. bits 48t .. 48t+47 of the
+// integer (p_t); the slot's 8-byte word t is bits 64t .. 64t+63, which is
+// (p_t >> 16t) | (p_{t+1} << (48 - 16t)) for t < 3 and zero for t = 3, so
+// one quad shift hands each lane its neighbour's bits and every lane stores
+// one word (a wave writes 512 contiguous bytes).
+template <int ELEM>
+__global__ __launch_bounds__(256) void mx6_quant_kernel(const uint4* __restrict__ x, uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales, int64_t nchunks, int rceil) {
+  for_chunks(x, nchunks, [&](const uint4& v, int64_t i) {
+    uint32_t m = chunk_absmax_bits(v);
+    m = max(m, quad_swap1(m));
+    m = max(m, quad_swap2(m));
+    uint32_t lo = 0, hi = 0;
+    uint32_t scale_byte = 0xFFu;  // NaN or Inf in the block: NaN scale, zero codes
+    if (m < 0x7F80u) {
+      const int e = mx_shared_exponent<ELEM>(m, rceil);
+      scale_byte = (uint32_t)(e + 127);
+      mx_encode_fp6x8<ELEM>(v.x, v.y, v.z, v.w, e, lo, hi);
+    }
+    const uint64_t p = ((uint64_t)hi << 32) | lo;
+    const uint32_t t = (uint32_t)i & 3u;
+    const uint64_t pn = ((uint64_t)quad_next(hi) << 32) | quad_next(lo);
+    const uint64_t word = t == 3u ? 0ull : (p >> (16 * t)) | (pn << (48 - 16 * t));
+    reinterpret_cast<uint64_t*>(codes)[i] = word;
+    if (t == 0u) scales[i >> 2] = (uint8_t)scale_byte;
   });
 }
 
@@ -290,12 +327,15 @@ hipError_t launch_mx_quant(int elem, int rceil, const uint16_t* x, int64_t rows,
   const int64_t nchunks = rows * cols / 8;
   if (nchunks == 0) return hipSuccess;
   const int grid = grid_for((nchunks + kBatch - 1) / kBatch, 8192);
+  const uint4* xv = (const uint4*)x;
   if (elem == 1)
-    hipLaunchKernelGGL(mx_quant_kernel<1>, dim3(grid), dim3(256), 0, stream, (const uint4*)x, codes, scales, nchunks,
-                       rceil);
+    hipLaunchKernelGGL(mx_quant_kernel<1>, dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks, rceil);
+  else if (elem == 2)
+    hipLaunchKernelGGL(mx_quant_kernel<2>, dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks, rceil);
+  else if (elem == 3)
+    hipLaunchKernelGGL(mx6_quant_kernel<3>, dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks, rceil);
   else
-    hipLaunchKernelGGL(mx_quant_kernel<2>, dim3(grid), dim3(256), 0, stream, (const uint4*)x, codes, scales, nchunks,
-                       rceil);
+    hipLaunchKernelGGL(mx6_quant_kernel<4>, dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks, rceil);
   return hipGetLastError();
 }
 
