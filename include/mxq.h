@@ -34,8 +34,9 @@
  *                                        E8M0.  The MXFP6 GEMM needs K % 128
  *                                        == 0 (MXQ_ERR_UNSUPPORTED otherwise)
  *                                        and 4-byte aligned scale pointers
- *                                        (MXQ_ERR_ALIGN); MXFP6 is not a
- *                                        requantization format.
+ *                                        (MXQ_ERR_ALIGN); MXFP6 codes are
+ *                                        GEMM operands, not a requantized
+ *                                        output format.
  *  - Every pointer is caller-owned DEVICE memory (the library never
  *    allocates or frees).  Base pointers of A, W, codes, out and workspace
  *    must be 16-byte aligned; scale and bias pointers need no alignment
@@ -187,7 +188,7 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K,
  *   act: 0 = none, 1 = GELU in its tanh form,
  *        0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))).
  *
- *   fmt, M, N, K, a_*, w_*, bias_bf16   as in mxq_gemm (MX formats only)
+ *   fmt, M, N, K, a_*, w_*, bias_bf16   as in mxq_gemm (MXFP8, MXFP6 or MXFP4)
  *   out_fmt        MXQ_FMT_MXFP8 or MXQ_FMT_MXFP4, optionally | MXQ_SCALE_RCEIL
  *   out_bf16       device bf16 [M, N], 16-byte aligned, or NULL: also store y
  *   out_codes      device, out: uint8 [M, N] (MXFP8) or [M, N/2] (MXFP4),
@@ -200,9 +201,10 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K,
  *                  writes a column range of a wider quantized matrix (pass
  *                  pointers offset to its first column, a multiple of 32
  *                  elements), e.g. one part of a concatenated activation.
- * Supported where N % 32 == 0, K % 128 == 0 (MXFP8 operands) or K % 256 == 0
- * (MXFP4 operands), and the scale rows are 4-byte aligned; other shapes
- * return MXQ_ERR_UNSUPPORTED.  Sizes otherwise as in mxq_gemm.
+ * Supported where N % 32 == 0, K % 128 == 0 (MXFP8 and MXFP6 operands) or
+ * K % 256 == 0 (MXFP4 operands), and the scale rows are 4-byte aligned; other
+ * shapes, and MXFP6 or NVFP4 as out_fmt, return MXQ_ERR_UNSUPPORTED.  Sizes
+ * otherwise as in mxq_gemm.
  */
 mxq_status mxq_gemm_requant(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void* a_codes,
                             const void* a_scales, const void* w_codes, const void* w_scales, const void* bias_bf16,

@@ -1160,7 +1160,7 @@ hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8
 
 bool mx_requant_supported(int elem, int64_t N, int64_t K, const uint8_t* a_scales, const uint8_t* w_scales) {
   const bool scales_aligned = (((uintptr_t)a_scales | (uintptr_t)w_scales) & 3) == 0;
-  return scales_aligned && N % 32 == 0 && (elem == 1 ? K % 128 == 0 : K % 256 == 0);
+  return scales_aligned && N % 32 == 0 && (elem == 2 ? K % 256 == 0 : K % 128 == 0);
 }
 
 template <int ELEM, int OELEM>
@@ -1190,6 +1190,16 @@ hipError_t launch_mx_gemm_requant(int elem, int out_elem, int out_rceil, int act
                                   hipStream_t stream) {
   const int64_t qld = codes_ld ? codes_ld : (out_elem == 1 ? N : N / 2);
   const int64_t sld = scales_ld ? scales_ld : N / 32;
+  if (elem == 3)
+    return out_elem == 1 ? launch_requant_act<3, 1>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales,
+                                                    bias, out_bf16, out_codes, out_scales, qld, sld, stream)
+                         : launch_requant_act<3, 2>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales,
+                                                    bias, out_bf16, out_codes, out_scales, qld, sld, stream);
+  if (elem == 4)
+    return out_elem == 1 ? launch_requant_act<4, 1>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales,
+                                                    bias, out_bf16, out_codes, out_scales, qld, sld, stream)
+                         : launch_requant_act<4, 2>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales,
+                                                    bias, out_bf16, out_codes, out_scales, qld, sld, stream);
   if (elem == 1 && out_elem == 1)
     return launch_requant_act<1, 1>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16,
                                     out_codes, out_scales, qld, sld, stream);

@@ -218,7 +218,8 @@ mxq_status mxq_gemm_requant(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K,
   if (!a_codes || !a_scales || !w_codes || !w_scales || !out_codes || !out_scales) return MXQ_ERR_NULL;
   if (st != MXQ_OK || !aligned16(a_codes) || !aligned16(w_codes) || !aligned16(out_codes)) return MXQ_ERR_ALIGN;
   if (out_bf16 && !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
-  if (fmt == MXQ_FMT_NVFP4 || out_fmt == MXQ_FMT_NVFP4 || is_fp6(fmt) || is_fp6(out_fmt) || (act != 0 && act != 1))
+  // operands MXFP8 / MXFP6 / MXFP4; outputs MXFP8 / MXFP4
+  if (fmt == MXQ_FMT_NVFP4 || out_fmt == MXQ_FMT_NVFP4 || is_fp6(out_fmt) || (act != 0 && act != 1))
     return MXQ_ERR_UNSUPPORTED;
   if (!mx_requant_supported(elem_of(fmt), N, K, (const uint8_t*)a_scales, (const uint8_t*)w_scales))
     return MXQ_ERR_UNSUPPORTED;

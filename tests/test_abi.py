@@ -139,6 +139,8 @@ def test_requant_argument_errors(lib):
     assert r(3, 4, 64, 128, P, P, P, P, None, 0, 1, None, P, P, 0, 0, None) == 6  # NVFP4 operands
     assert r(1, 4, 64, 128, P, P, P, P, None, 0, 3, None, P, P, 0, 0, None) == 6  # NVFP4 output
     assert r(1, 4, 64, 128, P, P, P, P, None, 5, 1, None, P, P, 0, 0, None) == 6  # unknown activation
+    assert r(4, 4, 64, 192, P, P, P, P, None, 0, 1, None, P, P, 0, 0, None) == 6  # K not a multiple of 128 (FP6)
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 4, None, P, P, 0, 0, None) == 6  # MXFP6 output
 
 
 RCEIL = 0x100  # MXQ_SCALE_RCEIL

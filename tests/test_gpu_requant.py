@@ -27,7 +27,8 @@ def dev():
 
 
 def _scheme(fmt):
-    return {"mxfp8": oracle.MXFP8, "mxfp4": oracle.MXFP4}[fmt]
+    return {"mxfp8": oracle.MXFP8, "mxfp4": oracle.MXFP4, "mxfp6_e2m3": oracle.MXFP6_E2M3,
+            "mxfp6_e3m2": oracle.MXFP6_E3M2}[fmt]
 
 
 def _bits_of(t):
@@ -66,7 +67,7 @@ def _case(fmt, out_fmt, act, M, N, K, dev, seed):
 
 @pytest.mark.parametrize("act", ["none", "gelu_tanh"])
 @pytest.mark.parametrize("fmt,out_fmt", [("mxfp8", "mxfp8"), ("mxfp8", "mxfp4"), ("mxfp4", "mxfp8"),
-                                         ("mxfp4", "mxfp4")])
+                                         ("mxfp4", "mxfp4"), ("mxfp6_e2m3", "mxfp8"), ("mxfp6_e3m2", "mxfp4")])
 def test_requant_matches_oracle(fmt, out_fmt, act, dev):
     import torch
 
@@ -74,7 +75,7 @@ def test_requant_matches_oracle(fmt, out_fmt, act, dev):
 
     # ragged rows and a column count that is a multiple of 32 but not of the tile width
     M, N = 300, 288
-    K = 256 if fmt == "mxfp8" else 512
+    K = 512 if fmt == "mxfp4" else 256
     log_case("requant", fmt, out_fmt, act, M, N, K)
     a_bits, w_bits, b_bits, qa, qw, bias, y, q1, q2 = _case(fmt, out_fmt, act, M, N, K, dev, 41)
     ca, sa = oracle.quantize_mx(a_bits, _scheme(fmt))
