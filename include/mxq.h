@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 7
+#define MXQ_ABI_VERSION 8
 
 typedef enum {
   MXQ_FMT_MXFP8 = 1, /* E4M3 codes, E8M0 scale per 32 K-elements */
@@ -88,9 +88,32 @@ typedef enum {
  * Either way e is clamped to [-127, 127].  The rule does not change the code
  * or scale formats: mxq_gemm and the input format of mxq_gemm_requant accept
  * and ignore the flag, and mxq_workspace_bytes ignores it.  With
- * MXQ_FMT_NVFP4, or with any other bit set, a call returns MXQ_ERR_FORMAT.
+ * MXQ_FMT_NVFP4, or with a bit other than the two flags here, a call returns
+ * MXQ_ERR_FORMAT.
  */
 #define MXQ_SCALE_RCEIL 0x100
+
+/*
+ * Packed scale layout flag (MX formats; a storage layout of our own, the
+ * weight pre-packing of a deployment: the pages fix no scale layout).  An MX
+ * scale tensor of `rows` rows and S = K/32 blocks per row is normally
+ * row-major [rows, S].  Packed, rows are padded to R = 32 * ceil(rows / 32)
+ * (R * S bytes, padding bytes unspecified) and block kb of row r sits at
+ *   (r / 32) * 32 S + (kb / P) * 32 P + (r % 32) * P + kb % P,
+ * P = 4 (MXFP8, MXFP6) or 8 (MXFP4): for each group of 32 rows, the scales
+ * of one GEMM K stage (128 / 256 elements) are one contiguous run, which the
+ * GEMM fetches in whole cache lines.  Needs K a multiple of 32 P and
+ * R * S < 2^32 (MXQ_ERR_UNSUPPORTED otherwise).  Meaning per call:
+ *   mxq_quantize           writes the scales packed;
+ *   mxq_gemm               both operands' scales are packed (4-byte aligned);
+ *   mxq_quant_gemm_fused   W's scales are packed (4-byte aligned); A is
+ *                          quantized into the workspace packed as well;
+ *   mxq_workspace_bytes    ignored;
+ * every other call returns MXQ_ERR_FORMAT for it, as does MXQ_FMT_NVFP4.
+ * Codes are unchanged, and results equal those of the row-major layout bit
+ * for bit.
+ */
+#define MXQ_SCALES_PACKED 0x200
 
 typedef enum {
   MXQ_OK = 0,

@@ -406,9 +406,9 @@ hipError_t launch_attention_fp8(int64_t BH, int64_t S, const uint16_t* q, const 
                                 uint16_t* out, uint8_t* ws, hipStream_t stream, int out_elem, int rceil, int64_t H,
                                 uint8_t* qcodes, uint8_t* qscales, int64_t qld, int64_t sld) {
   const AttentionLayout L = attention_layout(BH, S);
-  hipError_t e = launch_mx_quant(1, 0, q, BH * S, kD, ws + L.q_codes, ws + L.q_scales, stream);
+  hipError_t e = launch_mx_quant(1, 0, 0, q, BH * S, kD, ws + L.q_codes, ws + L.q_scales, stream);
   if (e != hipSuccess) return e;
-  e = launch_mx_quant(1, 0, k, BH * S, kD, ws + L.k_codes, ws + L.k_scales, stream);
+  e = launch_mx_quant(1, 0, 0, k, BH * S, kD, ws + L.k_codes, ws + L.k_scales, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(vt_quant_kernel, dim3((unsigned)(S / 64), (unsigned)BH), dim3(256), 0, stream, v,
                      ws + L.vt_codes, ws + L.vt_scales, (int)S);

@@ -577,7 +577,7 @@ __device__ __forceinline__ void store_tile_requant(const v16f (&acc)[TI][TJ], fl
 // and E8M0 scales (qcodes, qscales; rceil selects the round-up shared-exponent
 // rule), with the bf16 output also written when `out` is not null.  ACT:
 // activation applied before the bf16 rounding.
-template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS, int REQ = 0, int ACT = ACT_NONE>
+template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS, int REQ = 0, int ACT = ACT_NONE, int PK = 0>
 __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1) void mxp_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
     const uint8_t* __restrict__ Ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N,
@@ -639,8 +639,17 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
   const uint32_t rows_a = (uint32_t)min(BM, M - m0), rows_w = (uint32_t)min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * KB, rows_a * (uint32_t)KB);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * KB, rows_w * (uint32_t)KB);
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(As + (size_t)m0 * SK, rows_a * (uint32_t)SK);
-  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(Ws + (size_t)n0 * SK, rows_w * (uint32_t)SK);
+  // scale rows: row-major [rows, SK], or (PK) packed in 32-row groups, each
+  // group's bytes stage-major: group g, stage s, row r: the SDW dwords at
+  // g * 32 SK + s * 128 SDW + (r % 32) * 4 SDW, so that one stage's scales
+  // of 32 rows are one contiguous run (m0 and n0 are multiples of 32)
+  static_assert(BM % 32 == 0 && BN % 32 == 0, "whole 32-row scale groups per tile");
+  const __amdgpu_buffer_rsrc_t rsa =
+      PK ? make_rsrc(As + (size_t)m0 * SK, (rows_a + 31u) / 32u * 32u * (uint32_t)SK)
+         : make_rsrc(As + (size_t)m0 * SK, rows_a * (uint32_t)SK);
+  const __amdgpu_buffer_rsrc_t rsw =
+      PK ? make_rsrc(Ws + (size_t)n0 * SK, (rows_w + 31u) / 32u * 32u * (uint32_t)SK)
+         : make_rsrc(Ws + (size_t)n0 * SK, rows_w * (uint32_t)SK);
 
   // per-lane code DMA offsets without the K-step term: group g covers rows
   // RPG*g .. RPG*g+RPG-1, lane l row RPG*g + l/CPR, chunk l%CPR (swizzled)
@@ -658,8 +667,10 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
   for (int u = 0; u < SPW; ++u) {
     const int e = (wave * SPW + u) * 64 + lane;
     const int r = e / SDW, d = e % SDW;
-    soff[u] = r < BM ? (uint32_t)r * (uint32_t)SK + 4 * d
-            : r < ROWS ? (uint32_t)(r - BM) * (uint32_t)SK + 4 * d : kOutOfRange;
+    const int rr = r < BM ? r : r - BM;
+    const uint32_t o = PK ? (uint32_t)(rr / 32) * 32u * (uint32_t)SK + (uint32_t)((rr % 32) * 4 * SDW + 4 * d)
+                          : (uint32_t)rr * (uint32_t)SK + 4 * d;
+    soff[u] = r < ROWS ? o : kOutOfRange;
   }
   // Stage arrays are passed by reference so that the DMA builtin sees the
   // __shared__ object itself (a runtime-selected or returned LDS pointer makes
@@ -670,9 +681,10 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
       const int g = wave * CPW + u;
       lds_dma16(g * RPG < BM ? ra : rw, &st[g * 1024], coff[u], (uint32_t)(ks * SLAB));
     }
-    // scale bytes of stage ks: FP8 the dword of its 128-element K pair, FP4
-    // the SDW dwords of its 64-byte halves
-    const uint32_t sk = FP4 ? (uint32_t)(4 * SDW * ks) : (uint32_t)(4 * ((ks * SLAB) / 128));
+    // scale bytes of stage ks: FP8 / FP6 the dword of its 128 K-elements, FP4
+    // the SDW dwords of its 64-byte halves; packed: the stage's run of 32 rows
+    const uint32_t sk = PK ? (uint32_t)(ks * 128 * SDW)
+                      : FP4 ? (uint32_t)(4 * SDW * ks) : (uint32_t)(4 * ((ks * SLAB) / 128));
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
       const int gi = wave * SPW + u;
@@ -829,13 +841,13 @@ inline bool mx_prefer_wide_tile(int64_t M, int64_t N, int64_t cus) {
   return r320 * 320 < r256 * 256;
 }
 
-template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS, int REQ = 0, int ACT = ACT_NONE>
+template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS, int REQ = 0, int ACT = ACT_NONE, int PK = 0>
 hipError_t launch_mxp(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as, const uint8_t* w,
                       const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream,
                       uint8_t* qcodes = nullptr, uint8_t* qscales = nullptr, int rceil = 0, int64_t qld = 0,
                       int64_t sld = 0) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((mxp_gemm_kernel<ELEM, BM, BN, WM, WN, SLAB, NS, REQ, ACT>), dim3((unsigned)tiles),
+  hipLaunchKernelGGL((mxp_gemm_kernel<ELEM, BM, BN, WM, WN, SLAB, NS, REQ, ACT, PK>), dim3((unsigned)tiles),
                      dim3(64 * WM * WN), 0, stream, a, as, w, ws, bias, out, (int)M, (int)N, (int)K, qcodes, qscales,
                      rceil, qld, sld);
   return hipGetLastError();
@@ -1128,28 +1140,46 @@ __global__ __launch_bounds__(256) void bf16_generic_kernel(const uint16_t* __res
 #endif
 
 
-hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+namespace {
+// The main-path GEMM at 256 x 256 or 256 x 320 tiles; PK: packed scale rows.
+template <int ELEM, int PK>
+hipError_t launch_mx_main(bool wide, int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
+                          const uint8_t* w, const uint8_t* ws, const uint16_t* bias, uint16_t* out,
+                          hipStream_t stream) {
+  return wide ? launch_mxp<ELEM, 256, 320, 4, 2, 128, 2, 0, ACT_NONE, PK>(M, N, K, a, as, w, ws, bias, out, stream)
+              : launch_mxp<ELEM, 256, 256, 4, 2, 128, 2, 0, ACT_NONE, PK>(M, N, K, a, as, w, ws, bias, out, stream);
+}
+template <int PK>
+hipError_t launch_mx_main_elem(int elem, bool wide, int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                               const uint8_t* as, const uint8_t* w, const uint8_t* ws, const uint16_t* bias,
+                               uint16_t* out, hipStream_t stream) {
+  switch (elem) {
+    case 1: return launch_mx_main<1, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
+    case 2: return launch_mx_main<2, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
+    case 3: return launch_mx_main<3, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
+    case 4: return launch_mx_main<4, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
+  }
+  return hipErrorInvalidValue;
+}
+}  // namespace
+
+hipError_t launch_mx_gemm(int elem, int packed, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                           const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
                           const uint16_t* bias, uint16_t* out, hipStream_t stream) {
   // whole 128-element FP8 / FP6 stages or 256-element FP4 stages and 4-byte
   // aligned scale rows: the 32x32x64 path with LDS-DMA staging
   const bool scales_aligned = (((uintptr_t)a_scales | (uintptr_t)w_scales) & 3) == 0;
+  const bool whole_stages = K % (elem == 2 ? 256 : 128) == 0;
   // Tile width 256 or 320 columns (wave tiles 64 x 128 / 64 x 160): with one
   // workgroup per CU, the time is about (rounds of tiles) x (tile width), so
   // take the width with the smaller product; ties keep 256.
   const bool wide = mx_prefer_wide_tile(M, N, device_cu_count());
-  if (scales_aligned && elem == 1 && K % 128 == 0)
-    return wide ? launch_mxp<1, 256, 320, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream)
-                : launch_mxp<1, 256, 256, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
-  if (scales_aligned && elem == 2 && K % 256 == 0)
-    return wide ? launch_mxp<2, 256, 320, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream)
-                : launch_mxp<2, 256, 256, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
-  if (scales_aligned && elem == 3 && K % 128 == 0)
-    return wide ? launch_mxp<3, 256, 320, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream)
-                : launch_mxp<3, 256, 256, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
-  if (scales_aligned && elem == 4 && K % 128 == 0)
-    return wide ? launch_mxp<4, 256, 320, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream)
-                : launch_mxp<4, 256, 256, 4, 2, 128, 2>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+  if (packed) {
+    if (!scales_aligned || !whole_stages) return hipErrorInvalidValue;  // callers check the shape first
+    return launch_mx_main_elem<1>(elem, wide, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+  }
+  if (scales_aligned && whole_stages)
+    return launch_mx_main_elem<0>(elem, wide, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
   if (elem >= 3) return hipErrorInvalidValue;  // FP6 has no generic path: callers check the shape first
   if (elem == 1)
     return launch_tiled<MX8, MXQ_TILE_MX>(M, N, K, a_codes, a_scales, w_codes, w_scales, nullptr, nullptr, bias,

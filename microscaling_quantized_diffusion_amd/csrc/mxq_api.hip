@@ -21,13 +21,19 @@ bool valid_format(mxq_format fmt) {
 bool is_fp6(mxq_format fmt) { return fmt == MXQ_FMT_MXFP6_E2M3 || fmt == MXQ_FMT_MXFP6_E3M2; }
 
 // A format argument is a base format, optionally OR-ed with MXQ_SCALE_RCEIL
-// (MX formats only).  Splits it; false for anything else.
-bool split_format(mxq_format arg, mxq_format* base, int* rceil) {
+// and MXQ_SCALES_PACKED (MX formats only).  Splits it; false for anything
+// else.  Each entry point decides what the packed flag means for it.
+bool split_format(mxq_format arg, mxq_format* base, int* rceil, int* packed) {
   const int v = (int)arg;
   *base = (mxq_format)(v & 0xFF);
   *rceil = (v & MXQ_SCALE_RCEIL) ? 1 : 0;
-  if ((v & ~0xFF & ~MXQ_SCALE_RCEIL) != 0 || !valid_format(*base)) return false;
-  return !(*rceil && *base == MXQ_FMT_NVFP4);
+  *packed = (v & MXQ_SCALES_PACKED) ? 1 : 0;
+  if ((v & ~0xFF & ~MXQ_SCALE_RCEIL & ~MXQ_SCALES_PACKED) != 0 || !valid_format(*base)) return false;
+  return !((*rceil || *packed) && *base == MXQ_FMT_NVFP4);
+}
+bool split_format(mxq_format arg, mxq_format* base, int* rceil) {
+  int packed = 0;
+  return split_format(arg, base, rceil, &packed) && !packed;
 }
 
 // K must be a positive multiple of the block; sizes must fit the kernels'
@@ -47,6 +53,14 @@ size_t code_bytes(mxq_format fmt, int64_t rows, int64_t K) {
   return (size_t)rows * (size_t)(fmt == MXQ_FMT_MXFP8 || is_fp6(fmt) ? K : K / 2);
 }
 size_t scale_bytes(mxq_format fmt, int64_t rows, int64_t K) { return (size_t)rows * (size_t)(K / block_of(fmt)); }
+// The packed scale layout: whole K stages of the MX GEMM (128 elements of
+// FP8 / FP6, 256 of FP4), rows padded to whole groups of 32, and a block
+// count the quantizer indexes in 32 bits.
+int64_t stage_k(mxq_format fmt) { return fmt == MXQ_FMT_MXFP4 ? 256 : 128; }
+int64_t padded_rows(int64_t rows) { return (rows + 31) / 32 * 32; }
+bool packable(mxq_format fmt, int64_t rows, int64_t K) {
+  return fmt != MXQ_FMT_NVFP4 && K % stage_k(fmt) == 0 && padded_rows(rows) * (K / 32) < ((int64_t)1 << 32);
+}
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Fused workspace: [A codes | A scales | tensor scale (NVFP4) | amax partials (NVFP4)],
@@ -58,7 +72,8 @@ FusedLayout fused_layout(mxq_format fmt, int64_t M, int64_t K) {
   FusedLayout L{};
   L.codes = 0;
   L.scales = round256(code_bytes(fmt, M, K));
-  L.ts = L.scales + round256(scale_bytes(fmt, M, K));
+  // MX scales sized for padded rows, so the packed layout fits too
+  L.ts = L.scales + round256(scale_bytes(fmt, fmt == MXQ_FMT_NVFP4 ? M : padded_rows(M), K));
   L.partials = L.ts + (fmt == MXQ_FMT_NVFP4 ? 256 : 0);
   L.total = L.partials + (fmt == MXQ_FMT_NVFP4 ? round256((size_t)nvfp4_partials_count(M * K) * 4) : 0);
   return L;
@@ -99,8 +114,8 @@ int mxq_should_quantize(int64_t M, int64_t K, int64_t N) {
 
 size_t mxq_workspace_bytes(mxq_format fmt_arg, int64_t M, int64_t K, int fused) {
   mxq_format fmt;
-  int rceil;
-  if (!split_format(fmt_arg, &fmt, &rceil) || !valid_dim(M) || !valid_k(fmt, K)) return 0;
+  int rceil, packed;  // neither changes the workspace
+  if (!split_format(fmt_arg, &fmt, &rceil, &packed) || !valid_dim(M) || !valid_k(fmt, K)) return 0;
   if (fused) return fused_layout(fmt, M, K).total;
   if (fmt == MXQ_FMT_NVFP4) return round256((size_t)nvfp4_partials_count(M * K) * 4);
   return 0;
@@ -109,9 +124,10 @@ size_t mxq_workspace_bytes(mxq_format fmt_arg, int64_t M, int64_t K, int fused) 
 mxq_status mxq_quantize(mxq_format fmt_arg, const void* x_bf16, int64_t rows, int64_t cols, void* codes,
                         void* scales, float* tensor_scale, void* workspace, size_t workspace_bytes, void* stream) {
   mxq_format fmt;
-  int rceil;
-  if (!split_format(fmt_arg, &fmt, &rceil)) return MXQ_ERR_FORMAT;
+  int rceil, packed;
+  if (!split_format(fmt_arg, &fmt, &rceil, &packed)) return MXQ_ERR_FORMAT;
   if (!valid_dim(rows) || !valid_k(fmt, cols)) return MXQ_ERR_SHAPE;
+  if (packed && !packable(fmt, rows, cols)) return MXQ_ERR_UNSUPPORTED;
   if (rows == 0) return MXQ_OK;  // nothing to read or write, whatever the pointers
   if (!x_bf16 || !codes || !scales) return MXQ_ERR_NULL;
   if (fmt == MXQ_FMT_NVFP4 && !tensor_scale) return MXQ_ERR_NULL;
@@ -124,32 +140,33 @@ mxq_status mxq_quantize(mxq_format fmt_arg, const void* x_bf16, int64_t rows, in
   if (fmt == MXQ_FMT_NVFP4)
     return launch_status(launch_nvfp4_quant((const uint16_t*)x_bf16, rows, cols, (uint8_t*)codes, (uint8_t*)scales,
                                             tensor_scale, (uint32_t*)workspace, s));
-  return launch_status(launch_mx_quant(elem_of(fmt), rceil, (const uint16_t*)x_bf16, rows, cols, (uint8_t*)codes,
-                                       (uint8_t*)scales, s));
+  return launch_status(launch_mx_quant(elem_of(fmt), rceil, packed, (const uint16_t*)x_bf16, rows, cols,
+                                       (uint8_t*)codes, (uint8_t*)scales, s));
 }
 
 mxq_status mxq_gemm(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K, const void* a_codes, const void* a_scales,
                     const float* a_tensor_scale, const void* w_codes, const void* w_scales,
                     const float* w_tensor_scale, const void* bias_bf16, void* out_bf16, void* stream) {
   mxq_format fmt;
-  int rceil;  // quantizes nothing: the scale rule does not apply
-  if (!split_format(fmt_arg, &fmt, &rceil)) return MXQ_ERR_FORMAT;
+  int rceil, packed;  // quantizes nothing: the scale rule does not apply
+  if (!split_format(fmt_arg, &fmt, &rceil, &packed)) return MXQ_ERR_FORMAT;
   if (!valid_k(fmt, K) || !valid_gemm(M, N, K)) return MXQ_ERR_SHAPE;
+  if (packed && K % stage_k(fmt) != 0) return MXQ_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return MXQ_OK;  // empty output: nothing to launch, whatever the pointers
   if (!a_codes || !a_scales || !w_codes || !w_scales || !out_bf16) return MXQ_ERR_NULL;
   if (fmt == MXQ_FMT_NVFP4 && (!a_tensor_scale || !w_tensor_scale)) return MXQ_ERR_NULL;
   if (fmt != MXQ_FMT_NVFP4 && (a_tensor_scale || w_tensor_scale)) return MXQ_ERR_UNSUPPORTED;
   if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
   if (is_fp6(fmt) && K % 128 != 0) return MXQ_ERR_UNSUPPORTED;
-  if (is_fp6(fmt) && !aligned4(a_scales, w_scales)) return MXQ_ERR_ALIGN;
+  if ((is_fp6(fmt) || packed) && !aligned4(a_scales, w_scales)) return MXQ_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   if (fmt == MXQ_FMT_NVFP4)
     return launch_status(launch_nvfp4_gemm(M, N, K, (const uint8_t*)a_codes, (const uint8_t*)a_scales, a_tensor_scale,
                                            (const uint8_t*)w_codes, (const uint8_t*)w_scales, w_tensor_scale,
                                            (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s));
-  return launch_status(launch_mx_gemm(elem_of(fmt), M, N, K, (const uint8_t*)a_codes, (const uint8_t*)a_scales,
-                                      (const uint8_t*)w_codes, (const uint8_t*)w_scales, (const uint16_t*)bias_bf16,
-                                      (uint16_t*)out_bf16, s));
+  return launch_status(launch_mx_gemm(elem_of(fmt), packed, M, N, K, (const uint8_t*)a_codes,
+                                      (const uint8_t*)a_scales, (const uint8_t*)w_codes, (const uint8_t*)w_scales,
+                                      (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s));
 }
 
 mxq_status mxq_quant_gemm_fused(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K, const void* a_bf16,
@@ -157,16 +174,18 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt_arg, int64_t M, int64_t N, int64_
                                 const void* bias_bf16, void* out_bf16, void* workspace, size_t workspace_bytes,
                                 void* stream) {
   mxq_format fmt;
-  int rceil;
-  if (!split_format(fmt_arg, &fmt, &rceil)) return MXQ_ERR_FORMAT;
+  int rceil, packed;  // packed: W's scales are packed, and A's are written packed into the workspace
+  if (!split_format(fmt_arg, &fmt, &rceil, &packed)) return MXQ_ERR_FORMAT;
   if (!valid_k(fmt, K) || !valid_gemm(M, N, K)) return MXQ_ERR_SHAPE;
+  if (packed && !packable(fmt, M, K)) return MXQ_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return MXQ_OK;  // empty output: nothing to launch, whatever the pointers
   if (!a_bf16 || !w_codes || !w_scales || !out_bf16) return MXQ_ERR_NULL;
   if (fmt == MXQ_FMT_NVFP4 && !w_tensor_scale) return MXQ_ERR_NULL;
   if (fmt != MXQ_FMT_NVFP4 && w_tensor_scale) return MXQ_ERR_UNSUPPORTED;
   if (!aligned16(a_bf16) || !aligned16(w_codes) || !aligned16(out_bf16)) return MXQ_ERR_ALIGN;
   if (is_fp6(fmt) && K % 128 != 0) return MXQ_ERR_UNSUPPORTED;
-  if (is_fp6(fmt) && !aligned4(w_scales, w_scales)) return MXQ_ERR_ALIGN;  // the activation scales are in the workspace
+  // the activation scales are in the workspace (256-byte aligned)
+  if ((is_fp6(fmt) || packed) && !aligned4(w_scales, w_scales)) return MXQ_ERR_ALIGN;
   const FusedLayout L = fused_layout(fmt, M, K);
   if (!workspace || workspace_bytes < L.total) return MXQ_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MXQ_ERR_ALIGN;
@@ -183,10 +202,10 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt_arg, int64_t M, int64_t N, int64_
                           w_tensor_scale, (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s);
     return launch_status(e);
   }
-  e = launch_mx_quant(elem_of(fmt), rceil, (const uint16_t*)a_bf16, M, K, a_codes, a_scales, s);
+  e = launch_mx_quant(elem_of(fmt), rceil, packed, (const uint16_t*)a_bf16, M, K, a_codes, a_scales, s);
   if (e != hipSuccess) return MXQ_ERR_LAUNCH;
-  e = launch_mx_gemm(elem_of(fmt), M, N, K, a_codes, a_scales, (const uint8_t*)w_codes, (const uint8_t*)w_scales,
-                     (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s);
+  e = launch_mx_gemm(elem_of(fmt), packed, M, N, K, a_codes, a_scales, (const uint8_t*)w_codes,
+                     (const uint8_t*)w_scales, (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s);
   return launch_status(e);
 }
 

@@ -17,9 +17,10 @@ namespace mxq {
 // 2 = E2M1, 3 = E2M3, 4 = E3M2 (FP6 codes: a 32-byte slot per 32-element
 // block, element j at bits 6j of the slot's little-endian 192-bit integer,
 // then 8 zero bytes); rceil: 0 = floor shared-exponent rule, 1 = round-up
-// rule.
-hipError_t launch_mx_quant(int elem, int rceil, const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
-                           uint8_t* scales, hipStream_t stream);
+// rule; packed: scales in the GEMM's packed layout (32-row groups,
+// stage-major; needs rows * cols / 32 < 2^32 and whole stages in cols).
+hipError_t launch_mx_quant(int elem, int rceil, int packed, const uint16_t* x, int64_t rows, int64_t cols,
+                           uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 // NVFP4 quantizer (two kernels: global-amax partials, then block quantization).
 // `partials` holds nvfp4_partials_count(rows*cols) uint32 values.
@@ -28,8 +29,9 @@ hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t rows, int64_t cols, uin
                               float* tensor_scale, uint32_t* partials, hipStream_t stream);
 
 // MX GEMM (elem: 1 = E4M3, 2 = E2M1, 3 = E2M3, 4 = E3M2; the FP6 formats
-// need K % 128 == 0 and 4-byte aligned scale rows, else hipErrorInvalidValue).
-hipError_t launch_mx_gemm(int elem, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+// need K % 128 == 0 and 4-byte aligned scale rows, else hipErrorInvalidValue;
+// packed: both operands' scales in the packed layout, which needs the same).
+hipError_t launch_mx_gemm(int elem, int packed, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                           const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
                           const uint16_t* bias, uint16_t* out, hipStream_t stream);
 

@@ -66,13 +66,30 @@ __device__ __forceinline__ void for_chunks(const uint4* __restrict__ x, int64_t 
   }
 }
 
+// Byte offset of the scale of block b (row-major block index, srow blocks per
+// row).  PKS == 0: b itself.  PKS == 1: the packed layout the MX GEMM stages
+// from: rows in groups of 32, each group's scales stage-major with P blocks
+// per row and stage (P = 4: 128 elements of FP8 / FP6; P = 8: 256 elements of
+// FP4), so that one stage's scales of 32 rows are 32 P contiguous bytes.  The
+// host keeps the block count below 2^32 for PKS == 1.
+template <int P, int PKS>
+__device__ __forceinline__ size_t scale_offset(int64_t b, uint32_t srow) {
+  if constexpr (PKS == 0) {
+    return (size_t)b;
+  } else {
+    const uint32_t b32 = (uint32_t)b;
+    const uint32_t row = b32 / srow, kb = b32 - row * srow;
+    return (size_t)(row / 32u) * 32u * srow + (kb / P) * (32u * P) + (row % 32u) * P + kb % P;
+  }
+}
+
 // One lane = one 16-byte chunk (8 consecutive bf16); four lanes = one
 // 32-element block.  nchunks is a multiple of 4 and every quad of lanes
 // starts on a block boundary, so the whole quad is active together.
-template <int ELEM>
+template <int ELEM, int PKS>
 __global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__ x, uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales, int64_t nchunks,
-                                                       int rceil) {
+                                                       int rceil, uint32_t srow) {
   for_chunks(x, nchunks, [&](const uint4& v, int64_t i) {
     uint32_t m = chunk_absmax_bits(v);
     m = max(m, quad_swap1(m));
@@ -95,7 +112,7 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__
     }
     if (ELEM == 1) reinterpret_cast<uint2*>(codes)[i] = make_uint2(lo, hi);
     else reinterpret_cast<uint32_t*>(codes)[i] = lo;
-    if ((i & 3) == 0) scales[i >> 2] = (uint8_t)scale_byte;
+    if ((i & 3) == 0) scales[scale_offset<ELEM == 1 ? 4 : 8, PKS>(i >> 2, srow)] = (uint8_t)scale_byte;
   });
 }
 
@@ -108,9 +125,10 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__
 // (p_t >> 16t) | (p_{t+1} << (48 - 16t)) for t < 3 and zero for t = 3, so
 // one quad shift hands each lane its neighbour's bits and every lane stores
 // one word (a wave writes 512 contiguous bytes).
-template <int ELEM>
+template <int ELEM, int PKS>
 __global__ __launch_bounds__(256) void mx6_quant_kernel(const uint4* __restrict__ x, uint8_t* __restrict__ codes,
-                                                        uint8_t* __restrict__ scales, int64_t nchunks, int rceil) {
+                                                        uint8_t* __restrict__ scales, int64_t nchunks, int rceil,
+                                                        uint32_t srow) {
   for_chunks(x, nchunks, [&](const uint4& v, int64_t i) {
     uint32_t m = chunk_absmax_bits(v);
     m = max(m, quad_swap1(m));
@@ -127,7 +145,7 @@ __global__ __launch_bounds__(256) void mx6_quant_kernel(const uint4* __restrict_
     const uint64_t pn = ((uint64_t)quad_next(hi) << 32) | quad_next(lo);
     const uint64_t word = t == 3u ? 0ull : (p >> (16 * t)) | (pn << (48 - 16 * t));
     reinterpret_cast<uint64_t*>(codes)[i] = word;
-    if (t == 0u) scales[i >> 2] = (uint8_t)scale_byte;
+    if (t == 0u) scales[scale_offset<4, PKS>(i >> 2, srow)] = (uint8_t)scale_byte;
   });
 }
 
@@ -322,20 +340,32 @@ int grid_for(int64_t nchunks, int64_t cap) {
 
 }  // namespace
 
-hipError_t launch_mx_quant(int elem, int rceil, const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
-                           uint8_t* scales, hipStream_t stream) {
+template <int PKS>
+void launch_mx_quant_pks(int elem, int grid, hipStream_t stream, const uint4* xv, uint8_t* codes, uint8_t* scales,
+                         int64_t nchunks, int rceil, uint32_t srow) {
+  if (elem == 1)
+    hipLaunchKernelGGL((mx_quant_kernel<1, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks, rceil,
+                       srow);
+  else if (elem == 2)
+    hipLaunchKernelGGL((mx_quant_kernel<2, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks, rceil,
+                       srow);
+  else if (elem == 3)
+    hipLaunchKernelGGL((mx6_quant_kernel<3, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks,
+                       rceil, srow);
+  else
+    hipLaunchKernelGGL((mx6_quant_kernel<4, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks,
+                       rceil, srow);
+}
+
+hipError_t launch_mx_quant(int elem, int rceil, int packed, const uint16_t* x, int64_t rows, int64_t cols,
+                           uint8_t* codes, uint8_t* scales, hipStream_t stream) {
   const int64_t nchunks = rows * cols / 8;
   if (nchunks == 0) return hipSuccess;
   const int grid = grid_for((nchunks + kBatch - 1) / kBatch, 8192);
   const uint4* xv = (const uint4*)x;
-  if (elem == 1)
-    hipLaunchKernelGGL(mx_quant_kernel<1>, dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks, rceil);
-  else if (elem == 2)
-    hipLaunchKernelGGL(mx_quant_kernel<2>, dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks, rceil);
-  else if (elem == 3)
-    hipLaunchKernelGGL(mx6_quant_kernel<3>, dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks, rceil);
-  else
-    hipLaunchKernelGGL(mx6_quant_kernel<4>, dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks, rceil);
+  const uint32_t srow = (uint32_t)(cols / 32);
+  if (packed) launch_mx_quant_pks<1>(elem, grid, stream, xv, codes, scales, nchunks, rceil, srow);
+  else launch_mx_quant_pks<0>(elem, grid, stream, xv, codes, scales, nchunks, rceil, srow);
   return hipGetLastError();
 }
 

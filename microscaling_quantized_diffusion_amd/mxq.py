@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_PKG_DIR, "libmxq.so")
 
 FORMATS = {"mxfp8": 1, "mxfp4": 2, "nvfp4": 3, "mxfp6_e2m3": 4, "mxfp6_e3m2": 5}
 SCALE_RULES = {"floor": 0, "rceil": 0x100}  # MXQ_SCALE_RCEIL, OR-ed into the format argument
+SCALES_PACKED = 0x200  # MXQ_SCALES_PACKED: MX scales in the GEMM's packed layout (32-row groups, stage-major)
 BLOCK = {"mxfp8": 32, "mxfp4": 32, "nvfp4": 16, "mxfp6_e2m3": 32, "mxfp6_e3m2": 32}
 
 MXQ_OK = 0
@@ -124,6 +125,7 @@ class QTensor:
     scales: torch.Tensor
     tensor_scale: Optional[torch.Tensor]
     K: int
+    scales_packed: bool = False  # scales [32 * ceil(rows / 32), K / 32] in the packed layout of include/mxq.h
 
     @property
     def rows(self) -> int:
@@ -143,17 +145,21 @@ def workspace_bytes(fmt: str, M: int, K: int, fused: bool) -> int:
 
 
 def quantize(fmt: str, x: torch.Tensor, out: Optional[QTensor] = None,
-             workspace: Optional[torch.Tensor] = None, scale_rule: str = "floor") -> QTensor:
-    """mxq_quantize: bf16 [rows, K] -> QTensor (codes, scales, tensor scale)."""
+             workspace: Optional[torch.Tensor] = None, scale_rule: str = "floor",
+             packed_scales: bool = False) -> QTensor:
+    """mxq_quantize: bf16 [rows, K] -> QTensor (codes, scales, tensor scale).  `packed_scales` (MX formats)
+    writes the scales in the packed layout the GEMM fetches whole cache lines of (e.g. for weights quantized
+    once); a given `out` decides by its own `scales_packed`."""
     _require(x, torch.bfloat16, "x")
     rows, K = x.shape
-    f = _fmt(fmt, scale_rule)
     dev = x.device
     if out is None:
         codes = torch.empty((rows, code_cols(fmt, K)), dtype=torch.uint8, device=dev)
-        scales = torch.empty((rows, K // BLOCK[fmt]), dtype=torch.uint8, device=dev)
+        srows = (rows + 31) // 32 * 32 if packed_scales else rows
+        scales = torch.empty((srows, K // BLOCK[fmt]), dtype=torch.uint8, device=dev)
         ts = torch.empty(1, dtype=torch.float32, device=dev) if fmt == "nvfp4" else None
-        out = QTensor(fmt, codes, scales, ts, K)
+        out = QTensor(fmt, codes, scales, ts, K, packed_scales)
+    f = _fmt(fmt, scale_rule) | (SCALES_PACKED if out.scales_packed else 0)
     need = workspace_bytes(fmt, rows, K, False)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -168,10 +174,13 @@ def gemm(a: QTensor, w: QTensor, bias: Optional[torch.Tensor] = None,
     """mxq_gemm: quantized A [M, K] x quantized W [N, K]^T -> bf16 [M, N]."""
     if a.fmt != w.fmt or a.K != w.K:
         raise ValueError("A and W must share format and K")
+    if a.scales_packed != w.scales_packed:
+        raise ValueError("A and W must share the scale layout (both packed or both row-major)")
     M, N = a.rows, w.rows
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.codes.device)
-    _check("mxq_gemm", lib().mxq_gemm(_fmt(a.fmt), M, N, a.K, _ptr(a.codes), _ptr(a.scales), _ptr(a.tensor_scale),
+    f = _fmt(a.fmt) | (SCALES_PACKED if a.scales_packed else 0)
+    _check("mxq_gemm", lib().mxq_gemm(f, M, N, a.K, _ptr(a.codes), _ptr(a.scales), _ptr(a.tensor_scale),
                                       _ptr(w.codes), _ptr(w.scales), _ptr(w.tensor_scale), _ptr(bias), _ptr(out),
                                       _stream(out)))
     return out
@@ -192,9 +201,10 @@ def quant_gemm_fused(a: torch.Tensor, w: QTensor, bias: Optional[torch.Tensor] =
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=a.device)
     wsz = workspace.numel() * workspace.element_size()
+    f = _fmt(w.fmt, scale_rule) | (SCALES_PACKED if w.scales_packed else 0)
     _check("mxq_quant_gemm_fused",
-           lib().mxq_quant_gemm_fused(_fmt(w.fmt, scale_rule), M, N, K, _ptr(a), _ptr(w.codes), _ptr(w.scales),
-                                      _ptr(w.tensor_scale), _ptr(bias), _ptr(out), _ptr(workspace), wsz, _stream(a)))
+           lib().mxq_quant_gemm_fused(f, M, N, K, _ptr(a), _ptr(w.codes), _ptr(w.scales), _ptr(w.tensor_scale),
+                                      _ptr(bias), _ptr(out), _ptr(workspace), wsz, _stream(a)))
     return out
 
 
@@ -218,6 +228,8 @@ def gemm_requant(a: QTensor, w: QTensor, out_fmt: str, bias: Optional[torch.Tens
     values that were quantized.  `out` may hold column slices of wider code / scale matrices."""
     if a.fmt != w.fmt or a.K != w.K:
         raise ValueError("A and W must share format and K")
+    if a.scales_packed or w.scales_packed:
+        raise ValueError("mxq_gemm_requant takes row-major scales")
     if act not in ACTS:
         raise ValueError(f"unknown activation {act!r}")
     M, N = a.rows, w.rows

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert mxq.abi_version() == 7
+    assert mxq.abi_version() == 8
     for s in range(8):
         assert lib.mxq_status_string(s)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -153,7 +153,7 @@ def test_scale_rule_flag(lib):
     assert q(1 | RCEIL, P, 0, 32, P, P, None, None, 0, None) == 0  # empty: accepted format, no-op
     assert q(2 | RCEIL, None, 4, 32, P, P, None, None, 0, None) == 1  # passes the format check
     assert q(3 | RCEIL, P, 4, 32, P, P, P, P, 1 << 20, None) == 2  # NVFP4 has no such rule
-    assert q(1 | 0x200, P, 4, 32, P, P, None, None, 0, None) == 2  # unknown flag bit
+    assert q(1 | 0x400, P, 4, 32, P, P, None, None, 0, None) == 2  # unknown flag bit
     assert q(RCEIL, P, 4, 32, P, P, None, None, 0, None) == 2  # flag without a format
     assert g(1 | RCEIL, 4, 4, 32, None, P, None, P, P, None, None, P, None) == 1  # accepted and ignored
     assert f(2 | RCEIL, 64, 64, 64, P, P, P, None, None, P, None, 0, None) == 5  # passes to the workspace check
@@ -200,3 +200,25 @@ def test_requant_output_strides(lib):
     assert ar(1, 2, 256, 128, P, P, P, 1, None, P, 0, 0, P, need, None) == 1
     assert ar(1, 2, 256, 128, P, P, P, 1, P, P, 0, 0, P, need - 1, None) == 5
     assert ar(0, 2, 256, 128, None, None, None, 1, None, None, 0, 0, None, 0, None) == 0
+
+
+PACKED = 0x200  # MXQ_SCALES_PACKED
+
+
+def test_packed_scale_flag(lib):
+    """The packed scale layout flag: MX formats with whole GEMM stages only, rejected where it has no
+    meaning; every case returns before anything is launched."""
+    q, g, f, r = lib.mxq_quantize, lib.mxq_gemm, lib.mxq_quant_gemm_fused, lib.mxq_gemm_requant
+    assert q(3 | PACKED, P, 4, 128, P, P, P, P, 1 << 20, None) == 2  # NVFP4
+    assert q(1 | PACKED, P, 4, 96, P, P, None, None, 0, None) == 6  # K not whole 128-element stages (FP8)
+    assert q(2 | PACKED, P, 4, 128, P, P, None, None, 0, None) == 6  # K not whole 256-element stages (FP4)
+    assert q(1 | PACKED, P, 0, 128, P, P, None, None, 0, None) == 0  # empty
+    assert g(1 | PACKED, 4, 4, 192, P, P, None, P, P, None, None, P, None) == 6  # K % 128 != 0
+    assert g(1 | PACKED, 4, 4, 128, P, P + 1, None, P, P, None, None, P, None) == 4  # scales not 4-byte aligned
+    need = lib.mxq_workspace_bytes(1, 64, 128, 1)
+    assert lib.mxq_workspace_bytes(1 | PACKED, 64, 128, 1) == need
+    assert lib.mxq_workspace_bytes(1, 33, 128, 1) == 4352 + 256  # codes 33 x 128 (to 256 B), scales 64 x 4
+    assert f(1 | PACKED, 4, 64, 96, P, P, P, None, None, P, P, need, None) == 6  # K % 128 != 0
+    assert f(1 | PACKED, 4, 64, 128, P, P, P + 2, None, None, P, P, need, None) == 4  # W scales not aligned
+    assert r(1 | PACKED, 4, 64, 128, P, P, P, P, None, 0, 1, None, P, P, 0, 0, None) == 2  # not for requant
+    assert r(1, 4, 64, 128, P, P, P, P, None, 0, 1 | PACKED, None, P, P, 0, 0, None) == 2
