@@ -71,16 +71,32 @@ __device__ __forceinline__ void for_chunks(const uint4* __restrict__ x, int64_t 
 // from: rows in groups of 32, each group's scales stage-major with P blocks
 // per row and stage (P = 4: 128 elements of FP8 / FP6; P = 8: 256 elements of
 // FP4), so that one stage's scales of 32 rows are 32 P contiguous bytes.  The
-// host keeps the block count below 2^32 for PKS == 1.
+// host keeps the block count below 2^32 for PKS == 1 and passes the row
+// division as a multiply: row = (t + ((b - t) >> 1)) >> dsh with
+// t = umulhi(b, dmul), exact for every 32-bit b (the round-up method for
+// unsigned division by an invariant integer, Granlund and Montgomery).
+struct RowDiv {
+  uint32_t srow, dmul, dsh;
+};
 template <int P, int PKS>
-__device__ __forceinline__ size_t scale_offset(int64_t b, uint32_t srow) {
+__device__ __forceinline__ size_t scale_offset(int64_t b, const RowDiv& rd) {
   if constexpr (PKS == 0) {
     return (size_t)b;
   } else {
     const uint32_t b32 = (uint32_t)b;
-    const uint32_t row = b32 / srow, kb = b32 - row * srow;
-    return (size_t)(row / 32u) * 32u * srow + (kb / P) * (32u * P) + (row % 32u) * P + kb % P;
+    const uint32_t t = __umulhi(b32, rd.dmul);
+    const uint32_t row = (t + ((b32 - t) >> 1)) >> rd.dsh, kb = b32 - row * rd.srow;
+    return (size_t)(row / 32u) * 32u * rd.srow + (kb / P) * (32u * P) + (row % 32u) * P + kb % P;
   }
+}
+
+// Multiplier and shift of the row division for srow >= 2 blocks per row:
+// l = ceil(log2 srow), dmul = floor(2^32 (2^l - srow) / srow) + 1, dsh = l - 1.
+inline RowDiv row_div(uint32_t srow) {
+  uint32_t l = 0;
+  while ((1ull << l) < srow) ++l;
+  const uint64_t m = (((uint64_t)1 << 32) * (((uint64_t)1 << l) - srow)) / srow + 1;
+  return RowDiv{srow, (uint32_t)m, l - 1};
 }
 
 // One lane = one 16-byte chunk (8 consecutive bf16); four lanes = one
@@ -89,7 +105,7 @@ __device__ __forceinline__ size_t scale_offset(int64_t b, uint32_t srow) {
 template <int ELEM, int PKS>
 __global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__ x, uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales, int64_t nchunks,
-                                                       int rceil, uint32_t srow) {
+                                                       int rceil, RowDiv rd) {
   for_chunks(x, nchunks, [&](const uint4& v, int64_t i) {
     uint32_t m = chunk_absmax_bits(v);
     m = max(m, quad_swap1(m));
@@ -112,7 +128,7 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__
     }
     if (ELEM == 1) reinterpret_cast<uint2*>(codes)[i] = make_uint2(lo, hi);
     else reinterpret_cast<uint32_t*>(codes)[i] = lo;
-    if ((i & 3) == 0) scales[scale_offset<ELEM == 1 ? 4 : 8, PKS>(i >> 2, srow)] = (uint8_t)scale_byte;
+    if ((i & 3) == 0) scales[scale_offset<ELEM == 1 ? 4 : 8, PKS>(i >> 2, rd)] = (uint8_t)scale_byte;
   });
 }
 
@@ -128,7 +144,7 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__
 template <int ELEM, int PKS>
 __global__ __launch_bounds__(256) void mx6_quant_kernel(const uint4* __restrict__ x, uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales, int64_t nchunks, int rceil,
-                                                        uint32_t srow) {
+                                                        RowDiv rd) {
   for_chunks(x, nchunks, [&](const uint4& v, int64_t i) {
     uint32_t m = chunk_absmax_bits(v);
     m = max(m, quad_swap1(m));
@@ -145,7 +161,7 @@ __global__ __launch_bounds__(256) void mx6_quant_kernel(const uint4* __restrict_
     const uint64_t pn = ((uint64_t)quad_next(hi) << 32) | quad_next(lo);
     const uint64_t word = t == 3u ? 0ull : (p >> (16 * t)) | (pn << (48 - 16 * t));
     reinterpret_cast<uint64_t*>(codes)[i] = word;
-    if (t == 0u) scales[scale_offset<4, PKS>(i >> 2, srow)] = (uint8_t)scale_byte;
+    if (t == 0u) scales[scale_offset<4, PKS>(i >> 2, rd)] = (uint8_t)scale_byte;
   });
 }
 
@@ -342,19 +358,19 @@ int grid_for(int64_t nchunks, int64_t cap) {
 
 template <int PKS>
 void launch_mx_quant_pks(int elem, int grid, hipStream_t stream, const uint4* xv, uint8_t* codes, uint8_t* scales,
-                         int64_t nchunks, int rceil, uint32_t srow) {
+                         int64_t nchunks, int rceil, RowDiv rd) {
   if (elem == 1)
     hipLaunchKernelGGL((mx_quant_kernel<1, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks, rceil,
-                       srow);
+                       rd);
   else if (elem == 2)
     hipLaunchKernelGGL((mx_quant_kernel<2, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks, rceil,
-                       srow);
+                       rd);
   else if (elem == 3)
     hipLaunchKernelGGL((mx6_quant_kernel<3, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks,
-                       rceil, srow);
+                       rceil, rd);
   else
     hipLaunchKernelGGL((mx6_quant_kernel<4, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks,
-                       rceil, srow);
+                       rceil, rd);
 }
 
 hipError_t launch_mx_quant(int elem, int rceil, int packed, const uint16_t* x, int64_t rows, int64_t cols,
@@ -363,9 +379,10 @@ hipError_t launch_mx_quant(int elem, int rceil, int packed, const uint16_t* x, i
   if (nchunks == 0) return hipSuccess;
   const int grid = grid_for((nchunks + kBatch - 1) / kBatch, 8192);
   const uint4* xv = (const uint4*)x;
-  const uint32_t srow = (uint32_t)(cols / 32);
-  if (packed) launch_mx_quant_pks<1>(elem, grid, stream, xv, codes, scales, nchunks, rceil, srow);
-  else launch_mx_quant_pks<0>(elem, grid, stream, xv, codes, scales, nchunks, rceil, srow);
+  // packed scales need whole 128- or 256-element stages per row, so srow >= 4
+  const RowDiv rd = packed ? row_div((uint32_t)(cols / 32)) : RowDiv{(uint32_t)(cols / 32), 0u, 0u};
+  if (packed) launch_mx_quant_pks<1>(elem, grid, stream, xv, codes, scales, nchunks, rceil, rd);
+  else launch_mx_quant_pks<0>(elem, grid, stream, xv, codes, scales, nchunks, rceil, rd);
   return hipGetLastError();
 }
 
