@@ -323,7 +323,9 @@ class QuantLinear:
     @classmethod
     def from_weight(cls, fmt: str, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
                     keep_bf16: bool = True, quantize_weight: bool = True) -> "QuantLinear":
-        qw = quantize(fmt, w) if quantize_weight else None
+        # MX weights get the packed scale layout wherever K is whole GEMM stages (the faster GEMM path)
+        packed = fmt != "nvfp4" and w.shape[1] % (256 if fmt == "mxfp4" else 128) == 0
+        qw = quantize(fmt, w, packed_scales=packed) if quantize_weight else None
         return cls(fmt, w if keep_bf16 else None, qw, bias)
 
     def __call__(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,

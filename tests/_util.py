@@ -47,3 +47,16 @@ def bf16_out_to_f64(t):
 
 def log_case(*parts):
     print("CASE", *parts, flush=True)
+
+
+def row_major_scales(q) -> np.ndarray:
+    """A QTensor's scales as a row-major [rows, K/32] numpy array, undoing the packed layout if it has one
+    (block kb of row r at (r // 32) * 32 S + (kb // P) * 32 P + (r % 32) * P + kb % P, P = 8 for MXFP4 else 4)."""
+    s = q.scales.cpu().numpy()
+    if not getattr(q, "scales_packed", False):
+        return s
+    rows, S = q.rows, q.K // 32
+    P = 8 if q.fmt == "mxfp4" else 4
+    r = np.arange(rows)[:, None]
+    kb = np.arange(S)[None, :]
+    return s.reshape(-1)[(r // 32) * 32 * S + (kb // P) * 32 * P + (r % 32) * P + kb % P]

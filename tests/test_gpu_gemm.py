@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from microscaling_quantized_diffusion_amd.inputs import WORKLOADS, bf16_bits_from_f32, make_layer_inputs
-from tests._util import bf16_out_to_f64, gpu_or_skip, log_case, to_dev
+from tests._util import bf16_out_to_f64, gpu_or_skip, log_case, row_major_scales, to_dev
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -55,7 +55,7 @@ def _oracle_ref(fmt, qa, qw, bias=None):
 
 
 def _check_q(fmt, q, oq, rows=None):
-    c, s = q.codes.cpu().numpy(), q.scales.cpu().numpy()
+    c, s = q.codes.cpu().numpy(), row_major_scales(q)
     if rows is not None:
         c, s = c[rows], s[rows]
     assert np.array_equal(s, oq[1]), f"{fmt} scales differ"
