@@ -133,10 +133,10 @@ typedef enum {
  * "Section details").
  *
  * MX formats (OCP MX v1.0 shared exponent): per block of 32, amax = max|x|,
- * e = clamp(floor(log2 amax) - emax, -127, 127) with emax = 8 (E4M3) or
- * 2 (E2M1), e = -127 for an all-zero block; scale byte = e + 127; codes are
- * x / 2^e rounded to nearest-even with saturation at +-448 / +-6 (never NaN);
- * signed zeros keep their sign.  A block holding NaN/Inf gets scale 0xFF and
+ * e = clamp(floor(log2 amax) - emax, -127, 127) with emax = 8 (E4M3), 2 (E2M1,
+ * E2M3) or 4 (E3M2), e = -127 for an all-zero block; scale byte = e + 127;
+ * codes are x / 2^e rounded to nearest-even with saturation at +-448 / +-6 /
+ * +-7.5 / +-28 (never NaN); signed zeros keep their sign.  A block holding NaN/Inf gets scale 0xFF and
  * zero codes.  With MXQ_SCALE_RCEIL, e = clamp(ceil(log2(amax / max_elem)),
  * -127, 127) instead.
  *
@@ -147,11 +147,14 @@ typedef enum {
  * encoding of x / (dec(scale) * ts), each quotient rounded once.  Any NaN/Inf
  * in the tensor gives ts = NaN, scales 0x7F and zero codes.
  *
- *   fmt            MXQ_FMT_*, MX formats optionally | MXQ_SCALE_RCEIL
+ *   fmt            MXQ_FMT_*, MX formats optionally | MXQ_SCALE_RCEIL and / or
+ *                  | MXQ_SCALES_PACKED
  *   x_bf16         device, bf16 [rows, cols], 16-byte aligned
  *   rows, cols     rows >= 0; cols a positive multiple of the block size
- *   codes          device, out: uint8 [rows, cols] (MXFP8) or [rows, cols/2]
- *   scales         device, out: uint8 [rows, cols/32] (MX) or [rows, cols/16]
+ *   codes          device, out: uint8 [rows, cols] (MXFP8, MXFP6) or
+ *                  [rows, cols/2] (FP4)
+ *   scales         device, out: uint8 [rows, cols/32] (MX; packed:
+ *                  [32 ceil(rows/32), cols/32]) or [rows, cols/16] (NVFP4)
  *   tensor_scale   device float[1], out (NVFP4, required); must be NULL for MX
  *   workspace      device scratch of mxq_workspace_bytes(fmt, rows, cols, 0)
  *                  bytes (0 for MX, where it may be NULL)
