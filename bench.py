@@ -406,7 +406,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path runs on a single "
-              "MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+              "MI355X: tokens split across GPUs with no exchange, so one GPU's rate times N bounds the job)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
