@@ -35,6 +35,12 @@ hipError_t launch_mx_gemm(int elem, int packed, int64_t M, int64_t N, int64_t K,
                           const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
                           const uint16_t* bias, uint16_t* out, hipStream_t stream);
 
+// The MX main-path GEMM alone (whole stages: K % 128 == 0, FP4 K % 256 ==
+// 0; 4-byte aligned scale rows), which launch_mx_gemm takes for such shapes.
+hipError_t launch_mx_staged(int elem, int packed, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                            const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                            const uint16_t* bias, uint16_t* out, hipStream_t stream);
+
 // MX GEMM whose epilogue emits the output MX-quantized (out_elem: 1 = E4M3,
 // 2 = E2M1; E8M0 scales per 32 output columns, shared-exponent rule as in
 // launch_mx_quant), after an optional activation (act: 0 none, 1 GELU tanh

@@ -81,6 +81,7 @@ from .gemm import (  # noqa: F401
     bf16_round,
     gelu_tanh,
     gemm_error,
+    gemm_error_rows,
     rounding_mismatch_rate,
     gemm_bf16_ref,
     gemm_mx_ref,

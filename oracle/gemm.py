@@ -126,6 +126,31 @@ def gemm_error(y: np.ndarray, r: np.ndarray) -> float:
     return num / denom
 
 
+def gemm_error_rows(y: np.ndarray, r: np.ndarray) -> float:
+    """gemm_error applied to each row against that row's own max|r|, maximised over the rows.
+
+    The normwise gate divides by the largest |r| of the whole matrix, so an
+    error confined to rows of small magnitude (rows scaled by exp(N(0, 0.5)),
+    or outside the outlier channels) can hide under it; here each row answers
+    for itself.  A row whose reference is all zeros passes only if its outputs
+    are within their own rounding of zero.  Infinite if y holds NaN or Inf.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    if not np.all(np.isfinite(y)):
+        return float("inf")
+    if r.size == 0:
+        return 0.0
+    r2 = r.reshape(r.shape[0], -1)
+    excess = np.maximum(np.abs(y - r) - bf16_half_ulp(y), 0.0).reshape(r2.shape)
+    num = excess.max(axis=1)
+    den = np.abs(r2).max(axis=1)
+    if np.any((den == 0.0) & (num > 0.0)):
+        return float("inf")
+    ok = den > 0.0
+    return float((num[ok] / den[ok]).max()) if np.any(ok) else 0.0
+
+
 def rounding_mismatch_rate(y: np.ndarray, r: np.ndarray, rel: float = 1.0 / 16) -> float:
     """Fraction of the outputs with |r_i| >= rel * max|r| whose bf16 value differs from bf16_round(r_i).
 

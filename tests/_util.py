@@ -60,3 +60,38 @@ def row_major_scales(q) -> np.ndarray:
     r = np.arange(rows)[:, None]
     kb = np.arange(S)[None, :]
     return s.reshape(-1)[(r // 32) * 32 * S + (kb // P) * 32 * P + (r % 32) * P + kb % P]
+
+
+def oracle_rows(fn, bits: np.ndarray, *args, workers: int = 16, chunk: int = 1024):
+    """Apply a row-wise oracle quantizer (MX, or NVFP4 with its tensor scale given) to row chunks of `bits`
+    in a thread pool and concatenate the per-row outputs.  Rows are quantized independently, so the result
+    equals fn(bits, *args); NumPy releases the GIL inside the large array operations, which makes the
+    oracle affordable on full-size tensors.  The oracle itself is unchanged."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    parts = [np.ascontiguousarray(bits[r:r + chunk]) for r in range(0, bits.shape[0], chunk)]
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        res = list(ex.map(lambda p: fn(p, *args), parts))
+    out = [np.concatenate([r[i] for r in res]) for i in range(2)]
+    return tuple(out) + tuple(res[0][2:])
+
+
+def fused_workspace_a(fmt: str, M: int, K: int, ws, packed: bool):
+    """The activation codes [M, code bytes] and row-major scales [M, K/block] that mxq_quant_gemm_fused left
+    in its workspace.  The workspace layout is the library's own: codes at byte 0, then the scales at the next
+    256-byte boundary (MX scales in the packed layout when the weights' scales are packed, with rows padded
+    to whole groups of 32); a change there fails these tests loudly."""
+    cb = M * (K if fmt == "mxfp8" or fmt.startswith("mxfp6") else K // 2)
+    s0 = (cb + 255) // 256 * 256
+    blk = 16 if fmt == "nvfp4" else 32
+    S = K // blk
+    w = ws.cpu().numpy()
+    codes = w[:cb].reshape(M, -1)
+    if not packed:
+        return codes, w[s0:s0 + M * S].reshape(M, S)
+    P = 8 if fmt == "mxfp4" else 4
+    rows = (M + 31) // 32 * 32
+    flat = w[s0:s0 + rows * S]
+    r = np.arange(M)[:, None]
+    kb = np.arange(S)[None, :]
+    return codes, flat[(r // 32) * 32 * S + (kb // P) * 32 * P + (r % 32) * P + kb % P]

@@ -7,7 +7,8 @@ the fp64 reference r computed from the oracle's own codes:
   * codes, scales and tensor scales byte-exact;
   * max_i (|y_i - r_i| - halfulp_bf16(y_i))+ / max|r| <= 2e-3, i.e. the 2e-3
     normwise bound on the result before its bf16 output rounding (that
-    rounding alone may reach 2^-8 = 3.9e-3 of max|r|);
+    rounding alone may reach 2^-8 = 3.9e-3 of max|r|), and the same bound per
+    row against that row's own max|r|;
   * at most 1% of the outputs with |r_i| >= max|r|/16 differ from the
     nearest-even bf16 rounding of r_i (a truncating epilogue fails this)."""
 
@@ -25,10 +26,12 @@ MISMATCH = 0.01
 
 def _gate(y, r):
     err = oracle.gemm_error(y, r)
+    rows = oracle.gemm_error_rows(y, r)
     mis = oracle.rounding_mismatch_rate(y, r)
     raw = oracle.normwise_error(y, r)
-    print(f"gemm_error={err:.3e} raw_normwise={raw:.3e} rounding_mismatch={mis:.4f}", flush=True)
+    print(f"gemm_error={err:.3e} per_row={rows:.3e} raw_normwise={raw:.3e} rounding_mismatch={mis:.4f}", flush=True)
     assert err <= TOL, err
+    assert rows <= TOL, rows
     assert mis <= MISMATCH, mis
 
 

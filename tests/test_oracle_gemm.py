@@ -215,3 +215,49 @@ def test_gelu_tanh_close_to_erf_gelu():
     assert np.max(np.abs(no_cubic - exact)) > 5e-3
     off = 0.5 * x * (1.0 + np.tanh(1.01 * np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
     assert np.max(np.abs(off - exact)) > 1e-3
+
+
+def test_gelu_tanh_matches_torch_float64():
+    """Pinned to an independent implementation of the same tanh-form GELU: torch's CPU
+    gelu(approximate="tanh") in float64, over a dense grid and every finite bf16 value in [-12, 12].
+    Both round 1 + tanh(u), which cancels for large negative x, so the bound is absolute: a few fp64
+    ulps of |x| (2^-50 |x|).  A relative slip of 1e-6 in the cubic coefficient moves the function by
+    ~1e-8 and fails it by orders of magnitude."""
+    import torch
+
+    grid = np.linspace(-12.0, 12.0, 200001)
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    bvals = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    bvals = bvals[np.isfinite(bvals) & (np.abs(bvals) <= 12.0)]
+    x = np.concatenate([grid, bvals])
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    tol = 2.0 ** -50 * np.maximum(np.abs(x), 2.0 ** -30)
+    err = np.abs(gelu_tanh(x) - ref)
+    assert np.all(err <= tol), float(np.max(err / tol))
+    slipped = 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * (1 + 1e-6) * x ** 3)))
+    assert np.max(np.abs(slipped - ref) / tol) > 1e3
+    swapped = 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.047715 * x ** 3)))
+    assert np.max(np.abs(swapped - ref) / tol) > 1e3
+
+
+def test_gemm_error_rows_catches_errors_in_small_rows():
+    """An error confined to a row of small magnitude passes the normwise gate but not the per-row one;
+    correctly rounded outputs pass both; an all-zero reference row requires zero outputs."""
+    from oracle import bf16_round, gemm_error, gemm_error_rows
+
+    rng = np.random.default_rng(3)
+    r = rng.standard_normal((64, 96))
+    r[7] *= 1e-3                                   # a small-magnitude row
+    y = bf16_round(r)
+    assert gemm_error(y, r) == 0.0 and gemm_error_rows(y, r) == 0.0
+    bad = y.copy()
+    bad[7] = bf16_round(r[7] * 1.05)               # 5 % off, but only in the small row
+    assert gemm_error(bad, r) < 2e-3
+    assert gemm_error_rows(bad, r) > 2e-2
+    z = r.copy()
+    z[3] = 0.0
+    assert gemm_error_rows(bf16_round(z), z) == 0.0
+    nz = bf16_round(z)
+    nz[3, 5] = 1e-30
+    assert gemm_error_rows(nz, z) == float("inf")
+    assert gemm_error_rows(np.full_like(r, np.nan), r) == float("inf")
