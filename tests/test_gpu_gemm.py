@@ -1,8 +1,8 @@
 """GPU parity of the GEMM entry points against the CPU oracle.
 
-Small and ragged shapes (several tiles plus partial ones) are compared in full;
-the FLUX-shaped workloads run at full size in the launch configuration the
-benchmark times and are compared on sampled rows and columns.  Gates, against
+Small and ragged shapes (several tiles plus partial ones) are compared in full
+here; the FLUX-shaped workloads are compared in full at their real sizes in
+test_gpu_fullsize.py.  Gates, against
 the fp64 reference r computed from the oracle's own codes:
   * codes, scales and tensor scales byte-exact;
   * max_i (|y_i - r_i| - halfulp_bf16(y_i))+ / max|r| <= 2e-3, i.e. the 2e-3
@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import oracle
-from microscaling_quantized_diffusion_amd.inputs import WORKLOADS, bf16_bits_from_f32, make_layer_inputs
+from microscaling_quantized_diffusion_amd.inputs import bf16_bits_from_f32
 from tests._util import bf16_out_to_f64, gpu_or_skip, log_case, row_major_scales, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -173,76 +173,3 @@ def test_bf16_gemm(M, N, K, dev):
     out = mxq.gemm_bf16(to_dev(a_bits, dev), to_dev(w_bits, dev), to_dev(b_bits, dev))
     torch.cuda.synchronize()
     _gate(bf16_out_to_f64(out), oracle.gemm_bf16_ref(a_bits, w_bits, b_bits))
-
-
-# ------------------------------------------------------------ full size
-
-
-def _sampled_check(fmt, a_bits, w_bits, out, qa_dev, qw_dev, rng, nsamp=48):
-    M, K = a_bits.shape
-    N = w_bits.shape[0]
-    # random rows and columns plus the first and last ones (ragged tile edges)
-    rows = np.union1d(rng.choice(M, size=min(nsamp, M), replace=False), [0, M - 1])
-    cols = np.union1d(rng.choice(N, size=min(nsamp, N), replace=False), [0, N - 1])
-    ts_a = ts_w = None
-    if fmt == "nvfp4":
-        ts_a, ts_w = oracle.nvfp4_tensor_scale(a_bits), oracle.nvfp4_tensor_scale(w_bits)
-    oqa = _oracle_q(fmt, np.ascontiguousarray(a_bits[rows]), ts_a)
-    oqw = _oracle_q(fmt, np.ascontiguousarray(w_bits[cols]), ts_w)
-    if qa_dev is not None:
-        _check_q(fmt, qa_dev, oqa, rows)
-    _check_q(fmt, qw_dev, oqw, cols)
-    ref = _oracle_ref(fmt, oqa, oqw)
-    got = bf16_out_to_f64(out)[np.ix_(rows, cols)]
-    _gate(got, ref)
-
-
-@pytest.mark.parametrize("workload", ["mxfp8_1024", "flux_mlp_up_mxfp8", "flux_single_mxfp4", "flux_2048_nvfp4"])
-def test_full_size_workloads(workload, dev):
-    import torch
-
-    from microscaling_quantized_diffusion_amd import mxq
-
-    for li, layer in enumerate(WORKLOADS[workload].layers):
-        log_case("full", workload, layer.name, layer.M, layer.K, layer.N)
-        a_bits, w_bits = make_layer_inputs(layer, seed=li)
-        a = to_dev(a_bits, dev)
-        qw = mxq.quantize(layer.fmt, to_dev(w_bits, dev))
-        out = mxq.quant_gemm_fused(a, qw)
-        qa = mxq.quantize(layer.fmt, a)  # the fused call's codes, checked on sampled rows
-        torch.cuda.synchronize()
-        rng = np.random.default_rng(li)
-        if workload == "mxfp8_1024":
-            oqa, oqw = _oracle_q(layer.fmt, a_bits), _oracle_q(layer.fmt, w_bits)
-            _check_q(layer.fmt, qa, oqa)
-            _gate(bf16_out_to_f64(out), _oracle_ref(layer.fmt, oqa, oqw))
-        else:
-            _sampled_check(layer.fmt, a_bits, w_bits, out, qa, qw, rng)
-        del a, qw, out, qa
-        torch.cuda.empty_cache()
-
-
-@pytest.mark.parametrize("batch", [1, 4])
-def test_double_block_selective(batch, dev):
-    """One double-stream block's linears: MXFP8 where min(M,K,N) >= 1024, bf16 for the modulation linear."""
-    import torch
-
-    from microscaling_quantized_diffusion_amd import mxq
-
-    for li, layer in enumerate(WORKLOADS[f"flux_double_block_b{batch}"].layers):
-        log_case("block", batch, layer.name, layer.M, layer.K, layer.N)
-        a_bits, w_bits = make_layer_inputs(layer, seed=li)
-        a = to_dev(a_bits, dev)
-        lin = mxq.QuantLinear.from_weight(layer.fmt, to_dev(w_bits, dev),
-                                          quantize_weight=mxq.should_quantize(layer.M, layer.K, layer.N))
-        out = lin(a)
-        torch.cuda.synchronize()
-        rng = np.random.default_rng(li)
-        if mxq.should_quantize(layer.M, layer.K, layer.N):
-            _sampled_check(layer.fmt, a_bits, w_bits, out, None, lin.qweight, rng)
-        else:
-            assert layer.name == "modulation"
-            ref = oracle.gemm_bf16_ref(a_bits, w_bits)
-            _gate(bf16_out_to_f64(out), ref)
-        del a, lin, out
-        torch.cuda.empty_cache()
