@@ -945,9 +945,9 @@ hipError_t launch_mx_gemm(int elem, int packed, int64_t M, int64_t N, int64_t K,
   // workgroup per CU, the time is about (rounds of tiles) x (tile width), so
   // take the width with the smaller product; ties keep 256.
   const bool wide = mx_prefer_wide_tile(M, N, device_cu_count());
-  // 256-wide tiles: the early-published kernel (gemm_mx.hip)
-  if (!wide && scales_aligned && whole_stages)
-    return launch_mx_staged(elem, packed, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+  // the early-published kernel (gemm_mx.hip) where it supports the tile
+  if (scales_aligned && whole_stages && mx_staged_supports(elem, wide))
+    return launch_mx_staged(elem, packed, wide, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
   if (packed) {
     if (!scales_aligned || !whole_stages) return hipErrorInvalidValue;  // callers check the shape first
     return launch_mx_main_elem<1>(elem, wide, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);

@@ -48,12 +48,12 @@ namespace {
 // stage, half 0 then half 1), so both give identical outputs.  Requires
 // whole stages (K % 128 == 0, FP4 K % 256 == 0) and 4-byte aligned scale
 // rows; REQ / ACT / PK as in mxp_gemm_kernel.
-template <int ELEM, int REQ = 0, int ACT = ACT_NONE, int PK = 0, int WM = 4, int WN = 2, int D = 2>
+template <int ELEM, int REQ = 0, int ACT = ACT_NONE, int PK = 0, int WM = 4, int WN = 2, int D = 2, int BN = 256>
 __global__ __launch_bounds__(64 * WM * WN, 1) void mxe_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
     const uint8_t* __restrict__ Ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N,
     int K, uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales, int rceil, int64_t qld, int64_t sld) {
-  constexpr int BM = 256, BN = 256, NW = WM * WN;
+  constexpr int BM = 256, NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TJ = WTM / 32, TI = WTN / 32;  // activation / weight tiles of 32 rows per wave
   constexpr int ROWS = BM + BN;
@@ -308,37 +308,54 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void mxe_gemm_kernel(
   }
 }
 
-template <int ELEM, int REQ, int ACT, int PK>
+template <int ELEM, int REQ, int ACT, int PK, int BN, int D>
 hipError_t launch_mxe(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as, const uint8_t* w,
                       const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream, uint8_t* qcodes,
                       uint8_t* qscales, int rceil, int64_t qld, int64_t sld) {
-  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  constexpr int WM = 4, WN = 2, D = 2;
-  hipLaunchKernelGGL((mxe_gemm_kernel<ELEM, REQ, ACT, PK, WM, WN, D>), dim3((unsigned)tiles), dim3(64 * WM * WN),
-                     0, stream, a, as, w, ws, bias, out, (int)M, (int)N, (int)K, qcodes, qscales, rceil, qld, sld);
+  const int64_t tiles = ((M + 255) / 256) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL((mxe_gemm_kernel<ELEM, REQ, ACT, PK, 4, 2, D, BN>), dim3((unsigned)tiles), dim3(512), 0, stream,
+                     a, as, w, ws, bias, out, (int)M, (int)N, (int)K, qcodes, qscales, rceil, qld, sld);
   return hipGetLastError();
 }
 
+// 256 x 256 tiles with a two-group read lookahead; 256 x 320 tiles (160
+// accumulators per wave) with a one-group lookahead, which is what fits the
+// registers without spilling (FP8 and FP6 only: FP4 at 320 columns spills).
+template <int ELEM, int PK>
+hipError_t launch_mxe_tile(bool wide, int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
+                           const uint8_t* w, const uint8_t* ws, const uint16_t* bias, uint16_t* out,
+                           hipStream_t stream) {
+  if constexpr (ELEM != 2) {
+    if (wide)
+      return launch_mxe<ELEM, 0, ACT_NONE, PK, 320, 1>(M, N, K, a, as, w, ws, bias, out, stream, nullptr, nullptr, 0, 0,
+                                                       0);
+  }
+  return launch_mxe<ELEM, 0, ACT_NONE, PK, 256, 2>(M, N, K, a, as, w, ws, bias, out, stream, nullptr, nullptr, 0, 0,
+                                                   0);
+}
+
 template <int PK>
-hipError_t launch_mxe_elem(int elem, int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
+hipError_t launch_mxe_elem(int elem, bool wide, int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                            const uint8_t* w, const uint8_t* ws, const uint16_t* bias, uint16_t* out,
                            hipStream_t stream) {
   switch (elem) {
-    case 1: return launch_mxe<1, 0, ACT_NONE, PK>(M, N, K, a, as, w, ws, bias, out, stream, nullptr, nullptr, 0, 0, 0);
-    case 2: return launch_mxe<2, 0, ACT_NONE, PK>(M, N, K, a, as, w, ws, bias, out, stream, nullptr, nullptr, 0, 0, 0);
-    case 3: return launch_mxe<3, 0, ACT_NONE, PK>(M, N, K, a, as, w, ws, bias, out, stream, nullptr, nullptr, 0, 0, 0);
-    case 4: return launch_mxe<4, 0, ACT_NONE, PK>(M, N, K, a, as, w, ws, bias, out, stream, nullptr, nullptr, 0, 0, 0);
+    case 1: return launch_mxe_tile<1, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
+    case 2: return launch_mxe_tile<2, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
+    case 3: return launch_mxe_tile<3, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
+    case 4: return launch_mxe_tile<4, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_mx_staged(int elem, int packed, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+bool mx_staged_supports(int elem, bool wide) { return !(wide && elem == 2); }
+
+hipError_t launch_mx_staged(int elem, int packed, bool wide, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                             const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
                             const uint16_t* bias, uint16_t* out, hipStream_t stream) {
-  return packed ? launch_mxe_elem<1>(elem, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream)
-                : launch_mxe_elem<0>(elem, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+  return packed ? launch_mxe_elem<1>(elem, wide, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream)
+                : launch_mxe_elem<0>(elem, wide, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
 }
 
 }  // namespace mxq

@@ -35,9 +35,12 @@ hipError_t launch_mx_gemm(int elem, int packed, int64_t M, int64_t N, int64_t K,
                           const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
                           const uint16_t* bias, uint16_t* out, hipStream_t stream);
 
-// The MX main-path GEMM alone (whole stages: K % 128 == 0, FP4 K % 256 ==
-// 0; 4-byte aligned scale rows), which launch_mx_gemm takes for such shapes.
-hipError_t launch_mx_staged(int elem, int packed, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+// The early-published MX main-path GEMM (gemm_mx.hip): whole stages
+// (K % 128 == 0, FP4 K % 256 == 0) and 4-byte aligned scale rows; wide:
+// 256 x 320 tiles instead of 256 x 256, for the formats where
+// mx_staged_supports(elem, true) holds.
+bool mx_staged_supports(int elem, bool wide);
+hipError_t launch_mx_staged(int elem, int packed, bool wide, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                             const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
                             const uint16_t* bias, uint16_t* out, hipStream_t stream);
 
