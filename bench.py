@@ -6,20 +6,26 @@ with its bf16 epilogue, i.e. one ``mxq_quant_gemm_fused`` call on the FLUX-dev
 MLP up-projection at 1024x1024 (M = 4608 tokens, K = 3072, N = 12288).
 Weights are quantized once before timing.  Inputs rotate through several
 resident copies so the working set exceeds the 256 MB Infinity Cache; the
-same loops with one copy are reported under "hot", and socket power and
-graphics clocks (amd-smi) before, during a ~1.5 s run of the fused call, and
-after under "clocks".  ``--no-hot`` drops both (for counter runs, so that
-every GEMM dispatch belongs to the cold timed loops).
+same loops with one copy are reported under "hot".  The metric's second
+format is timed the same way on the FLUX single-stream linears in MXFP4
+(4608 x 3072 -> 21504 and 4608 x 15360 -> 3072) under "mxfp4".
+
+Timing: every loop is exactly K calls between one pair of HIP events on the
+launch stream, after at least W warm-up calls and at least 1.5 s of warm GPU
+time; per-call p10 / median / p90 come from a separate pass.  The roofline
+figure is the GEMM-only loop; its HBM traffic, clock and MFMA-busy fraction
+come from the committed rocprofv3 counter summary of the same kernel, when
+that summary was taken on the current GEMM sources.  ``--no-hot`` drops the
+hot-cache loops (for counter runs).
 
 Prints ONE JSON line.  ``--all`` adds the other FLUX-shaped workloads
-(MXFP4 single-stream linears, NVFP4 at 2048x2048, one double-stream block
-with selective bf16 fallback) under "extra", and the widened paths:
-producer-fused quantization ("producer_fused"), a block's linears eager vs
-HIP-graphed ("block_sequences"), block-scaled FP8 attention at the FLUX
-shape beside torch's bf16 attention ("attention"), the single-stream
-block's concatenated linear2 input built by the producers' epilogues
-("single_block_concat") and the quantizer under both shared-scale rules
-("scale_rules").
+(MXFP6, NVFP4 at 2048x2048, one double-stream block with selective bf16
+fallback) under "extra", and the widened paths: producer-fused quantization
+("producer_fused"), a block's linears eager vs HIP-graphed
+("block_sequences"), block-scaled FP8 attention at the FLUX shape beside
+torch's bf16 attention ("attention"), the single-stream block's concatenated
+linear2 input built by the producers' epilogues ("single_block_concat") and
+the quantizer under both shared-scale rules ("scale_rules").
 """
 
 from __future__ import annotations
@@ -28,9 +34,7 @@ import argparse
 import hashlib
 import json
 import os
-import subprocess
 import sys
-import threading
 import time
 
 import numpy as np
@@ -43,29 +47,38 @@ METRIC = "block-scaled GEMM TFLOP/s at FLUX DiT shapes (MXFP8/MXFP4); % of MFMA 
 PEAK_TFLOPS = {"mxfp8": 5000.0, "mxfp4": 10100.0, "mxfp6_e2m3": 10100.0, "mxfp6_e3m2": 10100.0, "nvfp4": 2500.0,
                "bf16": 2500.0}
 PEAK_HBM_GBS = 8000.0
-GEMM_SRC = os.path.join(ROOT, "microscaling_quantized_diffusion_amd", "csrc", "gemm.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mxfp8_flux_mlp_up_traffic.txt")
+CSRC = os.path.join(ROOT, "microscaling_quantized_diffusion_amd", "csrc")
+GEMM_SRCS = [os.path.join(CSRC, f) for f in ("gemm.hip", "gemm_mx.hip", "gemm_tile.h")]
+# counter summary of the headline GEMM kernel (HBM traffic, clock and MFMA busy from rocprofv3 --pmc runs)
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "mxe_gemm_mxfp8_flux_mlp_up_counters.txt")
 
 
 def _src_sha() -> str:
-    with open(GEMM_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in GEMM_SRCS:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
-def _traffic_bytes():
-    """HBM bytes per GEMM launch from the committed counter summary, if it matches the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
+def _profile_values(path=COUNTERS_FILE):
+    """key: value pairs of a committed counter summary, if it was taken on the current GEMM sources."""
+    if not os.path.exists(path):
+        return {}
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     if vals.get("gemm_source_sha256_16") != _src_sha():
-        return None
+        return {}
+    return vals
+
+
+def _float_or_none(v):
     try:
-        return float(vals["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
+        return float(v)
+    except (TypeError, ValueError):
         return None
 
 
@@ -75,72 +88,54 @@ def _upload(bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def _time_loop(fn, iters, warmup, dist=None):
-    """Average milliseconds per call, HIP events on torch's current stream (the stream the library launches on).
+WARM_MS = 1500.0  # minimum GPU time of warm-up before any timed loop
 
-    An event is recorded after every call, so ``dist`` (if given) receives the
-    p10 / median / p90 of the per-call times; the average is first to last
-    event over all ``iters`` calls."""
+
+def _time_loop(fn, iters, warmup, dist=None, warm_ms=None):
+    """Average milliseconds per call over exactly `iters` calls, timed with one pair of HIP events on torch's
+    current stream (the stream the library launches on) around the whole loop.
+
+    Before it: `warmup` calls, continued until at least `warm_ms` of GPU time has passed since the first,
+    because the first ~150 calls after an idle period run slower while clocks and power settle.  With `dist`,
+    a separate pass of `iters` calls with an event after each fills dist with the p10 / median / p90 of the
+    per-call times (per-call events perturb the average, so they stay out of the timed loop)."""
     import torch
 
-    for _ in range(warmup):
-        fn(0)
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
-    ev[0].record()
+    warm_ms = WARM_MS if warm_ms is None else warm_ms
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    done = 0
+    while True:
+        batch = max(1, warmup - done) if done < warmup else max(1, min(50, done))
+        for _ in range(batch):
+            fn(done)
+            done += 1
+        e1.record()
+        e1.synchronize()
+        if done >= warmup and e0.elapsed_time(e1) >= warm_ms:
+            break
+    e0.record()
     for i in range(iters):
         fn(i)
-        ev[i + 1].record()
-    torch.cuda.synchronize()
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / iters
     if dist is not None:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        ev[0].record()
+        for i in range(iters):
+            fn(i)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
         per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(iters)])
         dist.update(p10=float(np.percentile(per, 10)), p50=float(np.percentile(per, 50)),
-                    p90=float(np.percentile(per, 90)))
-    return ev[0].elapsed_time(ev[iters]) / iters
+                    p90=float(np.percentile(per, 90)), warmup_calls=done)
+    return ms
 
 
-def smi_sample():
-    """Socket power and graphics clocks from `amd-smi metric --power --clock --json` (a child process)."""
-    try:
-        out = subprocess.run(["amd-smi", "metric", "--power", "--clock", "--json"], capture_output=True, text=True,
-                             timeout=30).stdout
-        d = json.loads(out[out.index("{") if out.lstrip().startswith("{") else out.index("["):])
-        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
-        clks = [v["clk"]["value"] for k, v in g["clock"].items()
-                if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)
-                and isinstance(v["clk"].get("value"), (int, float))]
-        return {"socket_power_W": g["power"]["socket_power"]["value"],
-                "gfx_clk_MHz_mean": round(sum(clks) / len(clks), 1), "gfx_clk_MHz_min": min(clks),
-                "gfx_clk_MHz_max": max(clks)}
-    except Exception as e:  # noqa: BLE001 -- the reading is informational
-        return {"error": f"{type(e).__name__}: {e}"[:200]}
-
-
-def sustained_sample(fn, ms_per_call, seconds=1.5):
-    """Run fn(i) back to back for about `seconds` of GPU time and read power and clocks once meanwhile."""
-    import torch
-
-    n = max(1, int(seconds * 1e3 / max(ms_per_call, 1e-3)))
-    got = {}
-
-    def sampler():
-        time.sleep(seconds / 3)
-        got["s"] = smi_sample()
-
-    th = threading.Thread(target=sampler)
-    t0 = time.perf_counter()
-    th.start()
-    for i in range(n):
-        fn(i)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    th.join()
-    return {**got.get("s", {}), "calls": n, "ms_per_call": round(dt * 1e3 / n, 5)}
-
-
-def run_layer(layer, dev, steps, warmup, rotate, seed=0, sustain_s=0.0):
-    """Time fused / GEMM-only / quantize-only for one linear; returns a dict of figures.  With sustain_s > 0,
-    also runs the fused call back to back for that long and reads power and clocks under that load."""
+def run_layer(layer, dev, steps, warmup, rotate, seed=0):
+    """Time fused / GEMM-only / quantize-only for one linear, as the library is called in production: weights
+    pre-quantized once (MX scales in the packed layout), activations quantized per call.  Returns a dict."""
     import torch
 
     from microscaling_quantized_diffusion_amd import mxq
@@ -178,14 +173,12 @@ def run_layer(layer, dev, steps, warmup, rotate, seed=0, sustain_s=0.0):
     qa = [mxq.quantize(fmt, a, packed_scales=pk) for a in As]
     ms_gemm = _time_loop(lambda i: mxq.gemm(qa[i % rotate], Ws[i % rotate], None, out), steps, warmup, dist_gemm)
     ms_quant = _time_loop(lambda i: mxq.quantize(fmt, As[i % rotate], qa[i % rotate]), steps, warmup)
-    if sustain_s > 0:
-        res["under_load"] = sustained_sample(
-            lambda i: mxq.quant_gemm_fused(As[i % rotate], Ws[i % rotate], None, out, ws), ms_fused, sustain_s)
     # bytes the quantizer writes: MXFP6 stores each 24-byte block in a 32-byte slot
     code_b = M * K * (1.0 if fmt == "mxfp8" or fmt.startswith("mxfp6") else 0.5)
     scale_b = M * K / (16 if fmt == "nvfp4" else 32)
     quant_bytes = M * K * 2 + code_b + scale_b
     res.update(path=fmt, ms=ms_fused, ms_p10=dist_fused["p10"], ms_p50=dist_fused["p50"], ms_p90=dist_fused["p90"],
+               warmup_calls=dist_fused["warmup_calls"],
                gemm_ms_p10=dist_gemm["p10"], gemm_ms_p50=dist_gemm["p50"], gemm_ms_p90=dist_gemm["p90"],
                tflops=flops / ms_fused / 1e9, gemm_ms=ms_gemm,
                gemm_tflops=flops / ms_gemm / 1e9, quant_ms=ms_quant, quant_gbs=quant_bytes / ms_quant / 1e6,
@@ -385,25 +378,29 @@ def cpu_baseline(layer, sample_rows):
 
 
 def main():
+    global WARM_MS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # After an idle period the first ~150 calls of the fused MXFP8 step run 5-30 % slower while the chip's
-    # clocks and power settle (per-call HIP events on the FLUX MLP up-projection: 182 -> 226 us, then 175 us
-    # from about call 200 on); the default warm-up covers that, so the timed steps are the sustained rate.
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=300)
+    # Every timed loop is preceded by at least --warmup calls and at least WARM_MS of GPU time (after an idle
+    # period the first ~150 calls run 5-30 % slower while clocks and power settle).
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotate", type=int, default=8, help="resident input copies cycled through (cold L2/MALL)")
+    ap.add_argument("--warm-ms", type=float, default=WARM_MS,
+                    help="minimum warm GPU time before each timed loop (counter runs pass 0: every dispatch is "
+                         "then serialized and profiled)")
     ap.add_argument("--workload", default="flux_mlp_up_mxfp8")
     ap.add_argument("--all", action="store_true", help="also time the other FLUX-shaped workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hot", action="store_true",
-                    help="skip the hot-cache timing and the power/clock readings (profiling runs: every GEMM "
-                         "dispatch is then one of the cold timed loops)")
+                    help="skip the hot-cache timing (profiling runs: every GEMM dispatch is then one of the cold "
+                         "timed loops)")
     ap.add_argument("--cpu-rows", type=int, default=4608, help="activation rows the CPU oracle runs (capped at M)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, run three plain device-to-device copies of MIB MiB (the reference kernel "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
+    WARM_MS = args.warm_ms
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path runs on a single "
               "MI355X: tokens split across GPUs with no exchange, so one GPU's rate times N bounds the job)",
@@ -419,12 +416,12 @@ def main():
     dev = torch.device("cuda:0")
     layer = WORKLOADS[args.workload].layers[0]
     print(f"# timing {args.workload} {layer.M}x{layer.K}x{layer.N} {layer.fmt}", file=sys.stderr, flush=True)
-    smi_before = None if args.no_hot else smi_sample()
-    r = run_layer(layer, dev, args.steps, args.warmup, args.rotate, sustain_s=0.0 if args.no_hot else 1.5)
+    r = run_layer(layer, dev, args.steps, args.warmup, args.rotate)
 
     flops = 2.0 * layer.M * layer.N * layer.K
     gemm_s = r["gemm_ms"] / 1e3
-    traffic = _traffic_bytes()
+    prof = _profile_values()
+    elem = {"mxfp8": "E4M3", "mxfp4": "E2M1"}.get(layer.fmt, layer.fmt)
     line = {
         "metric": METRIC,
         "value": round(r["tflops"], 2),
@@ -432,6 +429,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_calls_done": r["warmup_calls"],
         "ms_per_step": round(r["ms"], 5),
         "ms_per_step_p10_p50_p90": [round(r["ms_p10"], 5), round(r["ms_p50"], 5), round(r["ms_p90"], 5)],
         "higher_is_better": True,
@@ -445,21 +443,36 @@ def main():
         "pct_of_mfma_peak": round(r["pct_peak_fused"], 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": f"mxp_gemm_kernel<{'FP8' if layer.fmt == 'mxfp8' else 'FP4'}>",
+            "kernel": f"mxe_gemm_kernel<{elem}> (GEMM-only calls, one event pair around the timed loop)",
             "achieved": round(flops / gemm_s / 1e12, 2),
             "peak": PEAK_TFLOPS[layer.fmt],
             "unit": "TFLOP/s",
             "frac": round(flops / gemm_s / 1e12 / PEAK_TFLOPS[layer.fmt], 4),
-            "traffic": traffic,
+            "traffic": _float_or_none(prof.get("hbm_bytes_per_launch")),
             "algorithmic_bytes": layer.M * layer.K + layer.N * layer.K + (layer.M + layer.N) * layer.K // 32
             + layer.M * layer.N * 2,
             "gemm_ms": round(r["gemm_ms"], 5),
             "gemm_ms_p10_p50_p90": [round(r["gemm_ms_p10"], 5), round(r["gemm_ms_p50"], 5),
                                     round(r["gemm_ms_p90"], 5)],
+            "counters": ({k: _float_or_none(prof.get(k)) for k in ("clock_GHz", "mfma_busy_frac",
+                                                                   "kernel_us_in_counter_run")}
+                         | {"source": os.path.relpath(COUNTERS_FILE, ROOT)}) if prof else None,
         },
         "quantizer": {"ms": round(r["quant_ms"], 5), "GB/s": round(r["quant_gbs"], 1),
                       "frac_of_hbm": round(r["quant_gbs"] / PEAK_HBM_GBS, 4)},
     }
+    # the metric's second format: the FLUX single-stream linears in MXFP4 (config 3), same calls and timing
+    line["mxfp4"] = []
+    for i, ly in enumerate(WORKLOADS["flux_single_mxfp4"].layers):
+        print(f"# timing flux_single_mxfp4/{ly.name} {ly.M}x{ly.K}x{ly.N}", file=sys.stderr, flush=True)
+        e = run_layer(ly, dev, args.steps, args.warmup, min(args.rotate, 4), seed=i)
+        line["mxfp4"].append({
+            "layer": ly.name, "M": ly.M, "K": ly.K, "N": ly.N, "rotating_copies": min(args.rotate, 4),
+            "fused_ms": round(e["ms"], 5), "fused_tflops": round(e["tflops"], 2),
+            "gemm_ms": round(e["gemm_ms"], 5), "gemm_tflops": round(e["gemm_tflops"], 2),
+            "gemm_frac_of_fp4_peak": round(e["gemm_tflops"] / PEAK_TFLOPS["mxfp4"], 4),
+            "fused_frac_of_fp4_peak": round(e["tflops"] / PEAK_TFLOPS["mxfp4"], 4),
+            "quant_ms": round(e["quant_ms"], 5), "quant_GB/s": round(e["quant_gbs"], 1)})
     if not args.no_hot:
         # the same loops with one resident input copy (weights and activations stay in L2 / MALL)
         print("# timing the hot-cache case (one input copy)", file=sys.stderr, flush=True)
@@ -467,13 +480,10 @@ def main():
         line["hot"] = {"rotating_copies": 1, "ms_per_step": round(h["ms"], 5), "tflops": round(h["tflops"], 2),
                        "gemm_ms": round(h["gemm_ms"], 5), "gemm_tflops": round(h["gemm_tflops"], 2),
                        "quant_ms": round(h["quant_ms"], 5), "quant_GB/s": round(h["quant_gbs"], 1)}
-        line["clocks"] = {"source": "amd-smi metric --power --clock --json", "before": smi_before,
-                          "under_load": r.get("under_load"), "after": smi_sample()}
     if args.all:
         leg_steps, leg_warm = max(10, args.steps // 2), max(3, args.warmup // 2)
         extra = []
-        for name in ("flux_single_mxfp4", "flux_mlp_up_mxfp6", "flux_2048_nvfp4", "flux_double_block_b1",
-                     "flux_double_block_b4"):
+        for name in ("flux_mlp_up_mxfp6", "flux_2048_nvfp4", "flux_double_block_b1", "flux_double_block_b4"):
             for i, ly in enumerate(WORKLOADS[name].layers):
                 print(f"# timing {name}/{ly.name}", file=sys.stderr, flush=True)
                 e = run_layer(ly, dev, leg_steps, leg_warm, min(args.rotate, 4), seed=i)
