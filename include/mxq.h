@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 8
+#define MXQ_ABI_VERSION 9
 
 typedef enum {
   MXQ_FMT_MXFP8 = 1, /* E4M3 codes, E8M0 scale per 32 K-elements */
@@ -124,7 +124,9 @@ typedef enum {
   MXQ_ERR_ALIGN = 4,       /* a 16-byte-aligned pointer is misaligned */
   MXQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than mxq_workspace_bytes() */
   MXQ_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
-  MXQ_ERR_LAUNCH = 7       /* a kernel launch failed (hipGetLastError after launch) */
+  MXQ_ERR_LAUNCH = 7,      /* a kernel launch failed (hipGetLastError after launch) */
+  MXQ_ERR_TOO_LARGE = 8    /* the problem needs more than the library's fixed scratch array
+                              (mxq_quant_gemm_fused_noalloc) */
 } mxq_status;
 
 /*
@@ -201,6 +203,26 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt, int64_t M, int64_t N, int64_t K,
                                 const void* w_codes, const void* w_scales, const float* w_tensor_scale,
                                 const void* bias_bf16, void* out_bf16, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/*
+ * mxq_quant_gemm_fused without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The activation codes and scales go into
+ * a fixed array inside the library, MXQ_NOALLOC_SCRATCH_BYTES on each GPU the
+ * library runs on, held until the process ends; the call allocates and frees
+ * nothing (the first call on a device only looks up the array's device
+ * address).  Arguments, checks and results are those of
+ * mxq_quant_gemm_fused with the same arguments, bit for bit; a problem whose
+ * mxq_workspace_bytes(fmt, M, K, 1) exceeds MXQ_NOALLOC_SCRATCH_BYTES returns
+ * MXQ_ERR_TOO_LARGE before any launch.  Every call on one GPU uses that GPU's
+ * one array and leaves its contents behind: calls that overlap on the same
+ * GPU (other streams, other host threads) race, and the caller must order
+ * them.
+ */
+#define MXQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+mxq_status mxq_quant_gemm_fused_noalloc(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void* a_bf16,
+                                        const void* w_codes, const void* w_scales, const float* w_tensor_scale,
+                                        const void* bias_bf16, void* out_bf16, void* stream);
 
 /*
  * Block-scaled GEMM whose epilogue emits the next layer's MX-quantized

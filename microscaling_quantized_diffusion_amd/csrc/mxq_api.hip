@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/mxq.h: argument validation,
 // workspace layout and kernel dispatch.  Every check runs before anything is
 // enqueued, so a failing call launches nothing.
+#include <mutex>
 #include <string.h>
 
 #include "mxq_internal.h"
@@ -81,6 +82,31 @@ FusedLayout fused_layout(mxq_format fmt, int64_t M, int64_t K) {
 
 mxq_status launch_status(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_ERR_LAUNCH; }
 
+// The fixed scratch of mxq_quant_gemm_fused_noalloc: one copy per GPU, in
+// the code object's zero-initialised data (nothing is allocated at run
+// time).  In host code `scratch` names a host-side stand-in, not the device
+// array: kernels get the address from hipGetSymbolAddress, looked up once
+// per device with that device current.
+__device__ __align__(256) uint8_t scratch[MXQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array, or nullptr if it
+// cannot be found (no current device, or the lookup failed).
+uint8_t* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = (uint8_t*)ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 // element format of an MX format: 1 = E4M3, 2 = E2M1, 3 = E2M3, 4 = E3M2
 int elem_of(mxq_format fmt) {
   return fmt == MXQ_FMT_MXFP8 ? 1 : fmt == MXQ_FMT_MXFP6_E2M3 ? 3 : fmt == MXQ_FMT_MXFP6_E3M2 ? 4 : 2;
@@ -102,6 +128,7 @@ const char* mxq_status_string(mxq_status s) {
     case MXQ_ERR_WORKSPACE: return "workspace missing or too small";
     case MXQ_ERR_UNSUPPORTED: return "unsupported request";
     case MXQ_ERR_LAUNCH: return "kernel launch failed";
+    case MXQ_ERR_TOO_LARGE: return "problem larger than the library's fixed scratch (MXQ_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -169,10 +196,16 @@ mxq_status mxq_gemm(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K, const v
                                       (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s));
 }
 
-mxq_status mxq_quant_gemm_fused(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K, const void* a_bf16,
-                                const void* w_codes, const void* w_scales, const float* w_tensor_scale,
-                                const void* bias_bf16, void* out_bf16, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+}  // extern "C"
+
+namespace {
+// mxq_quant_gemm_fused's checks and launches with the workspace given by
+// `get_ws`, which is called only once every argument check has passed; it
+// returns the workspace pointer and its size, or a status to return.
+template <typename GetWs>
+mxq_status fused_call(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K, const void* a_bf16, const void* w_codes,
+                      const void* w_scales, const float* w_tensor_scale, const void* bias_bf16, void* out_bf16,
+                      void* stream, GetWs get_ws) {
   mxq_format fmt;
   int rceil, packed;  // packed: W's scales are packed, and A's are written packed into the workspace
   if (!split_format(fmt_arg, &fmt, &rceil, &packed)) return MXQ_ERR_FORMAT;
@@ -187,10 +220,10 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt_arg, int64_t M, int64_t N, int64_
   // the activation scales are in the workspace (256-byte aligned)
   if ((is_fp6(fmt) || packed) && !aligned4(w_scales, w_scales)) return MXQ_ERR_ALIGN;
   const FusedLayout L = fused_layout(fmt, M, K);
-  if (!workspace || workspace_bytes < L.total) return MXQ_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return MXQ_ERR_ALIGN;
+  uint8_t* ws = nullptr;
+  const mxq_status wst = get_ws(L.total, &ws);
+  if (wst != MXQ_OK) return wst;
   hipStream_t s = (hipStream_t)stream;
-  uint8_t* ws = (uint8_t*)workspace;
   uint8_t* a_codes = ws + L.codes;
   uint8_t* a_scales = ws + L.scales;
   hipError_t e;
@@ -207,6 +240,33 @@ mxq_status mxq_quant_gemm_fused(mxq_format fmt_arg, int64_t M, int64_t N, int64_
   e = launch_mx_gemm(elem_of(fmt), packed, M, N, K, a_codes, a_scales, (const uint8_t*)w_codes,
                      (const uint8_t*)w_scales, (const uint16_t*)bias_bf16, (uint16_t*)out_bf16, s);
   return launch_status(e);
+}
+}  // namespace
+
+extern "C" {
+
+mxq_status mxq_quant_gemm_fused(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K, const void* a_bf16,
+                                const void* w_codes, const void* w_scales, const float* w_tensor_scale,
+                                const void* bias_bf16, void* out_bf16, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return fused_call(fmt_arg, M, N, K, a_bf16, w_codes, w_scales, w_tensor_scale, bias_bf16, out_bf16, stream,
+                    [&](size_t need, uint8_t** ws) {
+                      if (!workspace || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
+                      if (!aligned16(workspace)) return MXQ_ERR_ALIGN;
+                      *ws = (uint8_t*)workspace;
+                      return MXQ_OK;
+                    });
+}
+
+mxq_status mxq_quant_gemm_fused_noalloc(mxq_format fmt_arg, int64_t M, int64_t N, int64_t K, const void* a_bf16,
+                                        const void* w_codes, const void* w_scales, const float* w_tensor_scale,
+                                        const void* bias_bf16, void* out_bf16, void* stream) {
+  return fused_call(fmt_arg, M, N, K, a_bf16, w_codes, w_scales, w_tensor_scale, bias_bf16, out_bf16, stream,
+                    [&](size_t need, uint8_t** ws) {
+                      if (need > MXQ_NOALLOC_SCRATCH_BYTES) return MXQ_ERR_TOO_LARGE;
+                      *ws = device_scratch();
+                      return *ws ? MXQ_OK : MXQ_ERR_LAUNCH;
+                    });
 }
 
 namespace {

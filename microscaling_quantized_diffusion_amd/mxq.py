@@ -38,6 +38,7 @@ STATUS_NAMES = {
     5: "MXQ_ERR_WORKSPACE",
     6: "MXQ_ERR_UNSUPPORTED",
     7: "MXQ_ERR_LAUNCH",
+    8: "MXQ_ERR_TOO_LARGE",
 }
 
 # (name, restype, argtypes) of every exported entry point
@@ -46,6 +47,7 @@ SIGNATURES = {
     "mxq_quantize": (_I, [_I, _VP, _I64, _I64, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "mxq_gemm": (_I, [_I, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "mxq_quant_gemm_fused": (_I, [_I, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "mxq_quant_gemm_fused_noalloc": (_I, [_I, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "mxq_gemm_requant": (_I, [_I, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _I, _I, _VP, _VP, _VP, _I64, _I64,
                               _VP]),
     "mxq_attention_fp8_requant": (_I, [_I64, _I64, _I64, _I64, _VP, _VP, _VP, _I, _VP, _VP, _I64, _I64, _VP, _SZ,
@@ -205,6 +207,28 @@ def quant_gemm_fused(a: torch.Tensor, w: QTensor, bias: Optional[torch.Tensor] =
     _check("mxq_quant_gemm_fused",
            lib().mxq_quant_gemm_fused(f, M, N, K, _ptr(a), _ptr(w.codes), _ptr(w.scales), _ptr(w.tensor_scale),
                                       _ptr(bias), _ptr(out), _ptr(workspace), wsz, _stream(a)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MXQ_NOALLOC_SCRATCH_BYTES
+
+
+def quant_gemm_fused_noalloc(a: torch.Tensor, w: QTensor, bias: Optional[torch.Tensor] = None,
+                             out: Optional[torch.Tensor] = None, scale_rule: str = "floor") -> torch.Tensor:
+    """mxq_quant_gemm_fused_noalloc: as quant_gemm_fused, with the activation codes in the library's fixed
+    per-GPU scratch array instead of a workspace (pass `out` to allocate nothing at all).  Calls that
+    overlap on one GPU share that array and race."""
+    _require(a, torch.bfloat16, "a")
+    M, K = a.shape
+    if K != w.K:
+        raise ValueError("K mismatch")
+    N = w.rows
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    f = _fmt(w.fmt, scale_rule) | (SCALES_PACKED if w.scales_packed else 0)
+    _check("mxq_quant_gemm_fused_noalloc",
+           lib().mxq_quant_gemm_fused_noalloc(f, M, N, K, _ptr(a), _ptr(w.codes), _ptr(w.scales),
+                                              _ptr(w.tensor_scale), _ptr(bias), _ptr(out), _stream(a)))
     return out
 
 

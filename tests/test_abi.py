@@ -32,8 +32,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert mxq.abi_version() == 8
-    for s in range(8):
+    assert mxq.abi_version() == 9
+    for s in range(9):
         assert lib.mxq_status_string(s)
     assert b"unknown" in lib.mxq_status_string(99)
 
@@ -98,6 +98,22 @@ def test_fused_argument_errors(lib):
     assert f(1, 64, 64, 64, P, P, P, None, None, P, P + 4, need, None) == 4
     assert f(3, 64, 64, 64, P, P, P, None, None, P, P, 1 << 20, None) == 1
     assert f(1, 0, 64, 64, P, P, P, None, None, P, P, need, None) == 0
+
+
+def test_fused_noalloc_argument_errors(lib):
+    """The allocation-free fused call checks its arguments as the fused call does, and rejects a problem
+    beyond the fixed scratch array before touching the device."""
+    f = lib.mxq_quant_gemm_fused_noalloc
+    assert f(9, 64, 64, 64, P, P, P, None, None, P, None) == 2
+    assert f(1, 64, 64, 48, P, P, P, None, None, P, None) == 3
+    assert f(1, 64, 64, 64, None, P, P, None, None, P, None) == 1
+    assert f(1, 64, 64, 64, P, P, P, None, None, P + 2, None) == 4
+    assert f(3, 64, 64, 64, P, P, P, None, None, P, None) == 1  # NVFP4 needs W's tensor scale
+    assert f(1, 0, 64, 64, P, P, P, None, None, P, None) == 0  # empty: no-op
+    big = lib.mxq_workspace_bytes(1, 8192, 8192, 1)
+    assert big > mxq.NOALLOC_SCRATCH_BYTES
+    assert f(1, 8192, 64, 8192, P, P, P, None, None, P, None) == 8
+    assert b"scratch" in lib.mxq_status_string(8)
 
 
 def test_bf16_argument_errors(lib):
