@@ -9,10 +9,12 @@
 //     axis (one E8M0 scale per 32 tokens of each channel), the microscaling
 //     formats of the aitrends.kr MXFP8/NVFP4 article (Glossary "Microscaling
 //     Formats", "MXFP8");
-//   * scores from the dequantized codes (scaled MFMA, fp32 accumulate), an
-//     online softmax over 64-key tiles in key order, P = exp(s - running max)
-//     encoded as E4M3 at the fixed scale 2^8, O += P V with V's block scales,
-//     the row sum taken over the unquantized P; out = O / l in bf16.
+//   * scores from the dequantized codes (scaled MFMA, fp32 accumulate);
+//     P = exp(s - m) with m the row's maximum score over all keys, encoded as
+//     E4M3 at the fixed scale 2^8; O += P V with V's block scales; the row
+//     sum taken over the unquantized P; out = O / l in bf16.  The maximum is
+//     exact, not a running one: every P code depends on its own score and m
+//     only, whatever order or blocking the keys are visited in.
 //
 // Kernels
 //   vt_quant_kernel   V [S, 128] bf16 -> V^T codes [128, S] and scales
@@ -20,18 +22,21 @@
 //                     channels in LDS; each thread encodes one 32-token block
 //                     of one channel with the quantizer's block encoding.
 //   attn_fp8_kernel   one workgroup = 128 queries of one head (four waves of
-//                     32); key tiles of 64 double-buffered in LDS, filled by
-//                     LDS DMA one tile ahead (K rows and V^T rows XOR-swizzled
-//                     by 16-byte chunk through the DMA source offsets, as in
-//                     the GEMM staging; every wave issues five DMAs per tile).
-//                     Per tile and wave:
+//                     32), two passes over the keys, each through two LDS
+//                     stages filled by LDS DMA one tile ahead (K rows and V^T
+//                     rows XOR-swizzled by 16-byte chunk through the DMA
+//                     source offsets, as in the GEMM staging).
+//     pass 1          K alone, 128 keys per stage: the scores (the same MFMAs
+//                     as pass 2, so the same fp32 values) and their maximum;
+//     pass 2          K and V^T, 64 keys per stage (five DMAs per wave), per
+//                     tile and wave:
 //       S^T = K Q^T    four 32x32x64 scaled MFMAs (K rows are the A operand
 //                      from LDS, the wave's 32 queries the B operand, held in
 //                      registers for the whole loop);
-//       softmax        in the log2 domain: each lane holds 32 scores of one
-//                      query (16 of each 32-key tile), the running max is
-//                      combined with the other lane half by permlane32 swap;
-//                      P codes from v_cvt_scalef32_pk_fp8_f32 at scale 2^-8;
+//       softmax        in the log2 domain with pass 1's maximum: one fused
+//                      multiply-add and one exponential per score, no
+//                      rescaling; P codes from v_cvt_scalef32_pk_fp8_f32 at
+//                      scale 2^-8;
 //       P -> operand   the 32x32 accumulator gives lane half h keys 8i + 4h
 //                      + (0..3); the MFMA's B operand wants keys 16h .. 16h
 //                      + 15 of each 32-key tile, which two permlane32 swaps
@@ -88,6 +93,58 @@ __device__ __forceinline__ float max_half(float v) {
 __device__ __forceinline__ float sum_half(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The B operand of S^T for one 32-query block: lane (r32, q) holds its
+// query's channels 64 s + 16 q + (0..15) and 64 s + 32 + 16 q + (0..15), and
+// the E8M0 scales of channel blocks 2 s + q.
+struct QBlock {
+  uint4 c[2][2];
+  int sc[2];
+};
+__device__ __forceinline__ QBlock load_qblock(const uint8_t* qc, const uint8_t* qs, size_t row, int q) {
+  QBlock b;
+  const uint8_t* qp = qc + row * kD;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    b.c[s][0] = *reinterpret_cast<const uint4*>(qp + 64 * s + 16 * q);
+    b.c[s][1] = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 + 16 * q);
+  }
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(qs + row * 4);
+  b.sc[0] = (int)((w >> (8 * q)) & 0xFFu);
+  b.sc[1] = (int)((w >> (8 * (2 + q))) & 0xFFu);
+  return b;
+}
+
+// Scores of NT 32-key sub-tiles of a stage against NB 32-query blocks:
+// S^T rows krow0 + 32 tt + (0..31) (keys, the A operand from LDS: K rows
+// XOR-swizzled by 16-byte chunk, scales 4 bytes per row at kKsOff) x columns
+// = queries (the B operand, in registers).  Lane (query r32, half q) gets
+// keys krow0 + 32 tt + 8 i + 4 q + (0..3) in elements 4 i + (0..3).  A score
+// is the same fp32 value whichever call forms it: the same two MFMAs on the
+// same operand bytes, at the same row and column of the product.
+template <int NB, int NT>
+__device__ __forceinline__ void key_scores(const uint8_t* b, int krow0, const QBlock (&qb)[NB], int r32, int q,
+                                           att_v16f (&sacc)[NB][NT]) {
+  const int ksw = (r32 >> 1) & 7;  // K row swizzle (invariant under 32-row steps)
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) sacc[j][tt] = att_v16f{};
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const int krow = krow0 + 32 * tt + r32;
+      const uint8_t* kr = b + kKOff + krow * kD;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(kr + (((4 * s + q) ^ ksw) << 4));
+      const uint4 a1 = *reinterpret_cast<const uint4*>(kr + (((4 * s + 2 + q) ^ ksw) << 4));
+      const int ksc = b[kKsOff + krow * 4 + 2 * s + q];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        sacc[j][tt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            att_as_v8i(a0, a1), att_as_v8i(qb[j].c[s][0], qb[j].c[s][1]), sacc[j][tt], 0, 0, 0, ksc, 0, qb[j].sc[s]);
+    }
 }
 
 // Four fp32 values in [0, 1] -> four E4M3 codes of p * 2^8 (one dword, value k in byte k).
@@ -181,17 +238,8 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
   const bool qvalid = qrow < S;
   const int qr = qvalid ? qrow : S - 1;  // rows past S compute on a valid row and store nothing
 
-  // B operand of S^T: this lane's query, channels 64 s + (16 q .. 16 q + 15) and 64 s + 32 + (16 q ..)
-  const uint8_t* qp = qc + ((size_t)bh * S + qr) * kD;
-  uint4 qa[2][2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    qa[s][0] = *reinterpret_cast<const uint4*>(qp + 64 * s + 16 * q);
-    qa[s][1] = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 + 16 * q);
-  }
-  const uint32_t qsw = *reinterpret_cast<const uint32_t*>(qs + ((size_t)bh * S + qr) * 4);
-  const int qsc0 = (int)((qsw >> (8 * q)) & 0xFFu);        // channel block q of the first 64
-  const int qsc1 = (int)((qsw >> (8 * (2 + q))) & 0xFFu);  // block 2 + q
+  // B operand of S^T in pass 2: this wave's 32 queries
+  const QBlock qa[1] = {load_qblock(qc, qs, (size_t)bh * S + qr, q)};
 
   // DMA sources: this head's K codes, K scales, V^T codes and V^T scales
   const uint32_t head_bytes = (uint32_t)S * kD;
@@ -200,16 +248,19 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vtc + (size_t)bh * head_bytes, head_bytes);
   const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vts + (size_t)bh * (S / 64) * (2 * kD), (uint32_t)(S / 64) * (2 * kD));
   // Per-lane source offsets without the tile term.  A wave-wide 16-byte DMA
-  // fills 1 KiB of LDS in lane order: K rows 8 g .. 8 g + 7 (g = 2 wave + u),
-  // V^T rows 16 g .. 16 g + 15; each lane fetches the chunk whose swizzled
-  // position is its own.  Scales: wave 0 the tile's K scales, wave 1 its V^T
+  // fills 1 KiB of LDS in lane order: K rows 8 g .. 8 g + 7 of the tile
+  // (chunk g), V^T rows 16 g .. 16 g + 15; each lane fetches the chunk whose
+  // swizzled position is its own.  K row 8 g + x has swizzle ((8 g + x) >> 1)
+  // & 7 = (4 (g & 1) + (x >> 1)) & 7, so two per-lane K offsets serve every
+  // chunk (kbase[g & 1]; the row term 8 g * 128 goes into the wave-uniform
+  // offset).  Pass 2 scales: wave 0 the tile's K scales, wave 1 its V^T
   // scales (256 bytes each), waves 2 and 3 nothing (out of range, into the sink).
-  uint32_t koff[2], voff[2];
+  uint32_t kbase[2], voff[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
+    const int x = lane >> 3, kp = lane & 7;
+    kbase[u] = (uint32_t)x * kD + (uint32_t)((kp ^ ((4 * u + (x >> 1)) & 7)) << 4);
     const int g = 2 * wave + u;
-    const int kr = 8 * g + (lane >> 3), kp = lane & 7;
-    koff[u] = (uint32_t)kr * kD + (uint32_t)((kp ^ ((kr >> 1) & 7)) << 4);
     const int vr = 16 * g + (lane >> 2), vp = lane & 3;
     voff[u] = (uint32_t)vr * (uint32_t)S + (uint32_t)((vp ^ ((vr >> 2) & 3)) << 4);
   }
@@ -218,60 +269,92 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
   auto issue = [&](auto& st, int kv0) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      lds_dma16(rk, &st[kKOff + 1024 * (2 * wave + u)], koff[u], (uint32_t)kv0 * kD);
+      lds_dma16(rk, &st[kKOff + 1024 * (2 * wave + u)], kbase[u], (uint32_t)(kv0 + 8 * (2 * wave + u)) * kD);
       lds_dma16(rv, &st[kVOff + 1024 * (2 * wave + u)], voff[u], (uint32_t)kv0);
     }
     // tile kv0 / 64 of either scale array starts at byte 4 kv0
     lds_dma4(rsc, &st[kKsOff + 256 * wave], soff, (uint32_t)kv0 * 4);
   };
 
+  const int ntiles = S / kBK;
+
+  // Pass 1: the row maximum of the raw scores over all keys.  A stage holds
+  // 128 K rows (16 KiB over its K and V^T areas; chunk g = 4 wave + u) and
+  // their 512 scale bytes at kKsOff (waves 0 and 1); the tile after the last
+  // one is not loaded.  Wave w takes queries 64 (w & 1) + (0..63) of the
+  // workgroup (two 32-query blocks) against keys 64 (w >> 1) + (0..63) of
+  // each stage: eight MFMAs per stage and wave, as with 32 queries against
+  // all 128 keys, on half the LDS reads.  S is a multiple of 64, so a last
+  // stage past S holds 64 keys (the rest loads as zeros and is not read), all
+  // in the first key half.
+  auto issue_k = [&](auto& st, int kv0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int g = 4 * wave + u;
+      lds_dma16(rk, &st[kKOff + 1024 * g], kbase[u & 1], (uint32_t)(kv0 + 8 * g) * kD);
+    }
+    if (wave < 2) lds_dma4(rks, &st[kKsOff + 256 * wave], (uint32_t)lane * 4, (uint32_t)(kv0 + 64 * wave) * 4);
+  };
+  const int qhalf = wave & 1, khalf = wave >> 1;
+  QBlock qm[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = blockIdx.x * kBQ + 64 * qhalf + 32 * j + r32;
+    qm[j] = load_qblock(qc, qs, (size_t)bh * S + (row < S ? row : S - 1), q);
+  }
+  const int n1 = (S + 127) / 128;
+  float mx[2] = {-INFINITY, -INFINITY};
+  auto mstep = [&](auto& cur, auto& nxt, int t) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (t + 1 < n1) issue_k(nxt, (t + 1) * 128);
+    if (128 * t + 64 * khalf < S) {
+      att_v16f sacc[2][2];
+      key_scores<2, 2>(cur, 64 * khalf, qm, r32, q, sacc);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx[j] = fmaxf(mx[j], sacc[j][tt][r]);
+    }
+  };
+  issue_k(st0, 0);
+  int t = 0;
+  for (; t + 1 < n1; t += 2) {
+    mstep(st0, st1, t);
+    mstep(st1, st0, t + 1);
+  }
+  if (t < n1) mstep(st0, st1, t);
+  // the two key halves' maxima of every query meet in LDS
+  __shared__ float mpart[2][kBQ];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float v = max_half(mx[j]);
+    if (q == 0) mpart[khalf][64 * qhalf + 32 * j + r32] = v;
+  }
+  __builtin_amdgcn_s_barrier();  // every wave has read its last pass-1 stage and written its maxima
+  // p = exp2(s c_log2 - m): the maximum is taken over the raw scores (the
+  // scale c_log2 is positive), so the largest p is 1 up to the rounding of m
+  const float m = fmaxf(mpart[0][32 * wave + r32], mpart[1][32 * wave + r32]) * c_log2;
+
   att_v16f acc[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) acc[c] = att_v16f{};
-  float m = -INFINITY, l = 0.0f;
-  const int ksw = (r32 >> 1) & 7;  // K row swizzle (invariant under 32-row steps)
+  float l = 0.0f;
   const int vsw = (r32 >> 2) & 3;  // V^T row swizzle
-  const int ntiles = S / kBK;
 
-  // One tile: its DMA has landed in `cur` (own wait, then the barrier for
-  // everyone's); the next tile's DMA goes into `nxt`, which every wave has
+  // Pass 2, one tile: its DMA has landed in `cur` (own wait, then the barrier
+  // for everyone's); the next tile's DMA goes into `nxt`, which every wave has
   // finished reading (the last tile reloads itself, so the issue is
-  // unconditional); then scores, softmax and P V from `cur`.
+  // unconditional); then scores, P and P V from `cur`.
   auto step = [&](auto& cur, auto& nxt, int t) {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     issue(nxt, (t + 1 < ntiles ? t + 1 : t) * kBK);
     const uint8_t* b = cur;
-
-    // S^T tiles: keys 32 tt + (0..31) x the wave's 32 queries
-    att_v16f sacc[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) sacc[tt] = att_v16f{};
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int krow = 32 * tt + r32;
-        const uint8_t* kr = b + kKOff + krow * kD;
-        const uint4 a0 = *reinterpret_cast<const uint4*>(kr + (((4 * s + q) ^ ksw) << 4));
-        const uint4 a1 = *reinterpret_cast<const uint4*>(kr + (((4 * s + 2 + q) ^ ksw) << 4));
-        const int ksc = b[kKsOff + krow * 4 + 2 * s + q];
-        sacc[tt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(att_as_v8i(a0, a1),
-                                                                   att_as_v8i(qa[s][0], qa[s][1]), sacc[tt], 0, 0,
-                                                                   0, ksc, 0, s == 0 ? qsc0 : qsc1);
-      }
-
-    // online softmax in the log2 domain: the maximum is taken over the raw
-    // scores (the scale c_log2 is positive) and p = exp2(s c_log2 - m) is one
-    // fused multiply-add and one exponential per score
-    float mx = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[tt][r]);
-    mx = max_half(mx);
-    const float m_new = fmaxf(m, mx * c_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 at the first tile
+    att_v16f sacc[1][2];
+    key_scores<1, 2>(b, 0, qa, r32, q, sacc);
     float ls = 0.0f;
     uint32_t d[2][4];
 #pragma unroll
@@ -281,21 +364,12 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
         float p[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tt][4 * i + u], c_log2, -m_new));
+          p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][tt][4 * i + u], c_log2, -m));
           ls += p[u];
         }
         d[tt][i] = p_codes4(p[0], p[1], p[2], p[3]);
       }
-    l = l * alpha + ls;
-    m = m_new;
-    // once the running maxima settle, alpha is exactly 1 in every lane and the
-    // rescale is skipped (a wave-uniform branch; multiplying by 1 is exact)
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[c][r] *= alpha;
-    }
+    l += ls;
 
     // P codes into the B-operand layout: lane half q holds keys 16 q .. 16 q + 15 of each tile
     uint32_t pw[8];
@@ -318,8 +392,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
   };
 
   issue(st0, 0);
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
+  for (t = 0; t + 1 < ntiles; t += 2) {
     step(st0, st1, t);
     step(st1, st0, t + 1);
   }

@@ -7,7 +7,7 @@ point with a per-token correction of the quantization error, for a 1.16-1.18x
 speed-up.  The pages give no steps, so the following readings (the plainest
 block-scaled FP8 attention consistent with the rest of the pages' microscaling
 recipe) define the method, for one head with queries Q [Sq, D], keys K [Skv, D]
-and values V [Skv, D]:
+and values V [Skv, Dv]:
 
   1. Q and K are MXFP8-quantized along the head dimension D (E4M3 codes, one
      E8M0 scale per 32 channels of each token): the per-token scales correct
@@ -16,15 +16,16 @@ and values V [Skv, D]:
   2. V is MXFP8-quantized along the token axis (one E8M0 scale per 32
      consecutive tokens of each channel), the contraction axis of P V;
   3. scores s = Q^ K^T / sqrt(D) from the dequantized operands, exactly;
-  4. softmax online over key tiles of `kv_tile` keys in key order (the order a
-     single-pass kernel visits them): running max m, p = exp(s - m) <= 1,
-     accumulator and row sum rescaled by exp(m_old - m_new);
+  4. the plain softmax numerator p = exp(s - m) with m the exact maximum of
+     the query's scores over all keys, so 0 < p <= 1 and the largest p is 1;
   5. p is E4M3-quantized with the fixed scale 2**8 (p * 256 <= 256 < 448, so
      never saturated), and P^ V^ is accumulated;
-  6. the row sum l accumulates the unquantized p; the output is acc / l.
+  6. the row sum l is that of the unquantized p; the output is (P^ V^) / l.
 
-Everything is float64; the only approximations are the format encodings the
-method itself applies (steps 1, 2, 5) and float64 summation.
+No key tiling enters the definition: every P code depends only on its own
+score and the row's maximum.  Everything is float64; the only approximations
+are the format encodings the method itself applies (steps 1, 2, 5) and
+float64 summation.
 """
 
 from __future__ import annotations
@@ -68,113 +69,83 @@ def quantize_p(p: np.ndarray) -> np.ndarray:
     return decode_e4m3(encode(E4M3, np.ldexp(p, P_SCALE_EXP))) * 2.0 ** -P_SCALE_EXP
 
 
-def online_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, kv_tile: int = 64,
-                     quantize_probs: bool = True) -> np.ndarray:
-    """Steps 3-6 on float64 operands (one head): the online softmax over key tiles in order."""
-    Sq, D = q.shape
-    Skv = k.shape[0]
-    c = 1.0 / math.sqrt(D)
-    m = np.full(Sq, -np.inf)
-    l = np.zeros(Sq)
-    acc = np.zeros((Sq, v.shape[1]))
-    for t0 in range(0, Skv, kv_tile):
-        s = (q @ k[t0:t0 + kv_tile].T) * c
-        m_new = np.maximum(m, s.max(axis=1))
-        alpha = np.exp(m - m_new)  # 0 at the first tile (m = -inf)
-        p = np.exp(s - m_new[:, None])
-        ph = quantize_p(p) if quantize_probs else p
-        acc = acc * alpha[:, None] + ph @ v[t0:t0 + kv_tile]
-        l = l * alpha + p.sum(axis=1)
-        m = m_new
-    return acc / l[:, None]
+def softmax_numerators(q: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """Steps 3-4: p = exp(s - max over all keys of s), s = q k^T / sqrt(D); [Sq, Skv] float64."""
+    s = (q @ k.T) / math.sqrt(q.shape[1])
+    return np.exp(s - s.max(axis=1, keepdims=True))
 
 
-def attention_fp8_ref(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, kv_tile: int = 64,
-                      rows=None) -> np.ndarray:
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, quantize_probs: bool = True) -> np.ndarray:
+    """Steps 3-6 on the dequantized float64 operands of one head; with quantize_probs=False, step 5 is
+    left out (plain softmax attention of the dequantized operands)."""
+    p = softmax_numerators(q, k)
+    ph = quantize_p(p) if quantize_probs else p
+    return (ph @ v) / p.sum(axis=1, keepdims=True)
+
+
+def attention_fp8_ref(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, rows=None) -> np.ndarray:
     """The block-scaled FP8 attention of one head from bf16 bit patterns [S, D]; float64 [Sq, D].
 
     `rows` (optional) restricts the output to those query rows (each row is independent)."""
     t = quantize_qkv(q_bits, k_bits, v_bits)
     q = t["q"] if rows is None else t["q"][np.asarray(rows)]
-    return online_attention(q, t["k"], t["v"], kv_tile, True)
+    return attend(q, t["k"], t["v"], True)
 
 
 # E4M3 values >= 0 in increasing order (for the neighbours of a midpoint)
 _E4M3_GRID = np.unique(decode_e4m3(np.arange(0x7F)))
+_E4M3_MIDS = (_E4M3_GRID[1:] + _E4M3_GRID[:-1]) / 2
+
+
+def _ambiguous(q: np.ndarray, k: np.ndarray, score_eta: float, exp_eta: float):
+    """For every (query, key): p, whether p * 2^8 lies within the floating-point error bound of an E4M3
+    midpoint, and the two E4M3 neighbours (lo, hi) of that nearest midpoint."""
+    c = 1.0 / math.sqrt(q.shape[1])
+    A = np.abs(q) @ np.abs(k).T
+    # relative bound on p, per row: the score's error and that of the row maximum (each up to
+    # c * score_eta * max_j A), plus the exponential and the scaling
+    tol = c * score_eta * 2.0 * A.max(axis=1) + exp_eta
+    p = softmax_numerators(q, k)
+    x = np.ldexp(p, P_SCALE_EXP)
+    i = np.clip(np.searchsorted(_E4M3_MIDS, x), 1, len(_E4M3_MIDS) - 1)
+    mid = np.where(np.abs(_E4M3_MIDS[i - 1] - x) < np.abs(_E4M3_MIDS[i] - x), _E4M3_MIDS[i - 1], _E4M3_MIDS[i])
+    idx = np.searchsorted(_E4M3_GRID, mid)
+    near = np.abs(x - mid) <= x * tol[:, None]
+    return p, near, _E4M3_GRID[idx - 1], _E4M3_GRID[idx]
 
 
 def p_code_slack(q: np.ndarray, k: np.ndarray, v: np.ndarray, score_eta: float, exp_eta: float = 2.0 ** -20,
-                 kv_tile: int = 64, forced=None):
+                 forced=None):
     """Bound of what a valid other rounding of near-midpoint P codes can change in the output.
 
     Step 5 rounds p * 2^8 to E4M3, a decision taken from floating-point scores.
     A kernel that forms each score in a float accumulator of unit roundoff u
     over D products errs by at most gamma_D sum_d |q_d k_d| with gamma_D about
     D u (the recursive-summation bound), in the score itself and in the row's
-    running maximum.  `score_eta` is that relative bound (D * 2^-24 for fp32
-    and D = 128); `exp_eta` covers the exponential and the scaling.  For each
-    key whose p * 2^8 lies within the resulting relative distance of an E4M3
-    midpoint, either neighbour is a correct code; the returned slack [Sq, D]
-    sums, per output, one E4M3 step (divided by 2^8) times |v_j| rescaled to
-    the final maximum and divided by the final row sum, over those keys.
+    maximum.  `score_eta` is that relative bound (D * 2^-24 for fp32 and
+    D = 128); `exp_eta` covers the exponential and the scaling.  For each key
+    whose p * 2^8 lies within the resulting relative distance of an E4M3
+    midpoint, either neighbour is a correct code; the returned slack [Sq, Dv]
+    sums, per output, one E4M3 step (divided by 2^8) times |v_j| divided by
+    the row sum, over those keys.
 
     `forced` (optional, for checking the bound): a set of (row, key) pairs
     whose code is taken as the other neighbour of the nearest midpoint; the
     function then also returns the output computed with those codes.
     Returns (slack, out_forced or None)."""
-    Sq, D = q.shape
-    Skv = k.shape[0]
-    c = 1.0 / math.sqrt(D)
-    A = np.abs(q) @ np.abs(k).T
-    tol = c * score_eta * 2.0 * A.max(axis=1) + exp_eta  # relative bound on p, per row
-    mids = (_E4M3_GRID[1:] + _E4M3_GRID[:-1]) / 2
-    m = np.full(Sq, -np.inf)
-    l = np.zeros(Sq)
-    contrib = np.zeros((Sq, v.shape[1]))
-    acc = np.zeros((Sq, v.shape[1]))
-    for t0 in range(0, Skv, kv_tile):
-        s = (q @ k[t0:t0 + kv_tile].T) * c
-        m_new = np.maximum(m, s.max(axis=1))
-        alpha = np.exp(m - m_new)
-        p = np.exp(s - m_new[:, None])
-        x = np.ldexp(p, P_SCALE_EXP)
-        i = np.clip(np.searchsorted(mids, x), 1, len(mids) - 1)
-        near_mid = np.where(np.abs(mids[i - 1] - x) < np.abs(mids[i] - x), mids[i - 1], mids[i])
-        idx = np.searchsorted(_E4M3_GRID, near_mid)
-        step = _E4M3_GRID[idx] - _E4M3_GRID[idx - 1]
-        near = np.abs(x - near_mid) <= x * tol[:, None]
-        contrib = contrib * alpha[:, None] + (near * step * 2.0 ** -P_SCALE_EXP) @ np.abs(v[t0:t0 + kv_tile])
-        ph = quantize_p(p)
-        if forced:
-            for (r, j) in forced:
-                if t0 <= j < t0 + kv_tile:
-                    jj = j - t0
-                    lo, hi = _E4M3_GRID[idx[r, jj] - 1], _E4M3_GRID[idx[r, jj]]
-                    cur = ph[r, jj] * 2.0 ** P_SCALE_EXP
-                    ph[r, jj] = (hi if cur == lo else lo) * 2.0 ** -P_SCALE_EXP
-        acc = acc * alpha[:, None] + ph @ v[t0:t0 + kv_tile]
-        l = l * alpha + p.sum(axis=1)
-        m = m_new
-    slack = contrib / l[:, None]
-    return slack, (acc / l[:, None] if forced else None)
+    p, near, lo, hi = _ambiguous(q, k, score_eta, exp_eta)
+    l = p.sum(axis=1)
+    slack = ((near * (hi - lo) * 2.0 ** -P_SCALE_EXP) @ np.abs(v)) / l[:, None]
+    if not forced:
+        return slack, None
+    ph = quantize_p(p)
+    for (r, j) in forced:
+        cur = ph[r, j] * 2.0 ** P_SCALE_EXP
+        ph[r, j] = (hi[r, j] if cur == lo[r, j] else lo[r, j]) * 2.0 ** -P_SCALE_EXP
+    return slack, (ph @ v) / l[:, None]
 
 
-def near_midpoint_keys(q: np.ndarray, k: np.ndarray, score_eta: float, exp_eta: float = 2.0 ** -20,
-                       kv_tile: int = 64):
+def near_midpoint_keys(q: np.ndarray, k: np.ndarray, score_eta: float, exp_eta: float = 2.0 ** -20):
     """The (row, key) pairs whose P code p_code_slack treats as ambiguous."""
-    Sq, D = q.shape
-    c = 1.0 / math.sqrt(D)
-    A = np.abs(q) @ np.abs(k).T
-    tol = c * score_eta * 2.0 * A.max(axis=1) + exp_eta
-    mids = (_E4M3_GRID[1:] + _E4M3_GRID[:-1]) / 2
-    out = []
-    m = np.full(Sq, -np.inf)
-    for t0 in range(0, k.shape[0], kv_tile):
-        s = (q @ k[t0:t0 + kv_tile].T) * c
-        m = np.maximum(m, s.max(axis=1))
-        x = np.ldexp(np.exp(s - m[:, None]), P_SCALE_EXP)
-        i = np.clip(np.searchsorted(mids, x), 1, len(mids) - 1)
-        d = np.minimum(np.abs(mids[i - 1] - x), np.abs(mids[i] - x))
-        for r, j in zip(*np.nonzero(d <= x * tol[:, None])):
-            out.append((int(r), int(t0 + j)))
-    return out
+    _, near, _, _ = _ambiguous(q, k, score_eta, exp_eta)
+    return [(int(r), int(j)) for r, j in zip(*np.nonzero(near))]

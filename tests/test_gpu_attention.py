@@ -3,7 +3,7 @@
 The probabilities' E4M3 codes are decisions taken from floating-point scores:
 the kernel forms each score in the MFMA's fp32 accumulator, the oracle in
 fp64.  Where an unquantized p * 2^8 lies within the fp32 accumulation bound
-(D * 2^-24 of sum_d |q_d k_d|, for the score and the row's running maximum)
+(D * 2^-24 of sum_d |q_d k_d|, for the score and the row's maximum)
 of an E4M3 midpoint, both neighbours are correct codes; the oracle's
 p_code_slack bounds what the other choice changes in each output (about 0.3 %
 of the keys are such keys on these inputs).
@@ -61,12 +61,12 @@ def _gate(y, r, slack):
 def _check_head(out_head, q, k, v, rows=None):
     tq = att.quantize_qkv(q, k, v)
     qd = tq["q"] if rows is None else tq["q"][np.asarray(rows)]
-    r = att.online_attention(qd, tq["k"], tq["v"], 64, True)
+    r = att.attend(qd, tq["k"], tq["v"])
     slack, _ = att.p_code_slack(qd, tq["k"], tq["v"], ETA)
     amb = len(att.near_midpoint_keys(qd, tq["k"], ETA))
     y = bf16_out_to_f64(out_head)
     err = _gate(y, r, slack)
-    err_unq = _gate(y, att.online_attention(qd, tq["k"], tq["v"], 64, quantize_probs=False), slack)
+    err_unq = _gate(y, att.attend(qd, tq["k"], tq["v"], quantize_probs=False), slack)
     print(f"attention error {err:.3e} (vs P unquantized {err_unq:.3e}), ambiguous P codes {amb} of "
           f"{qd.shape[0] * tq['k'].shape[0]}", flush=True)
     assert amb <= 0.01 * qd.shape[0] * tq["k"].shape[0]
@@ -89,6 +89,20 @@ def test_attention_peaked_scores(dev):
     """Larger Q and K make each query attend to a few keys (max-dominated rows)."""
     log_case("attention peaked")
     q, k, v = _inputs(1, 2, 256, seed=3, spread=3.0)
+    out = _run(q, k, v, dev).cpu()
+    for h in range(2):
+        _check_head(out[0, h], q[0, h], k[0, h], v[0, h])
+
+
+def test_attention_max_in_last_key_tile(dev):
+    """Every query's largest score is on the last key (channel 0 of Q is 3 and of that key 24), which sits
+    in the last, half-filled 128-key tile of the maximum pass at S = 320: the P codes of all earlier keys
+    are taken relative to it."""
+    log_case("attention max in last tile")
+    q, k, v = _inputs(1, 2, 320, seed=13)
+    q, k = q.copy(), k.copy()
+    q[..., 0] = bf16_bits_from_f32(np.full((1,), 3.0, dtype=np.float32))[0]
+    k[..., -1, 0] = bf16_bits_from_f32(np.full((1,), 24.0, dtype=np.float32))[0]
     out = _run(q, k, v, dev).cpu()
     for h in range(2):
         _check_head(out[0, h], q[0, h], k[0, h], v[0, h])

@@ -1,11 +1,15 @@
 """Pins for the oracle's block-scaled FP8 attention.
 
-Pinned by: the textbook softmax attention (online bookkeeping with P
-unquantized, several tile sizes, a ragged last tile), a closed form (equal
-scores give the mean of V), an exact power-of-two scaling invariant of V, a
-direct single-tile formula whose P encoding is an argmin over the E4M3 code
-table (the exact reference's encoder), the token axis of V's block scales, and
-the size of the quantization error against unquantized attention.
+Pinned by: torch's scaled_dot_product_attention in float64 on the CPU (the
+plain softmax attention, with Sq != Skv and Dv != D so that a transposed
+operand or a wrong scale fails), a closed form (equal scores give the mean of
+V), a second closed form (one dominant key: P is one-hot after encoding, while
+the row sum keeps every unquantized p), an exact power-of-two scaling
+invariant of V, invariance under permuting whole 32-token key blocks (which a
+P relative to a running maximum over key tiles would break), a direct formula
+whose P encoding is an argmin over the E4M3 code table (the exact reference's
+encoder), the token axis of V's block scales, and the size of the quantization
+error against unquantized attention.
 """
 
 import math
@@ -31,15 +35,23 @@ def _qkv(rng, S, D=128, spread=1.0):
     return q, k, v
 
 
-@pytest.mark.parametrize("tile", [16, 64, 100])
-def test_online_softmax_equals_textbook(tile):
-    """With P unquantized, the online algorithm is exact algebra: any tile size (100 leaves a ragged
-    last tile) reproduces softmax(q k^T / sqrt(D)) v to float64 rounding."""
+def _sdpa(q, k, v):
+    import torch
+
+    t = [torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))[None, None] for x in (q, k, v)]
+    return torch.nn.functional.scaled_dot_product_attention(*t)[0, 0].numpy()
+
+
+def test_attend_unquantized_equals_torch_sdpa():
+    """With step 5 left out, the oracle is plain softmax attention: torch's scaled_dot_product_attention
+    (math path, float64, CPU) on 70 queries, 300 keys, D = 64 and Dv = 48."""
     rng = np.random.default_rng(1)
-    q, k, v = (rng.standard_normal((300, 64)) * s for s in (2.0, 2.0, 1.0))
-    got = att.online_attention(q, k, v, kv_tile=tile, quantize_probs=False)
-    want = att.attention_ref(q, k, v)
-    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+    q, k = (rng.standard_normal((n, 64)) * 2.0 for n in (70, 300))
+    v = rng.standard_normal((300, 48))
+    want = _sdpa(q, k, v)
+    for got in (att.attend(q, k, v, quantize_probs=False), att.attention_ref(q, k, v)):
+        assert got.shape == (70, 48)
+        assert np.max(np.abs(got - want)) <= 1e-13 * np.max(np.abs(want))
 
 
 def test_equal_scores_give_the_mean_of_v():
@@ -66,22 +78,60 @@ def test_v_power_of_two_scaling_is_exact():
     assert np.array_equal(b, a * 256.0)
 
 
-def test_single_tile_direct_formula():
-    """One key tile: O = sum_j p^_j v_j / sum_j p_j with p = exp(s - max s) and p^ the nearest E4M3
-    value of p * 2^8 (argmin over the code table, ties to the even code) divided by 2^8."""
+def test_direct_formula_with_argmin_encoder():
+    """O = sum_j p^_j v_j / sum_j p_j with p = exp(s - max over all keys of s) and p^ the nearest E4M3
+    value of p * 2^8 (argmin over the code table, ties to the even code) divided by 2^8; 64 queries
+    against 160 keys."""
     rng = np.random.default_rng(4)
-    S, D = 64, 128
-    q, k, v = _qkv(rng, S, spread=1.5)
-    t = att.quantize_qkv(q, k, v)
-    s = t["q"] @ t["k"].T / math.sqrt(D)
+    q = _bits(rng.standard_normal((64, 128)) * 1.5)
+    k = _bits(rng.standard_normal((160, 128)) * 1.5)
+    v = _bits(rng.standard_normal((160, 128)))
+    t = att.quantize_qkv(_bits(rng.standard_normal((160, 128))), k, v)
+    tq = att.quantize_qkv(q, q, q)
+    s = tq["q"] @ t["k"].T / math.sqrt(128)
     p = np.exp(s - s.max(axis=1, keepdims=True))
+    table = dict(exact.e4m3_table())
     ph = np.empty_like(p)
     for idx, val in np.ndenumerate(p):
-        code = exact.e4m3_encode(Fraction(float(val)) * 256, False)
-        ph[idx] = float(dict(exact.e4m3_table())[code]) / 256.0
+        ph[idx] = float(table[exact.e4m3_encode(Fraction(float(val)) * 256, False)]) / 256.0
     want = (ph @ t["v"]) / p.sum(axis=1, keepdims=True)
-    got = att.attention_fp8_ref(q, k, v, kv_tile=64)
+    got = att.attend(tq["q"], t["k"], t["v"])
     assert np.max(np.abs(got - want)) <= 1e-13 * np.max(np.abs(want))
+
+
+def test_one_dominant_key():
+    """Query 4 e_0 and key 0 = 64 e_0 give score 256 / sqrt(128) = 22.6; every other key is orthogonal
+    to the query (score 0), so its p = exp(-22.6) < 2^-18 encodes to 0 at the scale 2^8.  P^ is one-hot
+    and the output is v^_0 / l, where l = 1 + 191 exp(-22.6) keeps the unquantized p (a row sum of
+    the quantized p would give v^_0 exactly)."""
+    rng = np.random.default_rng(9)
+    S, D = 192, 128
+    q = np.zeros((1, D))
+    q[0, 0] = 4.0
+    k = rng.standard_normal((S, D))
+    k[:, 0] = 0.0
+    k[0] = 0.0
+    k[0, 0] = 64.0
+    t = att.quantize_qkv(_bits(np.repeat(q, S, axis=0)), _bits(k), _bits(rng.standard_normal((S, D))))
+    got = att.attend(t["q"][:1], t["k"], t["v"])
+    pe = math.exp(-256.0 / math.sqrt(D))
+    want = t["v"][0] / (1.0 + (S - 1) * pe)
+    assert np.max(np.abs(got[0] - want)) <= 1e-15 * np.max(np.abs(want))
+    assert np.max(np.abs(got[0] - t["v"][0])) > 1e-9 * np.max(np.abs(want))
+
+
+def test_key_block_permutation_invariance():
+    """Permuting whole 32-token blocks of K and V together permutes V's block scales with them and
+    leaves every P code unchanged (each depends on its score and the row's maximum only), so the
+    output moves by float64 summation order alone.  A P taken relative to a running maximum over key
+    tiles changes with the key order by whole E4M3 steps."""
+    rng = np.random.default_rng(10)
+    S = 256
+    q, k, v = _qkv(rng, S, spread=1.5)
+    perm = np.concatenate([np.arange(32 * b, 32 * b + 32) for b in (5, 2, 7, 0, 3, 6, 1, 4)])
+    a = att.attention_fp8_ref(q, k, v)
+    b = att.attention_fp8_ref(q, k[perm], v[perm])
+    assert np.max(np.abs(a - b)) <= 1e-13 * np.max(np.abs(a))
 
 
 def test_v_scales_run_along_tokens():
@@ -136,7 +186,7 @@ def test_p_code_slack_covers_each_other_rounding():
     keys = att.near_midpoint_keys(t["q"], t["k"], eta)
     assert 5 <= len(keys) <= 0.05 * 192 * 192
     slack, _ = att.p_code_slack(t["q"], t["k"], t["v"], eta)
-    base = att.online_attention(t["q"], t["k"], t["v"])
+    base = att.attend(t["q"], t["k"], t["v"])
     for rk in keys[:40]:
         _, forced = att.p_code_slack(t["q"], t["k"], t["v"], eta, forced={rk})
         d = np.abs(forced - base)
