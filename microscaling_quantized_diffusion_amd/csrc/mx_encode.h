@@ -105,24 +105,23 @@ __device__ __forceinline__ uint32_t mx_encode_fp4x4(uint32_t into, uint32_t w0, 
   return into;
 }
 
-// Eight bf16 values (four dwords, element order low half first) -> eight
-// E2M3 (ELEM 3) / E3M2 (ELEM 4) codes of x / 2^e, element j at bits 6j of the
-// 48-bit result (lo: bits 0..31, hi: bits 32..47).  The gfx950 conversions
-// v_cvt_scalef32_pk32_fp6_bf16 / _bf6_bf16 (32 elements, element j at bits 6j
-// of six dwords, dividing by the scale operand) were measured equal to the
-// RNE-saturating encoding for every finite bf16 and every e in [-127, 127],
-// with the sign of zero kept.  The 24 unused inputs are zeros (code 0).
+// One 32-element block (four chunks of eight bf16, element order low half
+// first) -> its E2M3 (ELEM 3) / E3M2 (ELEM 4) codes of x / 2^e, element j at
+// bits 6 j of six dwords.  The gfx950 conversions
+// v_cvt_scalef32_pk32_fp6_bf16 / _bf6_bf16 (dividing by the scale operand)
+// were measured equal to the RNE-saturating encoding for every finite bf16
+// and every e in [-127, 127], with the sign of zero kept.
 template <int ELEM>
-__device__ __forceinline__ void mx_encode_fp6x8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, int e,
-                                                uint32_t& lo, uint32_t& hi) {
+__device__ __forceinline__ void mx_encode_fp6x32(const uint4 (&v)[4], int e, uint32_t (&out)[6]) {
   static_assert(ELEM == 3 || ELEM == 4, "FP6 element");
-  const mx_u32x16 in = {w0, w1, w2, w3, 0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  const mx_u32x16 in = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w,
+                        v[2].x, v[2].y, v[2].z, v[2].w, v[3].x, v[3].y, v[3].z, v[3].w};
   const mx_bf16x32 xv = __builtin_bit_cast(mx_bf16x32, in);
   mx_u32x6 r;
   if constexpr (ELEM == 3) r = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(xv, mx_pow2f(e));
   else r = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(xv, mx_pow2f(e));
-  lo = r[0];
-  hi = r[1] & 0xFFFFu;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) out[i] = r[i];
 }
 
 }  // namespace mxq

@@ -7,47 +7,34 @@
 // rule of the OCP Microscaling Formats v1.0 specification (which also defines
 // the 6-bit E2M3 and E3M2 elements).
 //
-// Both quantizers are HBM-streaming kernels: every lane owns one 16-byte
-// chunk (8 bf16) per iteration, loaded with one 128-bit load, so a wave reads
-// 1 KiB of contiguous memory per instruction.  A 32-element MX block is four
-// consecutive lanes (a DPP quad), a 16-element NVFP4 block two lanes; block
-// maxima are exchanged with DPP quad permutes, no LDS.  The shared exponent
-// comes from integer arithmetic on the bf16 bit patterns; MX element codes
-// from the hardware bf16 -> FP8 / FP4 conversions, whose rounding was
-// measured equal to the definition for every input (FP8 after a clamp, see
-// below) and the bf16 -> FP6 conversions (measured exact, see
-// mx_encode_fp6x8); NVFP4 codes, whose divisor is not a power of two, from
-// exact comparisons against per-block thresholds.
+// Both quantizers are HBM-streaming kernels in which one lane owns one block
+// (MX: 32 elements, four 16-byte chunks, 64 contiguous bytes; NVFP4: 16
+// elements, two chunks); the longer NVFP4 encoder loads the next block of the
+// lane's grid-stride sequence before it encodes the current one.  The shared exponent comes from integer arithmetic on the bf16
+// bit patterns; MX element codes from the hardware bf16 -> FP8 / FP4 / FP6
+// conversions, whose rounding was measured equal to the definition for
+// every input (FP8 after a clamp, see mx_encode.h).  NVFP4 codes, whose
+// divisor is not a power of two, come from exact comparisons against the
+// block's seven E2M1 midpoint thresholds, taken from per-workgroup tables
+// indexed by the block's scale code.
 #include "mx_encode.h"
 #include "mxq_internal.h"
 
 namespace mxq {
 namespace {
 
-__device__ __forceinline__ uint32_t quad_swap1(uint32_t v) {  // lanes 0<->1, 2<->3 of each quad
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t quad_swap2(uint32_t v) {  // lanes 0<->2, 1<->3 of each quad
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t quad_next(uint32_t v) {  // lane t of each quad gets lane min(t + 1, 3)
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xF9, 0xF, 0xF, false);
-}
-
 // Largest |x| (as bf16 magnitude bits) of the 8 elements in a 16-byte chunk.
 __device__ __forceinline__ uint32_t chunk_absmax_bits(const uint4& v) {
   return max(mx_absmax_bits4(v.x, v.y), mx_absmax_bits4(v.z, v.w));
 }
 
-// Loads in flight per lane: each lane issues kBatch independent 16-byte loads
-// (grid-stride apart) before processing them, so that a CU keeps enough bytes
-// in flight to cover HBM latency; the stride is a multiple of 256 chunks, so
-// block-aligned lane groups stay aligned.
+// Loads in flight per lane in the global-maximum pass: each lane issues
+// kBatch independent 16-byte loads (grid-stride apart) before taking their
+// maxima, so that a CU keeps enough bytes in flight to cover HBM latency.
 constexpr int kBatch = 4;
 
 // Calls f(v, i) for every chunk i < nchunks of this lane, kBatch loads at a
-// time.  `i < nchunks` is uniform over any lane group whose chunks share a
-// block, because nchunks is a multiple of the group size.
+// time.
 template <typename F>
 __device__ __forceinline__ void for_chunks(const uint4* __restrict__ x, int64_t nchunks, F&& f) {
   const int64_t stride = (int64_t)gridDim.x * 256;
@@ -99,69 +86,80 @@ inline RowDiv row_div(uint32_t srow) {
   return RowDiv{srow, (uint32_t)m, l - 1};
 }
 
-// One lane = one 16-byte chunk (8 consecutive bf16); four lanes = one
-// 32-element block.  nchunks is a multiple of 4 and every quad of lanes
-// starts on a block boundary, so the whole quad is active together.
-template <int ELEM, int PKS>
-__global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__ x, uint8_t* __restrict__ codes,
-                                                       uint8_t* __restrict__ scales, int64_t nchunks,
-                                                       int rceil, RowDiv rd) {
-  for_chunks(x, nchunks, [&](const uint4& v, int64_t i) {
-    uint32_t m = chunk_absmax_bits(v);
-    m = max(m, quad_swap1(m));
-    m = max(m, quad_swap2(m));
-
-    uint32_t scale_byte;
-    uint32_t lo = 0, hi = 0;  // FP8: codes 0-3, 4-7; FP4: lo = codes 0-7
-    if (m >= 0x7F80u) {  // NaN or Inf in the block: NaN scale, zero codes
-      scale_byte = 0xFFu;
-    } else {
-      const int e = mx_shared_exponent<ELEM>(m, rceil);
-      scale_byte = (uint32_t)(e + 127);
-      if constexpr (ELEM == 1) {
-        lo = mx_encode_fp8x4(v.x, v.y, e);
-        hi = mx_encode_fp8x4(v.z, v.w, e);
-      } else {
-        lo = mx_encode_fp4x4<0>(0u, v.x, v.y, e);
-        lo = mx_encode_fp4x4<2>(lo, v.z, v.w, e);
-      }
-    }
-    if (ELEM == 1) reinterpret_cast<uint2*>(codes)[i] = make_uint2(lo, hi);
-    else reinterpret_cast<uint32_t*>(codes)[i] = lo;
-    if ((i & 3) == 0) scales[scale_offset<ELEM == 1 ? 4 : 8, PKS>(i >> 2, rd)] = (uint8_t)scale_byte;
-  });
+// Calls encode(b, v) for every block b < nblocks of this lane's grid-stride
+// sequence, v holding the block's CH 16-byte chunks.
+template <int CH, typename F>
+__device__ __forceinline__ void for_blocks(const uint4* __restrict__ x, int64_t nblocks, F&& encode) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblocks; b += stride) {
+    uint4 v[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) v[c] = x[CH * b + c];
+    encode(b, v);
+  }
 }
 
+// The same, with the next block's loads issued before the current block is
+// encoded (for encoders long enough to hide them behind).
+template <int CH, typename F>
+__device__ __forceinline__ void for_blocks_prefetched(const uint4* __restrict__ x, int64_t nblocks, F&& encode) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  auto load = [&](int64_t b, uint4 (&v)[CH]) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) v[c] = b < nblocks ? x[CH * b + c] : uint4{0u, 0u, 0u, 0u};
+  };
+  int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint4 va[CH], vb[CH];
+  load(b, va);
+  while (b < nblocks) {
+    load(b + stride, vb);
+    encode(b, va);
+    b += stride;
+    if (b >= nblocks) break;
+    load(b + stride, va);
+    encode(b, vb);
+    b += stride;
+  }
+}
 
-// ----------------------------------------------------------------- MXFP6
-// MXFP6 codes: each 32-element block is a 32-byte slot holding its 192-bit
-// code integer (element j at bits 6j, little-endian) and 8 zero bytes.  Lane
-// t of a quad encodes elements 8t .. 8t+7, i.e. bits 48t .. 48t+47 of the
-// integer (p_t); the slot's 8-byte word t is bits 64t .. 64t+63, which is
-// (p_t >> 16t) | (p_{t+1} << (48 - 16t)) for t < 3 and zero for t = 3, so
-// one quad shift hands each lane its neighbour's bits and every lane stores
-// one word (a wave writes 512 contiguous bytes).
+// One lane = one 32-element block (four chunks, 64 contiguous bytes): its
+// largest magnitude, shared exponent, element codes and scale byte.  Codes:
+// FP8 32 bytes, FP4 16 bytes, FP6 a 32-byte slot holding the block's 192-bit
+// code integer (element j at bits 6 j, little-endian) and 8 zero bytes.
 template <int ELEM, int PKS>
-__global__ __launch_bounds__(256) void mx6_quant_kernel(const uint4* __restrict__ x, uint8_t* __restrict__ codes,
-                                                        uint8_t* __restrict__ scales, int64_t nchunks, int rceil,
-                                                        RowDiv rd) {
-  for_chunks(x, nchunks, [&](const uint4& v, int64_t i) {
-    uint32_t m = chunk_absmax_bits(v);
-    m = max(m, quad_swap1(m));
-    m = max(m, quad_swap2(m));
-    uint32_t lo = 0, hi = 0;
-    uint32_t scale_byte = 0xFFu;  // NaN or Inf in the block: NaN scale, zero codes
-    if (m < 0x7F80u) {
-      const int e = mx_shared_exponent<ELEM>(m, rceil);
-      scale_byte = (uint32_t)(e + 127);
-      mx_encode_fp6x8<ELEM>(v.x, v.y, v.z, v.w, e, lo, hi);
+__global__ __launch_bounds__(256) void mx_quant_kernel(const uint4* __restrict__ x, uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales, int64_t nblocks, int rceil,
+                                                       RowDiv rd) {
+  for_blocks<4>(x, nblocks, [&](int64_t b, const uint4 (&v)[4]) {
+    const uint32_t m = max(max(chunk_absmax_bits(v[0]), chunk_absmax_bits(v[1])),
+                           max(chunk_absmax_bits(v[2]), chunk_absmax_bits(v[3])));
+    const bool nonfinite = m >= 0x7F80u;  // NaN or Inf in the block: NaN scale, zero codes
+    const int e = nonfinite ? 0 : mx_shared_exponent<ELEM>(m, rceil);
+    const uint32_t keep = nonfinite ? 0u : 0xFFFFFFFFu;
+    if constexpr (ELEM == 1) {
+      uint32_t c[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        c[2 * k] = mx_encode_fp8x4(v[k].x, v[k].y, e) & keep;
+        c[2 * k + 1] = mx_encode_fp8x4(v[k].z, v[k].w, e) & keep;
+      }
+      uint4* dst = reinterpret_cast<uint4*>(codes + 32 * b);
+      dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
+      dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
+    } else if constexpr (ELEM == 2) {
+      uint32_t c[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        c[k] = mx_encode_fp4x4<2>(mx_encode_fp4x4<0>(0u, v[k].x, v[k].y, e), v[k].z, v[k].w, e) & keep;
+      *reinterpret_cast<uint4*>(codes + 16 * b) = make_uint4(c[0], c[1], c[2], c[3]);
+    } else {
+      uint32_t r[6];
+      mx_encode_fp6x32<ELEM>(v, e, r);
+      uint4* dst = reinterpret_cast<uint4*>(codes + 32 * b);
+      dst[0] = make_uint4(r[0] & keep, r[1] & keep, r[2] & keep, r[3] & keep);
+      dst[1] = make_uint4(r[4] & keep, r[5] & keep, 0u, 0u);
     }
-    const uint64_t p = ((uint64_t)hi << 32) | lo;
-    const uint32_t t = (uint32_t)i & 3u;
-    const uint64_t pn = ((uint64_t)quad_next(hi) << 32) | quad_next(lo);
-    const uint64_t word = t == 3u ? 0ull : (p >> (16 * t)) | (pn << (48 - 16 * t));
-    reinterpret_cast<uint64_t*>(codes)[i] = word;
-    if (t == 0u) scales[scale_offset<4, PKS>(i >> 2, rd)] = (uint8_t)scale_byte;
+    scales[scale_offset<ELEM == 2 ? 8 : 4, PKS>(b, rd)] = nonfinite ? 0xFFu : (uint8_t)(e + 127);
   });
 }
 
@@ -185,22 +183,6 @@ __global__ __launch_bounds__(256) void absmax_partials_kernel(const uint4* __res
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) partials[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
-}
-
-// E4M3 code of a positive, finite double q (nearest even, saturating at 448).
-__device__ __forceinline__ uint32_t e4m3_encode_pos(double q) {
-  if (q >= 448.0) return 0x7Eu;
-  const uint64_t u = (uint64_t)__double_as_longlong(q);
-  const int E = (int)((u >> 52) & 0x7FF) - 1023;
-  if (E >= -6) {
-    const uint64_t mant = u & 0xFFFFFFFFFFFFFull;
-    uint32_t c = ((uint32_t)(E + 7) << 3) | (uint32_t)(mant >> 49);
-    const uint64_t rem = mant & ((1ull << 49) - 1);
-    const uint64_t half = 1ull << 48;
-    c += (rem > half || (rem == half && (c & 1u))) ? 1u : 0u;
-    return c;
-  }
-  return (uint32_t)rint(q * 512.0);  // subnormal grid step 2^-9; rint rounds half to even
 }
 
 __device__ __forceinline__ double e4m3_decode_pos(uint32_t c) {
@@ -233,32 +215,98 @@ __device__ __forceinline__ uint32_t midpoint_threshold_f32(float a, float ts, bo
   return (e > 0.0f || (e == 0.0f && !tie_up)) ? pb + 1u : pb;
 }
 
-// E2M1 code magnitudes (0..7) of 8 bf16 values against the 7 thresholds,
-// with the sign bit of each input kept, packed 4 bits per element (element j
-// in bits 4j .. 4j + 3).
-__device__ __forceinline__ uint32_t e2m1_codes8(const uint4& v, const uint32_t (&V)[7], bool keep_sign) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t o = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t h = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
-    const uint32_t a = (h & 0x7FFFu) << 16;  // |x| as float32 bits
-    uint32_t k = 0;
-#pragma unroll
-    for (int t = 0; t < 7; ++t) k += (a >= V[t]) ? 1u : 0u;
-    if (keep_sign) k |= (h >> 12) & 8u;
-    o |= k << (4 * j);
+// The seven E2M1 midpoint thresholds (0.25 .. 5 times the block scale
+// dec(sc) * ts) as float32 bit patterns V: |x| rounds above midpoint t
+// exactly when |x| >= V[t].  Ties go to the even code, i.e. up after odd
+// codes.
+__device__ __forceinline__ void nv_thresholds(uint32_t sc, float ts, double ts64, bool fast, uint32_t (&V)[7]) {
+  if (fast) {
+    const float d = (float)e4m3_decode_pos(sc);  // exact
+    V[0] = midpoint_threshold_f32(0.25f * d, ts, false);
+    V[1] = midpoint_threshold_f32(0.75f * d, ts, true);
+    V[2] = midpoint_threshold_f32(1.25f * d, ts, false);
+    V[3] = midpoint_threshold_f32(1.75f * d, ts, true);
+    V[4] = midpoint_threshold_f32(2.5f * d, ts, false);
+    V[5] = midpoint_threshold_f32(3.5f * d, ts, true);
+    V[6] = midpoint_threshold_f32(5.0f * d, ts, false);
+  } else {
+    const double s = e4m3_decode_pos(sc) * ts64;  // <= 28 significant bits: exact
+    // t * s has <= 31 significant bits: exact in double
+    V[0] = midpoint_threshold(0.25 * s, false);
+    V[1] = midpoint_threshold(0.75 * s, true);
+    V[2] = midpoint_threshold(1.25 * s, false);
+    V[3] = midpoint_threshold(1.75 * s, true);
+    V[4] = midpoint_threshold(2.5 * s, false);
+    V[5] = midpoint_threshold(3.5 * s, true);
+    V[6] = midpoint_threshold(5.0 * s, false);
   }
-  return o;
 }
 
-// Phase 2: one lane per 16-element block (two 16-byte chunks): block scale,
-// thresholds, element codes.
+// A float32 threshold V as the smallest bf16 magnitude pattern h with
+// (h << 16) >= V, which decides every bf16 |x| the same way, capped at 0x8000
+// (above every magnitude pattern), in both 16-bit halves.
+__device__ __forceinline__ uint32_t thr16x2(uint32_t V) {
+  uint32_t c = (V >> 16) + ((V & 0xFFFFu) != 0u ? 1u : 0u);
+  c = min(c, 0x8000u);
+  return c | (c << 16);
+}
+
+typedef unsigned short nv_u16x2 __attribute__((ext_vector_type(2)));
+typedef short nv_s16x2 __attribute__((ext_vector_type(2)));
+// 0xFFFF in each 16-bit half where a < t, else 0 (a, t <= 0x8000 in each
+// half, so the sign of the 16-bit difference decides): one packed subtract
+// and one packed arithmetic shift, the shift count in a register for both
+// halves.
+__device__ __forceinline__ uint32_t lt_mask16x2(uint32_t a, uint32_t t) {
+  const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_bit_cast(nv_u16x2, a) - __builtin_bit_cast(nv_u16x2, t));
+  uint32_t m;
+  asm("v_pk_ashrrev_i16 %0, %1, %2" : "=v"(m) : "v"(0x000F000Fu), "v"(d));
+  return m;
+}
+__device__ __forceinline__ uint32_t sel_mask(uint32_t m, uint32_t x, uint32_t y) { return (m & x) | (~m & y); }
+
+// Two bf16 (one dword) -> their E2M1 codes in bits 0..3 and 16..19: the
+// magnitude is the number of thresholds T[0..6] (packed, sorted) at or below
+// |x|, found by a three-level search; signmask keeps the sign bits.
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t w, const uint32_t (&T)[7], uint32_t signmask) {
+  const uint32_t a = w & 0x7FFF7FFFu;
+  const uint32_t m1 = lt_mask16x2(a, T[3]);
+  const uint32_t m2 = lt_mask16x2(a, sel_mask(m1, T[1], T[5]));
+  const uint32_t m3 = lt_mask16x2(a, sel_mask(m1, sel_mask(m2, T[0], T[2]), sel_mask(m2, T[4], T[6])));
+  const uint32_t k = ((m1 & 0x00040004u) | (m2 & 0x00020002u) | (m3 & 0x00010001u)) ^ 0x00070007u;
+  return k | ((w >> 12) & signmask);
+}
+// Eight bf16 (one chunk) -> eight E2M1 codes, element j in bits 4 j .. 4 j + 3.
+__device__ __forceinline__ uint32_t e2m1_codes8(const uint4& v, const uint32_t (&T)[7], uint32_t signmask) {
+  uint32_t u0 = e2m1_pair(v.x, T, signmask), u1 = e2m1_pair(v.y, T, signmask);
+  uint32_t u2 = e2m1_pair(v.z, T, signmask), u3 = e2m1_pair(v.w, T, signmask);
+  u0 |= u0 >> 12;  // byte 0: the pair's two codes
+  u1 |= u1 >> 12;
+  u2 |= u2 >> 12;
+  u3 |= u3 >> 12;
+  return (u0 & 0xFFu) | ((u1 & 0xFFu) << 8) | ((u2 & 0xFFu) << 16) | (u3 << 24);
+}
+
+// Phase 2: one lane per 16-element block (two chunks).  Every workgroup first
+// takes the global maximum from the partials and builds two tables in LDS
+// from the tensor scale ts:
+//   thr[c]  the seven packed element thresholds of scale code c (c = 0 and
+//           0x7F: above every magnitude);
+//   up[c]   the smallest bf16 magnitude pattern B whose block scale B / (6 ts)
+//           rounds (nearest even E4M3, saturating at 448) to a code above c.
+// A block's scale code is then the hardware E4M3 rounding of the float32
+// estimate bm * fl(1 / (6 ts)), whose relative error (a few units of 2^-24)
+// moves it by at most one code, corrected exactly against up[c0 - 1] and
+// up[c0]; below ts = 2^-60 the estimate is not used and a binary search over
+// up[] finds the code.  A nonzero block's code is at least 1.
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restrict__ x, int64_t nchunks,
                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                           float* __restrict__ ts_out,
                                                           const uint32_t* __restrict__ partials, int npartials) {
   __shared__ uint32_t red[4];
+  __shared__ uint4 thr[128][2];
+  __shared__ uint16_t up[128];
+  __shared__ uint32_t fix[128];  // up[c - 1] (0 for c = 0) | up[c] << 16
   uint32_t g = 0;
   for (int j = threadIdx.x; j < npartials; j += 256) g = max(g, partials[j]);
   g = wave_max(g);
@@ -283,72 +331,64 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
   const double ts64 = (double)ts;
   const bool fast = !nonfinite && ts >= 0x1p-60f;  // uniform
 
-  const int64_t nblocks = nchunks / 2;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t b0 = (int64_t)blockIdx.x * 256 + threadIdx.x; b0 < nblocks; b0 += stride * kBatch) {
-    uint4 v[kBatch][2];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t b = b0 + u * stride;
-      if (b < nblocks) {
-        v[u][0] = x[2 * b];
-        v[u][1] = x[2 * b + 1];
-      } else {
-        v[u][0] = v[u][1] = uint4{0u, 0u, 0u, 0u};
+  {
+    const int t = threadIdx.x;
+    if (t < 128) {
+      uint32_t u = 0x8000u;
+      if (t < 0x7E && !nonfinite) {
+        // midpoint of codes t and t + 1 (<= 5 significant bits) times 6 ts: exact in double
+        const double mid = 0.5 * (e4m3_decode_pos((uint32_t)t) + e4m3_decode_pos((uint32_t)t + 1u));
+        const uint32_t V = midpoint_threshold(mid * 6.0 * ts64, ((t + 1) & 1) == 0);
+        u = thr16x2(V) & 0xFFFFu;
       }
+      up[t] = (uint16_t)u;
     }
+    const int c = t >> 1;  // thread pair 2c, 2c + 1 fills thr[c]
+    uint32_t V[7];
+    if (c == 0 || c == 0x7F || nonfinite) {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t b = b0 + u * stride;
-      if (b >= nblocks) continue;
-      const uint32_t bm = max(chunk_absmax_bits(v[u][0]), chunk_absmax_bits(v[u][1]));
-      uint32_t sc;
-      uint32_t V[7];
-      if (nonfinite || bm == 0) {
-        sc = nonfinite ? 0x7Fu : 0u;
-#pragma unroll
-        for (int j = 0; j < 7; ++j) V[j] = 0xFFFFFFFFu;
-      } else {
-        // block scale: one rounding of B / (6 ts); operands exact in double and
-        // the division correctly rounded, so the E4M3 rounding sees the exact
-        // quotient's decisions (a non-tie quotient is >= ~2^-32 relative away
-        // from any E4M3 midpoint).
-        const double q = (double)bf16_to_f32(bm) / (6.0 * ts64);
-        sc = e4m3_encode_pos(q);
-        if (sc == 0) sc = 1;
-        // E2M1 midpoints between codes j and j+1 (0.25 .. 5 times the scale);
-        // ties go to the even code, i.e. up after odd codes.
-        if (fast) {
-          const float d = (float)e4m3_decode_pos(sc);  // exact
-          V[0] = midpoint_threshold_f32(0.25f * d, ts, false);
-          V[1] = midpoint_threshold_f32(0.75f * d, ts, true);
-          V[2] = midpoint_threshold_f32(1.25f * d, ts, false);
-          V[3] = midpoint_threshold_f32(1.75f * d, ts, true);
-          V[4] = midpoint_threshold_f32(2.5f * d, ts, false);
-          V[5] = midpoint_threshold_f32(3.5f * d, ts, true);
-          V[6] = midpoint_threshold_f32(5.0f * d, ts, false);
-        } else {
-          const double s = e4m3_decode_pos(sc) * ts64;  // <= 28 significant bits: exact
-          // t * s has <= 31 significant bits: exact in double
-          V[0] = midpoint_threshold(0.25 * s, false);
-          V[1] = midpoint_threshold(0.75 * s, true);
-          V[2] = midpoint_threshold(1.25 * s, false);
-          V[3] = midpoint_threshold(1.75 * s, true);
-          V[4] = midpoint_threshold(2.5 * s, false);
-          V[5] = midpoint_threshold(3.5 * s, true);
-          V[6] = midpoint_threshold(5.0 * s, false);
-        }
-      }
-      const uint32_t lo = e2m1_codes8(v[u][0], V, !nonfinite);
-      const uint32_t hi = e2m1_codes8(v[u][1], V, !nonfinite);
-      reinterpret_cast<uint2*>(codes)[b] = make_uint2(lo, hi);
-      scales[b] = (uint8_t)sc;
+      for (int j = 0; j < 7; ++j) V[j] = 0xFFFFFFFFu;
+    } else {
+      nv_thresholds((uint32_t)c, ts, ts64, fast, V);
     }
+    if ((t & 1) == 0) thr[c][0] = make_uint4(thr16x2(V[0]), thr16x2(V[1]), thr16x2(V[2]), thr16x2(V[3]));
+    else thr[c][1] = make_uint4(thr16x2(V[4]), thr16x2(V[5]), thr16x2(V[6]), 0x80008000u);
   }
+  __syncthreads();
+  if (threadIdx.x < 128) fix[threadIdx.x] = (threadIdx.x ? (uint32_t)up[threadIdx.x - 1] : 0u) | ((uint32_t)up[threadIdx.x] << 16);
+  __syncthreads();
+
+  const float inv6ts = 1.0f / (6.0f * ts);
+  const uint32_t signmask = nonfinite ? 0u : 0x00080008u;
+  for_blocks_prefetched<2>(x, nchunks / 2, [&](int64_t b, const uint4 (&v)[2]) {
+    const uint32_t bm = max(chunk_absmax_bits(v[0]), chunk_absmax_bits(v[1]));
+    uint32_t c = 0;
+    if (nonfinite) {
+      c = 0x7Fu;
+    } else if (bm != 0) {
+      if (fast) {
+        const float qf = fminf(bf16_to_f32(bm) * inv6ts, 448.0f);
+        const uint32_t c0 =
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(nv_s16x2{0, 0}, qf, qf, 1.0f, false)) &
+            0x7Fu;
+        const uint32_t f = fix[c0];
+        c = c0 + (bm >= (f >> 16) ? 1u : 0u) - (bm < (f & 0xFFFFu) ? 1u : 0u);
+      } else {
+#pragma unroll
+        for (uint32_t step = 64; step >= 1; step >>= 1)
+          if (c + step <= 0x7Eu && bm >= up[c + step - 1]) c += step;
+      }
+      c = max(c, 1u);
+    }
+    const uint4 T0 = thr[c][0], T1 = thr[c][1];
+    const uint32_t T[7] = {T0.x, T0.y, T0.z, T0.w, T1.x, T1.y, T1.z};
+    reinterpret_cast<uint2*>(codes)[b] = make_uint2(e2m1_codes8(v[0], T, signmask), e2m1_codes8(v[1], T, signmask));
+    scales[b] = (uint8_t)c;
+  });
 }
 
-int grid_for(int64_t nchunks, int64_t cap) {
-  int64_t g = (nchunks + 255) / 256;
+int grid_for(int64_t nlanes, int64_t cap) {
+  int64_t g = (nlanes + 255) / 256;
   if (g > cap) g = cap;
   if (g < 1) g = 1;
   return (int)g;
@@ -358,31 +398,37 @@ int grid_for(int64_t nchunks, int64_t cap) {
 
 template <int PKS>
 void launch_mx_quant_pks(int elem, int grid, hipStream_t stream, const uint4* xv, uint8_t* codes, uint8_t* scales,
-                         int64_t nchunks, int rceil, RowDiv rd) {
+                         int64_t nblocks, int rceil, RowDiv rd) {
   if (elem == 1)
-    hipLaunchKernelGGL((mx_quant_kernel<1, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks, rceil,
+    hipLaunchKernelGGL((mx_quant_kernel<1, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nblocks, rceil,
                        rd);
   else if (elem == 2)
-    hipLaunchKernelGGL((mx_quant_kernel<2, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks, rceil,
+    hipLaunchKernelGGL((mx_quant_kernel<2, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nblocks, rceil,
                        rd);
   else if (elem == 3)
-    hipLaunchKernelGGL((mx6_quant_kernel<3, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks,
-                       rceil, rd);
+    hipLaunchKernelGGL((mx_quant_kernel<3, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nblocks, rceil,
+                       rd);
   else
-    hipLaunchKernelGGL((mx6_quant_kernel<4, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nchunks,
-                       rceil, rd);
+    hipLaunchKernelGGL((mx_quant_kernel<4, PKS>), dim3(grid), dim3(256), 0, stream, xv, codes, scales, nblocks, rceil,
+                       rd);
 }
+
+// Workgroups per launch: one block per lane up to the cap, beyond it a
+// grid-stride sequence of blocks per lane (measured on the FLUX activations:
+// 1024 workgroups for the 32-element MX blocks, 2048 for the NVFP4 pass).
+constexpr int64_t kMxGridCap = 1024;
+constexpr int64_t kNvGridCap = 2048;
 
 hipError_t launch_mx_quant(int elem, int rceil, int packed, const uint16_t* x, int64_t rows, int64_t cols,
                            uint8_t* codes, uint8_t* scales, hipStream_t stream) {
-  const int64_t nchunks = rows * cols / 8;
-  if (nchunks == 0) return hipSuccess;
-  const int grid = grid_for((nchunks + kBatch - 1) / kBatch, 8192);
+  const int64_t nblocks = rows * cols / 32;
+  if (nblocks == 0) return hipSuccess;
+  const int grid = grid_for(nblocks, kMxGridCap);
   const uint4* xv = (const uint4*)x;
   // packed scales need whole 128- or 256-element stages per row, so srow >= 4
   const RowDiv rd = packed ? row_div((uint32_t)(cols / 32)) : RowDiv{(uint32_t)(cols / 32), 0u, 0u};
-  if (packed) launch_mx_quant_pks<1>(elem, grid, stream, xv, codes, scales, nchunks, rceil, rd);
-  else launch_mx_quant_pks<0>(elem, grid, stream, xv, codes, scales, nchunks, rceil, rd);
+  if (packed) launch_mx_quant_pks<1>(elem, grid, stream, xv, codes, scales, nblocks, rceil, rd);
+  else launch_mx_quant_pks<0>(elem, grid, stream, xv, codes, scales, nblocks, rceil, rd);
   return hipGetLastError();
 }
 
@@ -401,7 +447,7 @@ hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t rows, int64_t cols, uin
   hipLaunchKernelGGL(absmax_partials_kernel, dim3(P), dim3(256), 0, stream, (const uint4*)x, nchunks, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int grid = grid_for((nchunks / 2 + kBatch - 1) / kBatch, 4096);
+  const int grid = grid_for(nchunks / 2, kNvGridCap);
   hipLaunchKernelGGL(nvfp4_quant_kernel, dim3(grid), dim3(256), 0, stream, (const uint4*)x, nchunks, codes, scales,
                      tensor_scale, (const uint32_t*)partials, P);
   return hipGetLastError();
