@@ -808,7 +808,8 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
 // ---------------------------------------------------------------- skinny M
 // out[m, n] for M <= MMAX activation rows: an HBM stream of W, bound by
 // bandwidth (W is read once; 2 FLOP per 2 bytes per activation row).  The
-// activations sit in LDS.  LPR lanes (8, 16 or 32) share one W row and read
+// activations sit in LDS, padded with zero rows to MMAX, so the inner loop
+// has no branch on M.  LPR lanes (8, 16 or 32) share one W row and read
 // 16 * LPR contiguous bytes per instruction, so a wave-wide load covers whole
 // lines; each lane keeps U such loads in flight, multiplies bf16 pairs with
 // v_dot2_f32_bf16 (exact products, fp32 accumulation), and the partial sums
@@ -816,72 +817,86 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
 // a lane shuffle across rows.  64 / LPR W rows per wave: finer row groups
 // spread N over the SIMDs more evenly.
 template <int MMAX, int LPR>
-__global__ __launch_bounds__(256) void bf16_skinny_kernel(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(1024) void bf16_skinny_kernel(const uint16_t* __restrict__ A,
                                                           const uint16_t* __restrict__ W,
                                                           const uint16_t* __restrict__ bias,
                                                           uint16_t* __restrict__ out, int M, int N, int K) {
   constexpr int U = 8;  // 16-byte W loads in flight per lane
-  extern __shared__ uint4 sAv[];  // [M][K/8]
+  extern __shared__ uint4 sAv[];  // [MMAX][K/8], rows M .. MMAX - 1 zero
   const int kc = K / 8;
-  for (int c = threadIdx.x; c < M * kc; c += 256) sAv[c] = reinterpret_cast<const uint4*>(A)[c];
+  for (int c = threadIdx.x; c < MMAX * kc; c += blockDim.x)
+    sAv[c] = c < M * kc ? reinterpret_cast<const uint4*>(A)[c] : uint4{0u, 0u, 0u, 0u};
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   constexpr int RPW = 64 / LPR;                    // W rows per wave
   const int sub = lane % LPR;                      // lane within its row
-  const int n = (blockIdx.x * 4 + wave) * RPW + lane / LPR;
-  const bool valid = n < N;
-  const uint4* wrow = reinterpret_cast<const uint4*>(W + (size_t)(valid ? n : 0) * K);
-  float acc[MMAX];
+  const int ngroups = (N + nwaves * RPW - 1) / (nwaves * RPW);
+  // the workgroup's groups of nwaves * RPW W rows, grid-stride: the
+  // activations are staged once per workgroup
+  for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+    const int n = (grp * nwaves + wave) * RPW + lane / LPR;
+    const bool valid = n < N;
+    const uint4* wrow = reinterpret_cast<const uint4*>(W + (size_t)(valid ? n : 0) * K);
+    float acc[MMAX];
 #pragma unroll
-  for (int m = 0; m < MMAX; ++m) acc[m] = 0.f;
-  auto dot8 = [](const uint4& w, const uint4& a, float c) {
-    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), __builtin_bit_cast(bf16x2, a.x), c, false);
-    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), __builtin_bit_cast(bf16x2, a.y), c, false);
-    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), __builtin_bit_cast(bf16x2, a.z), c, false);
-    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), __builtin_bit_cast(bf16x2, a.w), c, false);
-    return c;
-  };
-  for (int c0 = sub; c0 < kc; c0 += LPR * U) {
-    uint4 x[U];
+    for (int m = 0; m < MMAX; ++m) acc[m] = 0.f;
+    auto dot8 = [](const uint4& w, const uint4& a, float c) {
+      c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), __builtin_bit_cast(bf16x2, a.x), c, false);
+      c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), __builtin_bit_cast(bf16x2, a.y), c, false);
+      c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), __builtin_bit_cast(bf16x2, a.z), c, false);
+      c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), __builtin_bit_cast(bf16x2, a.w), c, false);
+      return c;
+    };
+    for (int c0 = sub; c0 < kc; c0 += LPR * U) {
+      uint4 x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + LPR * u;
-      x[u] = (valid && c < kc) ? wrow[c] : uint4{0u, 0u, 0u, 0u};
-    }
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + LPR * u;
+        x[u] = (valid && c < kc) ? wrow[c] : uint4{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + LPR * u;
-      if (c < kc) {
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + LPR * u;
+        // a branch per W chunk (uniform except in the last chunk of K), which
+        // also keeps the compiler from hoisting all U x MMAX activation reads
+        if (c < kc) {
 #pragma unroll
-        for (int m = 0; m < MMAX; ++m)
-          if (m < M) acc[m] = dot8(x[u], sAv[m * kc + c], acc[m]);
+          for (int m = 0; m < MMAX; ++m) acc[m] = dot8(x[u], sAv[m * kc + c], acc[m]);
+        }
       }
     }
-  }
-  // sum over the 8 lanes of the row group: xor 1, xor 2 (quad permutes), then
-  // the mirrored quad of the half row
-  auto dpp_add = [](float v, int ctrl) {
-    int o;
-    if (ctrl == 0xB1) o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false);
-    else if (ctrl == 0x4E) o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false);
-    else o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false);
-    return v + __int_as_float(o);
-  };
+    // sum over the 8 lanes of the row group: xor 1, xor 2 (quad permutes), then
+    // the mirrored quad of the half row
+    auto dpp_add = [](float v, int ctrl) {
+      int o;
+      if (ctrl == 0xB1) o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false);
+      else if (ctrl == 0x4E) o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false);
+      else o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false);
+      return v + __int_as_float(o);
+    };
 #pragma unroll
-  for (int m = 0; m < MMAX; ++m) {
-    if (m < M) {
-      float v = dpp_add(acc[m], 0xB1);
-      v = dpp_add(v, 0x4E);
-      v = dpp_add(v, 0x141);  // now the sum of each 8-lane half row
-      if constexpr (LPR >= 16) v += __shfl_xor(v, 8, 64);
-      if constexpr (LPR >= 32) v += __shfl_xor(v, 16, 64);
-      if (sub == 0 && valid) {
-        const float b = bias ? bf16_to_f32(bias[n]) : 0.f;
-        out[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v + b);
+    for (int m = 0; m < MMAX; ++m) {
+      if (m < M) {
+        float v = dpp_add(acc[m], 0xB1);
+        v = dpp_add(v, 0x4E);
+        v = dpp_add(v, 0x141);  // now the sum of each 8-lane half row
+        if constexpr (LPR >= 16) v += __shfl_xor(v, 8, 64);
+        if constexpr (LPR >= 32) v += __shfl_xor(v, 16, 64);
+        if (sub == 0 && valid) {
+          const float b = bias ? bf16_to_f32(bias[n]) : 0.f;
+          out[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v + b);
+        }
       }
     }
   }
 }
+
+// Skinny bf16 path: lanes per W row (each wave-wide load covers whole lines
+// of 32 rows' 512-byte runs), the largest activation row count, and its
+// activations' LDS bound (the whole LDS of a CU).
+constexpr int kSkinnyLPR = 32;
+constexpr int kSkinnyMaxRows = 16;
+constexpr size_t kSkinnyMaxLds = 160 * 1024;
 
 // Any K (row starts need not be 16-byte aligned): one thread per output.
 __global__ __launch_bounds__(256) void bf16_generic_kernel(const uint16_t* __restrict__ A,
@@ -1041,17 +1056,32 @@ hipError_t launch_bf16_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* a, 
                        out, (int)M, (int)N, (int)K);
     return hipGetLastError();
   }
-  const size_t lds = (size_t)M * K * 2;
-#ifndef MXQ_SKINNY_LPR
-#define MXQ_SKINNY_LPR 32
-#endif
-  if (M <= 4 && lds <= 64 * 1024) {
-    constexpr int LPR = MXQ_SKINNY_LPR;
-    const int rows_per_wg = 4 * (64 / LPR);  // 4 waves
-    const unsigned grid = (unsigned)((N + rows_per_wg - 1) / rows_per_wg);
-    hipLaunchKernelGGL((bf16_skinny_kernel<4, LPR>), dim3(grid), dim3(256), lds, stream, a, w, bias, out, (int)M,
-                       (int)N, (int)K);
-    return hipGetLastError();
+  // up to 16 activation rows: the W stream of bf16_skinny_kernel with 4, 8
+  // or 16 LDS activation rows (up to 160 KiB; above 64 KiB the kernel's
+  // dynamic-LDS limit is raised first)
+  const int mmax = M <= 4 ? 4 : M <= 8 ? 8 : 16;
+  const size_t lds = (size_t)mmax * K * 2;
+  if (M <= kSkinnyMaxRows && lds <= kSkinnyMaxLds) {
+    // 4 waves per workgroup for up to 4 rows, 16 above (more waves share one
+    // staged copy of the activations); as many workgroups as fit the CUs'
+    // LDS, each looping over groups of W rows
+    const int threads = mmax == 4 ? 256 : 1024;
+    const int64_t rows_per_wg = (threads / 64) * (64 / kSkinnyLPR);
+    const int64_t groups = (N + rows_per_wg - 1) / rows_per_wg;
+    const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(2048 / threads, (int64_t)(kSkinnyMaxLds / std::max<size_t>(lds, 1))));
+    const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(groups, per_cu * device_cu_count()));
+    auto run = [&](auto kern) -> hipError_t {
+      if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, stream, a, w, bias, out, (int)M, (int)N, (int)K);
+      return hipGetLastError();
+    };
+    if (mmax == 4) return run(&bf16_skinny_kernel<4, kSkinnyLPR>);
+    if (mmax == 8) return run(&bf16_skinny_kernel<8, kSkinnyLPR>);
+    return run(&bf16_skinny_kernel<16, kSkinnyLPR>);
   }
   return launch_tiled<BF16, MXQ_TILE_BF16>(M, N, K, a, nullptr, w, nullptr, nullptr, nullptr, bias, out, stream);
 }

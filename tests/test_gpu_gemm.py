@@ -156,7 +156,10 @@ def test_identity_weights(dev):
 
 
 BF16_SHAPES = [(1, 18432, 3072), (4, 18432, 3072), (16, 512, 1024), (37, 300, 64), (200, 260, 1024), (5, 7, 40),
-               (300, 200, 40), (1, 1, 8)]
+               (300, 200, 40), (1, 1, 8),
+               # the skinny W stream at 5..16 rows: a ragged N, the modulation shape, and 128 KiB of activations
+               (5, 1001, 3072), (13, 777, 1024), (8, 18432, 3072), (16, 18432, 3072), (16, 1000, 4096),
+               (17, 300, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", BF16_SHAPES)
