@@ -266,17 +266,23 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
   }
   const uint32_t soff = wave < 2 ? (uint32_t)lane * 4 : kOutOfRange;
   const __amdgpu_buffer_rsrc_t rsc = wave == 1 ? rvs : rks;
-  auto issue = [&](auto& st, int kv0) {
+  const int ntiles = S / kBK;
+  // Pass-2 stage j holds K of tile j and V^T of tile j - 1 with their scales
+  // (tile t of either scale array starts at byte 256 t).  A missing tile (K
+  // past the last, V before the first) reads a zero-length range: zeros.
+  const __amdgpu_buffer_rsrc_t rnone = make_rsrc(kc, 0u);
+  auto issue = [&](auto& st, int j) {
+    const bool hk = j < ntiles, hv = j >= 1 && j - 1 < ntiles;
+    const __amdgpu_buffer_rsrc_t rkj = hk ? rk : rnone, rvj = hv ? rv : rnone;
+    const uint32_t ko = hk ? (uint32_t)j * kBK * kD : 0u, vo = hv ? (uint32_t)(j - 1) * kBK : 0u;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      lds_dma16(rk, &st[kKOff + 1024 * (2 * wave + u)], kbase[u], (uint32_t)(kv0 + 8 * (2 * wave + u)) * kD);
-      lds_dma16(rv, &st[kVOff + 1024 * (2 * wave + u)], voff[u], (uint32_t)kv0);
+      lds_dma16(rkj, &st[kKOff + 1024 * (2 * wave + u)], kbase[u], ko + (uint32_t)(8 * (2 * wave + u)) * kD);
+      lds_dma16(rvj, &st[kVOff + 1024 * (2 * wave + u)], voff[u], vo);
     }
-    // tile kv0 / 64 of either scale array starts at byte 4 kv0
-    lds_dma4(rsc, &st[kKsOff + 256 * wave], soff, (uint32_t)kv0 * 4);
+    const bool hs = wave == 1 ? hv : hk;
+    lds_dma4(hs ? rsc : rnone, &st[kKsOff + 256 * wave], soff, hs ? (wave == 1 ? vo : ko / kD) * 4u : 0u);
   };
-
-  const int ntiles = S / kBK;
 
   // Pass 1: the row maximum of the raw scores over all keys.  A stage holds
   // 128 K rows (16 KiB over its K and V^T areas; chunk g = 4 wave + u) and
@@ -344,17 +350,9 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
   float l = 0.0f;
   const int vsw = (r32 >> 2) & 3;  // V^T row swizzle
 
-  // Pass 2, one tile: its DMA has landed in `cur` (own wait, then the barrier
-  // for everyone's); the next tile's DMA goes into `nxt`, which every wave has
-  // finished reading (the last tile reloads itself, so the issue is
-  // unconditional); then scores, P and P V from `cur`.
-  auto step = [&](auto& cur, auto& nxt, int t) {
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    issue(nxt, (t + 1 < ntiles ? t + 1 : t) * kBK);
-    const uint8_t* b = cur;
-    att_v16f sacc[1][2];
-    key_scores<1, 2>(b, 0, qa, r32, q, sacc);
+  // P codes of one tile's scores (p = exp2(s c_log2 - m), with the row sum of
+  // the unquantized p added to l), then O^T += V^T P^T with V^T from `b`
+  auto softmax_pv = [&](const uint8_t* b, const att_v16f (&sc)[1][2]) {
     float ls = 0.0f;
     uint32_t d[2][4];
 #pragma unroll
@@ -364,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
         float p[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][tt][4 * i + u], c_log2, -m));
+          p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][tt][4 * i + u], c_log2, -m));
           ls += p[u];
         }
         d[tt][i] = p_codes4(p[0], p[1], p[2], p[3]);
@@ -391,13 +389,33 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(const uint8_t* __restr
     }
   };
 
+  // Pass 2, step j (1 <= j <= ntiles): stage j has landed in `cur` (own wait,
+  // then the barrier for everyone's); stage j + 1 goes into `nxt`, which every
+  // wave has finished reading.  The scores of tile j (MFMAs; zeros for
+  // j = ntiles, unused) are issued first, so that the matrix cores form them
+  // while the VALU turns the previous tile's scores into P codes; then P V of
+  // tile j - 1.
+  auto step = [&](auto& cur, auto& nxt, int j, att_v16f (&snew)[1][2], const att_v16f (&sold)[1][2]) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    issue(nxt, j + 1);
+    key_scores<1, 2>(cur, 0, qa, r32, q, snew);
+    softmax_pv(cur, sold);
+  };
+
+  att_v16f sa[1][2], sb[1][2];
   issue(st0, 0);
-  for (t = 0; t + 1 < ntiles; t += 2) {
-    step(st0, st1, t);
-    step(st1, st0, t + 1);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  issue(st1, 1);
+  key_scores<1, 2>(st0, 0, qa, r32, q, sa);  // scores of tile 0
+  int j = 1;
+  for (; j + 1 <= ntiles; j += 2) {
+    step(st1, st0, j, sb, sa);
+    step(st0, st1, j + 1, sa, sb);
   }
-  if (t < ntiles) step(st0, st1, t);
-  wait_vmcnt<0>();  // the last (redundant) DMA lands before the workgroup's LDS is released
+  if (j == ntiles) step(st1, st0, j, sb, sa);
+  wait_vmcnt<0>();  // the last (empty) DMA lands before the workgroup's LDS is released
 
   // out = O / l: lane (query, q) holds channels 32 c + 8 i + 4 q + (0..3)
   const float inv = 1.0f / sum_half(l);
