@@ -77,3 +77,34 @@ def test_noalloc_rejects_too_large(dev):
     assert e.value.status == 8
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())  # nothing was launched
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+def test_noalloc_in_graph_replays(fmt, dev):
+    """The call it exists for: captured in a HIP graph (it allocates nothing, so capture needs no memory pool
+    of its own).  Three replays, each after eager library work that reuses the same per-GPU scratch with
+    another shape; every replay equals the workspace call bit for bit."""
+    import torch
+
+    from microscaling_quantized_diffusion_amd import mxq
+
+    M, K, N = 1024, 2048, 768
+    g = torch.Generator(device=dev).manual_seed(21)
+    a = (torch.randn((M, K), generator=g, device=dev) * 2.0).to(torch.bfloat16)
+    qw = mxq.quantize(fmt, (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16),
+                      packed_scales=fmt != "nvfp4")
+    want = mxq.quant_gemm_fused(a, qw)
+    out = torch.empty_like(want)
+    a2 = (torch.randn((300, 1024), generator=g, device=dev)).to(torch.bfloat16)
+    qw2 = mxq.quantize(fmt, (torch.randn((200, 1024), generator=g, device=dev) * 0.02).to(torch.bfloat16),
+                       packed_scales=fmt != "nvfp4")
+    out2 = torch.empty((300, 200), dtype=torch.bfloat16, device=dev)
+    graph = mxq.GraphedCall(lambda: mxq.quant_gemm_fused_noalloc(a, qw, None, out))
+    for rep in range(3):
+        log_case("noalloc graph", fmt, rep)
+        out.zero_()
+        mxq.quant_gemm_fused_noalloc(a2, qw2, None, out2)  # eager work over the same scratch
+        torch.cuda.synchronize()
+        graph()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), (fmt, rep)
