@@ -57,10 +57,15 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "mxe_gemm_mxfp8_flux_mlp_up_count
 
 
 def _src_sha() -> str:
+    """Hash of the GEMM sources' code: every line with its // comment and surrounding blanks removed, blank lines
+    skipped, so that comment edits keep a counter summary valid while any code change invalidates it."""
     h = hashlib.sha256()
     for f in GEMM_SRCS:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -4,16 +4,21 @@
 // aitrends.kr MXFP8/NVFP4 article ("Section details": quantized weights times
 // dynamically quantized activations; second "Evidence" block: small layers
 // stay in bf16).  Kernels:
-//   mxp_gemm_kernel   MXFP8 / MXFP6 / MXFP4 main path: 256x256 or 256x320 tiles,
-//                     scaled 32x32x64 MFMA (hardware E8M0 block scales),
-//                     two-stage LDS-DMA ring of 128-byte K slabs.
+//   mxe_gemm_kernel   (gemm_mx.hip) the MX main path: whole-stage MXFP8 /
+//                     MXFP6 / MXFP4 GEMMs on 256x256 or 256x320 tiles, scaled
+//                     32x32x64 MFMA (hardware E8M0 block scales), two-stage
+//                     LDS-DMA ring of 128-byte K slabs, stages published early.
+//   mxp_gemm_kernel   the same tiles and ring with the stage published at its
+//                     start: MXFP4 on 256x320 tiles (the early-published
+//                     kernel's registers do not fit them) and the GEMM whose
+//                     epilogue quantizes its output for the next layer.
 //   nv4_gemm_kernel   NVFP4 main path: the same tile and ring; codes widened
 //                     to f16 with the E4M3 block scale applied (exact), f16
 //                     32x32x16 MFMA, tensor scales in the epilogue.
 //   gemm_kernel       generic 16x16 path for every mode (MX8 / MX4 / NV4 /
 //                     BF16) and shape: K not a multiple of the main paths'
 //                     slab, unaligned scale rows, and the bf16 MFMA GEMM.
-//   bf16_skinny_kernel / bf16_generic_kernel   bf16 fallback for a few
+//   bf16_skinny_kernel / bf16_generic_kernel   bf16 fallback for up to 16
 //                     activation rows (an HBM stream of W) and for K % 8 != 0.
 // Weights are the MFMA "A" operand and activations the "B" operand, so a
 // lane's accumulators are consecutive output columns of one output row.
@@ -914,7 +919,8 @@ __global__ __launch_bounds__(256) void bf16_generic_kernel(const uint16_t* __res
 
 }  // namespace
 
-// Tile shapes (BM activation rows x BN weight rows, WM x WN waves).
+// Tile shapes of the generic path (BM activation rows x BN weight rows,
+// WM x WN waves).
 #ifndef MXQ_TILE_MX
 #define MXQ_TILE_MX 256, 256, 2, 2
 #endif
