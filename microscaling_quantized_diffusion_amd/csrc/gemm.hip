@@ -364,8 +364,9 @@ hipError_t launch_tiled(int64_t M, int64_t N, int64_t K, const void* a, const ui
 //   MFMAs first, and the younger one then runs alone on LDS latency.  Wave
 //   priorities (s_setprio around MFMA groups), deeper read pipelines, an L2
 //   prefetch of the next K slab and fewer scale DMAs all left the time
-//   unchanged; removing the LDS operand reads or the DMA does not, so the
-//   loop is bound by LDS traffic (reads + DMA writes) and its latency.
+//   unchanged.  The operand reads use about a third of the LDS's measured
+//   256 B/clk read bandwidth at full MFMA rate, so the loop is bound by LDS
+//   latency and the per-stage barrier, not by LDS bytes.
 // * Epilogue.  (+ bias) -> bf16 RNE; each wave stages 32 output rows at a
 //   time through the idle stage buffers (16-byte row pad) and writes whole
 //   256-byte row segments with 16-byte stores, so L2 sees full-line writes.

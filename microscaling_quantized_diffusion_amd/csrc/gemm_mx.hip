@@ -229,7 +229,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void mxe_gemm_kernel(
   // prologue: stage 0 published, stage 1 in flight, stage 0's first reads.
   // The full wait also retires every scalar load of kernel arguments: one
   // still pending inside the loop (SMEM completes out of order) would turn
-  // each LDS wait there into lgkmcnt(0).
+  // each LDS wait there into lgkmcnt(0).  The empty asm makes the epilogue's
+  // arguments load here; left alone, the compiler issues their loads after
+  // this wait and the first LDS wait of every loop pass becomes lgkmcnt(0).
+  if constexpr (REQ == 0) {
+    asm volatile("" ::"s"(bias), "s"(out));
+  } else {
+    asm volatile("" ::"s"(bias), "s"(out), "s"(qcodes), "s"(qscales), "s"(rceil), "s"(qld), "s"(sld));
+  }
   issue(st0, 0, true);
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
