@@ -14,9 +14,10 @@
 // bit patterns; MX element codes from the hardware bf16 -> FP8 / FP4 / FP6
 // conversions, whose rounding was measured equal to the definition for
 // every input (FP8 after a clamp, see mx_encode.h).  NVFP4 codes, whose
-// divisor is not a power of two, come from exact comparisons against the
-// block's seven E2M1 midpoint thresholds, taken from per-workgroup tables
-// indexed by the block's scale code.
+// divisor is not a power of two, are the number of the block's seven E2M1
+// midpoint thresholds at or below |x|: one read of a per-workgroup byte table
+// of the scale code's significand class (or, for tiny tensor scales, a
+// search over the thresholds themselves).
 #include "mx_encode.h"
 #include "mxq_internal.h"
 
@@ -287,13 +288,42 @@ __device__ __forceinline__ uint32_t e2m1_codes8(const uint4& v, const uint32_t (
   return (u0 & 0xFFu) | ((u1 & 0xFFu) << 8) | ((u2 & 0xFFu) << 16) | (u3 << 24);
 }
 
+// Class tables.  dec(c) = 2^E d with d in [1, 2) one of eight significands
+// (1 + k / 8), so for ts >= 2^-60 (every threshold a normal float32 and bf16)
+// the seven thresholds of code c are those of the representative code
+// 0x38 | k (dec = d) shifted by E in the bf16 exponent field: T_j(c) =
+// T_j(0x38 | k) + 128 E, since rounding, the FMA residual and the round-up to
+// bf16 all commute with scaling by 2^E there.  So the E2M1 magnitude of a bf16
+// |x| under code c is tab_k[min(sat(|x| - (T_0(c) - 1)), kNvTab - 1)] with
+// tab_k[i] = #{j : T_j(0x38 | k) - T_0(0x38 | k) < i}: one byte-table read per
+// element in place of the threshold search.
+constexpr int kNvTab = 640;  // bytes per class table (T_6 - T_0 <= 4.33 binades = 555 bf16 steps)
+
+typedef unsigned short nv_us2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_elementwise_max(__builtin_bit_cast(nv_us2, a), __builtin_bit_cast(nv_us2, b)));
+}
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_elementwise_min(__builtin_bit_cast(nv_us2, a), __builtin_bit_cast(nv_us2, b)));
+}
+// max(a - b, 0) in each 16-bit half
+__device__ __forceinline__ uint32_t pk_sub_sat_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(__builtin_bit_cast(nv_us2, a),
+                                                                    __builtin_bit_cast(nv_us2, b)));
+}
+
 // Phase 2: one lane per 16-element block (two chunks).  Every workgroup first
-// takes the global maximum from the partials and builds two tables in LDS
+// takes the global maximum from the partials and builds its tables in LDS
 // from the tensor scale ts:
-//   thr[c]  the seven packed element thresholds of scale code c (c = 0 and
-//           0x7F: above every magnitude);
 //   up[c]   the smallest bf16 magnitude pattern B whose block scale B / (6 ts)
-//           rounds (nearest even E4M3, saturating at 448) to a code above c.
+//           rounds (nearest even E4M3, saturating at 448) to a code above c;
+//   for ts >= 2^-60: the eight class tables, and per code c the offset
+//           T_0(c) - 1 and its class;
+//   otherwise (and should a class-table check fail): thr[c], the seven
+//           packed element thresholds of code c (c = 0 and 0x7F: above every
+//           magnitude), searched per element.
 // A block's scale code is then the hardware E4M3 rounding of the float32
 // estimate bm * fl(1 / (6 ts)), whose relative error (a few units of 2^-24)
 // moves it by at most one code, corrected exactly against up[c0 - 1] and
@@ -306,7 +336,11 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
   __shared__ uint32_t red[4];
   __shared__ uint4 thr[128][2];
   __shared__ uint16_t up[128];
-  __shared__ uint32_t fix[128];  // up[c - 1] (0 for c = 0) | up[c] << 16
+  __shared__ uint32_t fix[128];    // up[c - 1] (0 for c = 0) | up[c] << 16
+  __shared__ uint32_t cinfo[128];  // T_0(c) - 1 | class table offset << 16
+  __shared__ uint16_t rep[8][8];   // T_0 .. T_6 of the representative codes 0x38 | k
+  __shared__ __attribute__((aligned(16))) uint8_t ctab[8 * kNvTab];
+  __shared__ uint32_t tab_bad;
   uint32_t g = 0;
   for (int j = threadIdx.x; j < npartials; j += 256) g = max(g, partials[j]);
   g = wave_max(g);
@@ -330,38 +364,69 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = ts;
   const double ts64 = (double)ts;
   const bool fast = !nonfinite && ts >= 0x1p-60f;  // uniform
+  const int t = threadIdx.x;
 
-  {
-    const int t = threadIdx.x;
-    if (t < 128) {
-      uint32_t u = 0x8000u;
-      if (t < 0x7E && !nonfinite) {
-        // midpoint of codes t and t + 1 (<= 5 significant bits) times 6 ts: exact in double
-        const double mid = 0.5 * (e4m3_decode_pos((uint32_t)t) + e4m3_decode_pos((uint32_t)t + 1u));
-        const uint32_t V = midpoint_threshold(mid * 6.0 * ts64, ((t + 1) & 1) == 0);
-        u = thr16x2(V) & 0xFFFFu;
-      }
-      up[t] = (uint16_t)u;
+  if (t < 128) {
+    uint32_t u = 0x8000u;
+    if (t < 0x7E && !nonfinite) {
+      // midpoint of codes t and t + 1 (<= 5 significant bits) times 6 ts: exact in double
+      const double mid = 0.5 * (e4m3_decode_pos((uint32_t)t) + e4m3_decode_pos((uint32_t)t + 1u));
+      const uint32_t V = midpoint_threshold(mid * 6.0 * ts64, ((t + 1) & 1) == 0);
+      u = thr16x2(V) & 0xFFFFu;
     }
-    const int c = t >> 1;  // thread pair 2c, 2c + 1 fills thr[c]
+    up[t] = (uint16_t)u;
+  }
+  if (t == 0) tab_bad = fast ? 0u : 1u;
+  if (fast && t < 8) {
     uint32_t V[7];
-    if (c == 0 || c == 0x7F || nonfinite) {
+    nv_thresholds(0x38u | (uint32_t)t, ts, ts64, true, V);
 #pragma unroll
-      for (int j = 0; j < 7; ++j) V[j] = 0xFFFFFFFFu;
-    } else {
-      nv_thresholds((uint32_t)c, ts, ts64, fast, V);
-    }
-    if ((t & 1) == 0) thr[c][0] = make_uint4(thr16x2(V[0]), thr16x2(V[1]), thr16x2(V[2]), thr16x2(V[3]));
-    else thr[c][1] = make_uint4(thr16x2(V[4]), thr16x2(V[5]), thr16x2(V[6]), 0x80008000u);
+    for (int j = 0; j < 7; ++j) rep[t][j] = (uint16_t)(thr16x2(V[j]) & 0xFFFFu);
   }
   __syncthreads();
-  if (threadIdx.x < 128) fix[threadIdx.x] = (threadIdx.x ? (uint32_t)up[threadIdx.x - 1] : 0u) | ((uint32_t)up[threadIdx.x] << 16);
+  if (t < 128) fix[t] = (t ? (uint32_t)up[t - 1] : 0u) | ((uint32_t)up[t] << 16);
+  if (fast) {
+    if (t < 128) {
+      uint32_t ci = 0x7FFFu;  // codes 0 and 0x7F: every magnitude maps to entry 0, code 0
+      if (t != 0 && t != 0x7F) {
+        const float d = (float)e4m3_decode_pos((uint32_t)t);  // exact
+        const uint32_t k = (__float_as_uint(d) >> 20) & 7u;
+        const uint32_t t0 = thr16x2(midpoint_threshold_f32(0.25f * d, ts, false)) & 0xFFFFu;
+        const uint32_t t6 = thr16x2(midpoint_threshold_f32(5.0f * d, ts, false)) & 0xFFFFu;
+        if (t6 - t0 != (uint32_t)rep[k][6] - (uint32_t)rep[k][0]) tab_bad = 1u;
+        ci = (t0 - 1u) | ((k * (uint32_t)kNvTab) << 16);
+      }
+      cinfo[t] = ci;
+    }
+    if (t < 8) {
+      // at most one step in any 20 consecutive entries, and the last entry is 7
+#pragma unroll
+      for (int j = 0; j < 6; ++j)
+        if ((int)rep[t][j + 1] - (int)rep[t][j] < kNvTab / 32 + 1) tab_bad = 1u;
+      if ((int)rep[t][6] - (int)rep[t][0] > kNvTab - 2) tab_bad = 1u;
+    }
+    // thread t fills entries s .. s + 19 of class k's table
+    const int k = t >> 5, s = (t & 31) * (kNvTab / 32);
+    const int r0 = rep[k][0];
+    uint32_t v0 = 0;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) v0 += ((int)rep[k][j] - r0 < s) ? 1u : 0u;
+    const int nxt = v0 < 7 ? (int)rep[k][v0] - r0 + 1 : (1 << 20);  // first entry above the next threshold
+    uint32_t* dst = reinterpret_cast<uint32_t*>(ctab + k * kNvTab + s);
+#pragma unroll
+    for (int dd = 0; dd < kNvTab / 128; ++dd) {
+      const int q = nxt - (s + 4 * dd);
+      const uint32_t step = q <= 0 ? 0x01010101u : q >= 4 ? 0u : (0x01010101u << (8 * q));
+      dst[dd] = v0 * 0x01010101u + step;
+    }
+  }
   __syncthreads();
+  const bool table = __builtin_amdgcn_readfirstlane(tab_bad) == 0u;  // uniform: implies fast
 
   const float inv6ts = 1.0f / (6.0f * ts);
-  const uint32_t signmask = nonfinite ? 0u : 0x00080008u;
-  for_blocks_prefetched<2>(x, nchunks / 2, [&](int64_t b, const uint4 (&v)[2]) {
-    const uint32_t bm = max(chunk_absmax_bits(v[0]), chunk_absmax_bits(v[1]));
+  // the block's scale code from its largest magnitude bm (fast: estimate and
+  // exact correction; otherwise the binary search over up[])
+  auto scale_code = [&](uint32_t bm) {
     uint32_t c = 0;
     if (nonfinite) {
       c = 0x7Fu;
@@ -380,6 +445,58 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
       }
       c = max(c, 1u);
     }
+    return c;
+  };
+
+  if (table) {
+    constexpr uint32_t kCap2 = (uint32_t)(kNvTab - 1) * 0x10001u;
+    for_blocks_prefetched<2>(x, nchunks / 2, [&](int64_t b, const uint4 (&v)[2]) {
+      const uint32_t w[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
+      uint32_t a[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] = w[i] & 0x7FFF7FFFu;
+      const uint32_t m = pk_max_u16(pk_max_u16(pk_max_u16(a[0], a[1]), pk_max_u16(a[2], a[3])),
+                                    pk_max_u16(pk_max_u16(a[4], a[5]), pk_max_u16(a[6], a[7])));
+      const uint32_t c = scale_code(max(m & 0xFFFFu, m >> 16));
+      const uint32_t ci = cinfo[c];
+      const uint32_t base2 = (ci & 0xFFFFu) * 0x10001u;
+      const uint8_t* tb = ctab + (ci >> 16);
+      uint32_t out[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t u[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t d = pk_min_u16(pk_sub_sat_u16(a[4 * h + p], base2), kCap2);
+          // codes in bits 0..3 and 16..19 with their signs, then byte 0 holds both
+          uint32_t e = (uint32_t)tb[d & 0xFFFFu] | ((uint32_t)tb[d >> 16] << 16) | ((w[4 * h + p] >> 12) & 0x00080008u);
+          u[p] = e | (e >> 12);
+        }
+        out[h] = (u[0] & 0xFFu) | ((u[1] & 0xFFu) << 8) | ((u[2] & 0xFFu) << 16) | (u[3] << 24);
+      }
+      reinterpret_cast<uint2*>(codes)[b] = make_uint2(out[0], out[1]);
+      scales[b] = (uint8_t)c;
+    });
+    return;
+  }
+
+  {
+    const int c = t >> 1;  // thread pair 2c, 2c + 1 fills thr[c]
+    uint32_t V[7];
+    if (c == 0 || c == 0x7F || nonfinite) {
+#pragma unroll
+      for (int j = 0; j < 7; ++j) V[j] = 0xFFFFFFFFu;
+    } else {
+      nv_thresholds((uint32_t)c, ts, ts64, fast, V);
+    }
+    if ((t & 1) == 0) thr[c][0] = make_uint4(thr16x2(V[0]), thr16x2(V[1]), thr16x2(V[2]), thr16x2(V[3]));
+    else thr[c][1] = make_uint4(thr16x2(V[4]), thr16x2(V[5]), thr16x2(V[6]), 0x80008000u);
+  }
+  __syncthreads();
+
+  const uint32_t signmask = nonfinite ? 0u : 0x00080008u;
+  for_blocks_prefetched<2>(x, nchunks / 2, [&](int64_t b, const uint4 (&v)[2]) {
+    const uint32_t c = scale_code(max(chunk_absmax_bits(v[0]), chunk_absmax_bits(v[1])));
     const uint4 T0 = thr[c][0], T1 = thr[c][1];
     const uint32_t T[7] = {T0.x, T0.y, T0.z, T0.w, T1.x, T1.y, T1.z};
     reinterpret_cast<uint2*>(codes)[b] = make_uint2(e2m1_codes8(v[0], T, signmask), e2m1_codes8(v[1], T, signmask));

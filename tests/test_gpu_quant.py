@@ -169,6 +169,40 @@ def test_nvfp4_block_and_element_sweep(dev):
         _assert_same("nvfp4", sweep, dev)
 
 
+def _every_code_window(g_bits, step=8, window_binades=5):
+    """Block maxima every `step` bf16 patterns from the tensor maximum G down through every E4M3 scale
+    code (18.5 binades, to below the smallest subnormal code), each block holding its maximum and then
+    15 of the magnitude patterns in the `window_binades` below it (all of them over a maximum's blocks),
+    with alternating signs."""
+    blocks = []
+    for bm in range(g_bits, max(g_bits - int(18.5 * 128), 1), -step):
+        pats = np.arange(max(bm - window_binades * 128, 1), bm, dtype=np.uint32)
+        pats = pats | ((np.arange(pats.size, dtype=np.uint32) & 1) << 15)
+        pad = (-pats.size) % 15
+        pats = np.concatenate([pats, np.zeros(pad, np.uint32)]).reshape(-1, 15)
+        blk = np.empty((pats.shape[0], 16), np.uint32)
+        blk[:, 0] = bm
+        blk[:, 1:] = pats
+        blocks.append(blk)
+    flat = np.concatenate(blocks).reshape(-1).astype(np.uint16)
+    flat = np.concatenate([flat, np.zeros((-flat.size) % 1024, np.uint16)])
+    return flat.reshape(-1, 1024)
+
+
+@pytest.mark.parametrize("g_bits", [0x4528, 0x3F80, 0x2A31])
+def test_nvfp4_every_scale_code_window(g_bits, dev):
+    """Block maxima spanning every E4M3 scale code, subnormal codes included, each with every bf16
+    magnitude in the five binades below it (both signs): every code's seven element thresholds are
+    crossed, whichever table or search the kernel takes them from.  Tensor scales 1, 2^-11.4 and
+    2^-53.9 (all above 2^-60)."""
+    bits = _every_code_window(g_bits)
+    log_case("nvfp4 every code", hex(g_bits), bits.shape)
+    _assert_same("nvfp4", bits, dev)
+    # every scale code 1 .. 0x7E occurs
+    _, sc, _ = _oracle_quant("nvfp4", bits)
+    assert set(range(1, 0x7F)) <= set(np.unique(sc).tolist())
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_deterministic(fmt, dev):
     a, _ = make_layer_inputs(WORKLOADS["mxfp8_1024"].layers[0], seed=3, M=300, K=512, N=8)
