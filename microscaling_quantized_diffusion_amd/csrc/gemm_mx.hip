@@ -21,10 +21,18 @@ namespace {
 //   of stage k (all issued by then), so after the barrier the slot of stage k
 //   takes the DMA of stage k+2, and the reads of stage k+1's first groups are
 //   in flight while stage k's last 2D MFMAs run.
-// * DMA spread.  The next-but-one stage's DMA is issued a few instructions at
-//   a time between the 2D MFMAs that follow the barrier, not as one burst:
-//   a burst from every wave at once fills the texture unit's command queue
-//   and stalls the issuing waves (SQ_VMEM_TA_CMD_FIFO_FULL).
+// * DMA spread.  A stage's DMA is issued a few instructions at a time between
+//   MFMAs, not as one burst: a burst from every wave at once fills the
+//   texture unit's command queue and stalls the issuing waves
+//   (SQ_VMEM_TA_CMD_FIFO_FULL), and with them the matrix pipe.  The slot of
+//   stage k is free from the barrier in stage k - 1 on, so stage k + 1's DMA
+//   is split: its first SPL instructions go between the 2D MFMAs after that
+//   barrier, the rest between the MFMAs of stage k's first E groups, which
+//   leaves U - D - E groups for the last of them to land before the wait
+//   that publishes the stage.  Measured on the FLUX MXFP8 shapes with
+//   bit-identical outputs: 256 x 256 tiles 2-6 % faster with E = 2 than with
+//   the whole DMA after the barrier (E = 3..6 lose it again), 256 x 320 tiles
+//   5-8 % faster with E = 6 (E = 2: 2 %); MXFP4 2-3 % faster with E = 2.
 // * Scales.  One dword per row and stage holds the stage's four E8M0 bytes
 //   (FP4: two dwords), one LDS read per tile and stage.  A lane shifts it
 //   right by 8q and the MFMA's byte select picks the block: byte 2h is block
@@ -48,7 +56,7 @@ namespace {
 // stage, half 0 then half 1), so both give identical outputs.  Requires
 // whole stages (K % 128 == 0, FP4 K % 256 == 0) and 4-byte aligned scale
 // rows; REQ / ACT / PK as in mxp_gemm_kernel.
-template <int ELEM, int REQ = 0, int ACT = ACT_NONE, int PK = 0, int WM = 4, int WN = 2, int D = 2, int BN = 256>
+template <int ELEM, int REQ = 0, int ACT = ACT_NONE, int PK = 0, int WM = 4, int WN = 2, int D = 2, int BN = 256, int E = 0>
 __global__ __launch_bounds__(64 * WM * WN, 1) void mxe_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
     const uint8_t* __restrict__ Ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N,
@@ -152,6 +160,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void mxe_gemm_kernel(
     });
   };
   constexpr int PER = CPW + SPW;  // DMA instructions per wave and stage
+  // instructions [0, SPL) of a stage's DMA go after the barrier that frees
+  // its slot, [SPL, PER) into the first E groups of the stage after it
+  constexpr int SPL = E == 0 ? PER : (PER * D + D + E - 1) / (D + E);
+  static_assert(E + D < U, "the stage's last DMA is issued before the wait that publishes it");
   auto issue = [&](auto& st, int ks, bool valid) {
     issue_range(st, ks, valid, std::integral_constant<int, 0>{}, std::integral_constant<int, PER>{});
   };
@@ -240,7 +252,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void mxe_gemm_kernel(
   issue(st0, 0, true);
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
-  issue(st1, 1, nks > 1);
+  issue_range(st1, 1, nks > 1, std::integral_constant<int, 0>{}, std::integral_constant<int, SPL>{});
   static_for<D>([&](auto gc) { read_group(st0, I0{}, gc); });
 
   // Stage ks in slot p = ks % 2.
@@ -268,17 +280,25 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void mxe_gemm_kernel(
         read_group(nxt, P1{}, std::integral_constant<int, g + D - U>{});
       }
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (g + D < U) {
+      if constexpr (g < E) {
+        // the rest of stage ks + 1's DMA into the other slot, spread over
+        // the MFMAs of this stage's first E groups
+        constexpr int NH = E * TJ, s0 = g * TJ;
+        mfma_group(p_c, gc, [&](auto jc) {
+          constexpr int sl = s0 + decltype(jc)::value;
+          issue_range(nxt, ks + 1, ks + 1 < nks, std::integral_constant<int, SPL + sl * (PER - SPL) / NH>{},
+                      std::integral_constant<int, SPL + (sl + 1) * (PER - SPL) / NH>{});
+        });
+      } else if constexpr (g + D < U) {
         mfma_group(p_c, gc, [](auto) {});
       } else {
-        // the DMA of stage ks + 2 into this slot, spread over the D * TJ
-        // MFMAs after the barrier so that no wave stalls on a full TA
-        // command queue with its MFMA pipe idle
+        // the first SPL DMA instructions of stage ks + 2 into this slot,
+        // spread over the D * TJ MFMAs after the barrier
         constexpr int NSL = D * TJ, s0 = (g + D - U) * TJ;
         mfma_group(p_c, gc, [&](auto jc) {
           constexpr int sl = s0 + decltype(jc)::value;
-          issue_range(cur, ks + 2, ks + 2 < nks, std::integral_constant<int, sl * PER / NSL>{},
-                      std::integral_constant<int, (sl + 1) * PER / NSL>{});
+          issue_range(cur, ks + 2, ks + 2 < nks, std::integral_constant<int, sl * SPL / NSL>{},
+                      std::integral_constant<int, (sl + 1) * SPL / NSL>{});
         });
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -315,29 +335,30 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void mxe_gemm_kernel(
   }
 }
 
-template <int ELEM, int REQ, int ACT, int PK, int BN, int D>
+template <int ELEM, int REQ, int ACT, int PK, int BN, int D, int E>
 hipError_t launch_mxe(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as, const uint8_t* w,
                       const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream, uint8_t* qcodes,
                       uint8_t* qscales, int rceil, int64_t qld, int64_t sld) {
   const int64_t tiles = ((M + 255) / 256) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((mxe_gemm_kernel<ELEM, REQ, ACT, PK, 4, 2, D, BN>), dim3((unsigned)tiles), dim3(512), 0, stream,
+  hipLaunchKernelGGL((mxe_gemm_kernel<ELEM, REQ, ACT, PK, 4, 2, D, BN, E>), dim3((unsigned)tiles), dim3(512), 0, stream,
                      a, as, w, ws, bias, out, (int)M, (int)N, (int)K, qcodes, qscales, rceil, qld, sld);
   return hipGetLastError();
 }
 
-// 256 x 256 tiles with a two-group read lookahead; 256 x 320 tiles (160
-// accumulators per wave) with a one-group lookahead, which is what fits the
-// registers without spilling (FP8 and FP6 only: FP4 at 320 columns spills).
+// 256 x 256 tiles with a two-group read lookahead and the DMA spread over
+// two head groups; 256 x 320 tiles (160 accumulators per wave) with a
+// one-group lookahead, which is what fits the registers without spilling
+// (FP8 and FP6 only: FP4 at 320 columns spills), and six head groups.
 template <int ELEM, int PK>
 hipError_t launch_mxe_tile(bool wide, int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                            const uint8_t* w, const uint8_t* ws, const uint16_t* bias, uint16_t* out,
                            hipStream_t stream) {
   if constexpr (ELEM != 2) {
     if (wide)
-      return launch_mxe<ELEM, 0, ACT_NONE, PK, 320, 1>(M, N, K, a, as, w, ws, bias, out, stream, nullptr, nullptr, 0, 0,
+      return launch_mxe<ELEM, 0, ACT_NONE, PK, 320, 1, 6>(M, N, K, a, as, w, ws, bias, out, stream, nullptr, nullptr, 0, 0,
                                                        0);
   }
-  return launch_mxe<ELEM, 0, ACT_NONE, PK, 256, 2>(M, N, K, a, as, w, ws, bias, out, stream, nullptr, nullptr, 0, 0,
+  return launch_mxe<ELEM, 0, ACT_NONE, PK, 256, 2, 2>(M, N, K, a, as, w, ws, bias, out, stream, nullptr, nullptr, 0, 0,
                                                    0);
 }
 
