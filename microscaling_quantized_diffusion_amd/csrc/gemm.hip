@@ -966,10 +966,14 @@ hipError_t launch_mx_gemm(int elem, int packed, int64_t M, int64_t N, int64_t K,
   // Tile width 256 or 320 columns (wave tiles 64 x 128 / 64 x 160): with one
   // workgroup per CU, the time is about (rounds of tiles) x (tile width), so
   // take the width with the smaller product; ties keep 256.
-  const bool wide = mx_prefer_wide_tile(M, N, device_cu_count());
-  // the early-published kernel (gemm_mx.hip) where it supports the tile
-  if (scales_aligned && whole_stages && mx_staged_supports(elem, wide))
-    return launch_mx_staged(elem, packed, wide, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+  // The early-published kernel (gemm_mx.hip) also takes 384 x 192 tiles
+  // where their rounds fit the CUs better (mx_prefer_tall_tile).
+  const int64_t cus = device_cu_count();
+  const bool wide = mx_prefer_wide_tile(M, N, cus);
+  const MxTile tile = mx_prefer_tall_tile(M, N, cus) ? MX_TILE_384x192 : wide ? MX_TILE_256x320 : MX_TILE_256x256;
+  // the early-published kernel where it supports the tile
+  if (scales_aligned && whole_stages && mx_staged_supports(elem, tile))
+    return launch_mx_staged(elem, packed, tile, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
   if (packed) {
     if (!scales_aligned || !whole_stages) return hipErrorInvalidValue;  // callers check the shape first
     return launch_mx_main_elem<1>(elem, wide, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);

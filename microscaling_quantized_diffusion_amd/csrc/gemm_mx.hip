@@ -6,9 +6,9 @@ namespace mxq {
 namespace {
 
 // ------------------------------------------------------------------------
-// MX main path, early-published stages.  One 256 x 256 output tile per
-// workgroup, eight waves as 4 x 2 (64 x 128 outputs each, 128 fp32
-// accumulators), scaled 32x32x64 MFMA, a two-stage LDS ring of 128-byte K
+// MX main path, early-published stages.  One BM x BN output tile per
+// workgroup (256 x 256, 256 x 320 or 384 x 192), eight waves as 4 x 2 (e.g.
+// 64 x 128 outputs each, 128 fp32 accumulators), scaled 32x32x64 MFMA, a two-stage LDS ring of 128-byte K
 // slabs per row for both operands (128 FP8 / FP6-slot or 256 FP4 elements),
 // filled by LDS DMA with the stage's scale dwords; 16-byte chunks
 // XOR-swizzled by row (the LDS image of mxp_gemm_kernel).
@@ -56,12 +56,12 @@ namespace {
 // stage, half 0 then half 1), so both give identical outputs.  Requires
 // whole stages (K % 128 == 0, FP4 K % 256 == 0) and 4-byte aligned scale
 // rows; REQ / ACT / PK as in mxp_gemm_kernel.
-template <int ELEM, int REQ = 0, int ACT = ACT_NONE, int PK = 0, int WM = 4, int WN = 2, int D = 2, int BN = 256, int E = 0>
+template <int ELEM, int REQ = 0, int ACT = ACT_NONE, int PK = 0, int WM = 4, int WN = 2, int D = 2, int BN = 256, int E = 0, int BM = 256>
 __global__ __launch_bounds__(64 * WM * WN, 1) void mxe_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
     const uint8_t* __restrict__ Ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N,
     int K, uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales, int rceil, int64_t qld, int64_t sld) {
-  constexpr int BM = 256, NW = WM * WN;
+  constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TJ = WTM / 32, TI = WTN / 32;  // activation / weight tiles of 32 rows per wave
   constexpr int ROWS = BM + BN;
@@ -73,7 +73,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void mxe_gemm_kernel(
   constexpr int STAGE = CODE_BYTES + SGROUPS * 256;
   constexpr int CPW = CODE_BYTES / 1024 / NW, SPW = SGROUPS / NW;
   constexpr int U = H * TI;                     // MFMA groups per stage
-  constexpr int NSLOT = D + 1 <= 2 ? 2 : D + 1 <= 4 ? 4 : 8;  // weight register slots (groups in flight)
+  // weight register slots (groups in flight): the smallest divisor of U above
+  // D, so that group g of every stage uses slot g % NSLOT
+  constexpr int NSLOT = U % (D + 1) == 0 ? D + 1 : U % (D + 2) == 0 ? D + 2 : U % (D + 3) == 0 ? D + 3 : U;
   static_assert(U % NSLOT == 0 && D < NSLOT && D <= U / 2, "slot rotation");
   static_assert(BM % RPG == 0 && (BM * SDW) % 64 == 0, "a DMA group never straddles the A/W boundary");
   constexpr int FMT = ELEM == 1 ? 0 : ELEM == 2 ? 4 : ELEM == 3 ? 2 : 3;  // E4M3, E2M1, E2M3, E3M2
@@ -335,12 +337,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void mxe_gemm_kernel(
   }
 }
 
-template <int ELEM, int REQ, int ACT, int PK, int BN, int D, int E>
+template <int ELEM, int REQ, int ACT, int PK, int BN, int D, int E, int BM = 256>
 hipError_t launch_mxe(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as, const uint8_t* w,
                       const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream, uint8_t* qcodes,
                       uint8_t* qscales, int rceil, int64_t qld, int64_t sld) {
-  const int64_t tiles = ((M + 255) / 256) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((mxe_gemm_kernel<ELEM, REQ, ACT, PK, 4, 2, D, BN, E>), dim3((unsigned)tiles), dim3(512), 0, stream,
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL((mxe_gemm_kernel<ELEM, REQ, ACT, PK, 4, 2, D, BN, E, BM>), dim3((unsigned)tiles), dim3(512), 0, stream,
                      a, as, w, ws, bias, out, (int)M, (int)N, (int)K, qcodes, qscales, rceil, qld, sld);
   return hipGetLastError();
 }
@@ -348,42 +350,48 @@ hipError_t launch_mxe(int64_t M, int64_t N, int64_t K, const uint8_t* a, const u
 // 256 x 256 tiles with a two-group read lookahead and the DMA spread over
 // two head groups; 256 x 320 tiles (160 accumulators per wave) with a
 // one-group lookahead, which is what fits the registers without spilling
-// (FP8 and FP6 only: FP4 at 320 columns spills), and six head groups.
+// (FP8 and FP6 only: FP4 at 320 columns spills), and six head groups;
+// 384 x 192 tiles (144 accumulators, three MFMA tiles each way per wave) with
+// a one-group lookahead and three head groups (E = 3 measured 1-2 % faster
+// than E = 2 or 4 on the FLUX shapes).
 template <int ELEM, int PK>
-hipError_t launch_mxe_tile(bool wide, int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
+hipError_t launch_mxe_tile(MxTile tile, int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                            const uint8_t* w, const uint8_t* ws, const uint16_t* bias, uint16_t* out,
                            hipStream_t stream) {
+  if (tile == MX_TILE_384x192)
+    return launch_mxe<ELEM, 0, ACT_NONE, PK, 192, 1, 3, 384>(M, N, K, a, as, w, ws, bias, out, stream, nullptr, nullptr,
+                                                             0, 0, 0);
   if constexpr (ELEM != 2) {
-    if (wide)
+    if (tile == MX_TILE_256x320)
       return launch_mxe<ELEM, 0, ACT_NONE, PK, 320, 1, 6>(M, N, K, a, as, w, ws, bias, out, stream, nullptr, nullptr, 0, 0,
-                                                       0);
+                                                          0);
   }
   return launch_mxe<ELEM, 0, ACT_NONE, PK, 256, 2, 2>(M, N, K, a, as, w, ws, bias, out, stream, nullptr, nullptr, 0, 0,
-                                                   0);
+                                                      0);
 }
 
 template <int PK>
-hipError_t launch_mxe_elem(int elem, bool wide, int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
-                           const uint8_t* w, const uint8_t* ws, const uint16_t* bias, uint16_t* out,
-                           hipStream_t stream) {
+hipError_t launch_mxe_elem(int elem, MxTile tile, int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                           const uint8_t* as, const uint8_t* w, const uint8_t* ws, const uint16_t* bias,
+                           uint16_t* out, hipStream_t stream) {
   switch (elem) {
-    case 1: return launch_mxe_tile<1, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
-    case 2: return launch_mxe_tile<2, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
-    case 3: return launch_mxe_tile<3, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
-    case 4: return launch_mxe_tile<4, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
+    case 1: return launch_mxe_tile<1, PK>(tile, M, N, K, a, as, w, ws, bias, out, stream);
+    case 2: return launch_mxe_tile<2, PK>(tile, M, N, K, a, as, w, ws, bias, out, stream);
+    case 3: return launch_mxe_tile<3, PK>(tile, M, N, K, a, as, w, ws, bias, out, stream);
+    case 4: return launch_mxe_tile<4, PK>(tile, M, N, K, a, as, w, ws, bias, out, stream);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-bool mx_staged_supports(int elem, bool wide) { return !(wide && elem == 2); }
+bool mx_staged_supports(int elem, MxTile tile) { return !(tile == MX_TILE_256x320 && elem == 2); }
 
-hipError_t launch_mx_staged(int elem, int packed, bool wide, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
-                            const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
-                            const uint16_t* bias, uint16_t* out, hipStream_t stream) {
-  return packed ? launch_mxe_elem<1>(elem, wide, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream)
-                : launch_mxe_elem<0>(elem, wide, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+hipError_t launch_mx_staged(int elem, int packed, MxTile tile, int64_t M, int64_t N, int64_t K,
+                            const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
+                            const uint8_t* w_scales, const uint16_t* bias, uint16_t* out, hipStream_t stream) {
+  return packed ? launch_mxe_elem<1>(elem, tile, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream)
+                : launch_mxe_elem<0>(elem, tile, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
 }
 
 }  // namespace mxq

@@ -241,5 +241,19 @@ inline bool mx_prefer_wide_tile(int64_t M, int64_t N, int64_t cus) {
   return r320 * 320 < r256 * 256;
 }
 
+// 384 x 192 tiles (the MX main path only) when ceil(tiles / CUs) * tile area,
+// taken 5 % larger, is below that of the 256-row tile the rule above picks:
+// 4608 x 12288 is 768 tiles of 384 x 192, three full rounds on 256 CUs,
+// against 702 tiles of 256 x 320 whose third round leaves 66 CUs idle.  The
+// 5 % is what a 384 x 192 tile measured slower per output than a 256 x 320
+// one at equal rounds (nine MFMA tiles per wave instead of ten per barrier).
+inline bool mx_prefer_tall_tile(int64_t M, int64_t N, int64_t cus) {
+  const int64_t tm = (M + 255) / 256;
+  const int64_t c256 = (tm * ((N + 255) / 256) + cus - 1) / cus * (256 * 256);
+  const int64_t c320 = (tm * ((N + 319) / 320) + cus - 1) / cus * (256 * 320);
+  const int64_t c384 = (((M + 383) / 384) * ((N + 191) / 192) + cus - 1) / cus * (384 * 192);
+  return c384 * 21 < (c320 < c256 ? c320 : c256) * 20;
+}
+
 }  // namespace
 }  // namespace mxq

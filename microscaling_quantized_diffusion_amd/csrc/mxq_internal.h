@@ -35,14 +35,15 @@ hipError_t launch_mx_gemm(int elem, int packed, int64_t M, int64_t N, int64_t K,
                           const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
                           const uint16_t* bias, uint16_t* out, hipStream_t stream);
 
+// Output tile of the early-published MX main-path GEMM.
+enum MxTile { MX_TILE_256x256 = 0, MX_TILE_256x320 = 1, MX_TILE_384x192 = 2 };
 // The early-published MX main-path GEMM (gemm_mx.hip): whole stages
-// (K % 128 == 0, FP4 K % 256 == 0) and 4-byte aligned scale rows; wide:
-// 256 x 320 tiles instead of 256 x 256, for the formats where
-// mx_staged_supports(elem, true) holds.
-bool mx_staged_supports(int elem, bool wide);
-hipError_t launch_mx_staged(int elem, int packed, bool wide, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
-                            const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
-                            const uint16_t* bias, uint16_t* out, hipStream_t stream);
+// (K % 128 == 0, FP4 K % 256 == 0) and 4-byte aligned scale rows, for the
+// formats and tiles where mx_staged_supports(elem, tile) holds.
+bool mx_staged_supports(int elem, MxTile tile);
+hipError_t launch_mx_staged(int elem, int packed, MxTile tile, int64_t M, int64_t N, int64_t K,
+                            const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
+                            const uint8_t* w_scales, const uint16_t* bias, uint16_t* out, hipStream_t stream);
 
 // MX GEMM whose epilogue emits the output MX-quantized (out_elem: 1 = E4M3,
 // 2 = E2M1; E8M0 scales per 32 output columns, shared-exponent rule as in

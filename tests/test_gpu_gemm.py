@@ -137,6 +137,31 @@ def test_gemm_wide_tiles_ragged(fmt, dev):
     _gate(bf16_out_to_f64(out), _oracle_ref(fmt, oqa, oqw))
 
 
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_gemm_tall_tiles_ragged(fmt, dev):
+    """A shape that fits one round of 384 x 192 tiles but needs two at 256 rows
+    (so the 384 x 192 tile is taken on a 256-CU device), with 4 rows and 52
+    columns of the last tiles empty, compared in full; the packed scale layout
+    gives the same output bit for bit."""
+    import torch
+
+    from microscaling_quantized_diffusion_amd import mxq
+
+    M, N, K = 380, 49100, 256
+    log_case("gemm tall", fmt, M, N, K)
+    rng = np.random.default_rng(11)
+    a_bits = bf16_bits_from_f32((rng.standard_normal((M, K)) * np.exp(rng.normal(0, 0.5, (M, 1)))).astype(np.float32))
+    w_bits = bf16_bits_from_f32((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    a, w = to_dev(a_bits, dev), to_dev(w_bits, dev)
+    qa, qw = mxq.quantize(fmt, a), mxq.quantize(fmt, w)
+    out = mxq.gemm(qa, qw)
+    out_p = mxq.gemm(mxq.quantize(fmt, a, packed_scales=True), mxq.quantize(fmt, w, packed_scales=True))
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_p.view(torch.int16))
+    oqa, oqw = _oracle_q(fmt, a_bits), _oracle_q(fmt, w_bits)
+    _gate(bf16_out_to_f64(out), _oracle_ref(fmt, oqa, oqw))
+
+
 def test_identity_weights(dev):
     """W = I reproduces bf16(dequant(A)) exactly (one nonzero product per output)."""
     import torch
