@@ -95,7 +95,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void mxe_gemm_kernel(
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const uint32_t id = xcd_contiguous_id(blockIdx.x, gridDim.x);
-  constexpr int GROUP = 8;
+  // tiles grouped by GROUP M-tiles: 32 tiles in flight per XCD then span
+  // 8 x 4 tiles (256-row tiles) or 4 x 8 (384 x 192: 3072 distinct rows per
+  // round instead of 3840; measured 4 % faster with cold weights than 8)
+  constexpr int GROUP = BM == 384 ? 4 : 8;
   const int group = (int)(id / (uint32_t)(GROUP * tiles_n));
   const int first_m = group * GROUP;
   const int gsz = min(tiles_m - first_m, GROUP);
