@@ -51,7 +51,7 @@ PEAK_TFLOPS = {"mxfp8": 5000.0, "mxfp4": 10100.0, "mxfp6_e2m3": 10100.0, "mxfp6_
                "bf16": 2500.0}
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "microscaling_quantized_diffusion_amd", "csrc")
-GEMM_SRCS = [os.path.join(CSRC, f) for f in ("gemm.hip", "gemm_mx.hip", "gemm_tile.h")]
+GEMM_SRCS = [os.path.join(CSRC, f) for f in ("gemm.hip", "gemm_mx.hip", "gemm_mx_kernel.h", "gemm_mx_requant.hip", "gemm_tile.h")]
 # counter summary of the headline GEMM kernel (HBM traffic, clock and MFMA busy from rocprofv3 --pmc runs)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "mxe_gemm_mxfp8_flux_mlp_up_counters.txt")
 

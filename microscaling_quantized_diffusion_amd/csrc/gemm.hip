@@ -4,14 +4,16 @@
 // aitrends.kr MXFP8/NVFP4 article ("Section details": quantized weights times
 // dynamically quantized activations; second "Evidence" block: small layers
 // stay in bf16).  Kernels:
-//   mxe_gemm_kernel   (gemm_mx.hip) the MX main path: whole-stage MXFP8 /
-//                     MXFP6 / MXFP4 GEMMs on 256x256 or 256x320 tiles, scaled
-//                     32x32x64 MFMA (hardware E8M0 block scales), two-stage
-//                     LDS-DMA ring of 128-byte K slabs, stages published early.
+//   mxe_gemm_kernel   (gemm_mx_kernel.h) the MX main path: whole-stage
+//                     MXFP8 / MXFP6 / MXFP4 GEMMs on 256x256, 256x320 or
+//                     384x192 tiles, scaled 32x32x64 MFMA (hardware E8M0 block
+//                     scales), two-stage LDS-DMA ring of 128-byte K slabs,
+//                     stages published early; with a bf16 epilogue
+//                     (gemm_mx.hip) or one that quantizes its output for the
+//                     next layer (gemm_mx_requant.hip).
 //   mxp_gemm_kernel   the same tiles and ring with the stage published at its
 //                     start: MXFP4 on 256x320 tiles (the early-published
-//                     kernel's registers do not fit them) and the GEMM whose
-//                     epilogue quantizes its output for the next layer.
+//                     kernel's registers do not fit them).
 //   nv4_gemm_kernel   NVFP4 main path: the same tile and ring; codes widened
 //                     to f16 with the E4M3 block scale applied (exact), f16
 //                     32x32x16 MFMA, tensor scales in the epilogue.
@@ -993,26 +995,6 @@ bool mx_requant_supported(int elem, int64_t N, int64_t K, const uint8_t* a_scale
   return scales_aligned && N % 32 == 0 && (elem == 2 ? K % 256 == 0 : K % 128 == 0);
 }
 
-template <int ELEM, int OELEM>
-hipError_t launch_requant_act(int act, int rceil, int64_t M, int64_t N, int64_t K, const uint8_t* a,
-                              const uint8_t* as, const uint8_t* w, const uint8_t* ws, const uint16_t* bias,
-                              uint16_t* out, uint8_t* qcodes, uint8_t* qscales, int64_t qld, int64_t sld,
-                              hipStream_t stream) {
-  // tile width as for the bf16-output GEMM (256 or 320 columns)
-  const bool wide = mx_prefer_wide_tile(M, N, device_cu_count());
-  if (act == ACT_GELU_TANH)
-    return wide ? launch_mxp<ELEM, 256, 320, 4, 2, 128, 2, OELEM, ACT_GELU_TANH>(M, N, K, a, as, w, ws, bias, out,
-                                                                                 stream, qcodes, qscales, rceil, qld,
-                                                                                 sld)
-                : launch_mxp<ELEM, 256, 256, 4, 2, 128, 2, OELEM, ACT_GELU_TANH>(M, N, K, a, as, w, ws, bias, out,
-                                                                                 stream, qcodes, qscales, rceil, qld,
-                                                                                 sld);
-  return wide ? launch_mxp<ELEM, 256, 320, 4, 2, 128, 2, OELEM, ACT_NONE>(M, N, K, a, as, w, ws, bias, out, stream,
-                                                                          qcodes, qscales, rceil, qld, sld)
-              : launch_mxp<ELEM, 256, 256, 4, 2, 128, 2, OELEM, ACT_NONE>(M, N, K, a, as, w, ws, bias, out, stream,
-                                                                          qcodes, qscales, rceil, qld, sld);
-}
-
 hipError_t launch_mx_gemm_requant(int elem, int out_elem, int out_rceil, int act, int64_t M, int64_t N, int64_t K,
                                   const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
                                   const uint8_t* w_scales, const uint16_t* bias, uint16_t* out_bf16,
@@ -1020,27 +1002,15 @@ hipError_t launch_mx_gemm_requant(int elem, int out_elem, int out_rceil, int act
                                   hipStream_t stream) {
   const int64_t qld = codes_ld ? codes_ld : (out_elem == 1 ? N : N / 2);
   const int64_t sld = scales_ld ? scales_ld : N / 32;
-  if (elem == 3)
-    return out_elem == 1 ? launch_requant_act<3, 1>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales,
-                                                    bias, out_bf16, out_codes, out_scales, qld, sld, stream)
-                         : launch_requant_act<3, 2>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales,
-                                                    bias, out_bf16, out_codes, out_scales, qld, sld, stream);
-  if (elem == 4)
-    return out_elem == 1 ? launch_requant_act<4, 1>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales,
-                                                    bias, out_bf16, out_codes, out_scales, qld, sld, stream)
-                         : launch_requant_act<4, 2>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales,
-                                                    bias, out_bf16, out_codes, out_scales, qld, sld, stream);
-  if (elem == 1 && out_elem == 1)
-    return launch_requant_act<1, 1>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16,
-                                    out_codes, out_scales, qld, sld, stream);
-  if (elem == 1)
-    return launch_requant_act<1, 2>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16,
-                                    out_codes, out_scales, qld, sld, stream);
-  if (out_elem == 1)
-    return launch_requant_act<2, 1>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16,
-                                    out_codes, out_scales, qld, sld, stream);
-  return launch_requant_act<2, 2>(act, out_rceil, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out_bf16,
-                                  out_codes, out_scales, qld, sld, stream);
+  // the tiles of the bf16-output GEMM; FP4 operands take 256 x 256 where it
+  // would pick 256 x 320
+  const int64_t cus = device_cu_count();
+  MxTile tile = mx_prefer_tall_tile(M, N, cus)    ? MX_TILE_384x192
+                : mx_prefer_wide_tile(M, N, cus) ? MX_TILE_256x320
+                                                 : MX_TILE_256x256;
+  if (!mx_staged_supports(elem, tile)) tile = MX_TILE_256x256;
+  return launch_mx_staged_requant(elem, out_elem, out_rceil, act, tile, M, N, K, a_codes, a_scales, w_codes, w_scales,
+                                  bias, out_bf16, out_codes, out_scales, qld, sld, stream);
 }
 
 hipError_t launch_nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,

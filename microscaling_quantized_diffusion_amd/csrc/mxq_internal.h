@@ -44,6 +44,13 @@ bool mx_staged_supports(int elem, MxTile tile);
 hipError_t launch_mx_staged(int elem, int packed, MxTile tile, int64_t M, int64_t N, int64_t K,
                             const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
                             const uint8_t* w_scales, const uint16_t* bias, uint16_t* out, hipStream_t stream);
+// The same kernel with the requantizing epilogue (gemm_mx_requant.hip), as
+// launch_mx_gemm_requant describes it; tile 256 x 320 needs elem != 2.
+hipError_t launch_mx_staged_requant(int elem, int out_elem, int out_rceil, int act, MxTile tile, int64_t M, int64_t N,
+                                    int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                                    const uint8_t* w_codes, const uint8_t* w_scales, const uint16_t* bias,
+                                    uint16_t* out_bf16, uint8_t* out_codes, uint8_t* out_scales, int64_t qld,
+                                    int64_t sld, hipStream_t stream);
 
 // MX GEMM whose epilogue emits the output MX-quantized (out_elem: 1 = E4M3,
 // 2 = E2M1; E8M0 scales per 32 output columns, shared-exponent rule as in

@@ -166,3 +166,25 @@ def test_requant_full_size_mlp_up(dev):
     yc, ys = oracle.quantize_mx(_bits_of(ysel), oracle.MXFP8)
     assert np.array_equal(q.codes[ri].cpu().numpy(), yc)
     assert np.array_equal(q.scales[ri].cpu().numpy(), ys)
+
+
+@pytest.mark.parametrize("fmt,out_fmt,act", [("mxfp8", "mxfp8", "gelu_tanh"), ("mxfp4", "mxfp4", "none")])
+def test_requant_tall_tiles_ragged(fmt, out_fmt, act, dev):
+    """A shape that fits one round of 384 x 192 tiles but needs two at 256 rows (so the 384 x 192 tile is
+    taken on a 256-CU device), with 4 rows and 64 columns of the last tiles empty: y in full against the
+    oracle, every code and scale against the oracle's quantization of y."""
+    M, N, K = 380, 49088, 256
+    log_case("requant tall", fmt, out_fmt, act, M, N, K)
+    a_bits, w_bits, b_bits, qa, qw, bias, y, q1, q2 = _case(fmt, out_fmt, act, M, N, K, dev, 46)
+    ca, sa = oracle.quantize_mx(a_bits, _scheme(fmt))
+    cw, sw = oracle.quantize_mx(w_bits, _scheme(fmt))
+    r = oracle.gemm_mx_ref(ca, sa, cw, sw, _scheme(fmt), b_bits)
+    if act == "gelu_tanh":
+        r = oracle.gelu_tanh(r)
+    _gate(bf16_out_to_f64(y), r)
+    yc, ys = oracle.quantize_mx(_bits_of(y), _scheme(out_fmt))
+    assert np.array_equal(q1.scales.cpu().numpy(), ys)
+    assert np.array_equal(q1.codes.cpu().numpy(), yc)
+    import torch
+
+    assert torch.equal(q1.codes, q2.codes) and torch.equal(q1.scales, q2.scales)
