@@ -11,14 +11,16 @@ namespace {
 // ------------------------------------------------------------------------
 // MX main path, early-published stages.  One BM x BN output tile per
 // workgroup (256 x 256, 256 x 320 or 384 x 192), eight waves as 4 x 2 (e.g.
-// 64 x 128 outputs each, 128 fp32 accumulators), scaled 32x32x64 MFMA, a two-stage LDS ring of 128-byte K
-// slabs per row for both operands (128 FP8 / FP6-slot or 256 FP4 elements),
+// 64 x 128 outputs each, 128 fp32 accumulators), scaled 32x32x64 MFMA, a
+// two-stage LDS ring of 128-byte K slabs per row for both operands (128 FP8 /
+// FP6-slot or 256 FP4 elements),
 // filled by LDS DMA with the stage's scale dwords; 16-byte chunks
 // XOR-swizzled by row (the LDS image of mxp_gemm_kernel).
 //
-// * Schedule.  A stage is U = 8 MFMA groups (half h, weight tile i: the wave's
-//   two activation tiles of that half against weight tile i).  The LDS reads
-//   of group g + D (D = 2) are issued before the MFMAs of group g.  The
+// * Schedule.  A stage is U = 2 TI MFMA groups (half h, weight tile i: the
+//   wave's TJ activation tiles of that half against weight tile i; U = 8 on
+//   256 x 256 tiles).  The LDS reads of group g + D (D = 2 on 256 x 256, 1 on
+//   the wider tiles) are issued before the MFMAs of group g.  The
 //   barrier that publishes stage k+1 sits D groups before the end of stage k:
 //   each wave first waits for its own DMA of stage k+1 and for its own reads
 //   of stage k (all issued by then), so after the barrier the slot of stage k
@@ -35,7 +37,8 @@ namespace {
 //   that publishes the stage.  Measured on the FLUX MXFP8 shapes with
 //   bit-identical outputs: 256 x 256 tiles 2-6 % faster with E = 2 than with
 //   the whole DMA after the barrier (E = 3..6 lose it again), 256 x 320 tiles
-//   5-8 % faster with E = 6 (E = 2: 2 %); MXFP4 2-3 % faster with E = 2.
+//   5-8 % faster with E = 6 (E = 2: 2 %); MXFP4 2-3 % faster with E = 2;
+//   384 x 192 tiles best with E = 3, with cold weights as with hot.
 // * Scales.  One dword per row and stage holds the stage's four E8M0 bytes
 //   (FP4: two dwords), one LDS read per tile and stage.  A lane shifts it
 //   right by 8q and the MFMA's byte select picks the block: byte 2h is block
@@ -54,7 +57,8 @@ namespace {
 //   32 rows at 32 bytes each), and four waves of 128 x 128 with accumulators
 //   in AGPRs (10-20 % slower although it needs a third less LDS traffic: with
 //   one wave per SIMD every wait idles the matrix pipe).  Counters put the
-//   loop at ~43 % MFMA busy at the ~1.9 GHz the chip holds under this load.
+//   FLUX MLP up-projection (384 x 192 tiles) at ~55 % MFMA busy at the
+//   ~2.05 GHz the chip holds under this load.
 // The accumulation order per output is that of mxp_gemm_kernel (stage by
 // stage, half 0 then half 1), so both give identical outputs.  Requires
 // whole stages (K % 128 == 0, FP4 K % 256 == 0) and 4-byte aligned scale
