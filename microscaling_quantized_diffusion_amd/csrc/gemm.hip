@@ -373,16 +373,14 @@ hipError_t launch_tiled(int64_t M, int64_t N, int64_t K, const void* a, const ui
 //   time through the idle stage buffers (16-byte row pad) and writes whole
 //   256-byte row segments with 16-byte stores, so L2 sees full-line writes.
 // Requires whole stages (K % 128 == 0 for FP8 and FP6, K % 256 == 0 for FP4
-// at SLAB = 128) and 4-byte aligned scale rows.
-// REQ: 0 = bf16 output; 1 / 2 = the output MX-quantized to E4M3 / E2M1 codes
-// and E8M0 scales (qcodes, qscales; rceil selects the round-up shared-exponent
-// rule), with the bf16 output also written when `out` is not null.  ACT:
-// activation applied before the bf16 rounding.
-template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS, int REQ = 0, int ACT = ACT_NONE, int PK = 0>
+// at SLAB = 128) and 4-byte aligned scale rows.  The library runs it for
+// MXFP4 on 256 x 320 tiles only; every other whole-stage MX GEMM runs
+// mxe_gemm_kernel.
+template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS, int PK = 0>
 __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1) void mxp_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
     const uint8_t* __restrict__ Ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int N,
-    int K, uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales, int rceil, int64_t qld, int64_t sld) {
+    int K) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TJ = WTM / 32, TI = WTN / 32;  // 32 x 32 tiles per wave (M, N)
@@ -606,29 +604,15 @@ __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN) > 0 ? 8 / (WM * WN) : 1
   __builtin_amdgcn_s_barrier();
   const int ea = wave / WPS;
   uint8_t* region = (ea == 0 ? st0 : ea == 1 ? st1 : ea == 2 ? st2 : st3) + (wave % WPS) * EPI_BYTES;
-  if constexpr (REQ == 0) {
-    store_tile_bf16<TI, TJ, WTM, WTN, ACT>(acc, 1.0f, region, bias, out, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
-  } else {
-    store_tile_requant<TI, TJ, WTM, WTN, REQ, ACT>(acc, 1.0f, region, bias, qcodes, qscales, M, N, m0 + wm * WTM,
-                                                   n0 + wn * WTN, lane, rceil, qld, sld);
-    if (out) {
-      wait_lgkmcnt0();
-      __builtin_amdgcn_wave_barrier();
-      store_tile_bf16<TI, TJ, WTM, WTN, ACT>(acc, 1.0f, region, bias, out, M, N, m0 + wm * WTM, n0 + wn * WTN,
-                                             lane);
-    }
-  }
+  store_tile_bf16<TI, TJ, WTM, WTN>(acc, 1.0f, region, bias, out, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
-template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS, int REQ = 0, int ACT = ACT_NONE, int PK = 0>
+template <int ELEM, int BM, int BN, int WM, int WN, int SLAB, int NS, int PK = 0>
 hipError_t launch_mxp(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as, const uint8_t* w,
-                      const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream,
-                      uint8_t* qcodes = nullptr, uint8_t* qscales = nullptr, int rceil = 0, int64_t qld = 0,
-                      int64_t sld = 0) {
+                      const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((mxp_gemm_kernel<ELEM, BM, BN, WM, WN, SLAB, NS, REQ, ACT, PK>), dim3((unsigned)tiles),
-                     dim3(64 * WM * WN), 0, stream, a, as, w, ws, bias, out, (int)M, (int)N, (int)K, qcodes, qscales,
-                     rceil, qld, sld);
+  hipLaunchKernelGGL((mxp_gemm_kernel<ELEM, BM, BN, WM, WN, SLAB, NS, PK>), dim3((unsigned)tiles),
+                     dim3(64 * WM * WN), 0, stream, a, as, w, ws, bias, out, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
@@ -936,25 +920,12 @@ __global__ __launch_bounds__(256) void bf16_generic_kernel(const uint16_t* __res
 
 
 namespace {
-// The main-path GEMM at 256 x 256 or 256 x 320 tiles; PK: packed scale rows.
-template <int ELEM, int PK>
-hipError_t launch_mx_main(bool wide, int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
-                          const uint8_t* w, const uint8_t* ws, const uint16_t* bias, uint16_t* out,
-                          hipStream_t stream) {
-  return wide ? launch_mxp<ELEM, 256, 320, 4, 2, 128, 2, 0, ACT_NONE, PK>(M, N, K, a, as, w, ws, bias, out, stream)
-              : launch_mxp<ELEM, 256, 256, 4, 2, 128, 2, 0, ACT_NONE, PK>(M, N, K, a, as, w, ws, bias, out, stream);
-}
+// MXFP4 on 256 x 320 tiles, the one whole-stage MX GEMM the early-published
+// kernel does not run (its registers do not fit them); PK: packed scale rows.
 template <int PK>
-hipError_t launch_mx_main_elem(int elem, bool wide, int64_t M, int64_t N, int64_t K, const uint8_t* a,
-                               const uint8_t* as, const uint8_t* w, const uint8_t* ws, const uint16_t* bias,
-                               uint16_t* out, hipStream_t stream) {
-  switch (elem) {
-    case 1: return launch_mx_main<1, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
-    case 2: return launch_mx_main<2, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
-    case 3: return launch_mx_main<3, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
-    case 4: return launch_mx_main<4, PK>(wide, M, N, K, a, as, w, ws, bias, out, stream);
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_mx4_wide(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as, const uint8_t* w,
+                           const uint8_t* ws, const uint16_t* bias, uint16_t* out, hipStream_t stream) {
+  return launch_mxp<2, 256, 320, 4, 2, 128, 2, PK>(M, N, K, a, as, w, ws, bias, out, stream);
 }
 }  // namespace
 
@@ -973,15 +944,15 @@ hipError_t launch_mx_gemm(int elem, int packed, int64_t M, int64_t N, int64_t K,
   const int64_t cus = device_cu_count();
   const bool wide = mx_prefer_wide_tile(M, N, cus);
   const MxTile tile = mx_prefer_tall_tile(M, N, cus) ? MX_TILE_384x192 : wide ? MX_TILE_256x320 : MX_TILE_256x256;
-  // the early-published kernel where it supports the tile
-  if (scales_aligned && whole_stages && mx_staged_supports(elem, tile))
-    return launch_mx_staged(elem, packed, tile, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
-  if (packed) {
-    if (!scales_aligned || !whole_stages) return hipErrorInvalidValue;  // callers check the shape first
-    return launch_mx_main_elem<1>(elem, wide, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+  // the early-published kernel where it supports the tile, else (MXFP4 on
+  // 256 x 320 tiles) mxp_gemm_kernel
+  if (scales_aligned && whole_stages) {
+    if (mx_staged_supports(elem, tile))
+      return launch_mx_staged(elem, packed, tile, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+    return packed ? launch_mx4_wide<1>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream)
+                  : launch_mx4_wide<0>(M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
   }
-  if (scales_aligned && whole_stages)
-    return launch_mx_main_elem<0>(elem, wide, M, N, K, a_codes, a_scales, w_codes, w_scales, bias, out, stream);
+  if (packed) return hipErrorInvalidValue;  // callers check the shape first
   if (elem >= 3) return hipErrorInvalidValue;  // FP6 has no generic path: callers check the shape first
   if (elem == 1)
     return launch_tiled<MX8, MXQ_TILE_MX>(M, N, K, a_codes, a_scales, w_codes, w_scales, nullptr, nullptr, bias,

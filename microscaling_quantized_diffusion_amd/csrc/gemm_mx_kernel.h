@@ -62,7 +62,11 @@ namespace {
 // The accumulation order per output is that of mxp_gemm_kernel (stage by
 // stage, half 0 then half 1), so both give identical outputs.  Requires
 // whole stages (K % 128 == 0, FP4 K % 256 == 0) and 4-byte aligned scale
-// rows; REQ / ACT / PK as in mxp_gemm_kernel.
+// rows.  REQ: 0 = bf16 output; 1 / 2 = the output MX-quantized to E4M3 /
+// E2M1 codes and E8M0 scales (qcodes, qscales with row strides qld, sld;
+// rceil selects the round-up shared-exponent rule), with the bf16 output also
+// written when `out` is not null.  ACT: activation applied before the bf16
+// rounding.  PK: both operands' scales in the packed layout.
 template <int ELEM, int REQ = 0, int ACT = ACT_NONE, int PK = 0, int WM = 4, int WN = 2, int D = 2, int BN = 256, int E = 0, int BM = 256>
 __global__ __launch_bounds__(64 * WM * WN, 1) void mxe_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
